@@ -1,0 +1,196 @@
+// Decode attention: one new query row per sequence against its KV cache
+// ("Inside an LLM ...", Step 5: scaled dot-product scores q.k * 128^-0.5, softmax,
+// weighted sum of V; grouped-query attention where query heads 2g and 2g+1 both read
+// kv head g; a decode row sees every cached slot, so no mask).
+//
+// Split-K: the visible slots are cut into chunks of CHUNK keys; a block owns one
+// (sequence, kv head, chunk) and streams that chunk's K and V once for both query
+// heads of the group, keeping a running (max, sum, weighted V) per head. A combine
+// kernel merges the chunks' partial results with the usual max-rescaling.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+namespace {
+
+constexpr int CHUNK = 256;     // keys per block (64 per wave)
+constexpr int G = 2;           // query heads per kv head
+constexpr int PART = 2 + 128;  // (max, sum, acc[128]) per (chunk, head)
+
+__device__ __forceinline__ void ld8(const bf16* p, float* w) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[2 * i] = __uint_as_float(u[i] << 16);
+        w[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void ld8(const float* p, float* w) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// Merge running state (m2, l2, a2) into (m, l, a).
+__device__ __forceinline__ void merge(float& m, float& l, float* a, float m2, float l2, const float* a2) {
+    if (l2 == 0.f) return;
+    if (l == 0.f) {
+        m = m2; l = l2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = a2[i];
+        return;
+    }
+    const float mn = fmaxf(m, m2);
+    const float c1 = expf(m - mn), c2 = expf(m2 - mn);
+    l = l * c1 + l2 * c2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = a[i] * c1 + a2[i] * c2;
+    m = mn;
+}
+
+template <typename KT>
+__global__ __launch_bounds__(256) void k_attn_decode_part(
+    const float* __restrict__ q, const KT* __restrict__ kc, const KT* __restrict__ vc, int t_cap,
+    const int32_t* __restrict__ lens, int len_extra, int seq_base, int Hq, int Hkv, int nchunk,
+    float* __restrict__ part) {
+    __shared__ float sm[4][G][PART];
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int grp = lane >> 4, sub = lane & 15;
+    const int seq = seq_base + b;
+    const int T = min(lens[seq] + len_extra, t_cap);
+    const float scale = 0.088388346f;  // fl32(128^-0.5)
+
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float* qp = q + ((size_t)b * Hq + g * G + h) * 128 + sub * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[h][i] = qp[i];
+    }
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY; l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    }
+    const size_t head_base = ((size_t)seq * Hkv + g) * t_cap * 128;
+    const int kbeg = c * CHUNK + wid * 64;
+    const int kend = min(kbeg + 64, T);
+    for (int kk = kbeg + grp; kk < kend; kk += 4) {
+        float kv[8], vv[8];
+        ld8(kc + head_base + (size_t)kk * 128 + sub * 8, kv);
+        ld8(vc + head_base + (size_t)kk * 128 + sub * 8, vv);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d += qv[h][i] * kv[i];
+            const float s = sum16(d) * scale;
+            const float mn = fmaxf(m[h], s);
+            const float corr = expf(m[h] - mn);
+            const float p = expf(s - mn);
+            l[h] = l[h] * corr + p;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr + p * vv[i];
+            m[h] = mn;
+        }
+    }
+    // merge the four 16-lane groups of the wave (lanes sub, sub+16, sub+32, sub+48)
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float a2[8];
+            const float m2 = __shfl_xor(m[h], off, 64), l2 = __shfl_xor(l[h], off, 64);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(acc[h][i], off, 64);
+            merge(m[h], l[h], acc[h], m2, l2, a2);
+        }
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (sub == 0) { sm[wid][h][0] = m[h]; sm[wid][h][1] = l[h]; }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm[wid][h][2 + sub * 8 + i] = acc[h][i];
+        }
+    }
+    __syncthreads();
+    // merge the four waves: thread t < G*128 owns (head t / 128, dim t % 128)
+    if (threadIdx.x < G * 128) {
+        const int h = threadIdx.x >> 7, d = threadIdx.x & 127;
+        float M = -INFINITY;
+        for (int w = 0; w < 4; ++w)
+            if (sm[w][h][1] > 0.f) M = fmaxf(M, sm[w][h][0]);
+        float L = 0.f, A = 0.f;
+        for (int w = 0; w < 4; ++w) {
+            if (sm[w][h][1] > 0.f) {
+                const float cf = expf(sm[w][h][0] - M);
+                L += sm[w][h][1] * cf;
+                A += sm[w][h][2 + d] * cf;
+            }
+        }
+        float* pp = part + ((((size_t)b * Hkv + g) * nchunk + c) * G + h) * PART;
+        if (d == 0) { pp[0] = M; pp[1] = L; }
+        pp[2 + d] = A;
+    }
+}
+
+__global__ __launch_bounds__(128) void k_attn_decode_combine(
+    const float* __restrict__ part, const int32_t* __restrict__ lens, int len_extra, int seq_base,
+    int Hq, int Hkv, int nchunk, float* __restrict__ o) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int g = h / G, hh = h % G;
+    const int T = lens[seq_base + b] + len_extra;
+    const int nc = min(nchunk, (T + CHUNK - 1) / CHUNK);
+    const float* base = part + (((size_t)b * Hkv + g) * nchunk) * G * PART;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) {
+        const float* pp = base + ((size_t)c * G + hh) * PART;
+        if (pp[1] > 0.f) M = fmaxf(M, pp[0]);
+    }
+    float L = 0.f, A = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float* pp = base + ((size_t)c * G + hh) * PART;
+        if (pp[1] > 0.f) {
+            const float cf = expf(pp[0] - M);
+            L += pp[1] * cf;
+            A += pp[2 + d] * cf;
+        }
+    }
+    o[((size_t)b * Hq + h) * 128 + d] = L > 0.f ? A / L : 0.f;
+}
+
+}  // namespace
+
+size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T) {
+    const int nchunk = (max_T + CHUNK - 1) / CHUNK;
+    return (size_t)B * Hkv * nchunk * G * PART * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
+                              int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
+                              int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    if (Hq != G * Hkv) return hipErrorInvalidValue;
+    const int nchunk = (max_T + CHUNK - 1) / CHUNK;
+    dim3 grid(nchunk, Hkv, B);
+    if (kv_bf16)
+        hipLaunchKernelGGL(k_attn_decode_part<bf16>, grid, dim3(256), 0, s, q, (const bf16*)kc,
+                           (const bf16*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
+    else
+        hipLaunchKernelGGL(k_attn_decode_part<float>, grid, dim3(256), 0, s, q, (const float*)kc,
+                           (const float*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_decode_combine, dim3(Hq, B), dim3(128), 0, s, ws, lens, len_extra,
+                       seq_base, Hq, Hkv, nchunk, o);
+    return hipGetLastError();
+}
+
+}  // namespace q3

@@ -1,0 +1,206 @@
+// Prefill attention: causal grouped-query attention of M new rows of one sequence
+// ("Inside an LLM ...", Step 5: scores q.k * 128^-0.5, causal mask so a row never sees
+// a later slot, softmax, weighted sum of V; query heads 2g, 2g+1 read kv head g).
+//
+// Flash-style, on the matrix cores. A block owns 64 query rows of both query heads of
+// one kv head (four waves: head x 32-row half) and walks the key tiles (64 keys) up to
+// the causal limit of its last row, keeping a running max / sum per row (float32, base-2
+// exponentials) -- the n x n score matrix is never stored.
+//
+// Per key tile the waves compute S^T = K Q^T (A = K tile from LDS, B = the wave's Q rows
+// held in registers). In that accumulator layout a lane holds 4 consecutive keys of one
+// query row for each 16-key tile, which is exactly what the B operand of O^T = V^T P^T
+// needs once both operands agree on the order of the contraction (key) index; so the
+// probabilities go from accumulators to bf16 operands without touching LDS. V is stored
+// transposed in LDS ([dim][key]) for the A operand.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr int BQ = 64;    // query rows per block (per head)
+constexpr int BKV = 64;   // keys per tile
+
+// K tile: 64 rows (keys) x 16 chunks of 16 B; chunk c of row r at c ^ (r & 15).
+__device__ __forceinline__ int kidx(int key, int ck) { return key * 16 + (ck ^ (key & 15)); }
+// V^T tile: 128 rows (dims) x 8 chunks of 16 B (64 keys); chunk c of row d at c ^ (d & 7).
+__device__ __forceinline__ int vt_off(int d, int key) {  // offset in bf16 elements
+    const int ck = key >> 3;
+    return d * 64 + ((ck ^ (d & 7)) << 3) + (key & 7);
+}
+
+__global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q, const bf16* __restrict__ kc,
+                                                      const bf16* __restrict__ vc, int t_cap, int M, int t0,
+                                                      int Hq, int Hkv, bf16* __restrict__ o) {
+    __shared__ u32x4 sK[BKV * 16];
+    __shared__ bf16 sVT[128 * BKV];
+    const int nqt = (M + BQ - 1) / BQ;
+    const int qt = nqt - 1 - (int)blockIdx.x;   // heaviest (latest) query tiles first
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int h = g * 2 + (wid >> 1);
+    const int qbase = qt * BQ + (wid & 1) * 32;   // first row of this wave
+    const int l16 = lane & 15, lg = lane >> 4;
+    const float scale_log2 = 0.088388346f * 1.4426950408889634f;
+
+    // Q^T as B operand: lane holds q row (l16) of q-tile c, dims ks*32 + 8*lg .. +8.
+    bf16x8 qf[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int row = qbase + c * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row < M) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * M + row) * 128 + ks * 32 + lg * 8);
+            qf[c][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    f32x4 oacc[8][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) oacc[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+
+    const int block_last_row = min(M, (qt + 1) * BQ) - 1;
+    const int last_slot = t0 + block_last_row;
+    const int ntiles = last_slot / BKV + 1;
+    const bf16* kh = kc + (size_t)g * t_cap * 128;
+    const bf16* vh = vc + (size_t)g * t_cap * 128;
+
+    for (int kt = 0; kt < ntiles; ++kt) {
+        __syncthreads();
+        // stage K (row-major, swizzled) and V^T; slots beyond last_slot are zero-filled
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int qd = tid + 256 * j, key = qd >> 4, ck = qd & 15;
+            const int slot = kt * BKV + key;
+            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (slot <= last_slot) {
+                kv = *reinterpret_cast<const u32x4*>(kh + (size_t)slot * 128 + ck * 8);
+                vv = *reinterpret_cast<const u32x4*>(vh + (size_t)slot * 128 + ck * 8);
+            }
+            sK[kidx(key, ck)] = kv;
+            const unsigned int w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sVT[vt_off(ck * 8 + 2 * e, key)] = (bf16)(w[e] & 0xFFFFu);
+                sVT[vt_off(ck * 8 + 2 * e + 1, key)] = (bf16)(w[e] >> 16);
+            }
+        }
+        __syncthreads();
+
+        // S^T[key][row] for 4 key tiles x 2 row tiles
+        f32x4 s[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, sK[kidx(j * 16 + l16, ks * 4 + lg)]);
+                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], s[j][0], 0, 0, 0);
+                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], s[j][1], 0, 0, 0);
+            }
+        }
+        // scale, causal mask, online softmax (per query row = l16 of tile c)
+        const bool diag = (kt + 1) * BKV - 1 > t0 + qbase;   // some key may be after some row
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int qslot = t0 + qbase + c * 16 + l16;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = s[j][c][r] * scale_log2;
+                    if (diag) {
+                        const int kslot = kt * BKV + j * 16 + lg * 4 + r;
+                        if (kslot > qslot) v = -INFINITY;
+                    }
+                    s[j][c][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mnew = fmaxf(mrow[c], mx);
+            const float corr = exp2f(mrow[c] - mnew);   // 0 on the first tile (mrow = -inf)
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = exp2f(s[j][c][r] - mnew);
+                    s[j][c][r] = p;
+                    sum += p;
+                }
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            lrow[c] = lrow[c] * corr + sum;
+            mrow[c] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) oacc[dt][c] *= corr;
+        }
+        // P^T operands: for key block kb (32 keys = tiles 2kb, 2kb+1) lane group lg holds
+        // keys {32kb + 4lg + i, 32kb + 16 + 4lg + i : i < 4}; V^T uses the same order.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            bf16x8 pb[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                unsigned int w[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    w[e] = (unsigned)f2bf(s[2 * kb][c][2 * e]) | ((unsigned)f2bf(s[2 * kb][c][2 * e + 1]) << 16);
+                    w[2 + e] = (unsigned)f2bf(s[2 * kb + 1][c][2 * e]) | ((unsigned)f2bf(s[2 * kb + 1][c][2 * e + 1]) << 16);
+                }
+                const u32x4 pv = {w[0], w[1], w[2], w[3]};
+                pb[c] = __builtin_bit_cast(bf16x8, pv);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = dt * 16 + l16;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(&sVT[vt_off(d, kb * 32 + lg * 4)]);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(&sVT[vt_off(d, kb * 32 + 16 + lg * 4)]);
+                const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+                const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], oacc[dt][0], 0, 0, 0);
+                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], oacc[dt][1], 0, 0, 0);
+            }
+        }
+    }
+    // O^T accumulator: lane holds query row (l16) of tile c, dims dt*16 + 4*lg + r.
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int row = qbase + c * 16 + l16;
+        if (row >= M) continue;
+        const float inv = 1.0f / lrow[c];
+        bf16* orow = o + (size_t)row * Hq * 128 + h * 128;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const unsigned int w0 = (unsigned)f2bf(oacc[dt][c][0] * inv) | ((unsigned)f2bf(oacc[dt][c][1] * inv) << 16);
+            const unsigned int w1 = (unsigned)f2bf(oacc[dt][c][2] * inv) | ((unsigned)f2bf(oacc[dt][c][3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(orow + dt * 16 + lg * 4) = u32x2{w0, w1};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
+                               int M, int t0, int Hq, int Hkv, uint16_t* o, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (Hq != 2 * Hkv) return hipErrorInvalidValue;
+    dim3 grid((M + BQ - 1) / BQ, Hkv);
+    hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    return hipGetLastError();
+}
+
+}  // namespace q3

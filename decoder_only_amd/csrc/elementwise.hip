@@ -1,0 +1,191 @@
+// Embedding gather, RMSNorm, and the fused QK-norm + RoPE + KV-cache append.
+//
+// Sources ("Inside an LLM: Pure Python Inference for Qwen3-0.6B on MLX"):
+//   Step 2  -- the embedding is a row lookup in the [vocab, hidden] matrix;
+//   Step 3  -- RMSNorm: x / sqrt(mean(x^2) + eps) times a per-feature weight;
+//   Step 4  -- RoPE on split halves: pair (i, i + 64) of a 128-wide head turns by
+//              position * theta^(-i/64) (angles built in float32);
+//   Step 5  -- QK-norm (RMSNorm over each 128-wide q and k head, before RoPE) and
+//              the KV cache, which stores rotated keys and raw values.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+template <typename WT>
+__global__ void k_embed(const int32_t* __restrict__ tok, const WT* __restrict__ E,
+                        float* __restrict__ x, int d, int vocab, unsigned* err) {
+    const int r = blockIdx.x;
+    int t = tok[r];
+    const bool ok = (t >= 0) && (t < vocab);
+    if (!ok && threadIdx.x == 0) atomicOr(err, Q3_DEVERR_TOKEN);
+    const WT* src = E + (size_t)(ok ? t : 0) * d;
+    float* dst = x + (size_t)r * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = ok ? ldw(src, i) : 0.f;
+}
+
+hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
+                        int vocab, unsigned* err, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (wdt == DT_BF16)
+        hipLaunchKernelGGL(k_embed<bf16>, dim3(rows), dim3(256), 0, s, tok, (const bf16*)E, x, d, vocab, err);
+    else
+        hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, x, d, vocab, err);
+    return hipGetLastError();
+}
+
+template <typename OT>
+__global__ void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w,
+                          OT* __restrict__ out, int d, float eps) {
+    __shared__ float red[16];
+    const int r = blockIdx.x;
+    const float* xr = x + (size_t)r * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
+    ss = block_sum(ss, red);
+    const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+    OT* o = out + (size_t)r * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        const float v = (xr[i] * rs) * w[i];
+        if constexpr (sizeof(OT) == 2) o[i] = f2bf(v); else o[i] = v;
+    }
+}
+
+hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_bf16, int rows, int d,
+                          float eps, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (out_bf16)
+        hipLaunchKernelGGL(k_rmsnorm<bf16>, dim3(rows), dim3(256), 0, s, x, w, (bf16*)out, d, eps);
+    else
+        hipLaunchKernelGGL(k_rmsnorm<float>, dim3(rows), dim3(256), 0, s, x, w, (float*)out, d, eps);
+    return hipGetLastError();
+}
+
+// One wave per (row, head). Lane i owns the RoPE pair (i, i + 64) of the 128-wide head.
+// Returns the normalised and rotated pair; RMSNorm as (x * r) * w with r = 1/sqrt(mean + eps).
+__device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, const float* w, int i,
+                                               float eps, int pos, const float* inv_freq) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+    x1 = (x1 * r) * w[i];
+    x2 = (x2 * r) * w[i + 64];
+    // angle = fl32(fl32(pos) * f_i): one float32 multiply; cos/sin evaluated in double.
+    const float ang = __fmul_rn((float)pos, inv_freq[i]);
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, sn));
+    const float y2 = __fadd_rn(__fmul_rn(x1, sn), __fmul_rn(x2, c));
+    x1 = y1;
+    x2 = y2;
+}
+
+template <typename KT>
+__global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* __restrict__ positions,
+                                 const int32_t* __restrict__ lens, int seq_base,
+                                 const float* __restrict__ qn, const float* __restrict__ kn,
+                                 const float* __restrict__ inv_freq, float eps,
+                                 float* __restrict__ q_out, KT* __restrict__ kc, KT* __restrict__ vc,
+                                 int t_cap, int Hq, int Hkv) {
+    const int b = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
+    const int width = (Hq + 2 * Hkv) * 128;
+    const float* row = qkv + (size_t)b * width + hd * 128;
+    const int seq = seq_base + b;
+    const int slot = lens[seq];
+    if ((unsigned)slot >= (unsigned)t_cap) return;   // capacity is checked on the host
+    const int pos = positions ? positions[b] : slot;
+    float x1 = row[i], x2 = row[i + 64];
+    if (hd >= Hq + Hkv) {  // value head: stored as is
+        const int g = hd - Hq - Hkv;
+        const size_t base = (((size_t)seq * Hkv + g) * t_cap + slot) * 128;
+        stkv(vc, base + i, x1);
+        stkv(vc, base + i + 64, x2);
+        return;
+    }
+    norm_rope_pair(x1, x2, hd < Hq ? qn : kn, i, eps, pos, inv_freq);
+    if (hd < Hq) {
+        float* qo = q_out + ((size_t)b * Hq + hd) * 128;
+        qo[i] = x1;
+        qo[i + 64] = x2;
+    } else {
+        const int g = hd - Hq;
+        const size_t base = (((size_t)seq * Hkv + g) * t_cap + slot) * 128;
+        stkv(kc, base + i, x1);
+        stkv(kc, base + i + 64, x2);
+    }
+}
+
+hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
+                                 int seq_base, int B, const float* q_norm, const float* k_norm,
+                                 const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
+                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s) {
+    dim3 grid(B, Hq + 2 * Hkv);
+    if (kv_bf16)
+        hipLaunchKernelGGL(k_qk_rope_decode<bf16>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
+                           q_norm, k_norm, inv_freq, eps, q_out, (bf16*)kc, (bf16*)vc, t_cap, Hq, Hkv);
+    else
+        hipLaunchKernelGGL(k_qk_rope_decode<float>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
+                           q_norm, k_norm, inv_freq, eps, q_out, (float*)kc, (float*)vc, t_cap, Hq, Hkv);
+    return hipGetLastError();
+}
+
+__global__ void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
+                                  const float* __restrict__ qn, const float* __restrict__ kn,
+                                  const float* __restrict__ inv_freq, float eps,
+                                  bf16* __restrict__ q_out, bf16* __restrict__ kc, bf16* __restrict__ vc,
+                                  int t_cap, int Hq, int Hkv) {
+    const int r = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
+    const int width = (Hq + 2 * Hkv) * 128;
+    const float* row = qkv + (size_t)r * width + hd * 128;
+    const int slot = t0 + r;
+    float x1 = row[i], x2 = row[i + 64];
+    if (hd >= Hq + Hkv) {
+        const size_t base = ((size_t)(hd - Hq - Hkv) * t_cap + slot) * 128;
+        vc[base + i] = f2bf(x1);
+        vc[base + i + 64] = f2bf(x2);
+        return;
+    }
+    norm_rope_pair(x1, x2, hd < Hq ? qn : kn, i, eps, slot, inv_freq);
+    if (hd < Hq) {
+        bf16* qo = q_out + ((size_t)hd * M + r) * 128;
+        qo[i] = f2bf(x1);
+        qo[i + 64] = f2bf(x2);
+    } else {
+        const size_t base = ((size_t)(hd - Hq) * t_cap + slot) * 128;
+        kc[base + i] = f2bf(x1);
+        kc[base + i + 64] = f2bf(x2);
+    }
+}
+
+hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
+                                  const float* k_norm, const float* inv_freq, float eps,
+                                  uint16_t* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  int Hkv, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_qk_rope_prefill, dim3(M, Hq + 2 * Hkv), dim3(64), 0, s, qkv, M, t0, q_norm,
+                       k_norm, inv_freq, eps, q_out, kc, vc, t_cap, Hq, Hkv);
+    return hipGetLastError();
+}
+
+__global__ void k_len_advance(int32_t* lens, int seq_base, int B, int by) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) lens[seq_base + b] += by;
+}
+
+hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s) {
+    hipLaunchKernelGGL(k_len_advance, dim3((B + 255) / 256), dim3(256), 0, s, lens, seq_base, B, by);
+    return hipGetLastError();
+}
+
+__global__ void k_fill_u64(unsigned long long* dst, unsigned long long v, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = v;
+}
+
+hipError_t launch_fill_u64(unsigned long long* dst, unsigned long long v, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u64, dim3((n + 255) / 256), dim3(256), 0, s, dst, v, n);
+    return hipGetLastError();
+}
+
+}  // namespace q3

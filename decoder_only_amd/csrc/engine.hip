@@ -1,0 +1,458 @@
+// q3 engine: device weight store, KV cache, workspaces and the launch plans of prefill
+// and decode, behind the C ABI of include/q3.h.
+//
+// Pipeline ("Inside an LLM: Pure Python Inference for Qwen3-0.6B on MLX", "The
+// pipeline at a glance" and Steps 2-9): embed -> n_layers x [RMSNorm -> Q/K/V ->
+// QK-norm -> RoPE -> KV append -> GQA attention -> o_proj + residual -> RMSNorm ->
+// SwiGLU FFN + residual] -> final RMSNorm -> tied LM head -> sampling.
+//
+// Precision plan: decode rows keep float32 activations (bf16 or float32 weights, float32
+// accumulation). Prefill of a long prompt runs all rows but the last through the bf16
+// matrix-core path (bf16 activations into the GEMMs, float32 residual stream and
+// accumulation); the last row then goes through the float32 decode path, which gives
+// the same result as a full prefill by causality (a row only sees earlier slots).
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "q3.h"
+
+using namespace q3;
+
+namespace {
+constexpr int kPrefillMfmaMin = 16;   // prompts shorter than this run row by row
+}
+
+struct q3_engine {
+    q3_config cfg{};
+    hipStream_t stream = nullptr;
+    int device = 0;
+    std::string err = "ok";
+    std::vector<void*> allocs;
+
+    struct Layer {
+        void *wqkv, *wo, *wgu, *wd;
+        float *in_norm, *post_norm, *q_norm, *k_norm;
+    };
+    void* embed = nullptr;
+    std::vector<Layer> layers;
+    float* final_norm = nullptr;
+    float* inv_freq = nullptr;
+
+    void* kc = nullptr;
+    void* vc = nullptr;
+    size_t kv_layer_elems = 0, kv_seq_elems = 0;
+    int32_t* d_len = nullptr;
+    std::vector<int32_t> h_len;
+    unsigned* d_err = nullptr;
+
+    // decode workspace (max_batch rows)
+    float *x = nullptr, *h = nullptr, *qkv = nullptr, *q = nullptr, *o = nullptr, *a = nullptr;
+    float* logits = nullptr;
+    unsigned long long* amax = nullptr;
+    float* attn_ws = nullptr;
+    int attn_ws_T = 0;
+    void* sample_ws = nullptr;
+    const float* cur_logits = nullptr;
+    int cur_rows = 0;
+
+    // prefill workspace (grown on demand)
+    int pf_cap = 0;
+    float *pf_x = nullptr, *pf_qkv = nullptr;
+    uint16_t *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr, *pf_a = nullptr;
+
+    size_t wbytes() const { return cfg.weight_dtype == Q3_BF16 ? 2 : 4; }
+    size_t kvbytes() const { return cfg.kv_dtype == Q3_BF16 ? 2 : 4; }
+    int qkv_rows() const { return (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim; }
+
+    q3_status fail(q3_status st, const std::string& msg) {
+        err = msg;
+        return st;
+    }
+    bool hip_ok(hipError_t e, const char* what) {
+        if (e == hipSuccess) return true;
+        err = std::string(what) + ": " + hipGetErrorString(e);
+        return false;
+    }
+    void* alloc(size_t bytes) {
+        void* p = nullptr;
+        if (hipMalloc(&p, bytes < 256 ? 256 : bytes) != hipSuccess) return nullptr;
+        allocs.push_back(p);
+        return p;
+    }
+    void release(void* p) {
+        for (auto& q : allocs)
+            if (q == p) { hipFree(q); q = nullptr; }
+    }
+};
+
+#define HIPCHK(e, call)                                              \
+    do {                                                             \
+        if (!(e)->hip_ok((call), #call)) return Q3_ERR_HIP;          \
+    } while (0)
+
+// ---------------------------------------------------------------------------------
+// load
+// ---------------------------------------------------------------------------------
+
+namespace {
+
+bool is_norm(const std::string& leaf) {
+    return leaf == "input_layernorm" || leaf == "post_attention_layernorm" || leaf == "q_norm" ||
+           leaf == "k_norm" || leaf == "norm";
+}
+
+std::vector<float> to_f32(const q3_tensor& t) {
+    std::vector<float> out((size_t)t.numel);
+    if (t.dtype == Q3_F32) {
+        memcpy(out.data(), t.data, (size_t)t.numel * 4);
+    } else {
+        const uint16_t* s = (const uint16_t*)t.data;
+        for (int64_t i = 0; i < t.numel; ++i) {
+            uint32_t u = (uint32_t)s[i] << 16;
+            memcpy(&out[i], &u, 4);
+        }
+    }
+    return out;
+}
+
+}  // namespace
+
+static q3_status validate_config(const q3_config* c, std::string& why) {
+    if (!c) { why = "config is NULL"; return Q3_ERR_ARG; }
+    if (c->n_layers < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->ffn <= 0 ||
+        c->vocab <= 0 || c->max_batch <= 0 || c->max_seq <= 0) { why = "non-positive size in config"; return Q3_ERR_ARG; }
+    if (c->head_dim != 128) { why = "head_dim must be 128"; return Q3_ERR_ARG; }
+    if (c->n_heads != 2 * c->n_kv_heads) { why = "n_heads must be 2 * n_kv_heads"; return Q3_ERR_ARG; }
+    if (c->hidden % 128 || c->ffn % 128 || (c->n_heads * 128) % 128) { why = "hidden and ffn must be multiples of 128"; return Q3_ERR_ARG; }
+    if (c->vocab % 2) { why = "vocab must be even"; return Q3_ERR_ARG; }
+    if (c->tie_embeddings != 1) { why = "only a tied LM head is supported"; return Q3_ERR_ARG; }
+    if ((c->weight_dtype != Q3_F32 && c->weight_dtype != Q3_BF16) || (c->kv_dtype != Q3_F32 && c->kv_dtype != Q3_BF16)) { why = "bad dtype"; return Q3_ERR_ARG; }
+    if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) { why = "bad rms_eps or rope_theta"; return Q3_ERR_ARG; }
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int32_t n_weights,
+                             void* stream, q3_engine** out) {
+    if (!out) return Q3_ERR_ARG;
+    *out = nullptr;
+    std::string why;
+    q3_status st = validate_config(cfg, why);
+    if (st != Q3_OK) return st;
+    if (!weights || n_weights <= 0) return Q3_ERR_ARG;
+    const q3_config& c = *cfg;
+    std::unordered_map<std::string, const q3_tensor*> byname;
+    for (int i = 0; i < n_weights; ++i) {
+        if (!weights[i].name || !weights[i].data) return Q3_ERR_ARG;
+        byname[weights[i].name] = &weights[i];
+    }
+    const int d = c.hidden, dh = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
+    const size_t wb = c.weight_dtype == Q3_BF16 ? 2 : 4;
+
+    auto need = [&](const std::string& name, int64_t numel, bool norm, const q3_tensor** t) -> q3_status {
+        auto it = byname.find(name);
+        if (it == byname.end()) return Q3_ERR_SHAPE;
+        if (it->second->numel != numel) return Q3_ERR_SHAPE;
+        if (!norm && it->second->dtype != c.weight_dtype) return Q3_ERR_SHAPE;
+        if (norm && it->second->dtype != Q3_F32 && it->second->dtype != Q3_BF16) return Q3_ERR_SHAPE;
+        *t = it->second;
+        return Q3_OK;
+    };
+    // check every tensor before touching the device
+    const q3_tensor* t;
+    if ((st = need("model.embed_tokens.weight", (int64_t)V * d, false, &t)) != Q3_OK) return st;
+    if ((st = need("model.norm.weight", d, true, &t)) != Q3_OK) return st;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const std::string p = "model.layers." + std::to_string(l) + ".";
+        if ((st = need(p + "input_layernorm.weight", d, true, &t)) != Q3_OK) return st;
+        if ((st = need(p + "post_attention_layernorm.weight", d, true, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.q_norm.weight", dh, true, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.k_norm.weight", dh, true, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.q_proj.weight", (int64_t)Hq * dh * d, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.k_proj.weight", (int64_t)Hkv * dh * d, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.v_proj.weight", (int64_t)Hkv * dh * d, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "self_attn.o_proj.weight", (int64_t)d * Hq * dh, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "mlp.gate_proj.weight", (int64_t)F * d, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "mlp.up_proj.weight", (int64_t)F * d, false, &t)) != Q3_OK) return st;
+        if ((st = need(p + "mlp.down_proj.weight", (int64_t)d * F, false, &t)) != Q3_OK) return st;
+    }
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return Q3_ERR_HIP;
+
+    q3_engine* e = new q3_engine();
+    e->cfg = c;
+    e->stream = (hipStream_t)stream;
+    hipGetDevice(&e->device);
+    auto oom = [&]() { q3_free(e); return Q3_ERR_OOM; };
+
+    auto upload = [&](const void* src, size_t bytes) -> void* {
+        void* p = e->alloc(bytes);
+        if (p && hipMemcpy(p, src, bytes, hipMemcpyHostToDevice) != hipSuccess) return nullptr;
+        return p;
+    };
+    auto upload_norm = [&](const std::string& name) -> float* {
+        std::vector<float> f = to_f32(*byname[name]);
+        return (float*)upload(f.data(), f.size() * 4);
+    };
+
+    e->embed = upload(byname["model.embed_tokens.weight"]->data, (size_t)V * d * wb);
+    if (!e->embed) return oom();
+    if (!(e->final_norm = upload_norm("model.norm.weight"))) return oom();
+    e->layers.resize(c.n_layers);
+    std::vector<uint8_t> buf;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const std::string p = "model.layers." + std::to_string(l) + ".";
+        auto& L = e->layers[l];
+        // QKV packed as [q rows; k rows; v rows]
+        const size_t qb = (size_t)Hq * dh * d * wb, kb = (size_t)Hkv * dh * d * wb;
+        buf.resize(qb + 2 * kb);
+        memcpy(buf.data(), byname[p + "self_attn.q_proj.weight"]->data, qb);
+        memcpy(buf.data() + qb, byname[p + "self_attn.k_proj.weight"]->data, kb);
+        memcpy(buf.data() + qb + kb, byname[p + "self_attn.v_proj.weight"]->data, kb);
+        if (!(L.wqkv = upload(buf.data(), buf.size()))) return oom();
+        if (!(L.wo = upload(byname[p + "self_attn.o_proj.weight"]->data, (size_t)d * Hq * dh * wb))) return oom();
+        // gate/up interleaved in blocks of 16 rows: gate rows 16j..16j+15 then the same up rows
+        const size_t rowb = (size_t)d * wb;
+        buf.resize((size_t)2 * F * rowb);
+        const uint8_t* g = (const uint8_t*)byname[p + "mlp.gate_proj.weight"]->data;
+        const uint8_t* u = (const uint8_t*)byname[p + "mlp.up_proj.weight"]->data;
+        for (int j = 0; j < F / 16; ++j) {
+            memcpy(buf.data() + (size_t)(32 * j) * rowb, g + (size_t)(16 * j) * rowb, 16 * rowb);
+            memcpy(buf.data() + (size_t)(32 * j + 16) * rowb, u + (size_t)(16 * j) * rowb, 16 * rowb);
+        }
+        if (!(L.wgu = upload(buf.data(), buf.size()))) return oom();
+        if (!(L.wd = upload(byname[p + "mlp.down_proj.weight"]->data, (size_t)d * F * wb))) return oom();
+        if (!(L.in_norm = upload_norm(p + "input_layernorm.weight"))) return oom();
+        if (!(L.post_norm = upload_norm(p + "post_attention_layernorm.weight"))) return oom();
+        if (!(L.q_norm = upload_norm(p + "self_attn.q_norm.weight"))) return oom();
+        if (!(L.k_norm = upload_norm(p + "self_attn.k_norm.weight"))) return oom();
+    }
+    // RoPE frequencies f_i = theta^(-i/64), evaluated in double and rounded once to float
+    {
+        std::vector<float> f(dh / 2);
+        for (int i = 0; i < dh / 2; ++i) f[i] = (float)std::pow((double)c.rope_theta, -(double)i / (dh / 2));
+        if (!(e->inv_freq = (float*)upload(f.data(), f.size() * 4))) return oom();
+    }
+    // KV cache [L][S][Hkv][max_seq][dh]
+    e->kv_seq_elems = (size_t)Hkv * c.max_seq * dh;
+    e->kv_layer_elems = e->kv_seq_elems * c.max_batch;
+    const size_t kvb = e->kv_layer_elems * (size_t)(c.n_layers > 0 ? c.n_layers : 1) * e->kvbytes();
+    if (!(e->kc = e->alloc(kvb)) || !(e->vc = e->alloc(kvb))) return oom();
+    if (!(e->d_len = (int32_t*)e->alloc(sizeof(int32_t) * c.max_batch))) return oom();
+    if (hipMemset(e->d_len, 0, sizeof(int32_t) * c.max_batch) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
+    e->h_len.assign(c.max_batch, 0);
+    if (!(e->d_err = (unsigned*)e->alloc(sizeof(unsigned)))) return oom();
+    if (hipMemset(e->d_err, 0, sizeof(unsigned)) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
+    // decode workspace
+    const int B = c.max_batch;
+    if (!(e->x = (float*)e->alloc((size_t)B * d * 4))) return oom();
+    if (!(e->h = (float*)e->alloc((size_t)B * (d > F ? d : F) * 4))) return oom();
+    if (!(e->qkv = (float*)e->alloc((size_t)B * e->qkv_rows() * 4))) return oom();
+    if (!(e->q = (float*)e->alloc((size_t)B * Hq * dh * 4))) return oom();
+    if (!(e->o = (float*)e->alloc((size_t)B * Hq * dh * 4))) return oom();
+    if (!(e->a = (float*)e->alloc((size_t)B * F * 4))) return oom();
+    if (!(e->logits = (float*)e->alloc((size_t)B * V * 4))) return oom();
+    if (!(e->amax = (unsigned long long*)e->alloc((size_t)B * 8))) return oom();
+    if (!(e->sample_ws = e->alloc(sample_workspace_bytes(V, B)))) return oom();
+    e->attn_ws_T = c.max_seq;
+    if (!(e->attn_ws = (float*)e->alloc(attn_decode_workspace_bytes(B, Hkv, c.max_seq)))) return oom();
+    if (hipDeviceSynchronize() != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
+    *out = e;
+    return Q3_OK;
+}
+
+extern "C" void q3_free(q3_engine* e) {
+    if (!e) return;
+    hipStreamSynchronize(e->stream);
+    for (void* p : e->allocs)
+        if (p) hipFree(p);
+    delete e;
+}
+
+extern "C" const char* q3_last_error(const q3_engine* e) { return e ? e->err.c_str() : "engine is NULL"; }
+
+extern "C" int32_t q3_seq_len(const q3_engine* e, int32_t seq) {
+    if (!e || seq < 0 || seq >= e->cfg.max_batch) return -1;
+    return e->h_len[seq];
+}
+
+// ---------------------------------------------------------------------------------
+// decode rows (also the tail of a prefill)
+// ---------------------------------------------------------------------------------
+
+static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* positions,
+                            int seq_base, int B, float* logits_out, bool want_logits) {
+    const q3_config& c = e->cfg;
+    const int d = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
+    const int wdt = c.weight_dtype == Q3_BF16 ? DT_BF16 : DT_F32;
+    const int kvbf = c.kv_dtype == Q3_BF16;
+    hipStream_t s = e->stream;
+    int maxT = 0;
+    for (int b = 0; b < B; ++b) maxT = std::max(maxT, e->h_len[seq_base + b] + 1);
+    HIPCHK(e, launch_embed(tokens, e->embed, wdt, e->x, B, d, V, e->d_err, s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        const auto& L = e->layers[l];
+        char* kcl = (char*)e->kc + (size_t)l * e->kv_layer_elems * e->kvbytes();
+        char* vcl = (char*)e->vc + (size_t)l * e->kv_layer_elems * e->kvbytes();
+        HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, 0, B, d, c.rms_eps, s));
+        HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
+        HIPCHK(e, launch_qk_rope_decode(e->qkv, positions, e->d_len, seq_base, B, L.q_norm, L.k_norm,
+                                        e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq, Hq, Hkv, s));
+        HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, e->d_len, 1, seq_base, B, Hq, Hkv,
+                                     maxT, e->attn_ws, e->o, s));
+        HIPCHK(e, launch_gemv(L.wo, wdt, e->o, e->x, d, Hq * 128, B, GEMV_RESID, s));
+        HIPCHK(e, launch_rmsnorm(e->x, L.post_norm, e->h, 0, B, d, c.rms_eps, s));
+        HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
+        HIPCHK(e, launch_gemv(L.wd, wdt, e->a, e->x, d, F, B, GEMV_RESID, s));
+    }
+    if (want_logits) {
+        float* lg = logits_out ? logits_out : e->logits;
+        HIPCHK(e, launch_rmsnorm(e->x, e->final_norm, e->h, 0, B, d, c.rms_eps, s));
+        HIPCHK(e, launch_fill_u64(e->amax, 0ull, B, s));
+        HIPCHK(e, launch_lmhead(e->embed, wdt, e->h, lg, e->amax, V, d, B, e->d_err, s));
+        e->cur_logits = lg;
+        e->cur_rows = B;
+    }
+    HIPCHK(e, launch_len_advance(e->d_len, seq_base, B, 1, s));
+    for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;
+    return Q3_OK;
+}
+
+static q3_status ensure_prefill_ws(q3_engine* e, int M) {
+    if (M <= e->pf_cap) return Q3_OK;
+    const q3_config& c = e->cfg;
+    const int d = c.hidden, F = c.ffn, HD = c.n_heads * c.head_dim;
+    for (void* p : {(void*)e->pf_x, (void*)e->pf_qkv, (void*)e->pf_h, (void*)e->pf_q, (void*)e->pf_o, (void*)e->pf_a})
+        if (p) e->release(p);
+    e->pf_cap = 0;
+    if (!(e->pf_x = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
+    if (!(e->pf_qkv = (float*)e->alloc((size_t)M * e->qkv_rows() * 4))) return Q3_ERR_OOM;
+    if (!(e->pf_h = (uint16_t*)e->alloc((size_t)M * d * 2))) return Q3_ERR_OOM;
+    if (!(e->pf_q = (uint16_t*)e->alloc((size_t)M * HD * 2))) return Q3_ERR_OOM;
+    if (!(e->pf_o = (uint16_t*)e->alloc((size_t)M * HD * 2))) return Q3_ERR_OOM;
+    if (!(e->pf_a = (uint16_t*)e->alloc((size_t)M * F * 2))) return Q3_ERR_OOM;
+    e->pf_cap = M;
+    return Q3_OK;
+}
+
+// Rows tokens[0..M) of sequence `seq` at slots t0 .. t0+M-1 through the matrix-core path.
+static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, int M) {
+    const q3_config& c = e->cfg;
+    const int d = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
+    hipStream_t s = e->stream;
+    q3_status st = ensure_prefill_ws(e, M);
+    if (st != Q3_OK) return e->fail(st, "prefill workspace allocation failed");
+    const int t0 = e->h_len[seq];
+    HIPCHK(e, launch_embed(tokens, e->embed, DT_BF16, e->pf_x, M, d, V, e->d_err, s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        const auto& L = e->layers[l];
+        uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
+        uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 1, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_gemm(e->pf_h, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d, GEMM_F32, s));
+        HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
+                                         e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
+        HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, s));
+        HIPCHK(e, launch_gemm(e->pf_o, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 1, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_gemm(e->pf_h, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_BF16, s));
+        HIPCHK(e, launch_gemm(e->pf_a, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+    }
+    HIPCHK(e, launch_len_advance(e->d_len, seq, 1, M, s));
+    e->h_len[seq] += M;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens, int32_t n, float* logits) {
+    if (!e) return Q3_ERR_ARG;
+    if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
+    if (!tokens || n < 1) return e->fail(Q3_ERR_ARG, "tokens is NULL or n < 1");
+    if ((int64_t)e->h_len[seq] + n > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
+    q3_status st;
+    int done = 0;
+    if (e->cfg.weight_dtype == Q3_BF16 && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+        if ((st = run_prefill_mfma(e, seq, tokens, n - 1)) != Q3_OK) return st;
+        done = n - 1;
+    }
+    for (int i = done; i < n; ++i) {
+        if ((st = run_decode(e, tokens + i, nullptr, seq, 1, logits, i == n - 1)) != Q3_OK) return st;
+    }
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_decode_step(q3_engine* e, const int32_t* tokens, const int32_t* positions,
+                                    int32_t batch, float* logits) {
+    if (!e) return Q3_ERR_ARG;
+    if (!tokens || batch < 1 || batch > e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "bad tokens or batch");
+    for (int b = 0; b < batch; ++b)
+        if (e->h_len[b] + 1 > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
+    return run_decode(e, tokens, positions, 0, batch, logits, true);
+}
+
+extern "C" q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch, float temperature,
+                               float top_p, const float* uniforms, int32_t* tokens_out) {
+    if (!e) return Q3_ERR_ARG;
+    if (!tokens_out || batch < 1 || batch > e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "bad output or batch");
+    if (!(temperature >= 0.f)) return e->fail(Q3_ERR_ARG, "temperature must be >= 0");
+    if (temperature > 0.f && !uniforms) return e->fail(Q3_ERR_ARG, "uniforms required when temperature > 0");
+    const int V = e->cfg.vocab;
+    if (!logits) {
+        if (!e->cur_logits || batch > e->cur_rows) return e->fail(Q3_ERR_STATE, "no current logits for that many rows");
+        logits = e->cur_logits;
+    } else {
+        HIPCHK(e, launch_argmax_rows(logits, e->amax, V, batch, e->d_err, e->stream));
+    }
+    HIPCHK(e, launch_sample(logits, e->amax, V, batch, temperature, top_p, uniforms, tokens_out,
+                            e->sample_ws, e->stream));
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_reset(q3_engine* e, int32_t seq) {
+    if (!e) return Q3_ERR_ARG;
+    if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
+    int32_t zero = 0;
+    HIPCHK(e, hipMemcpyAsync(e->d_len + seq, &zero, 4, hipMemcpyHostToDevice, e->stream));
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    e->h_len[seq] = 0;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k, const void* v,
+                                  int32_t len) {
+    if (!e) return Q3_ERR_ARG;
+    const q3_config& c = e->cfg;
+    if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !k || !v || len < 0)
+        return e->fail(Q3_ERR_ARG, "bad kv_import arguments");
+    if (len > c.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
+    const size_t eb = e->kvbytes(), row = (size_t)c.head_dim * eb;
+    for (int g = 0; g < c.n_kv_heads; ++g) {
+        const size_t dst = ((size_t)layer * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems +
+                            (size_t)g * c.max_seq * c.head_dim) * eb;
+        const size_t src = (size_t)g * len * row;
+        if (len == 0) break;
+        HIPCHK(e, hipMemcpyAsync((char*)e->kc + dst, (const char*)k + src, len * row, hipMemcpyDefault, e->stream));
+        HIPCHK(e, hipMemcpyAsync((char*)e->vc + dst, (const char*)v + src, len * row, hipMemcpyDefault, e->stream));
+    }
+    HIPCHK(e, hipMemcpyAsync(e->d_len + seq, &len, 4, hipMemcpyHostToDevice, e->stream));
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    e->h_len[seq] = len;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_sync(q3_engine* e) {
+    if (!e) return Q3_ERR_ARG;
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    unsigned flags = 0, zero = 0;
+    HIPCHK(e, hipMemcpyAsync(&flags, e->d_err, 4, hipMemcpyDeviceToHost, e->stream));
+    HIPCHK(e, hipMemcpyAsync(e->d_err, &zero, 4, hipMemcpyHostToDevice, e->stream));
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    if (flags & Q3_DEVERR_TOKEN) return e->fail(Q3_ERR_TOKEN, "a token id outside [0, vocab) reached the device");
+    if (flags & Q3_DEVERR_NONFINITE) return e->fail(Q3_ERR_NUMERIC, "non-finite logits");
+    return Q3_OK;
+}

@@ -1,0 +1,73 @@
+// Launchers of the q3 HIP kernels (all enqueue on the given stream, never sync).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q3 {
+
+enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---- elementwise.hip
+// x[r, :] = E[tok[r], :] widened to float32. Out-of-range ids set Q3_DEVERR_TOKEN and give a zero row.
+hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
+                        int vocab, unsigned* err, hipStream_t s);
+// out[r, :] = rmsnorm(x[r, :]) * w, out float32 or bf16.
+hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_bf16, int rows, int d,
+                          float eps, hipStream_t s);
+// Decode rows: per-head RMSNorm of q and k, RoPE at the row's position, K/V append at
+// slot lens[seq]. qkv: [B][(Hq + 2 Hkv) * 128] float32. q_out: [B][Hq][128] float32.
+// kc/vc: layer base of the cache [S][Hkv][t_cap][128]. positions may be NULL (= slot).
+hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
+                                 int seq_base, int B, const float* q_norm, const float* k_norm,
+                                 const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
+                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s);
+// Prefill rows of one sequence at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] bf16.
+// kc/vc: cache of this (layer, sequence): [Hkv][t_cap][128] bf16.
+hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
+                                  const float* k_norm, const float* inv_freq, float eps,
+                                  uint16_t* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  int Hkv, hipStream_t s);
+// lens[seq_base + b] += by for b < B.
+hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s);
+// dst[i] = v for i < n (64-bit words); graph-safe replacement for a memset.
+hipError_t launch_fill_u64(unsigned long long* dst, unsigned long long v, int n, hipStream_t s);
+
+// ---- gemv.hip (decode projections: float32 activations, bf16 / float32 weights)
+enum GemvEpi { GEMV_STORE = 0, GEMV_RESID = 1, GEMV_SWIGLU = 2 };
+// y[b, n] (=, +=) sum_k W[n, k] x[b, k]. SWIGLU: W holds 2F rows in blocks of 16 gate rows
+// followed by the 16 matching up rows; y[b, j] = silu(gate_j) * up_j, j < F = N / 2.
+hipError_t launch_gemv(const void* W, int wdt, const float* x, float* y, int N, int K, int B,
+                       int epi, hipStream_t s);
+// LM head: logits[b, v] = sum_k E[v, k] h[b, k]; amax[b] = max over v of pack(logit, v).
+hipError_t launch_lmhead(const void* E, int wdt, const float* h, float* logits,
+                         unsigned long long* amax, int V, int K, int B, unsigned* err, hipStream_t s);
+
+// ---- attn_decode.hip (split-K GQA over the cache, one query row per sequence)
+// Visible keys of row b: slots 0 .. lens[seq_base + b] + len_extra - 1.
+size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T);
+hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
+                              int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
+                              int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s);
+
+// ---- gemm.hip (prefill projections on MFMA: bf16 A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
+enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_BF16 = 2, GEMM_BF16 = 3 };
+hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, void* C, int M, int N, int K, int epi,
+                       hipStream_t s);
+
+// ---- attn_prefill.hip (causal GQA flash attention on MFMA)
+// q: [Hq][M][128] bf16 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16; o: [M][Hq*128] bf16.
+hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
+                               int M, int t0, int Hq, int Hkv, uint16_t* o, hipStream_t s);
+
+// ---- sample.hip
+hipError_t launch_argmax_rows(const float* logits, unsigned long long* amax, int V, int B,
+                              unsigned* err, hipStream_t s);
+hipError_t launch_greedy(const unsigned long long* amax, int32_t* out, int B, hipStream_t s);
+size_t sample_workspace_bytes(int V, int B);
+hipError_t launch_sample(const float* logits, const unsigned long long* amax, int V, int B,
+                         float temperature, float top_p, const float* u, int32_t* out, void* ws,
+                         hipStream_t s);
+
+}  // namespace q3

@@ -1,0 +1,108 @@
+// Op-level C ABI (include/q3_ops.h): one kernel family per call, on caller buffers.
+#include <cmath>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "q3_ops.h"
+
+using namespace q3;
+
+namespace {
+
+// Scratch for ops that need it: allocated per call, released after the stream drains.
+struct Scratch {
+    void* p = nullptr;
+    hipStream_t s;
+    explicit Scratch(hipStream_t st) : s(st) {}
+    bool get(size_t bytes) { return hipMalloc(&p, bytes < 256 ? 256 : bytes) == hipSuccess; }
+    ~Scratch() {
+        if (p) {
+            hipStreamSynchronize(s);
+            hipFree(p);
+        }
+    }
+};
+
+q3_status st(hipError_t e) { return e == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
+
+}  // namespace
+
+extern "C" q3_status q3_op_rmsnorm(const float* x, const float* w, void* out, int32_t out_dtype, int32_t rows,
+                                   int32_t d, float eps, void* stream) {
+    if (!x || !w || !out || rows < 0 || d <= 0 || (out_dtype != Q3_F32 && out_dtype != Q3_BF16)) return Q3_ERR_ARG;
+    return st(launch_rmsnorm(x, w, out, out_dtype == Q3_BF16, rows, d, eps, (hipStream_t)stream));
+}
+
+extern "C" q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, int32_t N, int32_t K,
+                                int32_t B, int32_t epilogue, void* stream) {
+    if (!W || !x || !y || N <= 0 || K <= 0 || B < 0 || (w_dtype != Q3_F32 && w_dtype != Q3_BF16)) return Q3_ERR_ARG;
+    if (K % 8 || N % 2 || epilogue < 0 || epilogue > 2) return Q3_ERR_SHAPE;
+    if (epilogue == GEMV_SWIGLU && N % 32) return Q3_ERR_SHAPE;
+    return st(launch_gemv(W, w_dtype == Q3_BF16 ? DT_BF16 : DT_F32, x, y, N, K, B, epilogue, (hipStream_t)stream));
+}
+
+extern "C" q3_status q3_op_gemm(const uint16_t* A, const uint16_t* W, void* C, int32_t M, int32_t N, int32_t K,
+                                int32_t epilogue, void* stream) {
+    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 3) return Q3_ERR_ARG;
+    if (N % 128 || K % 64) return Q3_ERR_SHAPE;
+    return st(launch_gemm(A, W, C, M, N, K, epilogue, (hipStream_t)stream));
+}
+
+extern "C" q3_status q3_op_qk_norm_rope(const float* qkv, const float* q_norm, const float* k_norm,
+                                        const int32_t* positions, const int32_t* slots, int32_t B, int32_t n_heads,
+                                        int32_t n_kv_heads, float eps, float rope_theta, float* q_out,
+                                        void* k_cache, void* v_cache, int32_t kv_dtype, int32_t t_cap,
+                                        void* stream) {
+    if (!qkv || !q_norm || !k_norm || !positions || !slots || !q_out || !k_cache || !v_cache || B < 0 ||
+        n_heads <= 0 || n_kv_heads <= 0 || t_cap <= 0 || (kv_dtype != Q3_F32 && kv_dtype != Q3_BF16))
+        return Q3_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<float> f(64);
+    for (int i = 0; i < 64; ++i) f[i] = (float)std::pow((double)rope_theta, -(double)i / 64);
+    Scratch sc(s);
+    if (!sc.get(64 * sizeof(float))) return Q3_ERR_OOM;
+    if (hipMemcpyAsync(sc.p, f.data(), 64 * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess) return Q3_ERR_HIP;
+    return st(launch_qk_rope_decode(qkv, positions, slots, 0, B, q_norm, k_norm, (const float*)sc.p, eps, q_out,
+                                    k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, n_heads, n_kv_heads, s));
+}
+
+extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                       int32_t t_cap, const int32_t* lens, int32_t B, int32_t n_heads,
+                                       int32_t n_kv_heads, int32_t max_len, float* o, void* stream) {
+    if (!q || !k_cache || !v_cache || !lens || !o || B < 0 || t_cap <= 0 || max_len < 1 || max_len > t_cap ||
+        (kv_dtype != Q3_F32 && kv_dtype != Q3_BF16))
+        return Q3_ERR_ARG;
+    if (n_heads != 2 * n_kv_heads) return Q3_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    Scratch sc(s);
+    if (!sc.get(attn_decode_workspace_bytes(B, n_kv_heads, max_len))) return Q3_ERR_OOM;
+    return st(launch_attn_decode(q, k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, lens, 0, 0, B, n_heads,
+                                 n_kv_heads, max_len, (float*)sc.p, o, s));
+}
+
+extern "C" q3_status q3_op_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                        int32_t t_cap, int32_t M, int32_t t0, int32_t n_heads, int32_t n_kv_heads,
+                                        uint16_t* o, void* stream) {
+    if (!q || !k_cache || !v_cache || !o || M < 0 || t0 < 0 || t_cap <= 0 || (int64_t)t0 + M > t_cap) return Q3_ERR_ARG;
+    if (n_heads != 2 * n_kv_heads) return Q3_ERR_SHAPE;
+    return st(launch_attn_prefill(q, k_cache, v_cache, t_cap, M, t0, n_heads, n_kv_heads, o, (hipStream_t)stream));
+}
+
+extern "C" q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, float temperature, float top_p,
+                                  const float* uniforms, int32_t* tokens_out, void* stream) {
+    if (!logits || !tokens_out || B < 0 || V <= 0 || !(temperature >= 0.f)) return Q3_ERR_ARG;
+    if (temperature > 0.f && !uniforms) return Q3_ERR_ARG;
+    if (B == 0) return Q3_OK;
+    hipStream_t s = (hipStream_t)stream;
+    Scratch sc(s);
+    const size_t amax_bytes = (size_t)B * 8;
+    if (!sc.get(amax_bytes + sample_workspace_bytes(V, B) + 256)) return Q3_ERR_OOM;
+    unsigned long long* amax = (unsigned long long*)sc.p;
+    unsigned* err = (unsigned*)((char*)sc.p + amax_bytes);
+    void* ws = (char*)sc.p + amax_bytes + 256;
+    hipError_t e = hipMemsetAsync(err, 0, 4, s);
+    if (e == hipSuccess) e = launch_argmax_rows(logits, amax, V, B, err, s);
+    if (e == hipSuccess) e = launch_sample(logits, amax, V, B, temperature, top_p, uniforms, tokens_out, ws, s);
+    return st(e);
+}

@@ -1,0 +1,153 @@
+/*
+ * q3 -- C ABI of a Qwen3-0.6B-shaped decoder inference engine for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The calls follow the pipeline of "Inside an LLM: Pure Python Inference for
+ * Qwen3-0.6B on MLX" (section "The pipeline at a glance" and Step 9, the
+ * generation loop): load the weights, prefill a prompt into the KV cache, then
+ * run one decode step per new token and sample it.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are device memory of the engine's GPU (e.g. torch
+ *     tensors on that device); "host" pointers are ordinary CPU memory.
+ *   - Work is enqueued on the stream given to q3_load and is asynchronous: device
+ *     outputs are valid once that stream has been synchronised (q3_sync does it).
+ *   - Argument, shape and capacity errors are detected on the host before anything
+ *     is enqueued; the call then returns the error code and enqueues nothing.
+ *   - Errors that only the device can see (a token id outside [0, vocab), a
+ *     non-finite logit) set a sticky device error word that q3_sync reports.
+ *   - No exception crosses the ABI. An engine must be used from one thread at a time.
+ *   - q3_last_error returns a text for the last failing call on that engine.
+ */
+#ifndef Q3_H
+#define Q3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct q3_engine q3_engine;
+
+typedef enum {
+    Q3_OK = 0,
+    Q3_ERR_ARG = -1,       /* null pointer, bad enum, out-of-range scalar */
+    Q3_ERR_SHAPE = -2,     /* tensor shape/size does not match the config */
+    Q3_ERR_TOKEN = -3,     /* a token id outside [0, vocab) reached the device (sticky) */
+    Q3_ERR_CAPACITY = -4,  /* the KV cache of a sequence would exceed max_seq ("KV cache full") */
+    Q3_ERR_OOM = -5,       /* device allocation failed */
+    Q3_ERR_HIP = -6,       /* a HIP runtime call failed (also: no usable GPU) */
+    Q3_ERR_STATE = -7,     /* call not valid in the engine's current state */
+    Q3_ERR_NUMERIC = -8    /* a non-finite logit was produced (sticky) */
+} q3_status;
+
+typedef enum { Q3_F32 = 0, Q3_BF16 = 1 } q3_dtype;
+
+/* Model and capacity. Only the Qwen3 block structure is supported: head_dim 128,
+ * n_heads a multiple of n_kv_heads, hidden and ffn multiples of 128, a tied LM
+ * head (tie_embeddings must be 1). Step 4 of the article fixes rope_theta = 1e6
+ * and Step 3 rms_eps = 1e-6 for Qwen3-0.6B; both are taken from this struct. */
+typedef struct {
+    int32_t n_layers;      /* 28 for Qwen3-0.6B */
+    int32_t hidden;        /* 1024 */
+    int32_t n_heads;       /* 16 query heads */
+    int32_t n_kv_heads;    /* 8 key/value heads (grouped-query attention, Step 5) */
+    int32_t head_dim;      /* 128 */
+    int32_t ffn;           /* 3072 (SwiGLU, Step 6) */
+    int32_t vocab;         /* 151936 */
+    float rms_eps;         /* 1e-6 */
+    float rope_theta;      /* 1e6 */
+    int32_t tie_embeddings;/* must be 1: the LM head is the embedding matrix */
+    int32_t weight_dtype;  /* q3_dtype of the matrices: Q3_BF16, or Q3_F32 */
+    int32_t kv_dtype;      /* q3_dtype of the KV cache */
+    int32_t max_batch;     /* number of sequence slots (rows of a decode step) */
+    int32_t max_seq;       /* KV-cache capacity per sequence, in tokens */
+} q3_config;
+
+/* One named weight tensor in host memory, under the article's tensor names:
+ * model.embed_tokens.weight [vocab, hidden]; per layer i
+ * model.layers.{i}.input_layernorm.weight [hidden],
+ * model.layers.{i}.self_attn.{q,k,v,o}_proj.weight ([out, in], y = x W^T),
+ * model.layers.{i}.self_attn.{q,k}_norm.weight [head_dim],
+ * model.layers.{i}.post_attention_layernorm.weight [hidden],
+ * model.layers.{i}.mlp.{gate,up,down}_proj.weight; and model.norm.weight.
+ * Matrices must have dtype == weight_dtype; norm weights may be Q3_F32 or Q3_BF16.
+ * lm_head.weight, if given, is ignored (tied head). */
+typedef struct {
+    const char* name;
+    const void* data;      /* host */
+    int32_t dtype;         /* q3_dtype */
+    int64_t numel;
+} q3_tensor;
+
+/* Create an engine on the current HIP device: copies (and repacks) every weight
+ * to the device, reserves the KV cache (max_batch * max_seq slots per layer) and
+ * the decode workspace. `stream` is a hipStream_t (NULL = the null stream). The
+ * caller may free the host tensors when the call returns.
+ * Errors: Q3_ERR_ARG / Q3_ERR_SHAPE (config or a tensor missing / mis-sized),
+ * Q3_ERR_OOM, Q3_ERR_HIP (no device). On error *out is set to NULL. */
+q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int32_t n_weights,
+                  void* stream, q3_engine** out);
+
+/* Prefill (Step 9, "process all input tokens at once"): append the n tokens
+ * `tokens` (device int32 [n]) to sequence slot `seq`, at positions
+ * len(seq) .. len(seq)+n-1 where len(seq) is the slot's current cache length,
+ * running every layer and writing their K/V. If `logits` is not NULL it receives
+ * the logits of the last token (device float32 [vocab]); they are also kept as the
+ * engine's current logits for q3_sample. Errors: Q3_ERR_ARG (seq out of range,
+ * n < 1), Q3_ERR_CAPACITY (len + n > max_seq). */
+q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens, int32_t n,
+                     float* logits);
+
+/* One decode step (Step 9's loop body) for `batch` independent sequences: row b
+ * is sequence slot b, fed the token tokens[b] (device int32 [batch]) at RoPE
+ * position positions[b] (device int32 [batch]; NULL: each slot's current length,
+ * the article's pos = len(ids) - 1). The new K/V are written at slot index
+ * len(b), which then grows by one. Logits of all rows go to `logits` (device
+ * float32 [batch, vocab]) if not NULL, and are kept as the engine's current logits.
+ * Errors: Q3_ERR_ARG (batch outside [1, max_batch]), Q3_ERR_CAPACITY. */
+q3_status q3_decode_step(q3_engine* e, const int32_t* tokens, const int32_t* positions,
+                         int32_t batch, float* logits);
+
+/* Sampling (Step 8): for each of `batch` rows of `logits` (device float32
+ * [batch, vocab]; NULL: the engine's current logits), write one token id to
+ * tokens_out (device int32 [batch]). temperature == 0: argmax, lowest id on ties.
+ * Otherwise logits / temperature -> softmax -> order by (logit desc, id asc) ->
+ * keep the first #{k : cum_k < top_p} + 1 tokens (at most vocab) -> renormalise ->
+ * return the first kept token whose cumulative probability exceeds uniforms[b]
+ * (device float32 [batch], each in [0, 1)). Masses are float64, accumulated as
+ * 2^-s fixed point so the result does not depend on summation order.
+ * Errors: Q3_ERR_ARG (batch, temperature < 0, missing uniforms). */
+q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch, float temperature,
+                    float top_p, const float* uniforms, int32_t* tokens_out);
+
+/* Empty sequence slot `seq` (its cache length becomes 0). */
+q3_status q3_reset(q3_engine* e, int32_t seq);
+
+/* Fill slots 0 .. len-1 of one (sequence, layer) of the KV cache from k and v
+ * (host or device, kv_dtype, layout [n_kv_heads][len][head_dim]) -- a cache that
+ * was computed elsewhere. Sets the sequence's length to len once it is
+ * called for every layer with the same len (the length is set on each call).
+ * Errors: Q3_ERR_ARG, Q3_ERR_CAPACITY (len > max_seq). */
+q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k,
+                       const void* v, int32_t len);
+
+/* Current cache length of a sequence slot, as tracked by the host (-1 on error). */
+int32_t q3_seq_len(const q3_engine* e, int32_t seq);
+
+/* Wait for the engine's stream; report (and clear) the sticky device error word:
+ * Q3_ERR_TOKEN or Q3_ERR_NUMERIC, else Q3_OK (or Q3_ERR_HIP on a runtime error). */
+q3_status q3_sync(q3_engine* e);
+
+/* Text describing the last error on this engine (never NULL). */
+const char* q3_last_error(const q3_engine* e);
+
+/* Release all device memory of the engine. NULL is allowed. */
+void q3_free(q3_engine* e);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q3_H */

@@ -1,0 +1,74 @@
+"""Teacher-forced end-to-end comparison of the engine with the oracle (test infrastructure).
+
+The oracle's own token is fed to both sides at every step, so a single near-tie in
+the argmax cannot make the two runs diverge. Per step and row the comparison reports
+max-abs and relative-L2 logit error, whether the argmax agrees, and the oracle's
+top-2 logit gap.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List
+
+import numpy as np
+
+import oracle
+import synth
+from gpu_util import announce, rel_l2
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-3
+
+
+@dataclasses.dataclass
+class StepStat:
+    step: int
+    row: int
+    max_abs: float
+    rel: float
+    argmax_ok: bool
+    gap: float
+
+
+def top2_gap(l: np.ndarray) -> float:
+    t = np.partition(l.astype(np.float64), -2)[-2:]
+    return float(abs(t[1] - t[0]))
+
+
+def compare(step: int, row: int, got: np.ndarray, ref: np.ndarray) -> StepStat:
+    return StepStat(step, row, float(np.abs(got - ref).max()), rel_l2(got, ref),
+                    int(np.argmax(got)) == int(np.argmax(ref)), top2_gap(ref))
+
+
+def failures(stats: List[StepStat]) -> List[StepStat]:
+    return [s for s in stats if s.max_abs > MAX_ABS or s.rel > REL_L2 or not s.argmax_ok]
+
+
+def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None) -> List[StepStat]:
+    """Prefill a seeded prompt, then `steps` greedy decode steps, batch 1."""
+    import torch
+    from decoder_only_amd import q3
+
+    weights = synth.make_weights(w) if weights is None else weights
+    max_seq = prompt_len + steps + 1
+    model = oracle.Model(oracle.Config.from_workload(w), weights)
+    cache = model.new_cache(max_seq)
+    announce("e2e", w.name, w.n_layers, w.vocab, w.weight_dtype, prompt_len, steps)
+    eng = q3.Engine(q3.config(w, 1, max_seq), weights)
+    prompt = synth.prompt_tokens(w, prompt_len)
+    ref = model.forward(prompt, cache, 0)
+    logits = torch.empty(1, w.vocab, dtype=torch.float32, device="cuda")
+    eng.prefill(0, torch.from_numpy(prompt).cuda(), logits)
+    stats = []
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    for step in range(steps + 1):
+        eng.sync()
+        stats.append(compare(step, 0, logits[0].cpu().numpy(), ref))
+        if step == steps:
+            break
+        nxt = int(np.argmax(ref))
+        ref = model.forward([nxt], cache, prompt_len + step)
+        tok.fill_(nxt)
+        eng.decode_step(tok, None, logits)
+    eng.close()
+    return stats

@@ -1,0 +1,56 @@
+"""End-to-end teacher-forced parity of the engine against the live oracle (GPU)."""
+import numpy as np
+import pytest
+
+import synth
+from e2e import failures, run_single
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(stats):
+    worst = max(stats, key=lambda s: s.rel)
+    print(f"steps={len(stats)} worst rel-L2={worst.rel:.2e} (step {worst.step}) "
+          f"max-abs={max(s.max_abs for s in stats):.2e}")
+
+
+def test_toy_fp32_prefill_and_greedy_decode():
+    """Toy workload: 2 layers, fp32 weights and cache, 5-token prompt, 8 greedy steps."""
+    w = synth.workload("toy")
+    stats = run_single(w, w.prompt_len, w.decode_steps)
+    _report(stats)
+    assert not failures(stats), failures(stats)
+
+
+def test_toy_bf16_matrix_core_prefill():
+    """bf16 weights and cache, 512-token prompt: rows 0..510 take the matrix-core prefill
+    path (bf16 activations), the last row and the decode steps the float32 path."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_single(w, 512, 16)
+    _report(stats)
+    assert not failures(stats), failures(stats)
+
+
+def test_engine_capacity_and_token_errors():
+    import torch
+    from decoder_only_amd import q3
+    w = synth.workload("toy").with_(n_layers=1, vocab=512)
+    eng = q3.Engine(q3.config(w, 2, 8), synth.make_weights(w))
+    toks = torch.arange(9, dtype=torch.int32, device="cuda")
+    with pytest.raises(q3.Q3Error) as e:
+        eng.prefill(0, toks)                                 # 9 > max_seq 8
+    assert e.value.code == -4
+    eng.prefill(0, toks[:8])
+    assert eng.seq_len(0) == 8 and eng.seq_len(1) == 0
+    with pytest.raises(q3.Q3Error) as e:
+        eng.decode_step(toks[:1])                            # slot 0 is full
+    assert e.value.code == -4
+    eng.reset(0)
+    assert eng.seq_len(0) == 0
+    bad = torch.tensor([700], dtype=torch.int32, device="cuda")
+    eng.prefill(1, bad)
+    with pytest.raises(q3.Q3Error) as e:
+        eng.sync()
+    assert e.value.code == -3
+    eng.sync()                                               # the sticky word was cleared
+    eng.close()

@@ -1,0 +1,322 @@
+"""Per-kernel parity on the GPU: each q3_op_* call against the oracle on seeded inputs.
+
+Sizes span several tiles and a ragged tail; the full-shape cases check sampled
+outputs that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import announce, bf16_bits, bf16_dev, f32_of_bits, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q3():
+    import torch
+    from decoder_only_amd import q3 as mod
+    mod.load_library()
+    torch.cuda.set_device(0)
+    return mod
+
+
+def _bf16(x):
+    return synth.f32_to_bf16_bits(x)
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+@pytest.mark.parametrize("rows,d", [(1, 1024), (37, 1024), (5, 3072)])
+def test_rmsnorm(q3, rows, d):
+    import torch
+    announce("rmsnorm", rows, d)
+    x = synth.normal((1, rows, d), (rows, d), 0.7)
+    w = (1 + 0.1 * synth.normal((2, d), (d,))).astype(np.float32)
+    ref = oracle.rms_norm(x, w, 1e-6)
+    xt, wt = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    out = torch.empty(rows, d, dtype=torch.float32, device="cuda")
+    q3.op_rmsnorm(xt, wt, out, 1e-6)
+    outb = torch.empty(rows, d, dtype=torch.bfloat16, device="cuda")
+    q3.op_rmsnorm(xt, wt, outb, 1e-6)
+    torch.cuda.synchronize()
+    assert np.allclose(out.cpu().numpy(), ref, rtol=2e-6, atol=1e-6)
+    gotb = f32_of_bits(bf16_bits(outb))
+    assert np.all(np.abs(gotb - ref) <= np.abs(ref) * 2.0**-8 + 1e-30)
+
+
+# ------------------------------------------------------------------ GEMV (decode projections)
+
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+@pytest.mark.parametrize("N,K,B", [(4096, 1024, 1), (1024, 2048, 3), (1024, 3072, 8), (2048, 1024, 13)])
+def test_gemv_store_and_residual(q3, wdt, N, K, B):
+    import torch
+    announce("gemv", wdt, N, K, B)
+    W = synth.normal((3, N, K), (N, K), 0.02)
+    if wdt == "bf16":
+        Wb = _bf16(W)
+        W = f32_of_bits(Wb)
+        Wt = bf16_dev(Wb)
+    else:
+        Wt = torch.from_numpy(W).cuda()
+    x = synth.normal((4, B, K), (B, K))
+    ref = (x.astype(np.float64) @ W.T.astype(np.float64))
+    xt = torch.from_numpy(x).cuda()
+    y = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    q3.op_gemv(Wt, xt, y, q3.GEMV_STORE)
+    r0 = synth.normal((5, B, N), (B, N))
+    yr = torch.from_numpy(r0).cuda()
+    q3.op_gemv(Wt, xt, yr, q3.GEMV_RESID)
+    torch.cuda.synchronize()
+    scale = np.sqrt(K) * 0.02
+    assert np.abs(y.cpu().numpy() - ref).max() <= 1e-5 * scale
+    assert np.abs(yr.cpu().numpy() - (ref + r0)).max() <= 1e-5 * scale + 1e-6
+
+
+@pytest.mark.parametrize("B", [1, 9])
+def test_gemv_swiglu(q3, B):
+    import torch
+    announce("gemv swiglu", B)
+    F, K = 3072, 1024
+    g = f32_of_bits(_bf16(synth.normal((6, F, K), (F, K), 0.02)))
+    u = f32_of_bits(_bf16(synth.normal((7, F, K), (F, K), 0.02)))
+    packed = np.empty((2 * F, K), np.float32)
+    for j in range(F // 16):
+        packed[32 * j:32 * j + 16] = g[16 * j:16 * j + 16]
+        packed[32 * j + 16:32 * j + 32] = u[16 * j:16 * j + 16]
+    x = synth.normal((8, B, K), (B, K))
+    ref = oracle.silu(x @ g.T) * (x @ u.T)
+    y = torch.empty(B, F, dtype=torch.float32, device="cuda")
+    q3.op_gemv(bf16_dev(_bf16(packed)), torch.from_numpy(x).cuda(), y, q3.GEMV_SWIGLU)
+    torch.cuda.synchronize()
+    assert np.allclose(y.cpu().numpy(), ref, rtol=1e-4, atol=1e-5)
+
+
+# ------------------------------------------------------------------ GEMM (prefill, matrix cores)
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (77, 1024, 2048), (300, 4096, 1024), (129, 1024, 3072)])
+def test_gemm_f32_and_residual(q3, M, N, K):
+    import torch
+    announce("gemm", M, N, K)
+    A = _bf16(synth.normal((10, M, K), (M, K)))
+    W = _bf16(synth.normal((11, N, K), (N, K), 0.02))
+    ref = f32_of_bits(A).astype(np.float64) @ f32_of_bits(W).T.astype(np.float64)
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    q3.op_gemm(bf16_dev(A), bf16_dev(W), C, q3.GEMM_F32)
+    R0 = synth.normal((12, M, N), (M, N))
+    Cr = torch.from_numpy(R0).cuda()
+    q3.op_gemm(bf16_dev(A), bf16_dev(W), Cr, q3.GEMM_RESID_F32)
+    Cb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    q3.op_gemm(bf16_dev(A), bf16_dev(W), Cb, q3.GEMM_BF16)
+    torch.cuda.synchronize()
+    scale = np.sqrt(K) * 0.02
+    assert np.abs(C.cpu().numpy() - ref).max() <= 2e-5 * scale
+    assert np.abs(Cr.cpu().numpy() - (ref + R0)).max() <= 2e-5 * scale + 1e-6
+    gb = f32_of_bits(bf16_bits(Cb))
+    assert np.all(np.abs(gb - ref) <= np.abs(ref) * 2.0**-8 + 1e-5 * scale)
+
+
+def test_gemm_swiglu(q3):
+    import torch
+    announce("gemm swiglu")
+    M, F, K = 200, 3072, 1024
+    g = f32_of_bits(_bf16(synth.normal((13, F, K), (F, K), 0.02)))
+    u = f32_of_bits(_bf16(synth.normal((14, F, K), (F, K), 0.02)))
+    packed = np.empty((2 * F, K), np.float32)
+    for j in range(F // 16):
+        packed[32 * j:32 * j + 16] = g[16 * j:16 * j + 16]
+        packed[32 * j + 16:32 * j + 32] = u[16 * j:16 * j + 16]
+    A = _bf16(synth.normal((15, M, K), (M, K)))
+    Af = f32_of_bits(A)
+    ref = oracle.silu(Af @ g.T) * (Af @ u.T)
+    C = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    q3.op_gemm(bf16_dev(A), bf16_dev(_bf16(packed)), C, q3.GEMM_SWIGLU_BF16)
+    torch.cuda.synchronize()
+    got = f32_of_bits(bf16_bits(C))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-5)
+
+
+def test_gemm_full_prefill_shape_sampled_rows(q3):
+    import torch
+    announce("gemm 32767x4096x1024 sampled")
+    M, N, K = 32767, 4096, 1024
+    A = _bf16(synth.normal((16, M, K), (M, K)))
+    W = _bf16(synth.normal((17, N, K), (N, K), 0.02))
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    q3.op_gemm(bf16_dev(A), bf16_dev(W), C, q3.GEMM_F32)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(18).integers(0, M, 200), [0, 127, 128, M - 1]]))
+    ref = f32_of_bits(A[rows]).astype(np.float64) @ f32_of_bits(W).T.astype(np.float64)
+    assert np.abs(C.cpu().numpy()[rows] - ref).max() <= 2e-5 * np.sqrt(K) * 0.02
+
+
+# ------------------------------------------------------------------ QK-norm + RoPE + KV append
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_qk_norm_rope_append(q3, kv):
+    import torch
+    announce("qk_norm_rope", kv)
+    B, Hq, Hkv, T = 4, 16, 8, 40
+    qkv = synth.normal((20, B), (B, (Hq + 2 * Hkv) * 128), 0.6)
+    qn = (1 + 0.1 * synth.normal((21,), (128,))).astype(np.float32)
+    kn = (1 + 0.1 * synth.normal((22,), (128,))).astype(np.float32)
+    pos = np.array([0, 7, 4097, 33279], np.int32)
+    slots = np.array([0, 39, 5, 17], np.int32)
+    dt = torch.bfloat16 if kv == "bf16" else torch.float32
+    kc = torch.zeros(B, Hkv, T, 128, dtype=dt, device="cuda")
+    vc = torch.zeros(B, Hkv, T, 128, dtype=dt, device="cuda")
+    qo = torch.empty(B, Hq, 128, dtype=torch.float32, device="cuda")
+    q3.op_qk_norm_rope(torch.from_numpy(qkv).cuda(), torch.from_numpy(qn).cuda(), torch.from_numpy(kn).cuda(),
+                       torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(), Hq, Hkv, 1e-6, 1e6,
+                       qo, kc, vc)
+    torch.cuda.synchronize()
+    f = oracle.rope_inv_freq(128, 1e6)
+    kcf = kc.float().cpu().numpy()
+    vcf = vc.float().cpu().numpy()
+    for b in range(B):
+        q = qkv[b, :Hq * 128].reshape(Hq, 1, 128)
+        k = qkv[b, Hq * 128:(Hq + Hkv) * 128].reshape(Hkv, 1, 128)
+        v = qkv[b, (Hq + Hkv) * 128:].reshape(Hkv, 1, 128)
+        qr = oracle.apply_rope(oracle.rms_norm(q, qn, 1e-6), pos[b:b + 1], f)[:, 0]
+        kr = oracle.apply_rope(oracle.rms_norm(k, kn, 1e-6), pos[b:b + 1], f)[:, 0]
+        assert np.allclose(qo[b].cpu().numpy(), qr, rtol=1e-5, atol=2e-6)
+        if kv == "bf16":
+            kr_b = oracle.round_to_bf16(kr)
+            # rounding may flip by one bf16 ulp where the float32 inputs differ in the last bit
+            assert np.all(np.abs(kcf[b, :, slots[b]] - kr_b) <= np.abs(kr_b) * 2.0**-7 + 1e-30)
+            assert np.mean(kcf[b, :, slots[b]] == kr_b) > 0.99
+            assert np.array_equal(vcf[b, :, slots[b]], oracle.round_to_bf16(v[:, 0]))
+        else:
+            assert np.allclose(kcf[b, :, slots[b]], kr, rtol=1e-5, atol=2e-6)
+            assert np.array_equal(vcf[b, :, slots[b]], v[:, 0])
+        others = np.setdiff1d(np.arange(T), [slots[b]])
+        assert np.all(kcf[b][:, others] == 0) and np.all(vcf[b][:, others] == 0)
+
+
+# ------------------------------------------------------------------ decode attention (split-K)
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+@pytest.mark.parametrize("lens", [[1], [1, 300, 1000], [257, 256, 255, 513]])
+def test_attn_decode(q3, kv, lens):
+    import torch
+    announce("attn_decode", kv, lens)
+    B, Hq, Hkv = len(lens), 16, 8
+    t_cap = max(lens) + 3
+    q = synth.normal((30, B), (B, Hq, 128))
+    K = synth.normal((31, B), (B, Hkv, t_cap, 128))
+    V = synth.normal((32, B), (B, Hkv, t_cap, 128))
+    if kv == "bf16":
+        K, V = oracle.round_to_bf16(K), oracle.round_to_bf16(V)
+        dt = torch.bfloat16
+    else:
+        dt = torch.float32
+    o = torch.empty(B, Hq * 128, dtype=torch.float32, device="cuda")
+    q3.op_attn_decode(torch.from_numpy(q).cuda(), torch.from_numpy(K).to(dt).cuda(), torch.from_numpy(V).to(dt).cuda(),
+                      torch.tensor(lens, dtype=torch.int32, device="cuda"), o, max(lens))
+    torch.cuda.synchronize()
+    got = o.cpu().numpy()
+    for b, T in enumerate(lens):
+        ref = oracle.attend(q[b][:, None, :], K[b, :, :T], V[b, :, :T], T - 1)[0]
+        assert np.allclose(got[b], ref, rtol=1e-4, atol=2e-5), (b, np.abs(got[b] - ref).max())
+
+
+def test_attn_decode_full_shapes_sampled(q3):
+    """bs64 at 4097 keys and bs1 at 33280 keys (the batched-decode and long-context shapes)."""
+    import torch
+    for B, T, rows in [(64, 4097, [0, 17, 63]), (1, 33280, [0])]:
+        announce("attn_decode full", B, T)
+        Hq, Hkv = 16, 8
+        gen = torch.Generator(device="cuda").manual_seed(40 + B)
+        K = torch.randn(B, Hkv, T, 128, generator=gen, device="cuda").bfloat16()
+        V = torch.randn(B, Hkv, T, 128, generator=gen, device="cuda").bfloat16()
+        q = synth.normal((41, B), (B, Hq, 128))
+        o = torch.empty(B, Hq * 128, dtype=torch.float32, device="cuda")
+        lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+        q3.op_attn_decode(torch.from_numpy(q).cuda(), K, V, lens, o, T)
+        torch.cuda.synchronize()
+        got = o.cpu().numpy()
+        for b in rows:
+            Kb = K[b].float().cpu().numpy()
+            Vb = V[b].float().cpu().numpy()
+            ref = oracle.attend(q[b][:, None, :], Kb, Vb, T - 1)[0]
+            assert np.allclose(got[b], ref, rtol=1e-4, atol=2e-5), (B, b, np.abs(got[b] - ref).max())
+
+
+# ------------------------------------------------------------------ prefill attention (flash, matrix cores)
+
+@pytest.mark.parametrize("M,t0", [(1, 0), (63, 0), (64, 0), (65, 0), (200, 0), (130, 37), (1, 500)])
+def test_attn_prefill(q3, M, t0):
+    import torch
+    announce("attn_prefill", M, t0)
+    Hq, Hkv = 16, 8
+    t_cap = t0 + M + 5
+    q = _bf16(synth.normal((50, M, t0), (Hq, M, 128)))
+    K = _bf16(synth.normal((51, M, t0), (Hkv, t_cap, 128)))
+    V = _bf16(synth.normal((52, M, t0), (Hkv, t_cap, 128)))
+    o = torch.empty(M, Hq * 128, dtype=torch.bfloat16, device="cuda")
+    q3.op_attn_prefill(bf16_dev(q), bf16_dev(K), bf16_dev(V), t0, o)
+    torch.cuda.synchronize()
+    got = f32_of_bits(bf16_bits(o))
+    ref = oracle.attend(f32_of_bits(q), f32_of_bits(K)[:, :t0 + M], f32_of_bits(V)[:, :t0 + M], t0)
+    # probabilities enter the PV product as bf16 and the output is bf16
+    assert np.abs(got - ref).max() <= 3e-2, np.abs(got - ref).max()
+    assert rel_l2(got, ref) <= 8e-3
+
+
+def test_attn_prefill_long_sampled_rows(q3):
+    import torch
+    M, t0 = 32767, 0
+    announce("attn_prefill long", M)
+    Hq, Hkv = 16, 8
+    gen = torch.Generator(device="cuda").manual_seed(55)
+    q = torch.randn(Hq, M, 128, generator=gen, device="cuda").bfloat16()
+    K = torch.randn(Hkv, M, 128, generator=gen, device="cuda").bfloat16()
+    V = torch.randn(Hkv, M, 128, generator=gen, device="cuda").bfloat16()
+    o = torch.empty(M, Hq * 128, dtype=torch.bfloat16, device="cuda")
+    q3.op_attn_prefill(q, K, V, t0, o)
+    torch.cuda.synchronize()
+    qn, Kn, Vn = q.float().cpu().numpy(), K.float().cpu().numpy(), V.float().cpu().numpy()
+    got = o.float().cpu().numpy()
+    for i in [0, 1, 63, 64, 4095, 20000, M - 1]:
+        ref = oracle.attend(qn[:, i:i + 1], Kn[:, :i + 1], Vn[:, :i + 1], i)[0]
+        assert np.abs(got[i] - ref).max() <= 3e-2 and rel_l2(got[i], ref) <= 8e-3, i
+
+
+# ------------------------------------------------------------------ sampler
+
+def _sampler_case(q3, logits, T, p, us):
+    import torch
+    B, V = logits.shape
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    u = np.asarray(us, np.float32)
+    q3.op_sample(torch.from_numpy(logits).cuda(), T, p, torch.from_numpy(u).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    Tf, pf = float(np.float32(T)), float(np.float32(p))
+    for b in range(B):
+        want = oracle.sample(logits[b], Tf, pf, float(u[b]))
+        margin = oracle.sample_margin(logits[b], Tf, pf, float(u[b]))
+        if margin > 1e-9:
+            assert got[b] == want, (b, got[b], want, margin)
+
+
+@pytest.mark.parametrize("T,p", [(0.7, 0.9), (1.0, 0.95), (0.0, 0.9), (1.0, 1.0), (0.3, 0.5)])
+def test_sampler_matches_oracle(q3, T, p):
+    announce("sampler", T, p)
+    V, B = 151936, 6
+    logits = (synth.normal((60, int(T * 10), int(p * 100)), (B, V)) * 0.64).astype(np.float32)
+    us = np.random.default_rng(61).random(B)
+    _sampler_case(q3, logits, T, p, us)
+
+
+def test_sampler_ties_and_degenerate(q3):
+    announce("sampler ties")
+    V = 8192
+    flat = np.zeros((3, V), np.float32)                     # all equal: ordered by id
+    _sampler_case(q3, flat, 1.0, 0.5, [0.0, 0.5, 0.999])
+    coarse = np.round(synth.normal((62,), (4, V)) * 4) / 4  # many exact ties
+    _sampler_case(q3, coarse.astype(np.float32), 0.8, 0.9, [0.1, 0.4, 0.7, 0.95])
+    spiky = np.full((2, V), -30.0, np.float32)               # one dominant token
+    spiky[:, 1234] = 10.0
+    _sampler_case(q3, spiky, 1.0, 0.9, [0.0, 0.9999])
