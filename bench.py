@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of the q3 engine on one MI355X: Qwen3-0.6B-shaped decoder, synthetic data.
+
+Main line (`value`): decode tokens/s at batch 1 on the Qwen3-0.6B shape (28 layers,
+bf16 weights and KV cache, random-init weights ~N(0, 0.02), tied vocab 151936). One
+bench step is one whole generation: prefill a 5-token random prompt, then 128 greedy
+decode steps, each followed by on-device sampling whose token feeds the next step.
+value = 128 * steps / (wall time of the timed steps).
+
+Also reported (one JSON line): prefill tokens/s of a 2048-token prompt and batch-64
+decode tokens/s with 4096 pre-filled KV slots per sequence, the roofline of the
+dominant kernel (event-timed on the engine's stream), and the CPU oracle's decode
+rate on this host (a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-extras", action="store_true", help="skip the prefill and batch-64 lines")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); "
+              "the engine is single-GPU and has no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from decoder_only_amd import q3
+
+    torch.cuda.set_device(0)
+    w = synth.workload("bs1_short")
+    t = time.time()
+    weights = synth.make_weights(w)
+    log(f"weights generated in {time.time() - t:.1f}s")
+    max_batch, max_seq = 64, 4160
+    eng = q3.Engine(q3.config(w, max_batch, max_seq), weights)
+    log("engine loaded")
+
+    prompt = torch.from_numpy(synth.prompt_tokens(w)).cuda()
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    n_dec = w.decode_steps
+
+    def generation():
+        eng.reset(0)
+        eng.prefill(0, prompt)
+        eng.sample(tok, 0.0)
+        for _ in range(n_dec):
+            eng.decode_step(tok)
+            eng.sample(tok, 0.0)
+
+    for _ in range(args.warmup):
+        generation()
+    eng.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        generation()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eng.sync()
+    elapsed = t1 - t0
+    value = n_dec * args.steps / elapsed
+    ms_per_step = 1000.0 * elapsed / args.steps
+    log(f"bs1 decode: {value:.1f} tok/s, {ms_per_step:.2f} ms per generation")
+
+    # Roofline of the dominant kernel family (decode projections: most bytes per step),
+    # event-timed on the engine's stream over a second pass of the same steps.
+    eng.profile_begin(q3.PROF_GEMV)
+    for _ in range(args.steps):
+        generation()
+    prof = eng.profile_end()
+    gemv_gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
+    roofline = {"kernel": "decode GEMV (q/k/v, o, gate/up, down)", "bound": "hbm",
+                "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_us": round(1e3 * prof["ms"] / max(prof["launches"], 1), 3),
+                "bytes_per_launch": round(prof["bytes"] / max(prof["launches"], 1))}
+    eng.profile_begin(q3.PROF_DECODE_STEP)
+    for _ in range(args.steps):
+        generation()
+    step = eng.profile_end()
+    step_gbs = step["bytes"] / (step["ms"] / 1e3) / 1e9
+    extras = {"decode_step_us": round(1e3 * step["ms"] / step["launches"], 2),
+              "decode_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)}
+    log(f"GEMV {gemv_gbs:.0f} GB/s; whole decode step {extras['decode_step_us']} us "
+        f"({step_gbs:.0f} GB/s algorithmic)")
+
+    if not args.no_extras:
+        try:
+            extras.update(prefill_line(eng, w, q3, torch, synth))
+        except Exception as ex:  # the main line is still reported
+            extras["prefill_error"] = repr(ex)
+        try:
+            extras.update(bs64_line(eng, w, q3, torch, synth, max_seq))
+        except Exception as ex:
+            extras["bs64_error"] = repr(ex)
+
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cpu = cpu_baseline(w, weights, args.cpu_seconds)
+        except Exception as ex:
+            cpu = {"error": repr(ex)}
+    eng.close()
+
+    out = {
+        "metric": "decode tok/s (bs1, bs64) + prefill tok/s, Qwen3-0.6B shape; % of roofline",
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights/KV, f32 activations",
+        "data": "synthetic: random-init weights N(0,0.02), uniform random token ids",
+        "config": {"workload": "Qwen3-0.6B shape, batch 1, 5-token prompt + 128 greedy decode steps "
+                               "(one step = one generation)",
+                   "layers": w.n_layers, "hidden": w.hidden, "heads": f"{w.n_heads}q/{w.n_kv_heads}kv",
+                   "vocab": w.vocab, "global_batch": 1, "seq_len": w.prompt_len + w.decode_steps,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def prefill_line(eng, w, q3, torch, synth):
+    """2048-token prompt prefill (the long-prompt workload), timed alone."""
+    n = 2048
+    toks = torch.from_numpy(synth.prompt_tokens(w.with_(seed=1003), n)).cuda()
+    for _ in range(2):
+        eng.reset(0)
+        eng.prefill(0, toks)
+    eng.sync()
+    reps = 5
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        eng.reset(0)
+        eng.prefill(0, toks)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    eng.reset(0)
+    eng.profile_begin(q3.PROF_GEMM)
+    eng.prefill(0, toks)
+    g = eng.profile_end()
+    eng.reset(0)
+    eng.profile_begin(q3.PROF_ATTN_PREFILL)
+    eng.prefill(0, toks)
+    a = eng.profile_end()
+    eng.reset(0)
+    gt = g["flops"] / (g["ms"] / 1e3) / 1e12
+    at = a["flops"] / (a["ms"] / 1e3) / 1e12
+    log(f"prefill {n}: {n / dt:.0f} tok/s; GEMM {gt:.0f} TFLOP/s; attention {at:.0f} TFLOP/s")
+    return {"prefill2048_tok_s": round(n / dt, 1), "prefill2048_ms": round(1e3 * dt, 3),
+            "prefill_gemm_tflops": round(gt, 1), "prefill_gemm_frac": round(gt / BF16_PEAK_TFLOPS, 4),
+            "prefill_attn_tflops": round(at, 1)}
+
+
+def bs64_line(eng, w, q3, torch, synth, max_seq):
+    """64 sequences with 4096 pre-filled K/V slots each (synthetic N(0,1) bf16), greedy."""
+    B, T0, steps = 64, 4096, 8
+    gen = torch.Generator(device="cuda").manual_seed(1004)
+    for b in range(B):
+        for layer in range(w.n_layers):
+            kv = torch.randn(2, w.n_kv_heads, T0, w.head_dim, generator=gen, device="cuda").bfloat16()
+            eng.kv_import(b, layer, kv[0].contiguous(), kv[1].contiguous(), T0)
+    toks = torch.from_numpy(synth.batch_first_tokens(w.with_(seed=1004, batch=B))).cuda()
+    eng.decode_step(toks)
+    eng.sample(toks, 0.0)
+    eng.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.decode_step(toks)
+        eng.sample(toks, 0.0)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    eng.profile_begin(q3.PROF_ATTN_DECODE)
+    eng.decode_step(toks)
+    eng.sample(toks, 0.0)
+    a = eng.profile_end()
+    for b in range(B):
+        eng.reset(b)
+    ag = a["bytes"] / (a["ms"] / 1e3) / 1e9
+    log(f"bs64 decode: {B * steps / dt:.0f} tok/s; attention {ag:.0f} GB/s")
+    return {"bs64_decode_tok_s": round(B * steps / dt, 1), "bs64_step_ms": round(1e3 * dt / steps, 3),
+            "bs64_attn_gbs": round(ag, 1), "bs64_attn_hbm_frac": round(ag / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baseline(w, weights, budget_s):
+    """The oracle (NumPy) on this host: 5-token prefill, then decode steps until the budget."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    model = oracle.Model(oracle.Config.from_workload(w), weights)
+    cache = model.new_cache(w.max_seq)
+    prompt = synth.prompt_tokens(w)
+    logits = model.forward(prompt, cache, 0)
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or (time.perf_counter() - t0 < budget_s and n < w.decode_steps):
+        nxt = int(np.argmax(logits))
+        logits = model.forward([nxt], cache, w.prompt_len + n)
+        n += 1
+    dt = time.perf_counter() - t0
+    log(f"oracle: {n / dt:.2f} tok/s over {n} steps ({threads} threads)")
+    return {"value": round(n / dt, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch-1 Qwen3-0.6B shape, 5-token prefill then the first {n} greedy decode "
+                      f"steps ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -13,6 +13,10 @@
 // needs once both operands agree on the order of the contraction (key) index; so the
 // probabilities go from accumulators to bf16 operands without touching LDS. V is stored
 // transposed in LDS ([dim][key]) for the A operand.
+//
+// Precision: K and V are bf16 (the cache's own format, exact as operands). q (float32) and
+// the probabilities (float32) are each split into bf16 hi + lo parts and take two MFMAs,
+// so both products keep ~16 significant bits; the output is float32.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,9 +40,23 @@ __device__ __forceinline__ int vt_off(int d, int key) {  // offset in bf16 eleme
     return d * 64 + ((ck ^ (d & 7)) << 3) + (key & 7);
 }
 
-__global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q, const bf16* __restrict__ kc,
+__device__ __forceinline__ unsigned int pack2(bf16 a, bf16 b) { return (unsigned)a | ((unsigned)b << 16); }
+
+// 8 float32 -> bf16 hi parts and bf16 lo parts, as two 8-element operands.
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+    bf16 h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = f2bf(v[i]);
+        l[i] = f2bf(v[i] - bf2f(h[i]));
+    }
+    hi = __builtin_bit_cast(bf16x8, u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
+    lo = __builtin_bit_cast(bf16x8, u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
+}
+
+__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
                                                       const bf16* __restrict__ vc, int t_cap, int M, int t0,
-                                                      int Hq, int Hkv, bf16* __restrict__ o) {
+                                                      int Hq, int Hkv, float* __restrict__ o) {
     __shared__ u32x4 sK[BKV * 16];
     __shared__ bf16 sVT[128 * BKV];
     const int nqt = (M + BQ - 1) / BQ;
@@ -50,16 +68,22 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q
     const int l16 = lane & 15, lg = lane >> 4;
     const float scale_log2 = 0.088388346f * 1.4426950408889634f;
 
-    // Q^T as B operand: lane holds q row (l16) of q-tile c, dims ks*32 + 8*lg .. +8.
-    bf16x8 qf[2][4];
+    // Q^T as B operand (hi and lo parts): lane holds q row (l16) of q-tile c, dims
+    // ks*32 + 8*lg .. +8.
+    bf16x8 qh[2][4], ql[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int row = qbase + c * 16 + l16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < M) v = *reinterpret_cast<const u32x4*>(q + ((size_t)h * M + row) * 128 + ks * 32 + lg * 8);
-            qf[c][ks] = __builtin_bit_cast(bf16x8, v);
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (row < M) {
+                const f32x4* p = reinterpret_cast<const f32x4*>(q + ((size_t)h * M + row) * 128 + ks * 32 + lg * 8);
+                const f32x4 a = p[0], b = p[1];
+                v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+                v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+            }
+            split8(v, qh[c][ks], ql[c][ks]);
         }
     }
     f32x4 oacc[8][2];
@@ -106,8 +130,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 a = __builtin_bit_cast(bf16x8, sK[kidx(j * 16 + l16, ks * 4 + lg)]);
-                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], s[j][0], 0, 0, 0);
-                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], s[j][1], 0, 0, 0);
+                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[0][ks], s[j][0], 0, 0, 0);
+                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[1][ks], s[j][1], 0, 0, 0);
+                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[0][ks], s[j][0], 0, 0, 0);
+                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[1][ks], s[j][1], 0, 0, 0);
             }
         }
         // scale, causal mask, online softmax (per query row = l16 of tile c)
@@ -152,17 +178,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q
         // keys {32kb + 4lg + i, 32kb + 16 + 4lg + i : i < 4}; V^T uses the same order.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 pb[2];
+            bf16x8 ph[2], pl[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                unsigned int w[4];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    w[e] = (unsigned)f2bf(s[2 * kb][c][2 * e]) | ((unsigned)f2bf(s[2 * kb][c][2 * e + 1]) << 16);
-                    w[2 + e] = (unsigned)f2bf(s[2 * kb + 1][c][2 * e]) | ((unsigned)f2bf(s[2 * kb + 1][c][2 * e + 1]) << 16);
-                }
-                const u32x4 pv = {w[0], w[1], w[2], w[3]};
-                pb[c] = __builtin_bit_cast(bf16x8, pv);
+                const float pv[8] = {s[2 * kb][c][0], s[2 * kb][c][1], s[2 * kb][c][2], s[2 * kb][c][3],
+                                     s[2 * kb + 1][c][0], s[2 * kb + 1][c][1], s[2 * kb + 1][c][2], s[2 * kb + 1][c][3]};
+                split8(pv, ph[c], pl[c]);
             }
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
@@ -171,8 +192,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q
                 const u32x2 hi = *reinterpret_cast<const u32x2*>(&sVT[vt_off(d, kb * 32 + 16 + lg * 4)]);
                 const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
                 const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], oacc[dt][0], 0, 0, 0);
-                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], oacc[dt][1], 0, 0, 0);
+                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[0], oacc[dt][0], 0, 0, 0);
+                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[1], oacc[dt][1], 0, 0, 0);
+                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[0], oacc[dt][0], 0, 0, 0);
+                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[1], oacc[dt][1], 0, 0, 0);
             }
         }
     }
@@ -182,20 +205,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const bf16* __restrict__ q
         const int row = qbase + c * 16 + l16;
         if (row >= M) continue;
         const float inv = 1.0f / lrow[c];
-        bf16* orow = o + (size_t)row * Hq * 128 + h * 128;
+        float* orow = o + (size_t)row * Hq * 128 + h * 128;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const unsigned int w0 = (unsigned)f2bf(oacc[dt][c][0] * inv) | ((unsigned)f2bf(oacc[dt][c][1] * inv) << 16);
-            const unsigned int w1 = (unsigned)f2bf(oacc[dt][c][2] * inv) | ((unsigned)f2bf(oacc[dt][c][3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(orow + dt * 16 + lg * 4) = u32x2{w0, w1};
-        }
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<f32x4*>(orow + dt * 16 + lg * 4) =
+                f32x4{oacc[dt][c][0] * inv, oacc[dt][c][1] * inv, oacc[dt][c][2] * inv, oacc[dt][c][3] * inv};
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, uint16_t* o, hipStream_t s) {
+hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
+                               int M, int t0, int Hq, int Hkv, float* o, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (Hq != 2 * Hkv) return hipErrorInvalidValue;
     dim3 grid((M + BQ - 1) / BQ, Hkv);

@@ -132,7 +132,7 @@ hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, con
 __global__ void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
                                   const float* __restrict__ qn, const float* __restrict__ kn,
                                   const float* __restrict__ inv_freq, float eps,
-                                  bf16* __restrict__ q_out, bf16* __restrict__ kc, bf16* __restrict__ vc,
+                                  float* __restrict__ q_out, bf16* __restrict__ kc, bf16* __restrict__ vc,
                                   int t_cap, int Hq, int Hkv) {
     const int r = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
     const int width = (Hq + 2 * Hkv) * 128;
@@ -147,9 +147,9 @@ __global__ void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
     }
     norm_rope_pair(x1, x2, hd < Hq ? qn : kn, i, eps, slot, inv_freq);
     if (hd < Hq) {
-        bf16* qo = q_out + ((size_t)hd * M + r) * 128;
-        qo[i] = f2bf(x1);
-        qo[i + 64] = f2bf(x2);
+        float* qo = q_out + ((size_t)hd * M + r) * 128;
+        qo[i] = x1;
+        qo[i + 64] = x2;
     } else {
         const size_t base = ((size_t)(hd - Hq) * t_cap + slot) * 128;
         kc[base + i] = f2bf(x1);
@@ -159,7 +159,7 @@ __global__ void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
 
 hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
                                   const float* k_norm, const float* inv_freq, float eps,
-                                  uint16_t* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  float* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
                                   int Hkv, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_qk_rope_prefill, dim3(M, Hq + 2 * Hkv), dim3(64), 0, s, qkv, M, t0, q_norm,

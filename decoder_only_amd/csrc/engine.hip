@@ -7,10 +7,12 @@
 // SwiGLU FFN + residual] -> final RMSNorm -> tied LM head -> sampling.
 //
 // Precision plan: decode rows keep float32 activations (bf16 or float32 weights, float32
-// accumulation). Prefill of a long prompt runs all rows but the last through the bf16
-// matrix-core path (bf16 activations into the GEMMs, float32 residual stream and
-// accumulation); the last row then goes through the float32 decode path, which gives
-// the same result as a full prefill by causality (a row only sees earlier slots).
+// accumulation). Prefill of a long prompt runs all rows but the last through the
+// matrix-core path: float32 activations enter every MFMA product as a bf16 hi + lo pair
+// (two MFMAs; the bf16 weights and the bf16 K/V cache are exact operands), so the path
+// keeps ~16 significant bits where a single bf16 rounding would cost ~5e-3 relative
+// error in the logits. The last row then goes through the float32 decode path, which
+// gives the same result as a full prefill by causality (a row only sees earlier slots).
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -61,10 +63,19 @@ struct q3_engine {
     const float* cur_logits = nullptr;
     int cur_rows = 0;
 
+    // event timing of one kernel family (q3_profile_begin / q3_profile_end)
+    struct Prof {
+        int kind = -1;
+        std::vector<hipEvent_t> ev;   // pairs (start, stop)
+        size_t used = 0;
+        double bytes = 0, flops = 0;
+        int64_t launches = 0;
+    } prof;
+
     // prefill workspace (grown on demand)
     int pf_cap = 0;
-    float *pf_x = nullptr, *pf_qkv = nullptr;
-    uint16_t *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr, *pf_a = nullptr;
+    float *pf_x = nullptr, *pf_qkv = nullptr, *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr,
+          *pf_a = nullptr;
 
     size_t wbytes() const { return cfg.weight_dtype == Q3_BF16 ? 2 : 4; }
     size_t kvbytes() const { return cfg.kv_dtype == Q3_BF16 ? 2 : 4; }
@@ -90,6 +101,26 @@ struct q3_engine {
             if (q == p) { hipFree(q); q = nullptr; }
     }
 };
+
+// Record an event pair around one launch of the profiled kernel family.
+static void prof_mark(q3_engine* e, int kind, bool start, double bytes = 0, double flops = 0) {
+    auto& p = e->prof;
+    if (p.kind != kind) return;
+    if (start) {
+        while (p.ev.size() < p.used + 2) {
+            hipEvent_t ev;
+            if (hipEventCreate(&ev) != hipSuccess) return;
+            p.ev.push_back(ev);
+        }
+        hipEventRecord(p.ev[p.used], e->stream);
+        p.bytes += bytes;
+        p.flops += flops;
+        p.launches += 1;
+    } else {
+        hipEventRecord(p.ev[p.used + 1], e->stream);
+        p.used += 2;
+    }
+}
 
 #define HIPCHK(e, call)                                              \
     do {                                                             \
@@ -270,6 +301,7 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
 extern "C" void q3_free(q3_engine* e) {
     if (!e) return;
     hipStreamSynchronize(e->stream);
+    for (hipEvent_t ev : e->prof.ev) hipEventDestroy(ev);
     for (void* p : e->allocs)
         if (p) hipFree(p);
     delete e;
@@ -280,6 +312,35 @@ extern "C" const char* q3_last_error(const q3_engine* e) { return e ? e->err.c_s
 extern "C" int32_t q3_seq_len(const q3_engine* e, int32_t seq) {
     if (!e || seq < 0 || seq >= e->cfg.max_batch) return -1;
     return e->h_len[seq];
+}
+
+// Algorithmic K/V bytes read by one decode step (all layers): 2 * Hkv * 128 * kv bytes per
+// visible slot and layer.
+static double kv_read_bytes(const q3_engine* e, int seq_base, int B) {
+    const q3_config& c = e->cfg;
+    double slots = 0;
+    for (int b = 0; b < B; ++b) slots += e->h_len[seq_base + b] + 1;
+    return slots * 2.0 * c.n_kv_heads * c.head_dim * e->kvbytes() * c.n_layers;
+}
+
+// Algorithmic bytes of one decode step: every weight once (the tied embedding counted once,
+// as the LM head), norm weights, K/V reads and writes, embedding rows and logits.
+static double step_bytes(const q3_engine* e, int seq_base, int B) {
+    const q3_config& c = e->cfg;
+    const double wb = (double)e->wbytes();
+    const double per_layer = (double)e->qkv_rows() * c.hidden + (double)c.hidden * c.n_heads * c.head_dim +
+                             3.0 * c.ffn * c.hidden;
+    const double weights = wb * (per_layer * c.n_layers + (double)c.vocab * c.hidden);
+    const double norms = 4.0 * (c.n_layers * (2.0 * c.hidden + 2.0 * c.head_dim) + c.hidden);
+    const double kv_write = (double)B * c.n_layers * 2.0 * c.n_kv_heads * c.head_dim * e->kvbytes();
+    const double rows = (double)B * (c.hidden * wb + 4.0 * c.vocab);
+    return weights + norms + kv_read_bytes(e, seq_base, B) + kv_write + rows;
+}
+
+static double attn_prefill_flops(int M, int t0, int Hq) {
+    // QK^T and PV over the visible slots: 2 * 2 * 128 flops per (row, slot, head)
+    const double vis = (double)M * t0 + (double)M * (M + 1) / 2.0;
+    return 4.0 * 128.0 * Hq * vis;
 }
 
 // ---------------------------------------------------------------------------------
@@ -295,31 +356,46 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     hipStream_t s = e->stream;
     int maxT = 0;
     for (int b = 0; b < B; ++b) maxT = std::max(maxT, e->h_len[seq_base + b] + 1);
+    const double wb = (double)e->wbytes();
+    prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
     HIPCHK(e, launch_embed(tokens, e->embed, wdt, e->x, B, d, V, e->d_err, s));
     for (int l = 0; l < c.n_layers; ++l) {
         const auto& L = e->layers[l];
         char* kcl = (char*)e->kc + (size_t)l * e->kv_layer_elems * e->kvbytes();
         char* vcl = (char*)e->vc + (size_t)l * e->kv_layer_elems * e->kvbytes();
         HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, 0, B, d, c.rms_eps, s));
+        prof_mark(e, Q3_PROF_GEMV, true, wb * e->qkv_rows() * d + 4.0 * B * (d + e->qkv_rows()));
         HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
+        prof_mark(e, Q3_PROF_GEMV, false);
         HIPCHK(e, launch_qk_rope_decode(e->qkv, positions, e->d_len, seq_base, B, L.q_norm, L.k_norm,
                                         e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq, Hq, Hkv, s));
+        prof_mark(e, Q3_PROF_ATTN_DECODE, true, kv_read_bytes(e, seq_base, B) / c.n_layers);
         HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, e->d_len, 1, seq_base, B, Hq, Hkv,
                                      maxT, e->attn_ws, e->o, s));
+        prof_mark(e, Q3_PROF_ATTN_DECODE, false);
+        prof_mark(e, Q3_PROF_GEMV, true, wb * d * Hq * 128 + 4.0 * B * (Hq * 128 + 2 * d));
         HIPCHK(e, launch_gemv(L.wo, wdt, e->o, e->x, d, Hq * 128, B, GEMV_RESID, s));
+        prof_mark(e, Q3_PROF_GEMV, false);
         HIPCHK(e, launch_rmsnorm(e->x, L.post_norm, e->h, 0, B, d, c.rms_eps, s));
+        prof_mark(e, Q3_PROF_GEMV, true, wb * 2.0 * F * d + 4.0 * B * (d + F));
         HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
+        prof_mark(e, Q3_PROF_GEMV, false);
+        prof_mark(e, Q3_PROF_GEMV, true, wb * d * F + 4.0 * B * (F + 2 * d));
         HIPCHK(e, launch_gemv(L.wd, wdt, e->a, e->x, d, F, B, GEMV_RESID, s));
+        prof_mark(e, Q3_PROF_GEMV, false);
     }
     if (want_logits) {
         float* lg = logits_out ? logits_out : e->logits;
         HIPCHK(e, launch_rmsnorm(e->x, e->final_norm, e->h, 0, B, d, c.rms_eps, s));
         HIPCHK(e, launch_fill_u64(e->amax, 0ull, B, s));
+        prof_mark(e, Q3_PROF_LMHEAD, true, wb * V * d + 4.0 * B * (d + V));
         HIPCHK(e, launch_lmhead(e->embed, wdt, e->h, lg, e->amax, V, d, B, e->d_err, s));
+        prof_mark(e, Q3_PROF_LMHEAD, false);
         e->cur_logits = lg;
         e->cur_rows = B;
     }
     HIPCHK(e, launch_len_advance(e->d_len, seq_base, B, 1, s));
+    prof_mark(e, Q3_PROF_DECODE_STEP, false);
     for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;
     return Q3_OK;
 }
@@ -333,10 +409,10 @@ static q3_status ensure_prefill_ws(q3_engine* e, int M) {
     e->pf_cap = 0;
     if (!(e->pf_x = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
     if (!(e->pf_qkv = (float*)e->alloc((size_t)M * e->qkv_rows() * 4))) return Q3_ERR_OOM;
-    if (!(e->pf_h = (uint16_t*)e->alloc((size_t)M * d * 2))) return Q3_ERR_OOM;
-    if (!(e->pf_q = (uint16_t*)e->alloc((size_t)M * HD * 2))) return Q3_ERR_OOM;
-    if (!(e->pf_o = (uint16_t*)e->alloc((size_t)M * HD * 2))) return Q3_ERR_OOM;
-    if (!(e->pf_a = (uint16_t*)e->alloc((size_t)M * F * 2))) return Q3_ERR_OOM;
+    if (!(e->pf_h = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
+    if (!(e->pf_q = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
+    if (!(e->pf_o = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
+    if (!(e->pf_a = (float*)e->alloc((size_t)M * F * 4))) return Q3_ERR_OOM;
     e->pf_cap = M;
     return Q3_OK;
 }
@@ -354,15 +430,25 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
         const auto& L = e->layers[l];
         uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
         uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 1, M, d, c.rms_eps, s));
-        HIPCHK(e, launch_gemm(e->pf_h, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d, GEMM_F32, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 0, M, d, c.rms_eps, s));
+        prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * e->qkv_rows() * d);
+        HIPCHK(e, launch_gemm(e->pf_h, 1, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d, GEMM_F32, s));
+        prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
                                          e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
+        prof_mark(e, Q3_PROF_ATTN_PREFILL, true, 0, attn_prefill_flops(M, t0, Hq));
         HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, s));
-        HIPCHK(e, launch_gemm(e->pf_o, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 1, M, d, c.rms_eps, s));
-        HIPCHK(e, launch_gemm(e->pf_h, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_BF16, s));
-        HIPCHK(e, launch_gemm(e->pf_a, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+        prof_mark(e, Q3_PROF_ATTN_PREFILL, false);
+        prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * Hq * 128);
+        HIPCHK(e, launch_gemm(e->pf_o, 1, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+        prof_mark(e, Q3_PROF_GEMM, false);
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 0, M, d, c.rms_eps, s));
+        prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * 2 * F * d);
+        HIPCHK(e, launch_gemm(e->pf_h, 1, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_F32, s));
+        prof_mark(e, Q3_PROF_GEMM, false);
+        prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * F);
+        HIPCHK(e, launch_gemm(e->pf_a, 1, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+        prof_mark(e, Q3_PROF_GEMM, false);
     }
     HIPCHK(e, launch_len_advance(e->d_len, seq, 1, M, s));
     e->h_len[seq] += M;
@@ -454,5 +540,35 @@ extern "C" q3_status q3_sync(q3_engine* e) {
     HIPCHK(e, hipStreamSynchronize(e->stream));
     if (flags & Q3_DEVERR_TOKEN) return e->fail(Q3_ERR_TOKEN, "a token id outside [0, vocab) reached the device");
     if (flags & Q3_DEVERR_NONFINITE) return e->fail(Q3_ERR_NUMERIC, "non-finite logits");
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_profile_begin(q3_engine* e, int32_t kind) {
+    if (!e) return Q3_ERR_ARG;
+    if (kind < Q3_PROF_OFF || kind > Q3_PROF_ATTN_PREFILL) return e->fail(Q3_ERR_ARG, "bad profile kind");
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    e->prof.kind = kind;
+    e->prof.used = 0;
+    e->prof.bytes = e->prof.flops = 0;
+    e->prof.launches = 0;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, double* bytes,
+                                    double* flops) {
+    if (!e) return Q3_ERR_ARG;
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    double ms = 0;
+    for (size_t i = 0; i + 1 < e->prof.used; i += 2) {
+        float t = 0;
+        HIPCHK(e, hipEventElapsedTime(&t, e->prof.ev[i], e->prof.ev[i + 1]));
+        ms += t;
+    }
+    if (total_ms) *total_ms = ms;
+    if (launches) *launches = e->prof.launches;
+    if (bytes) *bytes = e->prof.bytes;
+    if (flops) *flops = e->prof.flops;
+    e->prof.kind = -1;
+    e->prof.used = 0;
     return Q3_OK;
 }

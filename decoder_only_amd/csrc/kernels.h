@@ -23,11 +23,11 @@ hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, con
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
                                  const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
                                  int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s);
-// Prefill rows of one sequence at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] bf16.
+// Prefill rows of one sequence at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] float32.
 // kc/vc: cache of this (layer, sequence): [Hkv][t_cap][128] bf16.
 hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
                                   const float* k_norm, const float* inv_freq, float eps,
-                                  uint16_t* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  float* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
                                   int Hkv, hipStream_t s);
 // lens[seq_base + b] += by for b < B.
 hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s);
@@ -51,15 +51,17 @@ hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, in
                               int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
                               int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s);
 
-// ---- gemm.hip (prefill projections on MFMA: bf16 A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
-enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_BF16 = 2, GEMM_BF16 = 3 };
-hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, void* C, int M, int N, int K, int epi,
+// ---- gemm.hip (prefill projections on MFMA: A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
+// A is bf16 (a_f32 = 0) or float32 split into bf16 hi + lo parts (a_f32 = 1, two MFMAs per tile).
+enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3 };
+hipError_t launch_gemm(const void* A, int a_f32, const uint16_t* W, void* C, int M, int N, int K, int epi,
                        hipStream_t s);
 
 // ---- attn_prefill.hip (causal GQA flash attention on MFMA)
-// q: [Hq][M][128] bf16 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16; o: [M][Hq*128] bf16.
-hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, uint16_t* o, hipStream_t s);
+// q: [Hq][M][128] float32 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16;
+// o: [M][Hq*128] float32.
+hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
+                               int M, int t0, int Hq, int Hkv, float* o, hipStream_t s);
 
 // ---- sample.hip
 hipError_t launch_argmax_rows(const float* logits, unsigned long long* amax, int V, int B,

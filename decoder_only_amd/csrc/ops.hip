@@ -42,11 +42,13 @@ extern "C" q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, 
     return st(launch_gemv(W, w_dtype == Q3_BF16 ? DT_BF16 : DT_F32, x, y, N, K, B, epilogue, (hipStream_t)stream));
 }
 
-extern "C" q3_status q3_op_gemm(const uint16_t* A, const uint16_t* W, void* C, int32_t M, int32_t N, int32_t K,
-                                int32_t epilogue, void* stream) {
-    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 3) return Q3_ERR_ARG;
+extern "C" q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
+                                int32_t K, int32_t epilogue, void* stream) {
+    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 3 ||
+        (a_dtype != Q3_F32 && a_dtype != Q3_BF16))
+        return Q3_ERR_ARG;
     if (N % 128 || K % 64) return Q3_ERR_SHAPE;
-    return st(launch_gemm(A, W, C, M, N, K, epilogue, (hipStream_t)stream));
+    return st(launch_gemm(A, a_dtype == Q3_F32, W, C, M, N, K, epilogue, (hipStream_t)stream));
 }
 
 extern "C" q3_status q3_op_qk_norm_rope(const float* qkv, const float* q_norm, const float* k_norm,
@@ -81,9 +83,9 @@ extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, cons
                                  n_kv_heads, max_len, (float*)sc.p, o, s));
 }
 
-extern "C" q3_status q3_op_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+extern "C" q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                         int32_t t_cap, int32_t M, int32_t t0, int32_t n_heads, int32_t n_kv_heads,
-                                        uint16_t* o, void* stream) {
+                                        float* o, void* stream) {
     if (!q || !k_cache || !v_cache || !o || M < 0 || t0 < 0 || t_cap <= 0 || (int64_t)t0 + M > t_cap) return Q3_ERR_ARG;
     if (n_heads != 2 * n_kv_heads) return Q3_ERR_SHAPE;
     return st(launch_attn_prefill(q, k_cache, v_cache, t_cap, M, t0, n_heads, n_kv_heads, o, (hipStream_t)stream));

@@ -22,12 +22,13 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
     "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import",
-    "q3_seq_len", "q3_sync", "q3_last_error", "q3_free",
+    "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
     "q3_op_attn_prefill", "q3_op_sample",
 ]
 GEMV_STORE, GEMV_RESID, GEMV_SWIGLU = 0, 1, 2
-GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_BF16, GEMM_BF16 = 0, 1, 2, 3
+PROF_DECODE_STEP, PROF_GEMV, PROF_LMHEAD, PROF_ATTN_DECODE, PROF_GEMM, PROF_ATTN_PREFILL = range(6)
+GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_F32, GEMM_BF16 = 0, 1, 2, 3
 
 
 class Q3Error(RuntimeError):
@@ -73,9 +74,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
         "q3_free": ([vp], None),
+        "q3_profile_begin": ([vp, i32], i32),
+        "q3_profile_end": ([vp, POINTER(ctypes.c_double), POINTER(c_int64), POINTER(ctypes.c_double),
+                            POINTER(ctypes.c_double)], i32),
         "q3_op_rmsnorm": ([vp, vp, vp, i32, i32, i32, f32, vp], i32),
         "q3_op_gemv": ([vp, i32, vp, vp, i32, i32, i32, i32, vp], i32),
-        "q3_op_gemm": ([vp, vp, vp, i32, i32, i32, i32, vp], i32),
+        "q3_op_gemm": ([vp, i32, vp, vp, i32, i32, i32, i32, vp], i32),
         "q3_op_qk_norm_rope": ([vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, i32, i32, vp], i32),
         "q3_op_attn_decode": ([vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, vp, vp], i32),
         "q3_op_attn_prefill": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, vp], i32),
@@ -200,6 +204,16 @@ class Engine:
     def sync(self) -> None:
         _check(load_library().q3_sync(self._h), "q3_sync", self._h)
 
+    def profile_begin(self, kind: int) -> None:
+        _check(load_library().q3_profile_begin(self._h, kind), "q3_profile_begin", self._h)
+
+    def profile_end(self) -> dict:
+        ms, n = ctypes.c_double(), c_int64()
+        by, fl = ctypes.c_double(), ctypes.c_double()
+        _check(load_library().q3_profile_end(self._h, byref(ms), byref(n), byref(by), byref(fl)),
+               "q3_profile_end", self._h)
+        return {"ms": ms.value, "launches": n.value, "bytes": by.value, "flops": fl.value}
+
 
 # ------------------------------------------------------------------------- op level
 
@@ -220,11 +234,13 @@ def op_gemv(W, x, y, epilogue: int = GEMV_STORE) -> None:
 
 
 def op_gemm(A, W, C, epilogue: int = GEMM_F32) -> None:
+    """A: bf16 or float32 [M, K]; W: bf16 [N, K]."""
     import torch
     M, K = A.shape
     N = W.shape[0]
-    _check(load_library().q3_op_gemm(_ptr(A, torch.bfloat16), _ptr(W, torch.bfloat16), _ptr(C), M, N, K,
-                                     epilogue, _stream()), "q3_op_gemm")
+    adt = F32 if A.dtype == torch.float32 else BF16
+    _check(load_library().q3_op_gemm(_ptr(A, (torch.bfloat16, torch.float32)), adt, _ptr(W, torch.bfloat16),
+                                     _ptr(C), M, N, K, epilogue, _stream()), "q3_op_gemm")
 
 
 def op_qk_norm_rope(qkv, q_norm, k_norm, positions, slots, n_heads, n_kv_heads, eps, theta,
@@ -252,9 +268,9 @@ def op_attn_prefill(q, k_cache, v_cache, t0: int, o) -> None:
     import torch
     Hq, M, _ = q.shape
     Hkv, t_cap, _ = k_cache.shape
-    _check(load_library().q3_op_attn_prefill(_ptr(q, torch.bfloat16), _ptr(k_cache, torch.bfloat16),
+    _check(load_library().q3_op_attn_prefill(_ptr(q, torch.float32), _ptr(k_cache, torch.bfloat16),
                                              _ptr(v_cache, torch.bfloat16), t_cap, M, t0, Hq, Hkv,
-                                             _ptr(o, torch.bfloat16), _stream()), "q3_op_attn_prefill")
+                                             _ptr(o, torch.float32), _stream()), "q3_op_attn_prefill")
 
 
 def op_sample(logits, temperature: float, top_p: float, uniforms, out) -> None:

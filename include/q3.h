@@ -143,6 +143,26 @@ q3_status q3_sync(q3_engine* e);
 /* Text describing the last error on this engine (never NULL). */
 const char* q3_last_error(const q3_engine* e);
 
+/* Event timing of one kernel family (section "Tracing" of the engine's design):
+ * between q3_profile_begin and q3_profile_end, every launch of that family on the
+ * engine's stream is bracketed by a pair of hipEvents. q3_profile_end synchronises and
+ * returns the summed kernel time in milliseconds, the number of launches, and the
+ * algorithmic bytes and flops of those launches (weights, K/V and activations each
+ * counted once; decode-step bytes count the tied embedding once, as the LM head).
+ * Any output pointer may be NULL. */
+typedef enum {
+    Q3_PROF_OFF = -1,
+    Q3_PROF_DECODE_STEP = 0,   /* one whole decode step (all layers, LM head) */
+    Q3_PROF_GEMV = 1,          /* decode projections (QKV, o, gate/up, down) */
+    Q3_PROF_LMHEAD = 2,        /* decode LM head + argmax */
+    Q3_PROF_ATTN_DECODE = 3,   /* decode attention (split-K + combine) */
+    Q3_PROF_GEMM = 4,          /* prefill projections on the matrix cores */
+    Q3_PROF_ATTN_PREFILL = 5   /* prefill flash attention */
+} q3_prof_kind;
+q3_status q3_profile_begin(q3_engine* e, int32_t kind);
+q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, double* bytes,
+                         double* flops);
+
 /* Release all device memory of the engine. NULL is allowed. */
 void q3_free(q3_engine* e);
 

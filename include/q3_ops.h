@@ -32,12 +32,14 @@ q3_status q3_op_rmsnorm(const float* x, const float* w, void* out, int32_t out_d
 q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, int32_t N, int32_t K,
                      int32_t B, int32_t epilogue, void* stream);
 
-/* Prefill projection on the matrix cores: C = A W^T, A bf16 [M][K], W bf16 [N][K]
- * (N % 128 == 0, K % 64 == 0), float32 accumulation. epilogue 0: C float32 [M][N];
- * 1: C float32 [M][N] += result; 2: SwiGLU (W packed as for q3_op_gemv), C bf16 [M][N/2];
- * 3: C bf16 [M][N]. */
-q3_status q3_op_gemm(const uint16_t* A, const uint16_t* W, void* C, int32_t M, int32_t N, int32_t K,
-                     int32_t epilogue, void* stream);
+/* Prefill projection on the matrix cores: C = A W^T, W bf16 [N][K] (N % 128 == 0,
+ * K % 64 == 0), float32 accumulation. A [M][K] is bf16 (a_dtype Q3_BF16), or float32
+ * (Q3_F32): then each element enters as a bf16 hi + lo pair, hi = bf16(a),
+ * lo = bf16(a - hi), two matrix-core products per tile (~2^-17 relative error).
+ * epilogue 0: C float32 [M][N]; 1: C float32 [M][N] += result; 2: SwiGLU (W packed as
+ * for q3_op_gemv), C float32 [M][N/2]; 3: C bf16 [M][N]. */
+q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
+                     int32_t K, int32_t epilogue, void* stream);
 
 /* Per-head QK-norm and RoPE of one decode row per sequence, plus the KV append
  * (Steps 4 and 5). qkv: float32 [B][(n_heads + 2 n_kv_heads) * 128] (q heads, k heads,
@@ -59,11 +61,12 @@ q3_status q3_op_attn_decode(const float* q, const void* k_cache, const void* v_c
                             int32_t n_kv_heads, int32_t max_len, float* o, void* stream);
 
 /* Causal prefill attention (Step 5) of M new rows at slots t0 .. t0+M-1 of one sequence:
- * q: bf16 [n_heads][M][128] (rotated); k_cache, v_cache: bf16 [n_kv_heads][t_cap][128] with
- * slots 0 .. t0+M-1 filled; row i sees slots j <= t0 + i. o: bf16 [M][n_heads * 128]. */
-q3_status q3_op_attn_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+ * q: float32 [n_heads][M][128] (rotated); k_cache, v_cache: bf16 [n_kv_heads][t_cap][128]
+ * with slots 0 .. t0+M-1 filled; row i sees slots j <= t0 + i. o: float32 [M][n_heads * 128].
+ * q and the softmax weights enter the matrix-core products as bf16 hi + lo pairs. */
+q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
                              int32_t t_cap, int32_t M, int32_t t0, int32_t n_heads, int32_t n_kv_heads,
-                             uint16_t* o, void* stream);
+                             float* o, void* stream);
 
 /* Sampling of B rows of float32 logits [B][V] (Step 8), same rule as q3_sample. */
 q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, float temperature, float top_p,

@@ -40,12 +40,29 @@ def compare(step: int, row: int, got: np.ndarray, ref: np.ndarray) -> StepStat:
                     int(np.argmax(got)) == int(np.argmax(ref)), top2_gap(ref))
 
 
-def failures(stats: List[StepStat]) -> List[StepStat]:
-    return [s for s in stats if s.max_abs > MAX_ABS or s.rel > REL_L2 or not s.argmax_ok]
+def failures(stats: List[StepStat], greedy: bool = True) -> List[StepStat]:
+    """Steps outside the logits bar; with greedy decoding the argmax must agree as well
+    (with sampling the argmax is not a decision of the method: the sampled tokens are
+    checked separately)."""
+    return [s for s in stats
+            if s.max_abs > MAX_ABS or s.rel > REL_L2 or (greedy and not s.argmax_ok)]
 
 
-def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None) -> List[StepStat]:
-    """Prefill a seeded prompt, then `steps` greedy decode steps, batch 1."""
+@dataclasses.dataclass
+class SamplerStat:
+    step: int
+    oracle_token: int
+    gpu_token: int          # engine's sampler on the oracle's logits
+    own_token: int          # engine's sampler on its own logits (reported, not gated)
+    margin: float
+
+
+def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
+               sampler_stats: List[SamplerStat] | None = None) -> List[StepStat]:
+    """Prefill a seeded prompt, then `steps` decode steps, batch 1, teacher-forced with the
+    oracle's tokens (greedy at temperature 0, else drawn with the workload's uniforms).
+    With sampling, the engine's sampler is also run on the oracle's own logits and must
+    return the oracle's token whenever the decision margin exceeds 1e-9."""
     import torch
     from decoder_only_amd import q3
 
@@ -56,17 +73,32 @@ def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None) -> 
     announce("e2e", w.name, w.n_layers, w.vocab, w.weight_dtype, prompt_len, steps)
     eng = q3.Engine(q3.config(w, 1, max_seq), weights)
     prompt = synth.prompt_tokens(w, prompt_len)
+    T, p = float(np.float32(w.temperature)), float(np.float32(w.top_p))
+    us = synth.uniforms(w, steps + 1)
+    u_dev = torch.from_numpy(us).cuda()
     ref = model.forward(prompt, cache, 0)
     logits = torch.empty(1, w.vocab, dtype=torch.float32, device="cuda")
+    ref_dev = torch.empty(1, w.vocab, dtype=torch.float32, device="cuda")
     eng.prefill(0, torch.from_numpy(prompt).cuda(), logits)
     stats = []
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    chk = torch.empty(1, dtype=torch.int32, device="cuda")
     for step in range(steps + 1):
         eng.sync()
         stats.append(compare(step, 0, logits[0].cpu().numpy(), ref))
+        if T == 0:
+            nxt = int(np.argmax(ref))
+        else:
+            nxt = oracle.sample(ref, T, p, float(us[step]))
+            if sampler_stats is not None:
+                eng.sample(chk, T, p, u_dev[step:step + 1], logits=logits)
+                own = int(chk.item())
+                ref_dev.copy_(torch.from_numpy(ref).view(1, -1))
+                eng.sample(chk, T, p, u_dev[step:step + 1], logits=ref_dev)
+                sampler_stats.append(SamplerStat(step, nxt, int(chk.item()), own,
+                                                 oracle.sample_margin(ref, T, p, float(us[step]))))
         if step == steps:
             break
-        nxt = int(np.argmax(ref))
         ref = model.forward([nxt], cache, prompt_len + step)
         tok.fill_(nxt)
         eng.decode_step(tok, None, logits)

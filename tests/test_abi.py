@@ -108,9 +108,10 @@ def test_null_engine_and_op_argument_errors(lib):
     assert lib.q3_last_error(None) == b"engine is NULL"
     lib.q3_free(None)
     fake = ctypes.c_void_p(0x1000)    # never dereferenced: shape checks come first
-    assert lib.q3_op_gemm(fake, fake, fake, 4, 100, 64, 0, None) == -2          # N % 128
-    assert lib.q3_op_gemm(fake, fake, fake, 4, 128, 60, 0, None) == -2          # K % 64
-    assert lib.q3_op_gemm(None, fake, fake, 4, 128, 64, 0, None) == -1
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 100, 64, 0, None) == -2       # N % 128
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 60, 0, None) == -2       # K % 64
+    assert lib.q3_op_gemm(None, 1, fake, fake, 4, 128, 64, 0, None) == -1
+    assert lib.q3_op_gemm(fake, 5, fake, fake, 4, 128, 64, 0, None) == -1       # bad A dtype
     assert lib.q3_op_gemv(fake, 1, fake, fake, 6, 12, 1, 0, None) == -2         # K % 8
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 7, 4, fake, None) == -2
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 8, 17, fake, None) == -1

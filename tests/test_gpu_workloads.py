@@ -1,0 +1,147 @@
+"""End-to-end teacher-forced parity at the full Qwen3-0.6B shape (28 layers, vocab 151936,
+bf16 weights and KV cache) on the five workloads' settings. Bar per step and row: logits
+max-abs <= 2e-2 and relative L2 <= 1e-3 against the float32 oracle, identical argmax;
+sampled tokens identical when the engine's sampler is given the oracle's logits and the
+same uniform (unless the decision is within 1e-9 of a boundary)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from e2e import MAX_ABS, REL_L2, SamplerStat, compare, failures, run_single
+from gpu_util import announce, rel_l2
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _summary(stats):
+    worst = max(stats, key=lambda s: s.rel)
+    return (f"{len(stats)} steps; worst rel-L2 {worst.rel:.2e} at step {worst.step}; "
+            f"max-abs {max(s.max_abs for s in stats):.2e}; "
+            f"argmax agreement {sum(s.argmax_ok for s in stats)}/{len(stats)}")
+
+
+@pytest.mark.timeout(900)
+def test_bs1_short_prompt_greedy():
+    """5-token prompt, 128 greedy decode steps."""
+    w = synth.workload("bs1_short")
+    stats = run_single(w, w.prompt_len, w.decode_steps)
+    print(_summary(stats))
+    assert not failures(stats), failures(stats)[:5]
+
+
+@pytest.mark.timeout(900)
+def test_prefill_2048_then_sampled_decode():
+    """2048-token prompt (matrix-core prefill), 256 decode steps at T=0.7, top-p 0.9."""
+    w = synth.workload("prefill2k")
+    samp = []
+    stats = run_single(w, w.prompt_len, w.decode_steps, sampler_stats=samp)
+    print(_summary(stats))
+    decided = [s for s in samp if s.margin > 1e-9]
+    print(f"sampler on oracle logits: {sum(s.gpu_token == s.oracle_token for s in decided)}/{len(decided)} "
+          f"identical; on own logits: {sum(s.own_token == s.oracle_token for s in samp)}/{len(samp)}")
+    assert not failures(stats, greedy=False), failures(stats, greedy=False)[:5]
+    assert all(s.gpu_token == s.oracle_token for s in decided), [s for s in decided if s.gpu_token != s.oracle_token]
+
+
+@pytest.mark.timeout(900)
+def test_batch64_prefilled_cache_greedy():
+    """64 sequences with 4096 pre-filled K/V slots at distinct positions, 64 greedy steps.
+    Rows are independent; the oracle follows a seeded subset of rows whose caches come from
+    the seeded generator, the other rows get random caches of the same shape."""
+    import torch
+    from decoder_only_amd import q3
+    w = synth.workload("bs64_ctx4k")
+    B, T0, steps = w.batch, w.prefilled, w.decode_steps
+    rows = [0, 21, 42, 63]
+    weights = synth.make_weights(w)
+    model = oracle.Model(oracle.Config.from_workload(w), weights)
+    announce("e2e bs64", rows)
+    eng = q3.Engine(q3.config(w, B, T0 + steps), weights)
+    caches = []
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    for b in range(B):
+        c = model.new_cache(T0 + steps) if b in rows else None
+        for layer in range(w.n_layers):
+            if b in rows:
+                kb, vb = synth.batch_kv(w, layer, b)
+                eng.kv_import(b, layer, kb, vb, T0)
+                c.load(layer, oracle.bf16_bits_to_f32(kb), oracle.bf16_bits_to_f32(vb), T0)
+            else:
+                kv = torch.randn(2, w.n_kv_heads, T0, w.head_dim, generator=gen, device="cuda").bfloat16()
+                eng.kv_import(b, layer, kv[0].contiguous(), kv[1].contiguous(), T0)
+        if c is not None:
+            c.length = T0
+            caches.append(c)
+    offsets = synth.batch_offsets(w)
+    toks = synth.batch_first_tokens(w)
+    logits = torch.empty(B, w.vocab, dtype=torch.float32, device="cuda")
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    stats = []
+    for t in range(steps):
+        pos = (offsets + T0 + t).astype(np.int32)
+        eng.decode_step(torch.from_numpy(toks).cuda(), torch.from_numpy(pos).cuda(), logits)
+        eng.sample(out, 0.0)
+        ref = model.forward_batch(toks[rows], caches, pos[rows])
+        eng.sync()
+        got = logits.cpu().numpy()
+        for i, b in enumerate(rows):
+            stats.append(compare(t, b, got[b], ref[i]))
+        toks = out.cpu().numpy().copy()          # unchecked rows follow their own argmax
+        toks[rows] = np.argmax(ref, axis=-1)     # checked rows are teacher-forced
+    eng.close()
+    print(_summary(stats))
+    assert not failures(stats), failures(stats)[:5]
+
+
+@pytest.mark.timeout(900)
+def test_prefill_32768_then_sampled_decode_against_stored_oracle():
+    """32768-token prompt, 512 decode steps at T=1.0, top-p 0.95, teacher-forced with the
+    oracle's tokens stored by tests/golden/make_goldens.py (the oracle's 32K prefill takes
+    many minutes on a CPU). Per step: the logits at 256 probe ids and the oracle's top 32,
+    relative L2 estimated from the probes (exact at step 0), argmax and norm."""
+    import torch
+    from decoder_only_amd import q3
+    path = os.path.join(GOLDEN, "prefill32k.npz")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle outputs not generated")
+    g = np.load(path)
+    w = synth.workload("prefill32k")
+    n_steps = len(g["tokens"]) - 1
+    announce("e2e prefill32k", n_steps)
+    weights = synth.make_weights(w)
+    eng = q3.Engine(q3.config(w, 1, w.prompt_len + n_steps + 1), weights)
+    prompt = torch.from_numpy(synth.prompt_tokens(w)).cuda()
+    logits = torch.empty(1, w.vocab, dtype=torch.float32, device="cuda")
+    eng.prefill(0, prompt, logits)
+    probe = g["probe_ids"]
+    V = w.vocab
+    bad = []
+    chk = torch.empty(1, dtype=torch.int32, device="cuda")
+    for s in range(n_steps + 1):
+        eng.sync()
+        got = logits[0].cpu().numpy()
+        if s == 0:
+            full = g["full_logits0"]
+            assert np.abs(got - full).max() <= MAX_ABS and rel_l2(got, full) <= REL_L2, (
+                np.abs(got - full).max(), rel_l2(got, full))
+            ref_dev = torch.from_numpy(full).cuda().view(1, -1)
+            u0 = torch.tensor([g["u"][0]], dtype=torch.float32, device="cuda")
+            eng.sample(chk, float(g["temperature"]), float(g["top_p"]), u0, logits=ref_dev)
+            if g["margin"][0] > 1e-9:
+                assert int(chk.item()) == int(g["tokens"][0])
+        d_probe = got[probe] - g["probe_vals"][s]
+        d_top = got[g["top_ids"][s]] - g["top_vals"][s]
+        mx = max(np.abs(d_probe).max(), np.abs(d_top).max())
+        rel_est = np.sqrt(V / len(probe) * np.sum(d_probe.astype(np.float64) ** 2)) / g["norm"][s]
+        am_ok = int(np.argmax(got)) == int(g["argmax"][s]) or g["gap"][s] < 1e-6
+        if mx > MAX_ABS or rel_est > REL_L2 or not am_ok:
+            bad.append((s, float(mx), float(rel_est), am_ok))
+        if s == n_steps:
+            break
+        eng.decode_step(torch.tensor([int(g["tokens"][s])], dtype=torch.int32, device="cuda"), None, logits)
+    eng.close()
+    assert not bad, bad[:5]
