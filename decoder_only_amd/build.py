@@ -25,6 +25,7 @@ SOURCES = [
     "gemm.hip",
     "attn_prefill.hip",
     "sample.hip",
+    "decode_mega.hip",
     "engine.hip",
     "ops.hip",
 ]

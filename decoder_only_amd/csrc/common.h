@@ -9,6 +9,7 @@
 // Sticky device error bits (reported by q3_sync).
 #define Q3_DEVERR_TOKEN 1u
 #define Q3_DEVERR_NONFINITE 2u
+#define Q3_DEVERR_SYNC 4u       // a cross-workgroup wait of the persistent decode kernel timed out
 
 namespace q3 {
 
@@ -30,23 +31,50 @@ __device__ __forceinline__ float ldw(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ void stkv(bf16* p, size_t i, float v) { p[i] = f2bf(v); }
 __device__ __forceinline__ void stkv(float* p, size_t i, float v) { p[i] = v; }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane reductions with DPP moves inside rows of 16 lanes (no LDS round trip) and
+// v_readlane across rows. DPP controls: quad_perm [1,0,3,2] and [2,3,0,1] swap neighbours
+// at distance 1 and 2; row_half_mirror / row_mirror reverse 8- and 16-lane groups, which
+// pair each half with the other one.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over aligned groups of 8 / 16 lanes; every lane of the group gets the sum. The lanes
+// of a group must be active together.
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    v += dpp_mov<kDppRowHalfMirror>(v);
     return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+    v = sum8(v);
+    v += dpp_mov<kDppRowMirror>(v);
+    return v;
+}
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+    return v;
+}
+
+// Whole-wave sum / max (all 64 lanes active); the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum16(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-// Sum over aligned groups of 16 lanes.
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = max16(v);
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 // Order-preserving map float32 -> uint32 (larger float -> larger key).

@@ -1,0 +1,749 @@
+// Persistent decode step: the whole forward pass of one decode step -- embedding, every
+// layer, final RMSNorm, tied LM head with fused argmax -- in ONE cooperative launch of
+// 256 workgroups (one per CU). ("Inside an LLM: Pure Python Inference for Qwen3-0.6B on
+// MLX", Steps 2-8; Step 9's decode loop runs one launch per generated token.)
+//
+// Why: a decode step streams 1.19 GB of bf16 weights (150 us at 8 TB/s) through ~170
+// small dependent operations; as separate kernels each costs ~4-8 us of launch and ramp.
+//
+// Synchronisation is dataflow, not barriers: every value one workgroup hands to another
+// is a 64-bit word (float bits | launch tag << 32) written with one coherent agent-scope
+// atomic store; the consumer polls exactly the words it needs until all carry this
+// launch's tag. One memory round trip thus carries both the data and the "it is ready"
+// signal (a grid barrier costs ~2 us on MI355X, plus a store acknowledgement before it
+// and a reload after it). Each layer has its own exchange buffers, so a word is written
+// once per launch; words left by an earlier or aborted launch carry an older tag and are
+// simply not ready yet.
+//
+// Per layer, for each row b (hops = dependent exchanges):
+//   A  poll x (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]              -> QKV words
+//   B  workgroup (g, j), kv group g = query heads 2g, 2g+1, j < 32: poll the group's
+//      q/k/v (512) -> QK-norm + RoPE -> KV append (j == 0) -> attention of both heads,
+//      recomputed by the 32 workgroups of the group -> rows 32j..32j+31 of
+//      Wo[:, 256g:256g+256] . o                                     -> P[g] words
+//      (long context: split-K partials per (group, chunk), a combine per group, then
+//       the O-projection partial from the combined output)
+//   R  rows 4w..4w+3: x' = x + P[0] + ... + P[7] (fixed order)        -> X' words
+//   C  poll x' (1024) -> RMSNorm -> gate/up rows of 12 SwiGLU columns -> A words
+//   D  poll a (3072) -> rows 4w..4w+3: x'' = x' + Wd a                -> next x words
+// then poll x, RMSNorm, 594 rows of the tied LM head per workgroup; each workgroup
+// writes its packed (logit, id) maximum per row, reduced by the sampling kernel. Each workgroup issues the loads of its next weight slice
+// right after finishing a phase, so HBM streaming overlaps the waiting.
+// Fixed shape: hidden 1024, 16 query / 8 kv heads of 128, FFN 3072, bf16 weights and KV
+// cache, 1..4 rows.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+namespace {
+
+constexpr int D = 1024, HQ = 16, HKV = 8, DH = 128, F = 3072, NQKV = 4096;
+constexpr int NWG = 256, NT = 256;
+constexpr int BMAX = 4;
+constexpr int PART = 2 + DH;     // (max, sum, acc[128]) per (chunk, head)
+constexpr int MAXCH = 32;        // attention chunks per kv group (long context)
+constexpr int SHORT_T = 256;     // visible slots up to which every group workgroup attends itself
+typedef unsigned long long u64;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// words per (layer, row) in each exchange buffer
+constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_XP = D, W_A = F, W_O = (size_t)HKV * 2 * DH;
+constexpr size_t W_PT = (size_t)HKV * MAXCH * 2 * PART;
+
+__device__ __forceinline__ void put(u64* p, float v, unsigned tag) {
+    __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 8 bf16 (one 16-byte chunk) dotted with 8 floats.
+__device__ __forceinline__ float dot8(const u32x4 w, const float* x) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s += __uint_as_float(w[i] << 16) * x[2 * i];
+        s += __uint_as_float(w[i] & 0xFFFF0000u) * x[2 * i + 1];
+    }
+    return s;
+}
+
+// Loads through global-address-space pointers: the weight pointers come from a table in
+// memory, so the compiler cannot infer their address space and would emit flat loads,
+// which also count against the LDS wait counter -- every LDS access or lane shuffle would
+// then wait for all weight prefetches in flight.
+#define GLOBAL_AS __attribute__((address_space(1)))
+__device__ __forceinline__ u32x4 ldw16(const bf16* p) { return *(const GLOBAL_AS u32x4*)(p); }
+__device__ __forceinline__ f32x4 ldf4(const float* p) { return *(const GLOBAL_AS f32x4*)(p); }
+__device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS float*)(p); }
+
+// Poll words src[idx(i)], i < n (n <= 16 * 256), into dst[i] until every one carries
+// `tag`. Thread t owns i = t + 256 k and re-reads only what it still misses. Returns
+// false after ~0.1 s without completion (the caller then leaves the kernel).
+template <typename IDX>
+__device__ __forceinline__ bool poll(const u64* src, IDX idx, int n, float* dst, unsigned tag, unsigned* err) {
+    unsigned todo = 0;
+    for (int k = 0; k < 16 && threadIdx.x + NT * k < n; ++k) todo |= 1u << k;
+    int spins = 0;
+    for (;;) {
+        if (todo) {
+            u64 v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (todo & (1u << k))
+                    v[k] = __hip_atomic_load(src + idx(threadIdx.x + NT * k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if ((todo & (1u << k)) && (unsigned)(v[k] >> 32) == tag) {
+                    dst[threadIdx.x + NT * k] = __uint_as_float((unsigned)v[k]);
+                    todo &= ~(1u << k);
+                }
+            }
+        }
+        if (__syncthreads_and(todo == 0)) return true;
+        if (++spins > (1 << 16)) {
+            if (threadIdx.x == 0) atomicOr(err, Q3_DEVERR_SYNC);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+struct Contig {
+    __device__ __forceinline__ size_t operator()(int i) const { return (size_t)i; }
+};
+
+struct Smem {
+    float act[BMAX][F];            // activations of the current phase (x, h, a)
+    float x0[BMAX][4];             // layer input x at this workgroup's residual rows 4w..4w+3
+    float xr[BMAX][4];             // x' at those rows
+    float red[BMAX][16];           // block reductions
+    float in[BMAX][4 * DH];        // polled group inputs: q (2 x 128), k (128), v (128)
+    float q[2][DH];                // rotated queries of the current group
+    float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
+    float o[BMAX][2 * DH];         // attention output of the group, per row
+    float wm[16][2][PART];         // attention state per (wave, 16-lane key group)
+    float att[2][PART];            // merged attention state (max, sum, acc) per head
+    float part[MAXCH * 2 * PART];  // polled chunk partials (long context combine)
+    float pr[BMAX * HKV * 4];      // polled O-projection partials of the residual rows
+    float gu[24][BMAX];            // gate/up results
+    MegaLayer layers[kMegaMaxLayers];
+};
+
+// Per-thread values loaded together with a phase's weight slice: the RMSNorm weights of
+// its 4 elements, and for phase B the QK-norm weights of its RoPE pair and the frequency.
+struct Pre {
+    f32x4 nw;
+    float qk1, qk2, fr;
+};
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ int clamp_tok(const MegaParams& p, int b) {
+    const int t = p.tokens[b];
+    return (t >= 0 && t < p.vocab) ? t : 0;
+}
+
+// act[b][:] = act[b][:] * rsqrt(mean(act[b]^2) + eps) * w  (act holds x on entry;
+// wv = w[4t .. 4t+3] for thread t)
+__device__ __forceinline__ void rmsnorm_act(const MegaParams& p, Smem& sm, int B, const f32x4 wv) {
+    const int k = threadIdx.x * 4;
+    for (int b = 0; b < B; ++b) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.act[b][k]);
+        float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        ss = block_sum256(ss, sm.red[b]);
+        const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.act[b][k + e] = (v[e] * r) * wv[e];
+    }
+    __syncthreads();
+}
+
+// QK-norm + RoPE of one 128-wide head held by a wave: lane i owns the pair (i, i + 64).
+__device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, float eps, int pos) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+    x1 = (x1 * r) * pre.qk1;
+    x2 = (x2 * r) * pre.qk2;
+    const float ang = __fmul_rn((float)pos, pre.fr);
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, sn));
+    const float y2 = __fadd_rn(__fmul_rn(x1, sn), __fmul_rn(x2, c));
+    x1 = y1;
+    x2 = y2;
+}
+
+// Polled q/k/v of group g (sm.in[b]) -> rotated q, bf16-rounded new k, v in shared memory;
+// `append` writes k, v into the cache at `slot`.
+__device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const Pre& pre, int layer, int b, int g, int pos,
+                           int slot, bool append) {
+    const int wid = threadIdx.x >> 6, i = threadIdx.x & 63;
+    const float* in = sm.in[b];                     // [q0 128 | q1 128 | k 128 | v 128]
+    float x1 = in[wid * DH + i], x2 = in[wid * DH + i + 64];
+    if (wid < 3) norm_rope(x1, x2, pre, p.eps, pos);
+    if (wid < 2) {
+        sm.q[wid][i] = x1;
+        sm.q[wid][i + 64] = x2;
+    } else {
+        const bf16 h1 = f2bf(x1), h2 = f2bf(x2);
+        float* dst = wid == 2 ? sm.kn : sm.vn;
+        dst[i] = bf2f(h1);
+        dst[i + 64] = bf2f(h2);
+        if (append) {
+            bf16* cache = (wid == 2 ? p.kc : p.vc) + (size_t)layer * p.kv_layer_elems +
+                          (size_t)(p.seq_base + b) * p.kv_seq_elems + ((size_t)g * p.t_cap + slot) * DH;
+            cache[i] = h1;
+            cache[i + 64] = h2;
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void merge_state(float& m, float& l, float* a, float m2, float l2, const float* a2) {
+    if (l2 == 0.f) return;
+    if (l == 0.f) {
+        m = m2; l = l2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = a2[i];
+        return;
+    }
+    const float mn = fmaxf(m, m2);
+    const float c1 = expf(m - mn), c2 = expf(m2 - mn);
+    l = l * c1 + l2 * c2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = a[i] * c1 + a2[i] * c2;
+    m = mn;
+}
+
+// Optional trace: thread 0 of workgroups 0 and NWG-1 records the 100 MHz real-time clock
+// at phase boundaries into p.trace[{0,1}][slot].
+__device__ __forceinline__ void trace_at(const MegaParams& p, int slot) {
+    if (p.trace && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == NWG - 1) && slot < p.trace_n)
+        p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
+// K/V registers of one block of 64 keys: thread (wave wid, 16-lane group grp, lane sub)
+// holds dims 8 sub .. 8 sub + 7 of keys base + 4 wid + grp + 16 i, i < 4.
+struct KVBlk {
+    u32x4 k[4], v[4];
+};
+
+__device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, int b, int g) {
+    return (size_t)layer * p.kv_layer_elems + (size_t)(p.seq_base + b) * p.kv_seq_elems + (size_t)g * p.t_cap * DH;
+}
+
+// Issue the loads of the block at `base` (keys < k1; slot T-1 is the new key, taken from
+// shared memory instead).
+__device__ __forceinline__ void kv_load(const MegaParams& p, size_t hb, int base, int k1, int T, KVBlk& blk) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kk = base + wid * 4 + grp + 16 * i;
+        if (kk < k1 && kk != T - 1) {
+            blk.k[i] = ldw16(p.kc + hb + (size_t)kk * DH + sub * 8);
+            blk.v[i] = ldw16(p.vc + hb + (size_t)kk * DH + sub * 8);
+        }
+    }
+}
+
+struct AttState {
+    float m[2], l[2], acc[2][8];
+};
+
+// Online-softmax update of both heads with the keys of one block.
+__device__ __forceinline__ void kv_compute(const Smem& sm, int base, int k1, int T, const KVBlk& blk,
+                                           const float (&qv)[2][8], AttState& st) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+    const float scale = 0.088388346f;   // fl32(128^-0.5)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kk = base + wid * 4 + grp + 16 * i;
+        if (kk < k1) {                  // uniform over the 16 lanes of a key
+            float kv[8], vv[8];
+            if (kk == T - 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kv[e] = sm.kn[sub * 8 + e]; vv[e] = sm.vn[sub * 8 + e]; }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kv[2 * e] = __uint_as_float(blk.k[i][e] << 16);
+                    kv[2 * e + 1] = __uint_as_float(blk.k[i][e] & 0xFFFF0000u);
+                    vv[2 * e] = __uint_as_float(blk.v[i][e] << 16);
+                    vv[2 * e + 1] = __uint_as_float(blk.v[i][e] & 0xFFFF0000u);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float dsum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dsum += qv[h][e] * kv[e];
+                const float sc = sum16(dsum) * scale;
+                const float mn = fmaxf(st.m[h], sc);
+                const float corr = expf(st.m[h] - mn);
+                const float pr = expf(sc - mn);
+                st.l[h] = st.l[h] * corr + pr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * corr + pr * vv[e];
+                st.m[h] = mn;
+            }
+        }
+    }
+}
+
+// Attention of both heads of the group for row b over slots [k0, k1) of T visible ones;
+// `blk` holds the block at k0 (loaded by the caller before it waited for q/k/v). Leaves
+// the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
+__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, KVBlk& blk) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+    float qv[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[h][e] = sm.q[h][sub * 8 + e];
+    AttState st;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        st.m[h] = -INFINITY;
+        st.l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+    }
+    KVBlk nxt;
+    for (int base = k0; base < k1; base += 128) {   // two register blocks in flight
+        kv_load(p, hb, base + 64, k1, T, nxt);
+        kv_compute(sm, base, k1, T, blk, qv, st);
+        kv_load(p, hb, base + 128, k1, T, blk);
+        kv_compute(sm, base + 64, k1, T, nxt, qv, st);
+    }
+    const int slot = wid * 4 + grp;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (sub == 0) { sm.wm[slot][h][0] = st.m[h]; sm.wm[slot][h][1] = st.l[h]; }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.wm[slot][h][2 + sub * 8 + e] = st.acc[h][e];
+    }
+    __syncthreads();
+    {
+        const int h = threadIdx.x >> 7, dd = threadIdx.x & 127;
+        float M = -INFINITY;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+            if (sm.wm[s2][h][1] > 0.f) M = fmaxf(M, sm.wm[s2][h][0]);
+        float Ls = 0.f, A = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            if (sm.wm[s2][h][1] > 0.f) {
+                const float cf = expf(sm.wm[s2][h][0] - M);
+                Ls += sm.wm[s2][h][1] * cf;
+                A += sm.wm[s2][h][2 + dd] * cf;
+            }
+        }
+        if (dd == 0) { sm.att[h][0] = M; sm.att[h][1] = Ls; }
+        sm.att[h][2 + dd] = A;
+    }
+    __syncthreads();
+}
+
+// P[b][g][32j + r] = Wo[32j + r, 256g:256g+256] . o[b]; thread t: row r = t >> 3,
+// 16-byte chunks sub + 8i (i < 4) of the 32 in the row segment.
+__device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, u64* P, int g, int j, int B, unsigned tag) {
+    const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    for (int b = 0; b < B; ++b) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += dot8(pf[i], &sm.o[b][(sub + 8 * i) * 8]);
+        s = sum8(s);
+        if (sub == 0) put(P + (size_t)b * W_P + (size_t)g * D + 32 * j + r, s, tag);
+    }
+}
+
+__device__ __forceinline__ void pf_oproj(const MegaLayer& L, u32x4* pf, int g, int j) {
+    const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const bf16* base = L.wo + (size_t)(32 * j + r) * (HQ * DH) + 256 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = ldw16(base + (sub + 8 * i) * 8);
+}
+
+// Rows of phase C: thread t < 192 owns row rr = t >> 3 (12 gate rows, then 12 up rows).
+__device__ __forceinline__ int gu_row(int w, int rr) {
+    const int col = 12 * w + (rr < 12 ? rr : rr - 12);
+    return 32 * (col >> 4) + (col & 15) + (rr < 12 ? 0 : 16);
+}
+
+__device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
+    const int r = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    const bf16* base = L.wqkv + (size_t)(16 * w + r) * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pf[i] = ldw16(base + (sub + 16 * i) * 8);
+    pre.nw = ldf4(L.in_norm + 4 * threadIdx.x);
+    const int i = threadIdx.x & 63;
+    const float* qk = (threadIdx.x >> 6) < 2 ? L.q_norm : L.k_norm;
+    pre.qk1 = ldf(qk + i);
+    pre.qk2 = ldf(qk + i + 64);
+    pre.fr = ldf(p.inv_freq + i);
+}
+__device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
+    const int rr = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    pre.nw = ldf4(L.post_norm + 4 * threadIdx.x);
+    if (rr >= 24) return;
+    const bf16* base = L.wgu + (size_t)gu_row(w, rr) * D;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pf[i] = ldw16(base + (sub + 8 * i) * 8);
+}
+__device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int w) {
+    const int rr = threadIdx.x >> 6, sub = threadIdx.x & 63;
+    const bf16* base = L.wd + (size_t)(4 * w + rr) * F;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pf[i] = ldw16(base + (sub + 64 * i) * 8);
+}
+
+// long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
+__device__ __forceinline__ void chunking(int T, int& nch, int& ch) {
+    nch = min(MAXCH, (T + 63) / 64);
+    ch = ((T + nch - 1) / nch + 63) & ~63;
+    nch = (T + ch - 1) / ch;
+}
+
+// index of element i of group gg's inputs within a row's QKV words:
+// q heads 2gg, 2gg+1 (256) | k head gg (128) | v head gg (128)
+__device__ __forceinline__ size_t group_word(int gg, int i) {
+    return i < 256 ? (size_t)256 * gg + i
+                   : (i < 384 ? (size_t)HQ * DH + DH * gg + (i - 256) : (size_t)(HQ + HKV) * DH + DH * gg + (i - 384));
+}
+
+__global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+    const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int B = p.B;
+    const unsigned tag = p.tag;
+    u32x4 pf[16];
+    Pre pre;
+    const int g = w >> 5, j = w & 31;       // kv group and row block of phase B
+
+    // layer table into shared memory (scalar loads would hold up every later LDS wait)
+    {
+        const int words = p.n_layers * (int)(sizeof(MegaLayer) / 4);
+        const unsigned* src = reinterpret_cast<const unsigned*>(p.layers);
+        unsigned* dst = reinterpret_cast<unsigned*>(sm.layers);
+        for (int i = tid; i < words; i += NT) dst[i] = *(const GLOBAL_AS unsigned*)(src + i);
+    }
+    if (w == 0 && tid < B) {
+        const int t = p.tokens[tid];
+        if (t < 0 || t >= p.vocab) atomicOr(p.err, Q3_DEVERR_TOKEN);
+    }
+    __syncthreads();
+    pf_qkv(p, sm.layers[0], pf, pre, w);
+    int tslot = 0;
+    trace_at(p, tslot++);
+
+    for (int layer = 0; layer < p.n_layers; ++layer) {
+        const MegaLayer& L = sm.layers[layer];
+        u64* X = p.ex + (size_t)layer * p.ex_layer;          // layer input x
+        u64* QKV = X + (size_t)BMAX * W_X;
+        u64* P = QKV + (size_t)BMAX * W_QKV;
+        u64* XP = P + (size_t)BMAX * W_P;
+        u64* A = XP + (size_t)BMAX * W_XP;
+        u64* O = A + (size_t)BMAX * W_A;                      // combined attention (long context)
+        u64* PT = O + (size_t)BMAX * W_O;                     // chunk partials (long context)
+        u64* Xn = X + p.ex_layer;                             // next layer's input
+
+        // ---------------- A: x -> RMSNorm -> QKV rows 16w .. 16w+15
+        for (int b = 0; b < B; ++b) {
+            if (layer == 0) {
+                const int t = clamp_tok(p, b);
+                for (int k = tid; k < D; k += NT) sm.act[b][k] = bf2f(p.embed[(size_t)t * D + k]);
+            } else if (!poll(X + (size_t)b * W_X, Contig{}, D, sm.act[b], tag, p.err)) {
+                return;
+            }
+        }
+        __syncthreads();
+        if (tid < 4 * B) sm.x0[tid >> 2][tid & 3] = sm.act[tid >> 2][4 * w + (tid & 3)];
+        trace_at(p, tslot++);
+        rmsnorm_act(p, sm, B, pre.nw);
+        {
+            const int r = tid >> 4, sub = tid & 15;
+            for (int b = 0; b < B; ++b) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s += dot8(pf[i], &sm.act[b][(sub + 16 * i) * 8]);
+                s = sum16(s);
+                if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s, tag);
+            }
+        }
+        pf_oproj(L, pf, g, j);
+        trace_at(p, tslot++);
+
+        // ---------------- B: attention of kv group g and its O-projection partial
+        int Tmax = 0;
+        for (int b = 0; b < B; ++b) Tmax = max(Tmax, p.slots[b] + 1);
+        if (Tmax <= SHORT_T) {
+            for (int b = 0; b < B; ++b) {
+                const int slot = p.slots[b], T = slot + 1;
+                const int pos = p.positions ? p.positions[b] : slot;
+                const size_t hb = kv_head_base(p, layer, b, g);
+                KVBlk blk;
+                kv_load(p, hb, 0, T, T, blk);                 // in flight while q/k/v arrive
+                const u64* qb = QKV + (size_t)b * W_QKV;
+                if (!poll(qb, [&](int i) { return group_word(g, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                if (b == 0) trace_at(p, tslot++);
+                group_prep(p, sm, pre, layer, b, g, pos, slot, j == 0);
+                attend(p, sm, hb, 0, T, T, blk);
+                const int h = tid >> 7, dd = tid & 127;
+                sm.o[b][h * DH + dd] = sm.att[h][1] > 0.f ? sm.att[h][2 + dd] / sm.att[h][1] : 0.f;
+                __syncthreads();
+            }
+        } else {
+            // B1: unit w = (group w % 8, chunk w / 8) attends its chunk, per row
+            const int gg = w & 7, c = w >> 3;
+            for (int b = 0; b < B; ++b) {
+                const int slot = p.slots[b], T = slot + 1;
+                const int pos = p.positions ? p.positions[b] : slot;
+                int nch, ch;
+                chunking(T, nch, ch);
+                if (c < nch) {
+                    const int k0 = c * ch, k1 = min(T, k0 + ch);
+                    const size_t hb = kv_head_base(p, layer, b, gg);
+                    KVBlk blk;
+                    kv_load(p, hb, k0, k1, T, blk);
+                    const u64* qb = QKV + (size_t)b * W_QKV;
+                    if (!poll(qb, [&](int i) { return group_word(gg, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                    if (b == 0) trace_at(p, tslot++);
+                    group_prep(p, sm, pre, layer, b, gg, pos, slot, k1 == T);
+                    attend(p, sm, hb, k0, k1, T, blk);
+                    u64* pt = PT + (size_t)b * W_PT + (((size_t)gg * MAXCH + c) * 2) * PART;
+                    for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART], tag);
+                    __syncthreads();
+                } else if (b == 0) {
+                    trace_at(p, tslot++);
+                }
+            }
+            // combine: workgroup 32g (j == 0) merges group g's chunks into O[b][g]
+            if (j == 0) {
+                for (int b = 0; b < B; ++b) {
+                    const int T = p.slots[b] + 1;
+                    int nch, ch;
+                    chunking(T, nch, ch);
+                    const u64* src = PT + (size_t)b * W_PT + ((size_t)g * MAXCH) * 2 * PART;
+                    for (int done = 0; done < nch * 2 * PART; done += 16 * NT) {   // pieces of 4096 words
+                        const int n = min(16 * NT, nch * 2 * PART - done);
+                        if (!poll(src + done, Contig{}, n, sm.part + done, tag, p.err)) return;
+                    }
+                    const int h = tid >> 7, dd = tid & 127;
+                    float M = -INFINITY;
+                    for (int c2 = 0; c2 < nch; ++c2) {
+                        const float* pp = sm.part + ((size_t)c2 * 2 + h) * PART;
+                        if (pp[1] > 0.f) M = fmaxf(M, pp[0]);
+                    }
+                    float Ls = 0.f, Acc = 0.f;
+                    for (int c2 = 0; c2 < nch; ++c2) {
+                        const float* pp = sm.part + ((size_t)c2 * 2 + h) * PART;
+                        if (pp[1] > 0.f) {
+                            const float cf = expf(pp[0] - M);
+                            Ls += pp[1] * cf;
+                            Acc += pp[2 + dd] * cf;
+                        }
+                    }
+                    put(O + (size_t)b * W_O + (size_t)g * 2 * DH + h * DH + dd, Ls > 0.f ? Acc / Ls : 0.f, tag);
+                    __syncthreads();
+                }
+            }
+            for (int b = 0; b < B; ++b)
+                if (!poll(O + (size_t)b * W_O + (size_t)g * 2 * DH, Contig{}, 2 * DH, sm.o[b], tag, p.err)) return;
+        }
+        trace_at(p, tslot++);
+        oproj_partial(sm, pf, P, g, j, B, tag);
+        pf_gu(L, pf, pre, w);
+        trace_at(p, tslot++);
+
+        // ---------------- R: x'[4w .. 4w+3] = x + P[0] + ... + P[7]
+        {
+            // word i: row b = i / 32, partial gg = (i / 4) % 8, element e = i % 4
+            auto pidx = [&](int i) -> size_t {
+                return (size_t)(i >> 5) * W_P + (size_t)((i >> 2) & 7) * D + 4 * w + (i & 3);
+            };
+            if (!poll(P, pidx, 32 * B, sm.pr, tag, p.err)) return;
+            if (tid < 4 * B) {
+                const int b = tid >> 2, e = tid & 3, n = 4 * w + e;
+                float xv = sm.x0[b][e];
+#pragma unroll
+                for (int gg = 0; gg < HKV; ++gg) xv += sm.pr[b * 32 + gg * 4 + e];
+                sm.xr[b][e] = xv;
+                put(XP + (size_t)b * W_XP + n, xv, tag);
+            }
+            __syncthreads();
+        }
+        trace_at(p, tslot++);
+
+        // ---------------- C: x' -> RMSNorm -> gate/up of 12 columns -> SwiGLU
+        for (int b = 0; b < B; ++b)
+            if (!poll(XP + (size_t)b * W_XP, Contig{}, D, sm.act[b], tag, p.err)) return;
+        trace_at(p, tslot++);
+        rmsnorm_act(p, sm, B, pre.nw);
+        {
+            const int rr = tid >> 3, sub = tid & 7;
+            for (int b = 0; b < B; ++b) {
+                float s = 0.f;
+                if (rr < 24) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s += dot8(pf[i], &sm.act[b][(sub + 8 * i) * 8]);
+                }
+                s = sum8(s);
+                if (rr < 24 && sub == 0) sm.gu[rr][b] = s;
+            }
+            __syncthreads();
+            if (tid < 12 * B) {
+                const int c = tid % 12, b = tid / 12;
+                const float gt = sm.gu[c][b], up = sm.gu[12 + c][b];
+                put(A + (size_t)b * W_A + 12 * w + c, gt / (1.0f + expf(-gt)) * up, tag);
+            }
+        }
+        pf_down(L, pf, w);
+        trace_at(p, tslot++);
+
+        // ---------------- D: rows 4w..4w+3 of down + residual
+        for (int b = 0; b < B; ++b)
+            if (!poll(A + (size_t)b * W_A, Contig{}, F, sm.act[b], tag, p.err)) return;
+        trace_at(p, tslot++);
+        {
+            const int rr = tid >> 6, sub = tid & 63;
+            const int n = 4 * w + rr;
+            for (int b = 0; b < B; ++b) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 6; ++i) s += dot8(pf[i], &sm.act[b][(sub + 64 * i) * 8]);
+                s = wave_sum(s);
+                if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s, tag);
+            }
+        }
+        if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
+        else pre.nw = ldf4(p.final_norm + 4 * tid);
+        trace_at(p, tslot++);
+        __syncthreads();
+    }
+
+    // ---------------- final RMSNorm + LM head rows [r0, r1) + per-workgroup argmax
+    const int r0 = (int)((long long)p.vocab * w / NWG), r1 = (int)((long long)p.vocab * (w + 1) / NWG);
+    const int rsub = tid >> 4, sub = tid & 15;   // 16 rows per pass, 16 lanes per row
+    u32x4 b0[8], b1[8], b2[8];                     // three passes: two loads in flight
+    auto load_rows = [&](int base, u32x4* dst) {
+        const int row = base + rsub;
+        if (row < r1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = ldw16(p.embed + (size_t)row * D + (sub + 16 * i) * 8);
+        }
+    };
+    load_rows(r0, b0);                             // in flight while the last layer finishes
+    load_rows(r0 + 16, b1);
+    {
+        const u64* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
+        for (int b = 0; b < B; ++b)
+            if (!poll(Xl + (size_t)b * W_X, Contig{}, D, sm.act[b], tag, p.err)) return;
+        __syncthreads();
+        trace_at(p, tslot++);
+        rmsnorm_act(p, sm, B, pre.nw);
+    }
+    u64 best[BMAX] = {0ull, 0ull, 0ull, 0ull};
+    bool bad = false;
+    {
+        auto rows_dot = [&](int base, const u32x4* wv) {
+            const int row = base + rsub;
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                if (b >= B) break;
+                float s = 0.f;
+                if (row < r1) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s += dot8(wv[i], &sm.act[b][(sub + 16 * i) * 8]);
+                }
+                s = sum16(s);
+                if (row < r1 && sub == 0) {
+                    p.logits[(size_t)b * p.vocab + row] = s;
+                    bad |= !isfinite(s);
+                    const u64 key = pack_argmax(s, (uint32_t)row);
+                    best[b] = key > best[b] ? key : best[b];
+                }
+            }
+        };
+        for (int base = r0; base < r1; base += 48) {
+            load_rows(base + 32, b2);
+            rows_dot(base, b0);
+            load_rows(base + 48, b0);
+            rows_dot(base + 16, b1);
+            load_rows(base + 64, b1);
+            rows_dot(base + 32, b2);
+        }
+    }
+    if (bad) atomicOr(p.err, Q3_DEVERR_NONFINITE);
+    __shared__ u64 wbest[4][BMAX];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) {
+        if (b >= B) break;
+        u64 v = best[b];
+        for (int o = 32; o >= 1; o >>= 1) {
+            const u64 t = __shfl_xor(v, o, 64);
+            v = t > v ? t : v;
+        }
+        if (lane == 0) wbest[tid >> 6][b] = v;
+    }
+    __syncthreads();
+    if (tid < B) {
+        u64 v = wbest[0][tid];
+        for (int wv = 1; wv < 4; ++wv) v = wbest[wv][tid] > v ? wbest[wv][tid] : v;
+        p.cand[(size_t)tid * NWG + w] = v;
+    }
+    trace_at(p, tslot++);
+}
+
+}  // namespace
+
+size_t decode_mega_exchange_words_per_layer() {
+    return (size_t)BMAX * (W_X + W_QKV + W_P + W_XP + W_A + W_O + W_PT);
+}
+
+// Tail of a persistent decode step: amax[b] = max over the 256 workgroup candidates of
+// row b (packed logit key | ~id), and the sequence lengths advance by one.
+__global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
+                            int seq_base, int B) {
+    const int b = blockIdx.x;
+    u64 v = cand[(size_t)b * NWG + threadIdx.x];
+    for (int o = 32; o >= 1; o >>= 1) {
+        const u64 t = __shfl_xor(v, o, 64);
+        v = t > v ? t : v;
+    }
+    __shared__ u64 r[4];
+    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < 4; ++i) v = r[i] > v ? r[i] : v;
+        amax[b] = v;
+        lens[seq_base + b] += 1;
+    }
+}
+
+hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
+                            int B, hipStream_t s) {
+    if (B < 1 || B > BMAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_mega_tail, dim3(B), dim3(NWG), 0, s, cand, amax, lens, seq_base, B);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mega(const MegaParams& p, hipStream_t s) {
+    if (p.B < 1 || p.B > BMAX) return hipErrorInvalidValue;
+    void* args[] = {(void*)&p};
+    return hipLaunchCooperativeKernel((const void*)k_decode_mega, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
+}
+
+hipError_t decode_mega_prepare() {
+    return hipFuncSetAttribute((const void*)k_decode_mega, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)sizeof(Smem));
+}
+
+}  // namespace q3

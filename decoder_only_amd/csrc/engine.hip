@@ -72,6 +72,17 @@ struct q3_engine {
         int64_t launches = 0;
     } prof;
 
+    // persistent decode kernel state (decode_mega.hip)
+    bool mega_ok = false;          // shape supported and co-residency possible
+    int decode_path = 0;           // 0 auto, 1 per-kernel launches, 2 persistent kernel
+    MegaLayer* d_layers = nullptr;
+    unsigned long long* m_ex = nullptr;      // tagged exchange words, (n_layers + 1) layers
+    size_t m_ex_layer = 0;
+    unsigned m_tag = 0;                      // tag of the last launch (words start at tag 0)
+    unsigned long long* m_cand = nullptr;    // per-workgroup argmax candidates
+    unsigned long long* m_trace = nullptr;   // caller's device buffer for phase timestamps
+    int m_trace_n = 0;
+
     // prefill workspace (grown on demand)
     int pf_cap = 0;
     float *pf_x = nullptr, *pf_qkv = nullptr, *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr,
@@ -293,6 +304,32 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
     if (!(e->sample_ws = e->alloc(sample_workspace_bytes(V, B)))) return oom();
     e->attn_ws_T = c.max_seq;
     if (!(e->attn_ws = (float*)e->alloc(attn_decode_workspace_bytes(B, Hkv, c.max_seq)))) return oom();
+    // persistent decode kernel: fixed layer shape, bf16 weights and cache, one workgroup per CU
+    {
+        hipDeviceProp_t prop;
+        int occ = 0;
+        const bool shape = d == 1024 && Hq == 16 && Hkv == 8 && dh == 128 && F == 3072 &&
+                           c.weight_dtype == Q3_BF16 && c.kv_dtype == Q3_BF16 && c.n_layers > 0;
+        if (shape && hipGetDeviceProperties(&prop, e->device) == hipSuccess && prop.multiProcessorCount == 256 &&
+            decode_mega_prepare() == hipSuccess) {
+            e->mega_ok = true;
+        }
+        (void)occ;
+        if (e->mega_ok) {
+            std::vector<MegaLayer> hl(c.n_layers);
+            for (int l = 0; l < c.n_layers; ++l) {
+                const auto& L = e->layers[l];
+                hl[l] = MegaLayer{(const uint16_t*)L.wqkv, (const uint16_t*)L.wo, (const uint16_t*)L.wgu,
+                                  (const uint16_t*)L.wd, L.in_norm, L.post_norm, L.q_norm, L.k_norm};
+            }
+            if (!(e->d_layers = (MegaLayer*)upload(hl.data(), hl.size() * sizeof(MegaLayer)))) return oom();
+            e->m_ex_layer = decode_mega_exchange_words_per_layer();
+            const size_t exb = ((size_t)c.n_layers + 1) * e->m_ex_layer * 8;
+            if (!(e->m_ex = (unsigned long long*)e->alloc(exb))) return oom();
+            if (hipMemset(e->m_ex, 0, exb) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
+            if (!(e->m_cand = (unsigned long long*)e->alloc((size_t)kMegaMaxRows * kMegaWorkgroups * 8))) return oom();
+        }
+    }
     if (hipDeviceSynchronize() != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
     *out = e;
     return Q3_OK;
@@ -357,6 +394,51 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     int maxT = 0;
     for (int b = 0; b < B; ++b) maxT = std::max(maxT, e->h_len[seq_base + b] + 1);
     const double wb = (double)e->wbytes();
+    // the persistent kernel always computes the logits (into the engine's buffer when the
+    // caller does not want them)
+    const bool use_mega = e->mega_ok && B <= kMegaMaxRows && e->decode_path != 1;
+    if (!use_mega && e->decode_path == 2) return e->fail(Q3_ERR_STATE, "persistent decode kernel not usable here");
+    if (use_mega) {
+        MegaParams mp{};
+        mp.n_layers = c.n_layers;
+        mp.vocab = V;
+        mp.B = B;
+        mp.seq_base = seq_base;
+        mp.t_cap = c.max_seq;
+        for (int b = 0; b < B; ++b) mp.slots[b] = e->h_len[seq_base + b];
+        mp.eps = c.rms_eps;
+        if (++e->m_tag == 0) {   // wrapped: words still hold old tags, so restart from a clean buffer
+            HIPCHK(e, launch_fill_u64(e->m_ex, 0ull, (int)(((size_t)c.n_layers + 1) * e->m_ex_layer), s));
+            e->m_tag = 1;
+        }
+        mp.tag = e->m_tag;
+        mp.layers = e->d_layers;
+        mp.embed = (const uint16_t*)e->embed;
+        mp.final_norm = e->final_norm;
+        mp.inv_freq = e->inv_freq;
+        mp.kc = (uint16_t*)e->kc;
+        mp.vc = (uint16_t*)e->vc;
+        mp.kv_layer_elems = e->kv_layer_elems;
+        mp.kv_seq_elems = e->kv_seq_elems;
+        mp.tokens = tokens;
+        mp.positions = positions;
+        mp.ex = e->m_ex;
+        mp.ex_layer = e->m_ex_layer;
+        float* lg = logits_out ? logits_out : e->logits;
+        mp.logits = lg;
+        mp.cand = e->m_cand;
+        mp.err = e->d_err;
+        mp.trace = e->m_trace;
+        mp.trace_n = e->m_trace_n;
+        prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
+        HIPCHK(e, launch_decode_mega(mp, s));
+        prof_mark(e, Q3_PROF_DECODE_STEP, false);
+        HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, seq_base, B, s));
+        e->cur_logits = lg;
+        e->cur_rows = B;
+        for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;
+        return Q3_OK;
+    }
     prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
     HIPCHK(e, launch_embed(tokens, e->embed, wdt, e->x, B, d, V, e->d_err, s));
     for (int l = 0; l < c.n_layers; ++l) {
@@ -538,6 +620,11 @@ extern "C" q3_status q3_sync(q3_engine* e) {
     HIPCHK(e, hipMemcpyAsync(&flags, e->d_err, 4, hipMemcpyDeviceToHost, e->stream));
     HIPCHK(e, hipMemcpyAsync(e->d_err, &zero, 4, hipMemcpyHostToDevice, e->stream));
     HIPCHK(e, hipStreamSynchronize(e->stream));
+    if (flags & Q3_DEVERR_SYNC) {
+        // a wait timed out and every workgroup left the kernel; later launches carry new tags,
+        // so nothing needs resetting
+        return e->fail(Q3_ERR_HIP, "persistent decode kernel: a cross-workgroup wait timed out");
+    }
     if (flags & Q3_DEVERR_TOKEN) return e->fail(Q3_ERR_TOKEN, "a token id outside [0, vocab) reached the device");
     if (flags & Q3_DEVERR_NONFINITE) return e->fail(Q3_ERR_NUMERIC, "non-finite logits");
     return Q3_OK;
@@ -570,5 +657,21 @@ extern "C" q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* lau
     if (flops) *flops = e->prof.flops;
     e->prof.kind = -1;
     e->prof.used = 0;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_set_decode_path(q3_engine* e, int32_t path) {
+    if (!e) return Q3_ERR_ARG;
+    if (path < 0 || path > 2) return e->fail(Q3_ERR_ARG, "decode path must be 0, 1 or 2");
+    if (path == 2 && !e->mega_ok) return e->fail(Q3_ERR_STATE, "persistent decode kernel not available for this model/GPU");
+    e->decode_path = path;
+    return Q3_OK;
+}
+
+extern "C" q3_status q3_profile_trace(q3_engine* e, unsigned long long* dev_out, int32_t n) {
+    if (!e) return Q3_ERR_ARG;
+    if (n < 0 || (n > 0 && !dev_out)) return e->fail(Q3_ERR_ARG, "bad trace buffer");
+    e->m_trace = n > 0 ? dev_out : nullptr;
+    e->m_trace_n = n;
     return Q3_OK;
 }

@@ -63,6 +63,42 @@ hipError_t launch_gemm(const void* A, int a_f32, const uint16_t* W, void* C, int
 hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
                                int M, int t0, int Hq, int Hkv, float* o, hipStream_t s);
 
+// ---- decode_mega.hip (whole decode step in one cooperative launch; fixed Qwen3-0.6B layer
+// shape: hidden 1024, 16/8 heads of 128, FFN 3072; bf16 weights and KV; 1..4 rows)
+struct MegaLayer {
+    const uint16_t *wqkv, *wo, *wgu, *wd;
+    const float *in_norm, *post_norm, *q_norm, *k_norm;
+};
+struct MegaParams {
+    int n_layers, vocab, B, seq_base, t_cap;
+    int slots[4];                   // cache slot (= current length) of each row
+    float eps;
+    unsigned tag;                   // launch tag (>= 1, increasing)
+    const MegaLayer* layers;        // device array [n_layers]
+    const uint16_t* embed;
+    const float *final_norm, *inv_freq;
+    uint16_t *kc, *vc;
+    size_t kv_layer_elems, kv_seq_elems;
+    const int32_t* tokens;
+    const int32_t* positions;       // may be NULL (position = slot)
+    unsigned long long* ex;         // tagged exchange words, (n_layers + 1) * ex_layer
+    size_t ex_layer;
+    float* logits;
+    unsigned long long* cand;       // [4][256] per-workgroup argmax candidates
+    unsigned* err;
+    unsigned long long* trace;      // optional phase timestamps [2][trace_n] (NULL: off)
+    int trace_n;
+};
+hipError_t decode_mega_prepare();
+hipError_t launch_decode_mega(const MegaParams& p, hipStream_t s);
+// argmax over the per-workgroup candidates and lens[seq_base + b] += 1 (after each launch)
+hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
+                            int B, hipStream_t s);
+size_t decode_mega_exchange_words_per_layer();
+constexpr int kMegaMaxRows = 4;
+constexpr int kMegaMaxLayers = 64;
+constexpr int kMegaWorkgroups = 256;
+
 // ---- sample.hip
 hipError_t launch_argmax_rows(const float* logits, unsigned long long* amax, int V, int B,
                               unsigned* err, hipStream_t s);

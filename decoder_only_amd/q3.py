@@ -23,6 +23,7 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
 EXPORTS = [
     "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import",
     "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
+    "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
     "q3_op_attn_prefill", "q3_op_sample",
 ]
@@ -75,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_last_error": ([vp], c_char_p),
         "q3_free": ([vp], None),
         "q3_profile_begin": ([vp, i32], i32),
+        "q3_set_decode_path": ([vp, i32], i32),
+        "q3_profile_trace": ([vp, vp, i32], i32),
         "q3_profile_end": ([vp, POINTER(ctypes.c_double), POINTER(c_int64), POINTER(ctypes.c_double),
                             POINTER(ctypes.c_double)], i32),
         "q3_op_rmsnorm": ([vp, vp, vp, i32, i32, i32, f32, vp], i32),
@@ -203,6 +206,16 @@ class Engine:
 
     def sync(self) -> None:
         _check(load_library().q3_sync(self._h), "q3_sync", self._h)
+
+    def set_decode_path(self, path: int) -> None:
+        """0 auto, 1 one launch per operation, 2 the persistent decode kernel."""
+        _check(load_library().q3_set_decode_path(self._h, path), "q3_set_decode_path", self._h)
+
+    def profile_trace(self, buf=None) -> None:
+        """Record phase timestamps of the persistent decode kernel into buf (device int64
+        [2, n]); None turns it off."""
+        n = 0 if buf is None else buf.shape[1]
+        _check(load_library().q3_profile_trace(self._h, _ptr(buf), n), "q3_profile_trace", self._h)
 
     def profile_begin(self, kind: int) -> None:
         _check(load_library().q3_profile_begin(self._h, kind), "q3_profile_begin", self._h)

@@ -163,6 +163,22 @@ q3_status q3_profile_begin(q3_engine* e, int32_t kind);
 q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, double* bytes,
                          double* flops);
 
+/* How decode rows run ("The pipeline at a glance": one forward pass per new token).
+ * 0 (default): one cooperative launch per decode step (every layer, the LM head and the
+ * argmax in a single persistent kernel separated by grid barriers) when the model has
+ * the Qwen3-0.6B layer shape (hidden 1024, 16/8 heads of 128, FFN 3072) with bf16
+ * weights and cache and the step has at most 4 rows; else one launch per operation.
+ * 1: always one launch per operation. 2: always the persistent kernel (Q3_ERR_STATE if
+ * the model or GPU does not allow it). */
+q3_status q3_set_decode_path(q3_engine* e, int32_t path);
+
+/* Phase timestamps of the persistent decode kernel: while enabled (n > 0), every launch
+ * writes the GPU's 100 MHz real-time clock at its phase boundaries (kernel start, then
+ * per layer before and after each grid barrier, then the end) as seen by the first and
+ * the last workgroup into dev_out (device uint64 [2][n]; row 0 first workgroup, row 1 last;
+ * slots past n are dropped). n = 0 turns it off. */
+q3_status q3_profile_trace(q3_engine* e, unsigned long long* dev_out, int32_t n);
+
 /* Release all device memory of the engine. NULL is allowed. */
 void q3_free(q3_engine* e);
 

@@ -58,7 +58,7 @@ class SamplerStat:
 
 
 def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
-               sampler_stats: List[SamplerStat] | None = None) -> List[StepStat]:
+               sampler_stats: List[SamplerStat] | None = None, decode_path: int = 0) -> List[StepStat]:
     """Prefill a seeded prompt, then `steps` decode steps, batch 1, teacher-forced with the
     oracle's tokens (greedy at temperature 0, else drawn with the workload's uniforms).
     With sampling, the engine's sampler is also run on the oracle's own logits and must
@@ -72,6 +72,7 @@ def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
     cache = model.new_cache(max_seq)
     announce("e2e", w.name, w.n_layers, w.vocab, w.weight_dtype, prompt_len, steps)
     eng = q3.Engine(q3.config(w, 1, max_seq), weights)
+    eng.set_decode_path(decode_path)
     prompt = synth.prompt_tokens(w, prompt_len)
     T, p = float(np.float32(w.temperature)), float(np.float32(w.top_p))
     us = synth.uniforms(w, steps + 1)

@@ -22,13 +22,35 @@ def test_toy_fp32_prefill_and_greedy_decode():
     assert not failures(stats), failures(stats)
 
 
-def test_toy_bf16_matrix_core_prefill():
+@pytest.mark.parametrize("path", [1, 2])
+def test_toy_bf16_matrix_core_prefill(path):
     """bf16 weights and cache, 512-token prompt: rows 0..510 take the matrix-core prefill
-    path (bf16 activations), the last row and the decode steps the float32 path."""
+    path, the last row and the decode steps the float32 decode path -- one launch per
+    operation (path 1) or the persistent decode kernel (path 2)."""
     w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
-    stats = run_single(w, 512, 16)
+    stats = run_single(w, 512, 16, decode_path=path)
     _report(stats)
     assert not failures(stats), failures(stats)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_toy_bf16_long_context_decode(path):
+    """Decode past one 256-slot attention chunk: the persistent kernel switches to its
+    split-K attention with a combine phase."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_single(w, 250, 20, decode_path=path)
+    _report(stats)
+    assert not failures(stats), failures(stats)
+
+
+def test_toy_fp32_rejects_persistent_path():
+    from decoder_only_amd import q3
+    w = synth.workload("toy").with_(n_layers=1)
+    eng = q3.Engine(q3.config(w, 1, 8), synth.make_weights(w))
+    with pytest.raises(q3.Q3Error) as e:
+        eng.set_decode_path(2)                               # fp32 weights: not supported
+    assert e.value.code == -7
+    eng.close()
 
 
 def test_engine_capacity_and_token_errors():
