@@ -40,6 +40,9 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill and batch-64 lines")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="dispatch the persistent decode kernel as an ordinary launch (for tracers "
+                         "that cannot follow cooperative launches)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); "
@@ -59,6 +62,8 @@ def main() -> int:
     log(f"weights generated in {time.time() - t:.1f}s")
     max_batch, max_seq = 64, 4160
     eng = q3.Engine(q3.config(w, max_batch, max_seq), weights)
+    if args.plain_launch:
+        eng.set_decode_path(3)
     log("engine loaded")
 
     prompt = torch.from_numpy(synth.prompt_tokens(w)).cuda()

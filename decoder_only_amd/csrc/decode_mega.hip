@@ -735,10 +735,14 @@ hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* 
     return hipGetLastError();
 }
 
-hipError_t launch_decode_mega(const MegaParams& p, hipStream_t s) {
-    if (p.B < 1 || p.B > BMAX) return hipErrorInvalidValue;
-    void* args[] = {(void*)&p};
-    return hipLaunchCooperativeKernel((const void*)k_decode_mega, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
+hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s) {
+    if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers) return hipErrorInvalidValue;
+    if (cooperative) {
+        void* args[] = {(void*)&p};
+        return hipLaunchCooperativeKernel((const void*)k_decode_mega, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
+    }
+    hipLaunchKernelGGL(k_decode_mega, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    return hipGetLastError();
 }
 
 hipError_t decode_mega_prepare() {

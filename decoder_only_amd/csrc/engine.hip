@@ -74,7 +74,7 @@ struct q3_engine {
 
     // persistent decode kernel state (decode_mega.hip)
     bool mega_ok = false;          // shape supported and co-residency possible
-    int decode_path = 0;           // 0 auto, 1 per-kernel launches, 2 persistent kernel
+    int decode_path = 0;           // 0 auto, 1 per-kernel launches, 2 persistent kernel, 3 auto with ordinary launch
     MegaLayer* d_layers = nullptr;
     unsigned long long* m_ex = nullptr;      // tagged exchange words, (n_layers + 1) layers
     size_t m_ex_layer = 0;
@@ -309,7 +309,7 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         hipDeviceProp_t prop;
         int occ = 0;
         const bool shape = d == 1024 && Hq == 16 && Hkv == 8 && dh == 128 && F == 3072 &&
-                           c.weight_dtype == Q3_BF16 && c.kv_dtype == Q3_BF16 && c.n_layers > 0;
+                           c.weight_dtype == Q3_BF16 && c.kv_dtype == Q3_BF16 && c.n_layers > 0 && c.n_layers <= kMegaMaxLayers;
         if (shape && hipGetDeviceProperties(&prop, e->device) == hipSuccess && prop.multiProcessorCount == 256 &&
             decode_mega_prepare() == hipSuccess) {
             e->mega_ok = true;
@@ -431,7 +431,7 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         mp.trace = e->m_trace;
         mp.trace_n = e->m_trace_n;
         prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
-        HIPCHK(e, launch_decode_mega(mp, s));
+        HIPCHK(e, launch_decode_mega(mp, e->decode_path != 3, s));
         prof_mark(e, Q3_PROF_DECODE_STEP, false);
         HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, seq_base, B, s));
         e->cur_logits = lg;
@@ -662,7 +662,7 @@ extern "C" q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* lau
 
 extern "C" q3_status q3_set_decode_path(q3_engine* e, int32_t path) {
     if (!e) return Q3_ERR_ARG;
-    if (path < 0 || path > 2) return e->fail(Q3_ERR_ARG, "decode path must be 0, 1 or 2");
+    if (path < 0 || path > 3) return e->fail(Q3_ERR_ARG, "decode path must be 0, 1, 2 or 3");
     if (path == 2 && !e->mega_ok) return e->fail(Q3_ERR_STATE, "persistent decode kernel not available for this model/GPU");
     e->decode_path = path;
     return Q3_OK;

@@ -90,7 +90,8 @@ struct MegaParams {
     int trace_n;
 };
 hipError_t decode_mega_prepare();
-hipError_t launch_decode_mega(const MegaParams& p, hipStream_t s);
+// cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.
+hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s);
 // argmax over the per-workgroup candidates and lens[seq_base + b] += 1 (after each launch)
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
                             int B, hipStream_t s);

@@ -208,7 +208,8 @@ class Engine:
         _check(load_library().q3_sync(self._h), "q3_sync", self._h)
 
     def set_decode_path(self, path: int) -> None:
-        """0 auto, 1 one launch per operation, 2 the persistent decode kernel."""
+        """0 auto, 1 one launch per operation, 2 always the persistent decode kernel,
+        3 auto with the persistent kernel dispatched as an ordinary launch."""
         _check(load_library().q3_set_decode_path(self._h, path), "q3_set_decode_path", self._h)
 
     def profile_trace(self, buf=None) -> None:

@@ -165,16 +165,20 @@ q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, doub
 
 /* How decode rows run ("The pipeline at a glance": one forward pass per new token).
  * 0 (default): one cooperative launch per decode step (every layer, the LM head and the
- * argmax in a single persistent kernel separated by grid barriers) when the model has
- * the Qwen3-0.6B layer shape (hidden 1024, 16/8 heads of 128, FFN 3072) with bf16
- * weights and cache and the step has at most 4 rows; else one launch per operation.
+ * argmax in a single persistent kernel whose 256 workgroups hand values to each other
+ * through tagged words in device memory) when the model has the Qwen3-0.6B layer shape
+ * (hidden 1024, 16/8 heads of 128, FFN 3072) with bf16 weights and cache, the GPU has
+ * 256 compute units and the step has at most 4 rows; else one launch per operation.
  * 1: always one launch per operation. 2: always the persistent kernel (Q3_ERR_STATE if
- * the model or GPU does not allow it). */
+ * the model or GPU does not allow it). 3: as 0, but the persistent kernel is dispatched as
+ * an ordinary launch (for tools that cannot trace cooperative launches): it then relies
+ * on all 256 workgroups being resident together, which holds when no other work shares
+ * the GPU; otherwise its bounded waits expire and q3_sync reports Q3_ERR_HIP. */
 q3_status q3_set_decode_path(q3_engine* e, int32_t path);
 
 /* Phase timestamps of the persistent decode kernel: while enabled (n > 0), every launch
  * writes the GPU's 100 MHz real-time clock at its phase boundaries (kernel start, then
- * per layer before and after each grid barrier, then the end) as seen by the first and
+ * per layer at each hand-over between workgroups, then the end) as seen by the first and
  * the last workgroup into dev_out (device uint64 [2][n]; row 0 first workgroup, row 1 last;
  * slots past n are dropped). n = 0 turns it off. */
 q3_status q3_profile_trace(q3_engine* e, unsigned long long* dev_out, int32_t n);
