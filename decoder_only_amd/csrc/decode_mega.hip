@@ -67,6 +67,36 @@ __device__ __forceinline__ float dot8(const u32x4 w, const float* x) {
     return s;
 }
 
+// sum over i < N of dot8(w[i], x[(first + step i) * 8 ...]): every shared-memory read is
+// issued before the first multiply, and each chunk has its own accumulator.
+template <int N>
+__device__ __forceinline__ float dot_chunks(const u32x4* w, const float* x, int first, int step) {
+    f32x4 a[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(x + (first + step * i) * 8);
+        a[2 * i] = src[0];
+        a[2 * i + 1] = src[1];
+    }
+    float part[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x4& v = a[2 * i + (e >> 1)];
+            t += __uint_as_float(w[i][e] << 16) * v[(e & 1) * 2];
+            t += __uint_as_float(w[i][e] & 0xFFFF0000u) * v[(e & 1) * 2 + 1];
+        }
+        part[i] = t;
+    }
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+        for (int i = 0; i + h < N; i += 2 * h) part[i] += part[i + h];
+    return part[0];
+}
+
 // Loads through global-address-space pointers: the weight pointers come from a table in
 // memory, so the compiler cannot infer their address space and would emit flat loads,
 // which also count against the LDS wait counter -- every LDS access or lane shuffle would
@@ -112,8 +142,20 @@ struct Contig {
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)i; }
 };
 
+constexpr int STAGE = 256;       // K/V rows staged in shared memory per shot
+
 struct Smem {
-    float act[BMAX][F];            // activations of the current phase (x, h, a)
+    union {
+        struct {
+            float act[BMAX][F];            // activations of the current phase (x, h, a)
+            float part[MAXCH * 2 * PART];  // polled chunk partials (long context combine)
+            float wm[16][2][PART];         // attention state per (wave, 16-lane key group)
+        } s;
+        struct {                           // attention: staged cache rows of one kv head
+            bf16 k[STAGE][DH];
+            bf16 v[STAGE][DH];
+        } kv;
+    } u;
     float x0[BMAX][4];             // layer input x at this workgroup's residual rows 4w..4w+3
     float xr[BMAX][4];             // x' at those rows
     float red[BMAX][16];           // block reductions
@@ -121,13 +163,12 @@ struct Smem {
     float q[2][DH];                // rotated queries of the current group
     float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
     float o[BMAX][2 * DH];         // attention output of the group, per row
-    float wm[16][2][PART];         // attention state per (wave, 16-lane key group)
     float att[2][PART];            // merged attention state (max, sum, acc) per head
-    float part[MAXCH * 2 * PART];  // polled chunk partials (long context combine)
     float pr[BMAX * HKV * 4];      // polled O-projection partials of the residual rows
     float gu[24][BMAX];            // gate/up results
     MegaLayer layers[kMegaMaxLayers];
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "shared memory of one CU");
 
 // Per-thread values loaded together with a phase's weight slice: the RMSNorm weights of
 // its 4 elements, and for phase B the QK-norm weights of its RoPE pair and the frequency.
@@ -154,12 +195,12 @@ __device__ __forceinline__ int clamp_tok(const MegaParams& p, int b) {
 __device__ __forceinline__ void rmsnorm_act(const MegaParams& p, Smem& sm, int B, const f32x4 wv) {
     const int k = threadIdx.x * 4;
     for (int b = 0; b < B; ++b) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.act[b][k]);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][k]);
         float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
         ss = block_sum256(ss, sm.red[b]);
         const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.act[b][k + e] = (v[e] * r) * wv[e];
+        for (int e = 0; e < 4; ++e) sm.u.s.act[b][k + e] = (v[e] * r) * wv[e];
     }
     __syncthreads();
 }
@@ -229,79 +270,52 @@ __device__ __forceinline__ void trace_at(const MegaParams& p, int slot) {
         p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
-// K/V registers of one block of 64 keys: thread (wave wid, 16-lane group grp, lane sub)
-// holds dims 8 sub .. 8 sub + 7 of keys base + 4 wid + grp + 16 i, i < 4.
-struct KVBlk {
-    u32x4 k[4], v[4];
-};
-
 __device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, int b, int g) {
     return (size_t)layer * p.kv_layer_elems + (size_t)(p.seq_base + b) * p.kv_seq_elems + (size_t)g * p.t_cap * DH;
 }
 
-// Issue the loads of the block at `base` (keys < k1; slot T-1 is the new key, taken from
-// shared memory instead).
-__device__ __forceinline__ void kv_load(const MegaParams& p, size_t hb, int base, int k1, int T, KVBlk& blk) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int kk = base + wid * 4 + grp + 16 * i;
-        if (kk < k1 && kk != T - 1) {
-            blk.k[i] = ldw16(p.kc + hb + (size_t)kk * DH + sub * 8);
-            blk.v[i] = ldw16(p.vc + hb + (size_t)kk * DH + sub * 8);
+#define LDS_AS __attribute__((address_space(3)))
+
+// Issue asynchronous copies of cache rows base .. base+n-1 (n <= STAGE) of one kv head into
+// sm.u.kv (row i <- slot base + i), global -> LDS without registers: one instruction moves
+// 4 rows (64 lanes x 16 bytes, lane l to byte 16 l). Complete after s_waitcnt + barrier.
+__device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t hb, int base, int n) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int r0 = 4 * wid; r0 < n; r0 += 16) {
+        const int r = r0 + (lane >> 4);
+        if (r < n) {
+            const size_t off = hb + (size_t)(base + r) * DH + (lane & 15) * 8;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + off), (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + off), (LDS_AS void*)&sm.u.kv.v[r0][0], 16, 0, 0);
         }
     }
+}
+
+// cached rows of [k0, k1) in the first shot (slot T-1 is the new key, kept in shared memory)
+__device__ __forceinline__ int first_shot(int k0, int k1, int T) {
+    return max(0, min(min(k1, T - 1), k0 + STAGE) - k0);
 }
 
 struct AttState {
     float m[2], l[2], acc[2][8];
 };
 
-// Online-softmax update of both heads with the keys of one block.
-__device__ __forceinline__ void kv_compute(const Smem& sm, int base, int k1, int T, const KVBlk& blk,
-                                           const float (&qv)[2][8], AttState& st) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
-    const float scale = 0.088388346f;   // fl32(128^-0.5)
+__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int kk = base + wid * 4 + grp + 16 * i;
-        if (kk < k1) {                  // uniform over the 16 lanes of a key
-            float kv[8], vv[8];
-            if (kk == T - 1) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { kv[e] = sm.kn[sub * 8 + e]; vv[e] = sm.vn[sub * 8 + e]; }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kv[2 * e] = __uint_as_float(blk.k[i][e] << 16);
-                    kv[2 * e + 1] = __uint_as_float(blk.k[i][e] & 0xFFFF0000u);
-                    vv[2 * e] = __uint_as_float(blk.v[i][e] << 16);
-                    vv[2 * e + 1] = __uint_as_float(blk.v[i][e] & 0xFFFF0000u);
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float dsum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dsum += qv[h][e] * kv[e];
-                const float sc = sum16(dsum) * scale;
-                const float mn = fmaxf(st.m[h], sc);
-                const float corr = expf(st.m[h] - mn);
-                const float pr = expf(sc - mn);
-                st.l[h] = st.l[h] * corr + pr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * corr + pr * vv[e];
-                st.m[h] = mn;
-            }
-        }
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
 }
 
-// Attention of both heads of the group for row b over slots [k0, k1) of T visible ones;
-// `blk` holds the block at k0 (loaded by the caller before it waited for q/k/v). Leaves
-// the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
-__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, KVBlk& blk) {
+// Attention of both heads of the group for row b over slots [k0, k1) of T visible ones.
+// The caller issued the first shot (kv_stage of first_shot(k0, k1, T) rows at k0) and
+// waited for it; longer ranges are staged here shot by shot. Thread (wave wid, 16-lane
+// group grp, lane sub) takes rows wid*4 + grp + 16 i, two rows per step, dims 8 sub ..
+// 8 sub + 7. Leaves the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
+__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+    const float scale = 0.088388346f;   // fl32(128^-0.5)
     float qv[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -315,35 +329,87 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
     }
-    KVBlk nxt;
-    for (int base = k0; base < k1; base += 128) {   // two register blocks in flight
-        kv_load(p, hb, base + 64, k1, T, nxt);
-        kv_compute(sm, base, k1, T, blk, qv, st);
-        kv_load(p, hb, base + 128, k1, T, blk);
-        kv_compute(sm, base + 64, k1, T, nxt, qv, st);
+    const int ce = min(k1, T - 1);                 // end of the cached rows in range
+    for (int base = k0;; base += STAGE) {
+        const int n = max(0, min(ce, base + STAGE) - base);
+        if (base != k0) {
+            __syncthreads();
+            kv_stage(p, sm, hb, base, n);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        const bool last = base + STAGE >= ce;
+        const int nk = n + ((last && k1 == T) ? 1 : 0);   // row n = the new key
+        for (int r = wid * 4 + grp; r < nk; r += 32) {     // uniform over 16 lanes
+            const int r2 = r + 16;
+            float ka[8], va[8], kb[8], vb[8];
+            if (r < n) {
+                unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.k[r][sub * 8]), ka);
+                unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][sub * 8]), va);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { ka[e] = sm.kn[sub * 8 + e]; va[e] = sm.vn[sub * 8 + e]; }
+            }
+            const bool two = r2 < nk;
+            if (two) {
+                if (r2 < n) {
+                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.k[r2][sub * 8]), kb);
+                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r2][sub * 8]), vb);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { kb[e] = sm.kn[sub * 8 + e]; vb[e] = sm.vn[sub * 8 + e]; }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kb[e] = 0.f; vb[e] = 0.f; }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float da = 0.f, db = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { da += qv[h][e] * ka[e]; db += qv[h][e] * kb[e]; }
+                const float sa = sum16(da) * scale;
+                const float sb = two ? sum16(db) * scale : -INFINITY;
+                const float mn = fmaxf(st.m[h], fmaxf(sa, sb));
+                const float corr = expf(st.m[h] - mn);
+                const float pa = expf(sa - mn), pb = expf(sb - mn);
+                st.l[h] = st.l[h] * corr + (pa + pb);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * corr + (pa * va[e] + pb * vb[e]);
+                st.m[h] = mn;
+            }
+        }
+        if (last) break;
     }
+    __syncthreads();                               // the staged rows share memory with wm
     const int slot = wid * 4 + grp;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (sub == 0) { sm.wm[slot][h][0] = st.m[h]; sm.wm[slot][h][1] = st.l[h]; }
+        if (sub == 0) { sm.u.s.wm[slot][h][0] = st.m[h]; sm.u.s.wm[slot][h][1] = st.l[h]; }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.wm[slot][h][2 + sub * 8 + e] = st.acc[h][e];
+        for (int e = 0; e < 8; ++e) sm.u.s.wm[slot][h][2 + sub * 8 + e] = st.acc[h][e];
     }
     __syncthreads();
     {
+        // branch-free so that all 48 shared-memory reads issue back to back; an empty state
+        // (sum 0, max -inf) gets weight 0
         const int h = threadIdx.x >> 7, dd = threadIdx.x & 127;
+        float mv[16], lv[16], av[16];
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            mv[s2] = sm.u.s.wm[s2][h][0];
+            lv[s2] = sm.u.s.wm[s2][h][1];
+            av[s2] = sm.u.s.wm[s2][h][2 + dd];
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2)
-            if (sm.wm[s2][h][1] > 0.f) M = fmaxf(M, sm.wm[s2][h][0]);
+        for (int s2 = 0; s2 < 16; ++s2) M = fmaxf(M, lv[s2] > 0.f ? mv[s2] : -INFINITY);
         float Ls = 0.f, A = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2) {
-            if (sm.wm[s2][h][1] > 0.f) {
-                const float cf = expf(sm.wm[s2][h][0] - M);
-                Ls += sm.wm[s2][h][1] * cf;
-                A += sm.wm[s2][h][2 + dd] * cf;
-            }
+            const float cf = lv[s2] > 0.f ? expf(mv[s2] - M) : 0.f;
+            Ls += lv[s2] * cf;
+            A += av[s2] * cf;
         }
         if (dd == 0) { sm.att[h][0] = M; sm.att[h][1] = Ls; }
         sm.att[h][2 + dd] = A;
@@ -356,9 +422,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 __device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, u64* P, int g, int j, int B, unsigned tag) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     for (int b = 0; b < B; ++b) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += dot8(pf[i], &sm.o[b][(sub + 8 * i) * 8]);
+        float s = dot_chunks<4>(pf, sm.o[b], sub, 8);
         s = sum8(s);
         if (sub == 0) put(P + (size_t)b * W_P + (size_t)g * D + 32 * j + r, s, tag);
     }
@@ -459,22 +523,19 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         for (int b = 0; b < B; ++b) {
             if (layer == 0) {
                 const int t = clamp_tok(p, b);
-                for (int k = tid; k < D; k += NT) sm.act[b][k] = bf2f(p.embed[(size_t)t * D + k]);
-            } else if (!poll(X + (size_t)b * W_X, Contig{}, D, sm.act[b], tag, p.err)) {
+                for (int k = tid; k < D; k += NT) sm.u.s.act[b][k] = bf2f(p.embed[(size_t)t * D + k]);
+            } else if (!poll(X + (size_t)b * W_X, Contig{}, D, sm.u.s.act[b], tag, p.err)) {
                 return;
             }
         }
         __syncthreads();
-        if (tid < 4 * B) sm.x0[tid >> 2][tid & 3] = sm.act[tid >> 2][4 * w + (tid & 3)];
+        if (tid < 4 * B) sm.x0[tid >> 2][tid & 3] = sm.u.s.act[tid >> 2][4 * w + (tid & 3)];
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
         {
             const int r = tid >> 4, sub = tid & 15;
             for (int b = 0; b < B; ++b) {
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) s += dot8(pf[i], &sm.act[b][(sub + 16 * i) * 8]);
-                s = sum16(s);
+                const float s = sum16(dot_chunks<8>(pf, sm.u.s.act[b], sub, 16));
                 if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s, tag);
             }
         }
@@ -484,18 +545,19 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         // ---------------- B: attention of kv group g and its O-projection partial
         int Tmax = 0;
         for (int b = 0; b < B; ++b) Tmax = max(Tmax, p.slots[b] + 1);
+        __syncthreads();                  // act (read above) shares memory with the K/V staging
         if (Tmax <= SHORT_T) {
             for (int b = 0; b < B; ++b) {
                 const int slot = p.slots[b], T = slot + 1;
                 const int pos = p.positions ? p.positions[b] : slot;
                 const size_t hb = kv_head_base(p, layer, b, g);
-                KVBlk blk;
-                kv_load(p, hb, 0, T, T, blk);                 // in flight while q/k/v arrive
+                kv_stage(p, sm, hb, 0, first_shot(0, T, T));   // in flight while q/k/v arrive
                 const u64* qb = QKV + (size_t)b * W_QKV;
                 if (!poll(qb, [&](int i) { return group_word(g, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
                 if (b == 0) trace_at(p, tslot++);
                 group_prep(p, sm, pre, layer, b, g, pos, slot, j == 0);
-                attend(p, sm, hb, 0, T, T, blk);
+                attend(p, sm, hb, 0, T, T);
                 const int h = tid >> 7, dd = tid & 127;
                 sm.o[b][h * DH + dd] = sm.att[h][1] > 0.f ? sm.att[h][2 + dd] / sm.att[h][1] : 0.f;
                 __syncthreads();
@@ -511,13 +573,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (c < nch) {
                     const int k0 = c * ch, k1 = min(T, k0 + ch);
                     const size_t hb = kv_head_base(p, layer, b, gg);
-                    KVBlk blk;
-                    kv_load(p, hb, k0, k1, T, blk);
+                    kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
                     const u64* qb = QKV + (size_t)b * W_QKV;
                     if (!poll(qb, [&](int i) { return group_word(gg, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                    __builtin_amdgcn_s_waitcnt(0);
                     if (b == 0) trace_at(p, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, pos, slot, k1 == T);
-                    attend(p, sm, hb, k0, k1, T, blk);
+                    attend(p, sm, hb, k0, k1, T);
                     u64* pt = PT + (size_t)b * W_PT + (((size_t)gg * MAXCH + c) * 2) * PART;
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART], tag);
                     __syncthreads();
@@ -534,17 +596,17 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     const u64* src = PT + (size_t)b * W_PT + ((size_t)g * MAXCH) * 2 * PART;
                     for (int done = 0; done < nch * 2 * PART; done += 16 * NT) {   // pieces of 4096 words
                         const int n = min(16 * NT, nch * 2 * PART - done);
-                        if (!poll(src + done, Contig{}, n, sm.part + done, tag, p.err)) return;
+                        if (!poll(src + done, Contig{}, n, sm.u.s.part + done, tag, p.err)) return;
                     }
                     const int h = tid >> 7, dd = tid & 127;
                     float M = -INFINITY;
                     for (int c2 = 0; c2 < nch; ++c2) {
-                        const float* pp = sm.part + ((size_t)c2 * 2 + h) * PART;
+                        const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
                         if (pp[1] > 0.f) M = fmaxf(M, pp[0]);
                     }
                     float Ls = 0.f, Acc = 0.f;
                     for (int c2 = 0; c2 < nch; ++c2) {
-                        const float* pp = sm.part + ((size_t)c2 * 2 + h) * PART;
+                        const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
                         if (pp[1] > 0.f) {
                             const float cf = expf(pp[0] - M);
                             Ls += pp[1] * cf;
@@ -584,17 +646,14 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
         // ---------------- C: x' -> RMSNorm -> gate/up of 12 columns -> SwiGLU
         for (int b = 0; b < B; ++b)
-            if (!poll(XP + (size_t)b * W_XP, Contig{}, D, sm.act[b], tag, p.err)) return;
+            if (!poll(XP + (size_t)b * W_XP, Contig{}, D, sm.u.s.act[b], tag, p.err)) return;
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
         {
             const int rr = tid >> 3, sub = tid & 7;
             for (int b = 0; b < B; ++b) {
                 float s = 0.f;
-                if (rr < 24) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) s += dot8(pf[i], &sm.act[b][(sub + 8 * i) * 8]);
-                }
+                if (rr < 24) s = dot_chunks<16>(pf, sm.u.s.act[b], sub, 8);
                 s = sum8(s);
                 if (rr < 24 && sub == 0) sm.gu[rr][b] = s;
             }
@@ -610,15 +669,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
         // ---------------- D: rows 4w..4w+3 of down + residual
         for (int b = 0; b < B; ++b)
-            if (!poll(A + (size_t)b * W_A, Contig{}, F, sm.act[b], tag, p.err)) return;
+            if (!poll(A + (size_t)b * W_A, Contig{}, F, sm.u.s.act[b], tag, p.err)) return;
         trace_at(p, tslot++);
         {
             const int rr = tid >> 6, sub = tid & 63;
             const int n = 4 * w + rr;
             for (int b = 0; b < B; ++b) {
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < 6; ++i) s += dot8(pf[i], &sm.act[b][(sub + 64 * i) * 8]);
+                float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 64);
                 s = wave_sum(s);
                 if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s, tag);
             }
@@ -645,7 +702,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     {
         const u64* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
         for (int b = 0; b < B; ++b)
-            if (!poll(Xl + (size_t)b * W_X, Contig{}, D, sm.act[b], tag, p.err)) return;
+            if (!poll(Xl + (size_t)b * W_X, Contig{}, D, sm.u.s.act[b], tag, p.err)) return;
         __syncthreads();
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
@@ -659,10 +716,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             for (int b = 0; b < BMAX; ++b) {
                 if (b >= B) break;
                 float s = 0.f;
-                if (row < r1) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) s += dot8(wv[i], &sm.act[b][(sub + 16 * i) * 8]);
-                }
+                if (row < r1) s = dot_chunks<8>(wv, sm.u.s.act[b], sub, 16);
                 s = sum16(s);
                 if (row < r1 && sub == 0) {
                     p.logits[(size_t)b * p.vocab + row] = s;
