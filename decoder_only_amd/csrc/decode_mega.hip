@@ -7,28 +7,31 @@
 // small dependent operations; as separate kernels each costs ~4-8 us of launch and ramp.
 //
 // Synchronisation is dataflow, not barriers: every value one workgroup hands to another
-// is a 64-bit word (float bits | launch tag << 32) written with one coherent agent-scope
-// atomic store; the consumer polls exactly the words it needs until all carry this
-// launch's tag. One memory round trip thus carries both the data and the "it is ready"
-// signal (a grid barrier costs ~2 us on MI355X, plus a store acknowledgement before it
-// and a reload after it). Each layer has its own exchange buffers, so a word is written
-// once per launch; words left by an earlier or aborted launch carry an older tag and are
-// simply not ready yet.
+// is a float32 word in an exchange buffer that holds a sentinel NaN pattern until it is
+// written, with one coherent (agent-scope) store; the consumer polls exactly the words it
+// needs, 16 bytes per load with the coherent-load bit, until none holds the sentinel.
+// One memory round trip thus carries both the data and the "it is ready" signal. Each
+// layer has its own buffers, so a word is written once per launch; the small tail kernel
+// that follows every launch puts the sentinel back into every word the launch used (also
+// after a launch that gave up waiting). On MI355X one all-to-all hand-over among 256
+// workgroups takes ~2.3 us this way (~1.2 us between two), so the layout below is built
+// around needing only four per layer.
 //
-// Per layer, for each row b (hops = dependent exchanges):
-//   A  poll x (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]              -> QKV words
+// Per layer, for each row b (hand-overs marked ->):
+//   A  poll x (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]                -> QKV words
 //   B  workgroup (g, j), kv group g = query heads 2g, 2g+1, j < 32: poll the group's
 //      q/k/v (512) -> QK-norm + RoPE -> KV append (j == 0) -> attention of both heads,
-//      recomputed by the 32 workgroups of the group -> rows 32j..32j+31 of
-//      Wo[:, 256g:256g+256] . o                                     -> P[g] words
-//      (long context: split-K partials per (group, chunk), a combine per group, then
-//       the O-projection partial from the combined output)
-//   R  rows 4w..4w+3: x' = x + P[0] + ... + P[7] (fixed order)        -> X' words
-//   C  poll x' (1024) -> RMSNorm -> gate/up rows of 12 SwiGLU columns -> A words
-//   D  poll a (3072) -> rows 4w..4w+3: x'' = x' + Wd a                -> next x words
+//      recomputed by the 32 workgroups of the group (K/V staged through LDS) -> rows
+//      32j..32j+31 of Wo[:, 256g:256g+256] . o, plus x for g = 0         -> P[g] words
+//      (long context: split-K partials per (group, chunk), merged again by every
+//       workgroup of the group, then the same O-projection partial)
+//   C  poll P (8 x 1024): x' = P[0] + ... + P[7] (fixed order) -> RMSNorm -> gate/up
+//      rows of 12 SwiGLU columns                                       -> A words
+//   D  poll a (3072) -> rows 4w..4w+3: x'' = x' + Wd a                  -> next x words
 // then poll x, RMSNorm, 594 rows of the tied LM head per workgroup; each workgroup
-// writes its packed (logit, id) maximum per row, reduced by the sampling kernel. Each workgroup issues the loads of its next weight slice
-// right after finishing a phase, so HBM streaming overlaps the waiting.
+// writes its packed (logit, id) maximum per row, reduced by a small tail kernel. Each
+// workgroup issues the loads of its next weight slice right after finishing a phase, so
+// HBM streaming overlaps the waiting.
 // Fixed shape: hidden 1024, 16 query / 8 kv heads of 128, FFN 3072, bf16 weights and KV
 // cache, 1..4 rows.
 #include "common.h"
@@ -49,11 +52,17 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 // words per (layer, row) in each exchange buffer
-constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_XP = D, W_A = F, W_O = (size_t)HKV * 2 * DH;
-constexpr size_t W_PT = (size_t)HKV * MAXCH * 2 * PART;
+constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_A = F;
+constexpr size_t W_PT = (size_t)MAXCH * HKV * 2 * PART;   // [chunk][group][head][PART]
+constexpr int PT_CHUNK = HKV * 2 * PART;                     // words per chunk index
 
-__device__ __forceinline__ void put(u64* p, float v, unsigned tag) {
-    __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+constexpr unsigned SENT = 0x7FC0DEADu;   // "not written yet" (a NaN no computation yields)
+constexpr int SC1 = 16;                  // cache-policy bit of an agent-coherent access
+
+__device__ __forceinline__ void put(float* p, float v) {
+    unsigned u = __float_as_uint(v);
+    if (u == SENT) u = 0x7FC00000u;      // keep real NaNs distinguishable from "not written"
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // 8 bf16 (one 16-byte chunk) dotted with 8 floats.
@@ -106,40 +115,48 @@ __device__ __forceinline__ u32x4 ldw16(const bf16* p) { return *(const GLOBAL_AS
 __device__ __forceinline__ f32x4 ldf4(const float* p) { return *(const GLOBAL_AS f32x4*)(p); }
 __device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS float*)(p); }
 
-// Poll words src[idx(i)], i < n (n <= 16 * 256), into dst[i] until every one carries
-// `tag`. Thread t owns i = t + 256 k and re-reads only what it still misses. Returns
-// false after ~0.1 s without completion (the caller then leaves the kernel).
-template <typename IDX>
-__device__ __forceinline__ bool poll(const u64* src, IDX idx, int n, float* dst, unsigned tag, unsigned* err) {
+// Poll the 16-byte chunks cidx(i), i < nch (nch <= K * 256; cidx = word offset of the
+// chunk's first word from `base`, a multiple of 4), into dst[4 i .. 4 i + 3] until none of
+// their words holds the sentinel. Thread t owns chunks t + 256 k and re-reads only those
+// it still misses; a wave leaves the loop as soon as all its lanes are done, then one
+// barrier joins the workgroup. `words` bounds the buffer (reads past it return zero
+// instead of touching other memory). Returns false after ~0.1 s without completion (the
+// caller then leaves the kernel, and so, through their own waits, do all others).
+template <int K, typename CIDX>
+__device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx, int nch, float* dst, unsigned* err) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(words * 4), 0x00020000);
     unsigned todo = 0;
-    for (int k = 0; k < 16 && threadIdx.x + NT * k < n; ++k) todo |= 1u << k;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if ((int)threadIdx.x + NT * k < nch) todo |= 1u << k;
     int spins = 0;
+    bool ok = true;
     for (;;) {
-        if (todo) {
-            u64 v[16];
+        u32x4 v[K];
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                if (todo & (1u << k))
-                    v[k] = __hip_atomic_load(src + idx(threadIdx.x + NT * k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < K; ++k)
+            if (todo & (1u << k))
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cidx(threadIdx.x + NT * k) * 4), 0, SC1);
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                if ((todo & (1u << k)) && (unsigned)(v[k] >> 32) == tag) {
-                    dst[threadIdx.x + NT * k] = __uint_as_float((unsigned)v[k]);
-                    todo &= ~(1u << k);
-                }
+        for (int k = 0; k < K; ++k) {
+            if ((todo & (1u << k)) && v[k][0] != SENT && v[k][1] != SENT && v[k][2] != SENT && v[k][3] != SENT) {
+                *reinterpret_cast<u32x4*>(dst + 4 * (threadIdx.x + NT * k)) = v[k];
+                todo &= ~(1u << k);
             }
         }
-        if (__syncthreads_and(todo == 0)) return true;
+        if (!__any(todo != 0)) break;
         if (++spins > (1 << 16)) {
-            if (threadIdx.x == 0) atomicOr(err, Q3_DEVERR_SYNC);
-            return false;
+            atomicOr(err, Q3_DEVERR_SYNC);
+            ok = false;
+            break;
         }
-        __builtin_amdgcn_s_sleep(2);
     }
+    return __syncthreads_and(ok);
 }
 
-struct Contig {
-    __device__ __forceinline__ size_t operator()(int i) const { return (size_t)i; }
+struct Contig {   // chunk i at word 4 i
+    __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
 };
 
 constexpr int STAGE = 256;       // K/V rows staged in shared memory per shot
@@ -156,15 +173,14 @@ struct Smem {
             bf16 v[STAGE][DH];
         } kv;
     } u;
-    float x0[BMAX][4];             // layer input x at this workgroup's residual rows 4w..4w+3
-    float xr[BMAX][4];             // x' at those rows
+    float xg[BMAX][32];            // layer input x at rows 32j..32j+31 (phase-B row block)
+    float xr[BMAX][4];             // x' at this workgroup's residual rows 4w..4w+3
     float red[BMAX][16];           // block reductions
     float in[BMAX][4 * DH];        // polled group inputs: q (2 x 128), k (128), v (128)
     float q[2][DH];                // rotated queries of the current group
     float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
     float o[BMAX][2 * DH];         // attention output of the group, per row
     float att[2][PART];            // merged attention state (max, sum, acc) per head
-    float pr[BMAX * HKV * 4];      // polled O-projection partials of the residual rows
     float gu[24][BMAX];            // gate/up results
     MegaLayer layers[kMegaMaxLayers];
 };
@@ -419,12 +435,14 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 
 // P[b][g][32j + r] = Wo[32j + r, 256g:256g+256] . o[b]; thread t: row r = t >> 3,
 // 16-byte chunks sub + 8i (i < 4) of the 32 in the row segment.
-__device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, u64* P, int g, int j, int B, unsigned tag) {
+// Group 0's partial also carries the residual x, so x' = P[0] + ... + P[7].
+__device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, float* P, int g, int j, int B) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<4>(pf, sm.o[b], sub, 8);
         s = sum8(s);
-        if (sub == 0) put(P + (size_t)b * W_P + (size_t)g * D + 32 * j + r, s, tag);
+        if (g == 0) s = sm.xg[b][r] + s;
+        if (sub == 0) put(P + (size_t)b * W_P + (size_t)g * D + 32 * j + r, s);
     }
 }
 
@@ -469,17 +487,17 @@ __device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int w) {
 }
 
 // long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
-__device__ __forceinline__ void chunking(int T, int& nch, int& ch) {
+__host__ __device__ __forceinline__ void chunking(int T, int& nch, int& ch) {
     nch = min(MAXCH, (T + 63) / 64);
     ch = ((T + nch - 1) / nch + 63) & ~63;
     nch = (T + ch - 1) / ch;
 }
 
-// index of element i of group gg's inputs within a row's QKV words:
-// q heads 2gg, 2gg+1 (256) | k head gg (128) | v head gg (128)
-__device__ __forceinline__ size_t group_word(int gg, int i) {
-    return i < 256 ? (size_t)256 * gg + i
-                   : (i < 384 ? (size_t)HQ * DH + DH * gg + (i - 256) : (size_t)(HQ + HKV) * DH + DH * gg + (i - 384));
+// word offset of chunk i (4 words) of group gg's inputs within a row's QKV words:
+// q heads 2gg, 2gg+1 (64 chunks) | k head gg (32) | v head gg (32)
+__device__ __forceinline__ size_t group_chunk(int gg, int i) {
+    return i < 64 ? (size_t)256 * gg + 4 * i
+                  : (i < 96 ? (size_t)HQ * DH + DH * gg + 4 * (i - 64) : (size_t)(HQ + HKV) * DH + DH * gg + 4 * (i - 96));
 }
 
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
@@ -487,7 +505,6 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int B = p.B;
-    const unsigned tag = p.tag;
     u32x4 pf[16];
     Pre pre;
     const int g = w >> 5, j = w & 31;       // kv group and row block of phase B
@@ -510,33 +527,31 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
     for (int layer = 0; layer < p.n_layers; ++layer) {
         const MegaLayer& L = sm.layers[layer];
-        u64* X = p.ex + (size_t)layer * p.ex_layer;          // layer input x
-        u64* QKV = X + (size_t)BMAX * W_X;
-        u64* P = QKV + (size_t)BMAX * W_QKV;
-        u64* XP = P + (size_t)BMAX * W_P;
-        u64* A = XP + (size_t)BMAX * W_XP;
-        u64* O = A + (size_t)BMAX * W_A;                      // combined attention (long context)
-        u64* PT = O + (size_t)BMAX * W_O;                     // chunk partials (long context)
-        u64* Xn = X + p.ex_layer;                             // next layer's input
+        float* X = p.ex + (size_t)layer * p.ex_layer;        // layer input x
+        float* QKV = X + (size_t)BMAX * W_X;
+        float* P = QKV + (size_t)BMAX * W_QKV;                // O-projection partials per kv group
+        float* A = P + (size_t)BMAX * W_P;
+        float* PT = A + (size_t)BMAX * W_A;                   // chunk partials (long context)
+        float* Xn = X + p.ex_layer;                           // next layer's input
 
         // ---------------- A: x -> RMSNorm -> QKV rows 16w .. 16w+15
         for (int b = 0; b < B; ++b) {
             if (layer == 0) {
                 const int t = clamp_tok(p, b);
                 for (int k = tid; k < D; k += NT) sm.u.s.act[b][k] = bf2f(p.embed[(size_t)t * D + k]);
-            } else if (!poll(X + (size_t)b * W_X, Contig{}, D, sm.u.s.act[b], tag, p.err)) {
+            } else if (!poll<1>(X + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) {
                 return;
             }
         }
         __syncthreads();
-        if (tid < 4 * B) sm.x0[tid >> 2][tid & 3] = sm.u.s.act[tid >> 2][4 * w + (tid & 3)];
+        if (tid < 32 * B) sm.xg[tid >> 5][tid & 31] = sm.u.s.act[tid >> 5][32 * j + (tid & 31)];
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
         {
             const int r = tid >> 4, sub = tid & 15;
             for (int b = 0; b < B; ++b) {
                 const float s = sum16(dot_chunks<8>(pf, sm.u.s.act[b], sub, 16));
-                if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s, tag);
+                if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s);
             }
         }
         pf_oproj(L, pf, g, j);
@@ -552,8 +567,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 const int pos = p.positions ? p.positions[b] : slot;
                 const size_t hb = kv_head_base(p, layer, b, g);
                 kv_stage(p, sm, hb, 0, first_shot(0, T, T));   // in flight while q/k/v arrive
-                const u64* qb = QKV + (size_t)b * W_QKV;
-                if (!poll(qb, [&](int i) { return group_word(g, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
+                    return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
                 if (b == 0) trace_at(p, tslot++);
                 group_prep(p, sm, pre, layer, b, g, pos, slot, j == 0);
@@ -574,79 +589,67 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     const int k0 = c * ch, k1 = min(T, k0 + ch);
                     const size_t hb = kv_head_base(p, layer, b, gg);
                     kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
-                    const u64* qb = QKV + (size_t)b * W_QKV;
-                    if (!poll(qb, [&](int i) { return group_word(gg, i); }, 4 * DH, sm.in[b], tag, p.err)) return;
+                    if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(gg, i); }, DH, sm.in[b],
+                                 p.err))
+                        return;
                     __builtin_amdgcn_s_waitcnt(0);
                     if (b == 0) trace_at(p, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, pos, slot, k1 == T);
                     attend(p, sm, hb, k0, k1, T);
-                    u64* pt = PT + (size_t)b * W_PT + (((size_t)gg * MAXCH + c) * 2) * PART;
-                    for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART], tag);
+                    float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
+                    for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
                     trace_at(p, tslot++);
                 }
             }
-            // combine: workgroup 32g (j == 0) merges group g's chunks into O[b][g]
-            if (j == 0) {
-                for (int b = 0; b < B; ++b) {
-                    const int T = p.slots[b] + 1;
-                    int nch, ch;
-                    chunking(T, nch, ch);
-                    const u64* src = PT + (size_t)b * W_PT + ((size_t)g * MAXCH) * 2 * PART;
-                    for (int done = 0; done < nch * 2 * PART; done += 16 * NT) {   // pieces of 4096 words
-                        const int n = min(16 * NT, nch * 2 * PART - done);
-                        if (!poll(src + done, Contig{}, n, sm.u.s.part + done, tag, p.err)) return;
-                    }
-                    const int h = tid >> 7, dd = tid & 127;
-                    float M = -INFINITY;
-                    for (int c2 = 0; c2 < nch; ++c2) {
-                        const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
-                        if (pp[1] > 0.f) M = fmaxf(M, pp[0]);
-                    }
-                    float Ls = 0.f, Acc = 0.f;
-                    for (int c2 = 0; c2 < nch; ++c2) {
-                        const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
-                        if (pp[1] > 0.f) {
-                            const float cf = expf(pp[0] - M);
-                            Ls += pp[1] * cf;
-                            Acc += pp[2 + dd] * cf;
-                        }
-                    }
-                    put(O + (size_t)b * W_O + (size_t)g * 2 * DH + h * DH + dd, Ls > 0.f ? Acc / Ls : 0.f, tag);
-                    __syncthreads();
+            // combine: every workgroup of group g merges the group's chunks itself (one
+            // hand-over instead of a combine workgroup followed by a broadcast)
+            for (int b = 0; b < B; ++b) {
+                const int T = p.slots[b] + 1;
+                int nch, ch;
+                chunking(T, nch, ch);
+                // chunk i: partial c = i / 65, 16-byte piece i % 65 of group g's 260 words
+                auto pidx = [&](int i) -> size_t {
+                    return (size_t)(i / 65) * PT_CHUNK + (size_t)g * 2 * PART + 4 * (i % 65);
+                };
+                if (!poll<9>(PT + (size_t)b * W_PT, W_PT, pidx, nch * 65, sm.u.s.part, p.err)) return;
+                const int h = tid >> 7, dd = tid & 127;
+                float M = -INFINITY;
+                for (int c2 = 0; c2 < nch; ++c2) {
+                    const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
+                    M = fmaxf(M, pp[1] > 0.f ? pp[0] : -INFINITY);
                 }
+                float Ls = 0.f, Acc = 0.f;
+                for (int c2 = 0; c2 < nch; ++c2) {
+                    const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
+                    const float cf = pp[1] > 0.f ? expf(pp[0] - M) : 0.f;
+                    Ls += pp[1] * cf;
+                    Acc += pp[2 + dd] * cf;
+                }
+                sm.o[b][h * DH + dd] = Ls > 0.f ? Acc / Ls : 0.f;
+                __syncthreads();
             }
-            for (int b = 0; b < B; ++b)
-                if (!poll(O + (size_t)b * W_O + (size_t)g * 2 * DH, Contig{}, 2 * DH, sm.o[b], tag, p.err)) return;
         }
         trace_at(p, tslot++);
-        oproj_partial(sm, pf, P, g, j, B, tag);
+        oproj_partial(sm, pf, P, g, j, B);
         pf_gu(L, pf, pre, w);
         trace_at(p, tslot++);
 
-        // ---------------- R: x'[4w .. 4w+3] = x + P[0] + ... + P[7]
-        {
-            // word i: row b = i / 32, partial gg = (i / 4) % 8, element e = i % 4
-            auto pidx = [&](int i) -> size_t {
-                return (size_t)(i >> 5) * W_P + (size_t)((i >> 2) & 7) * D + 4 * w + (i & 3);
-            };
-            if (!poll(P, pidx, 32 * B, sm.pr, tag, p.err)) return;
-            if (tid < 4 * B) {
-                const int b = tid >> 2, e = tid & 3, n = 4 * w + e;
-                float xv = sm.x0[b][e];
+        // ---------------- C: x' = P[0] + ... + P[7] -> RMSNorm -> gate/up of 12 columns -> SwiGLU
+        for (int b = 0; b < B; ++b) {
+            if (!poll<8>(P + (size_t)b * W_P, W_P, Contig{}, HKV * D / 4, sm.u.s.part, p.err)) return;
+            const int n = 4 * tid;
 #pragma unroll
-                for (int gg = 0; gg < HKV; ++gg) xv += sm.pr[b * 32 + gg * 4 + e];
-                sm.xr[b][e] = xv;
-                put(XP + (size_t)b * W_XP + n, xv, tag);
+            for (int e = 0; e < 4; ++e) {
+                float xv = sm.u.s.part[n + e];
+#pragma unroll
+                for (int gg = 1; gg < HKV; ++gg) xv += sm.u.s.part[gg * D + n + e];
+                sm.u.s.act[b][n + e] = xv;
             }
             __syncthreads();
         }
-        trace_at(p, tslot++);
-
-        // ---------------- C: x' -> RMSNorm -> gate/up of 12 columns -> SwiGLU
-        for (int b = 0; b < B; ++b)
-            if (!poll(XP + (size_t)b * W_XP, Contig{}, D, sm.u.s.act[b], tag, p.err)) return;
+        if (tid < 4 * B) sm.xr[tid >> 2][tid & 3] = sm.u.s.act[tid >> 2][4 * w + (tid & 3)];
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
         {
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             if (tid < 12 * B) {
                 const int c = tid % 12, b = tid / 12;
                 const float gt = sm.gu[c][b], up = sm.gu[12 + c][b];
-                put(A + (size_t)b * W_A + 12 * w + c, gt / (1.0f + expf(-gt)) * up, tag);
+                put(A + (size_t)b * W_A + 12 * w + c, gt / (1.0f + expf(-gt)) * up);
             }
         }
         pf_down(L, pf, w);
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
         // ---------------- D: rows 4w..4w+3 of down + residual
         for (int b = 0; b < B; ++b)
-            if (!poll(A + (size_t)b * W_A, Contig{}, F, sm.u.s.act[b], tag, p.err)) return;
+            if (!poll<3>(A + (size_t)b * W_A, W_A, Contig{}, F / 4, sm.u.s.act[b], p.err)) return;
         trace_at(p, tslot++);
         {
             const int rr = tid >> 6, sub = tid & 63;
@@ -677,7 +680,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             for (int b = 0; b < B; ++b) {
                 float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 64);
                 s = wave_sum(s);
-                if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s, tag);
+                if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s);
             }
         }
         if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
@@ -700,9 +703,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     load_rows(r0, b0);                             // in flight while the last layer finishes
     load_rows(r0 + 16, b1);
     {
-        const u64* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
+        const float* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
         for (int b = 0; b < B; ++b)
-            if (!poll(Xl + (size_t)b * W_X, Contig{}, D, sm.u.s.act[b], tag, p.err)) return;
+            if (!poll<1>(Xl + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
         __syncthreads();
         trace_at(p, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
@@ -759,33 +762,76 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 }  // namespace
 
 size_t decode_mega_exchange_words_per_layer() {
-    return (size_t)BMAX * (W_X + W_QKV + W_P + W_XP + W_A + W_O + W_PT);
+    return (size_t)BMAX * (W_X + W_QKV + W_P + W_A + W_PT);
 }
 
-// Tail of a persistent decode step: amax[b] = max over the 256 workgroup candidates of
-// row b (packed logit key | ~id), and the sequence lengths advance by one.
+// Tail of a persistent decode step, run after every launch (also one that gave up):
+// blocks b < B: amax[b] = max over the 256 workgroup candidates of row b (packed logit
+// key | ~id) and lens[seq_base + b] += 1; all blocks: the sentinel back into every
+// exchange word the launch may have written -- per layer, rows < B of x, q/k/v, P and a,
+// and pt_words words of chunk partials per row -- with coherent stores.
 __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
-                            int seq_base, int B) {
-    const int b = blockIdx.x;
-    u64 v = cand[(size_t)b * NWG + threadIdx.x];
-    for (int o = 32; o >= 1; o >>= 1) {
-        const u64 t = __shfl_xor(v, o, 64);
-        v = t > v ? t : v;
+                            int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words) {
+    if ((int)blockIdx.x < B) {
+        const int b = blockIdx.x;
+        u64 v = cand[(size_t)b * NWG + threadIdx.x];
+        for (int o = 32; o >= 1; o >>= 1) {
+            const u64 t = __shfl_xor(v, o, 64);
+            v = t > v ? t : v;
+        }
+        __shared__ u64 r[4];
+        if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 0; i < 4; ++i) v = r[i] > v ? r[i] : v;
+            amax[b] = v;
+            lens[seq_base + b] += 1;
+        }
     }
-    __shared__ u64 r[4];
-    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int i = 0; i < 4; ++i) v = r[i] > v ? r[i] : v;
-        amax[b] = v;
-        lens[seq_base + b] += 1;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)ex, (short)0, (int)((size_t)(n_layers + 1) * ex_layer * 4), 0x00020000);
+    const u32x4 sv = {SENT, SENT, SENT, SENT};
+    const int nseg = (n_layers + 1) * 5 * B;
+    for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
+        const int l = seg / (5 * B), kind = (seg % (5 * B)) / B, b = seg % B;
+        if (l == n_layers && kind != 0) continue;       // past the last layer only x exists
+        size_t off = (size_t)l * ex_layer;
+        int cnt;
+        if (kind == 0) { off += (size_t)b * W_X; cnt = (int)W_X; }
+        else if (kind == 1) { off += BMAX * W_X + (size_t)b * W_QKV; cnt = (int)W_QKV; }
+        else if (kind == 2) { off += BMAX * (W_X + W_QKV) + (size_t)b * W_P; cnt = (int)W_P; }
+        else if (kind == 3) { off += BMAX * (W_X + W_QKV + W_P) + (size_t)b * W_A; cnt = (int)W_A; }
+        else { off += BMAX * (W_X + W_QKV + W_P + W_A) + (size_t)b * W_PT; cnt = pt_words; }
+        for (int i = 4 * threadIdx.x; i < cnt; i += 4 * blockDim.x)
+            __builtin_amdgcn_raw_buffer_store_b128(sv, rs, (int)((off + i) * 4), 0, SC1);
     }
+}
+
+__global__ void k_mega_fill(float* ex, size_t words) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)ex, (short)0, (int)(words * 4), 0x00020000);
+    const u32x4 sv = {SENT, SENT, SENT, SENT};
+    for (size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x); i < words; i += 4 * (size_t)gridDim.x * blockDim.x)
+        __builtin_amdgcn_raw_buffer_store_b128(sv, rs, (int)(i * 4), 0, SC1);
 }
 
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, hipStream_t s) {
-    if (B < 1 || B > BMAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_mega_tail, dim3(B), dim3(NWG), 0, s, cand, amax, lens, seq_base, B);
+                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, hipStream_t s) {
+    if (B < 1 || B > BMAX || n_layers < 1 || ex_layer != decode_mega_exchange_words_per_layer())
+        return hipErrorInvalidValue;
+    int pt_words = 0;
+    if (Tmax > SHORT_T) {
+        int nch, ch;
+        chunking(Tmax, nch, ch);
+        pt_words = nch * PT_CHUNK;
+    }
+    hipLaunchKernelGGL(k_mega_tail, dim3(NWG), dim3(NT), 0, s, cand, amax, lens, seq_base, B, ex, ex_layer, n_layers,
+                       pt_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
+    if (words % 4 || words * 4 > 0x7FFFFFF0ull) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_mega_fill, dim3(1024), dim3(256), 0, s, ex, words);
     return hipGetLastError();
 }
 

@@ -76,9 +76,8 @@ struct q3_engine {
     bool mega_ok = false;          // shape supported and co-residency possible
     int decode_path = 0;           // 0 auto, 1 per-kernel launches, 2 persistent kernel, 3 auto with ordinary launch
     MegaLayer* d_layers = nullptr;
-    unsigned long long* m_ex = nullptr;      // tagged exchange words, (n_layers + 1) layers
+    float* m_ex = nullptr;                   // exchange words, (n_layers + 1) layers
     size_t m_ex_layer = 0;
-    unsigned m_tag = 0;                      // tag of the last launch (words start at tag 0)
     unsigned long long* m_cand = nullptr;    // per-workgroup argmax candidates
     unsigned long long* m_trace = nullptr;   // caller's device buffer for phase timestamps
     int m_trace_n = 0;
@@ -324,9 +323,9 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
             }
             if (!(e->d_layers = (MegaLayer*)upload(hl.data(), hl.size() * sizeof(MegaLayer)))) return oom();
             e->m_ex_layer = decode_mega_exchange_words_per_layer();
-            const size_t exb = ((size_t)c.n_layers + 1) * e->m_ex_layer * 8;
-            if (!(e->m_ex = (unsigned long long*)e->alloc(exb))) return oom();
-            if (hipMemset(e->m_ex, 0, exb) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
+            const size_t exw = ((size_t)c.n_layers + 1) * e->m_ex_layer;
+            if (!(e->m_ex = (float*)e->alloc(exw * 4))) return oom();
+            if (launch_mega_fill(e->m_ex, exw, e->stream) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
             if (!(e->m_cand = (unsigned long long*)e->alloc((size_t)kMegaMaxRows * kMegaWorkgroups * 8))) return oom();
         }
     }
@@ -407,11 +406,6 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         mp.t_cap = c.max_seq;
         for (int b = 0; b < B; ++b) mp.slots[b] = e->h_len[seq_base + b];
         mp.eps = c.rms_eps;
-        if (++e->m_tag == 0) {   // wrapped: words still hold old tags, so restart from a clean buffer
-            HIPCHK(e, launch_fill_u64(e->m_ex, 0ull, (int)(((size_t)c.n_layers + 1) * e->m_ex_layer), s));
-            e->m_tag = 1;
-        }
-        mp.tag = e->m_tag;
         mp.layers = e->d_layers;
         mp.embed = (const uint16_t*)e->embed;
         mp.final_norm = e->final_norm;
@@ -433,7 +427,8 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
         HIPCHK(e, launch_decode_mega(mp, e->decode_path != 3, s));
         prof_mark(e, Q3_PROF_DECODE_STEP, false);
-        HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, seq_base, B, s));
+        HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, seq_base, B, e->m_ex, e->m_ex_layer, c.n_layers, maxT,
+                                   s));
         e->cur_logits = lg;
         e->cur_rows = B;
         for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;

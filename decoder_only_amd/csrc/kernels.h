@@ -73,7 +73,6 @@ struct MegaParams {
     int n_layers, vocab, B, seq_base, t_cap;
     int slots[4];                   // cache slot (= current length) of each row
     float eps;
-    unsigned tag;                   // launch tag (>= 1, increasing)
     const MegaLayer* layers;        // device array [n_layers]
     const uint16_t* embed;
     const float *final_norm, *inv_freq;
@@ -81,7 +80,7 @@ struct MegaParams {
     size_t kv_layer_elems, kv_seq_elems;
     const int32_t* tokens;
     const int32_t* positions;       // may be NULL (position = slot)
-    unsigned long long* ex;         // tagged exchange words, (n_layers + 1) * ex_layer
+    float* ex;                      // exchange words (sentinel = not written), (n_layers + 1) * ex_layer
     size_t ex_layer;
     float* logits;
     unsigned long long* cand;       // [4][256] per-workgroup argmax candidates
@@ -92,9 +91,12 @@ struct MegaParams {
 hipError_t decode_mega_prepare();
 // cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s);
-// argmax over the per-workgroup candidates and lens[seq_base + b] += 1 (after each launch)
+// After each launch: argmax over the per-workgroup candidates, lens[seq_base + b] += 1,
+// and the sentinel back into the exchange words used (Tmax = longest visible length).
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, hipStream_t s);
+                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, hipStream_t s);
+// Sentinel into all `words` exchange words (at load).
+hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);
 size_t decode_mega_exchange_words_per_layer();
 constexpr int kMegaMaxRows = 4;
 constexpr int kMegaMaxLayers = 64;
