@@ -46,10 +46,11 @@ constexpr int NWG = 256, NT = 256;
 constexpr int BMAX = 4;
 constexpr int PART = 2 + DH;     // (max, sum, acc[128]) per (chunk, head)
 constexpr int MAXCH = 32;        // attention chunks per kv group (long context)
-constexpr int SHORT_T = 256;     // visible slots up to which every group workgroup attends itself
+constexpr int SHORT_T = 240;     // visible slots up to which every group workgroup attends itself
 typedef unsigned long long u64;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 // words per (layer, row) in each exchange buffer
 constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_A = F;
@@ -159,7 +160,8 @@ struct Contig {   // chunk i at word 4 i
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
 };
 
-constexpr int STAGE = 256;       // K/V rows staged in shared memory per shot
+constexpr int STAGE = 256;       // K/V rows of the staging area
+constexpr int SHOT = 240;        // cached rows staged per shot (the new key follows them)
 
 struct Smem {
     union {
@@ -181,6 +183,8 @@ struct Smem {
     float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
     float o[BMAX][2 * DH];         // attention output of the group, per row
     float att[2][PART];            // merged attention state (max, sum, acc) per head
+    float sp[2][STAGE];            // scores, then probabilities, of the staged keys per head
+    float hs[2][4];                // per-head softmax statistics of a shot
     float gu[24][BMAX];            // gate/up results
     MegaLayer layers[kMegaMaxLayers];
 };
@@ -309,12 +313,8 @@ __device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t h
 
 // cached rows of [k0, k1) in the first shot (slot T-1 is the new key, kept in shared memory)
 __device__ __forceinline__ int first_shot(int k0, int k1, int T) {
-    return max(0, min(min(k1, T - 1), k0 + STAGE) - k0);
+    return max(0, min(min(k1, T - 1), k0 + SHOT) - k0);
 }
-
-struct AttState {
-    float m[2], l[2], acc[2][8];
-};
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
@@ -324,111 +324,141 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
+// float32 x[8] -> bf16 hi and lo parts (x = hi + lo + O(2^-17 x)), as MFMA operands.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16 h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
+        const bf16 l0 = f2bf(x[2 * e] - bf2f(h0)), l1 = f2bf(x[2 * e + 1] - bf2f(h1));
+        h[e] = (unsigned)h0 | ((unsigned)h1 << 16);
+        l[e] = (unsigned)l0 | ((unsigned)l1 << 16);
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Attention of both heads of the group for row b over slots [k0, k1) of T visible ones.
 // The caller issued the first shot (kv_stage of first_shot(k0, k1, T) rows at k0) and
-// waited for it; longer ranges are staged here shot by shot. Thread (wave wid, 16-lane
-// group grp, lane sub) takes rows wid*4 + grp + 16 i, two rows per step, dims 8 sub ..
-// 8 sub + 7. Leaves the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
+// waited for it; longer ranges are staged here shot by shot (SHOT rows; the new key, kept
+// in shared memory, is appended as the row after the cached ones of the last shot).
+// Per shot: scores S^T = K q^T on the matrix cores (16 keys x 16 columns per tile, columns
+// 0 and 1 the two heads; K rows are exact bf16 operands, q is split into bf16 hi + lo),
+// then the shot's softmax statistics per head, then P.V on the vector units with 16 lane
+// groups of 16 lanes (8 dims per lane), and a rescale of the running state between shots.
+// Leaves the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
 __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
     const float scale = 0.088388346f;   // fl32(128^-0.5)
-    float qv[2][8];
+    bf16x8 qh[4], ql[4];                // B operand: lane holds q[head col][32 ks + 8 quad + i]
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        if (col < 2) {
+            split8(&sm.q[col][32 * ks + 8 * quad], qh[ks], ql[ks]);
+        } else {
+            qh[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            ql[ks] = qh[ks];
+        }
+    }
+    float Mh[2] = {-INFINITY, -INFINITY}, Lh[2] = {0.f, 0.f}, acc[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[h][e] = sm.q[h][sub * 8 + e];
-    AttState st;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        st.m[h] = -INFINITY;
-        st.l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
-    }
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     const int ce = min(k1, T - 1);                 // end of the cached rows in range
-    for (int base = k0;; base += STAGE) {
-        const int n = max(0, min(ce, base + STAGE) - base);
+    for (int base = k0;; base += SHOT) {
+        const int n = max(0, min(ce, base + SHOT) - base);
         if (base != k0) {
             __syncthreads();
             kv_stage(p, sm, hb, base, n);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        const bool last = base + STAGE >= ce;
-        const int nk = n + ((last && k1 == T) ? 1 : 0);   // row n = the new key
-        for (int r = wid * 4 + grp; r < nk; r += 32) {     // uniform over 16 lanes
-            const int r2 = r + 16;
-            float ka[8], va[8], kb[8], vb[8];
-            if (r < n) {
-                unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.k[r][sub * 8]), ka);
-                unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][sub * 8]), va);
-            } else {
+        const bool last = base + SHOT >= ce;
+        const bool with_new = last && k1 == T;
+        const int nk = n + (with_new ? 1 : 0);
+        if (with_new && tid < 32) {                // the new key / value as staged row n
+            const float* src = tid < 16 ? sm.kn : sm.vn;
+            bf16* dst = tid < 16 ? &sm.u.kv.k[n][0] : &sm.u.kv.v[n][0];
+            const int e0 = 8 * (tid & 15);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { ka[e] = sm.kn[sub * 8 + e]; va[e] = sm.vn[sub * 8 + e]; }
+            for (int e = 0; e < 8; ++e) dst[e0 + e] = f2bf(src[e0 + e]);   // exact: already bf16 values
+        }
+        __syncthreads();
+        // scores of 16-key tiles, tile t on wave t % 4
+        const int ntile = (nk + 15) >> 4;
+        for (int t = wid; t < ntile; t += 4) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][32 * ks + 8 * quad]);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sc, 0, 0, 0);
             }
-            const bool two = r2 < nk;
-            if (two) {
-                if (r2 < n) {
-                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.k[r2][sub * 8]), kb);
-                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r2][sub * 8]), vb);
-                } else {
+            if (col < 2) {                         // D[key 4 quad + r][head col]
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) { kb[e] = sm.kn[sub * 8 + e]; vb[e] = sm.vn[sub * 8 + e]; }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { kb[e] = 0.f; vb[e] = 0.f; }
+                for (int r = 0; r < 4; ++r) sm.sp[col][16 * t + 4 * quad + r] = sc[r] * scale;
             }
+        }
+        __syncthreads();
+        // softmax statistics of the shot: head h = tid / 128 over keys i and i + 128;
+        // hs[h][0..1] = maxima of the head's two waves, hs[h][2..3] = their sums
+        {
+            const int h = tid >> 7, i = tid & 127;
+            const float x0 = i < nk ? sm.sp[h][i] : -INFINITY;
+            const float x1 = i + 128 < nk ? sm.sp[h][i + 128] : -INFINITY;
+            const float wmx = wave_max(fmaxf(x0, x1));
+            if (lane == 0) sm.hs[h][wid & 1] = wmx;
+            __syncthreads();
+            const float Mn = fmaxf(Mh[h], fmaxf(sm.hs[h][0], sm.hs[h][1]));
+            const float p0 = i < nk ? expf(x0 - Mn) : 0.f;
+            const float p1 = i + 128 < nk ? expf(x1 - Mn) : 0.f;
+            sm.sp[h][i] = p0;
+            sm.sp[h][i + 128] = p1;
+            const float ws = wave_sum(p0 + p1);
+            if (lane == 0) sm.hs[h][2 + (wid & 1)] = ws;
+            __syncthreads();
+        }
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float da = 0.f, db = 0.f;
+        for (int h = 0; h < 2; ++h) {
+            const float Mn = fmaxf(Mh[h], fmaxf(sm.hs[h][0], sm.hs[h][1]));
+            const float corr = Lh[h] > 0.f ? expf(Mh[h] - Mn) : 0.f;
+            Lh[h] = Lh[h] * corr + (sm.hs[h][2] + sm.hs[h][3]);
+            Mh[h] = Mn;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { da += qv[h][e] * ka[e]; db += qv[h][e] * kb[e]; }
-                const float sa = sum16(da) * scale;
-                const float sb = two ? sum16(db) * scale : -INFINITY;
-                const float mn = fmaxf(st.m[h], fmaxf(sa, sb));
-                const float corr = expf(st.m[h] - mn);
-                const float pa = expf(sa - mn), pb = expf(sb - mn);
-                st.l[h] = st.l[h] * corr + (pa + pb);
+            for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
+        }
+        // P.V: lane group (wid, quad) takes keys wid*4 + quad + 16 i, lane col dims 8 col ..
+        for (int r = wid * 4 + quad; r < nk; r += 16) {
+            float v[8];
+            unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]), v);
+            const float p0 = sm.sp[0][r], p1 = sm.sp[1][r];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * corr + (pa * va[e] + pb * vb[e]);
-                st.m[h] = mn;
+            for (int e = 0; e < 8; ++e) {
+                acc[0][e] += p0 * v[e];
+                acc[1][e] += p1 * v[e];
             }
         }
         if (last) break;
     }
     __syncthreads();                               // the staged rows share memory with wm
-    const int slot = wid * 4 + grp;
+    const int slot = wid * 4 + quad;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (sub == 0) { sm.u.s.wm[slot][h][0] = st.m[h]; sm.u.s.wm[slot][h][1] = st.l[h]; }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.u.s.wm[slot][h][2 + sub * 8 + e] = st.acc[h][e];
-    }
+        for (int e = 0; e < 8; ++e) sm.u.s.wm[slot][h][8 * col + e] = acc[h][e];
     __syncthreads();
     {
-        // branch-free so that all 48 shared-memory reads issue back to back; an empty state
-        // (sum 0, max -inf) gets weight 0
-        const int h = threadIdx.x >> 7, dd = threadIdx.x & 127;
-        float mv[16], lv[16], av[16];
+        const int h = tid >> 7, dd = tid & 127;
+        float av[16];
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
-            mv[s2] = sm.u.s.wm[s2][h][0];
-            lv[s2] = sm.u.s.wm[s2][h][1];
-            av[s2] = sm.u.s.wm[s2][h][2 + dd];
-        }
-        float M = -INFINITY;
+        for (int s2 = 0; s2 < 16; ++s2) av[s2] = sm.u.s.wm[s2][h][dd];
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) M = fmaxf(M, lv[s2] > 0.f ? mv[s2] : -INFINITY);
-        float Ls = 0.f, A = 0.f;
+        for (int hh = 1; hh < 16; hh <<= 1)
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
-            const float cf = lv[s2] > 0.f ? expf(mv[s2] - M) : 0.f;
-            Ls += lv[s2] * cf;
-            A += av[s2] * cf;
-        }
-        if (dd == 0) { sm.att[h][0] = M; sm.att[h][1] = Ls; }
-        sm.att[h][2 + dd] = A;
+            for (int s2 = 0; s2 + hh < 16; s2 += 2 * hh) av[s2] += av[s2 + hh];
+        if (dd == 0) { sm.att[h][0] = Mh[h]; sm.att[h][1] = Lh[h]; }
+        sm.att[h][2 + dd] = av[0];
     }
     __syncthreads();
 }
