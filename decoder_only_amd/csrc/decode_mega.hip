@@ -160,6 +160,7 @@ struct Contig {   // chunk i at word 4 i
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
 };
 
+constexpr int TRACE_MAX = 400;   // phase timestamps kept per traced workgroup
 constexpr int STAGE = 256;       // K/V rows of the staging area
 constexpr int SHOT = 240;        // cached rows staged per shot (the new key follows them)
 
@@ -187,6 +188,7 @@ struct Smem {
     float hs[2][4];                // per-head softmax statistics of a shot
     float gu[24][BMAX];            // gate/up results
     MegaLayer layers[kMegaMaxLayers];
+    unsigned long long tr[TRACE_MAX];   // phase timestamps (trace only)
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "shared memory of one CU");
 
@@ -284,10 +286,16 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* a, float 
 }
 
 // Optional trace: thread 0 of workgroups 0 and NWG-1 records the 100 MHz real-time clock
-// at phase boundaries into p.trace[{0,1}][slot].
-__device__ __forceinline__ void trace_at(const MegaParams& p, int slot) {
-    if (p.trace && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == NWG - 1) && slot < p.trace_n)
-        p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + slot] = __builtin_amdgcn_s_memrealtime();
+// at phase boundaries, in shared memory (a global store here would hold up the next wait
+// on the memory counter); the kernel's end copies the marks to p.trace[{0,1}][slot].
+__device__ __forceinline__ void trace_at(const MegaParams& p, Smem& sm, int slot) {
+    if (p.trace && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == NWG - 1) && slot < TRACE_MAX)
+        sm.tr[slot] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void trace_flush(const MegaParams& p, const Smem& sm, int n) {
+    if (p.trace && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == NWG - 1))
+        for (int i = 0; i < n && i < p.trace_n && i < TRACE_MAX; ++i)
+            p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + i] = sm.tr[i];
 }
 
 __device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, int b, int g) {
@@ -299,14 +307,21 @@ __device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, i
 // Issue asynchronous copies of cache rows base .. base+n-1 (n <= STAGE) of one kv head into
 // sm.u.kv (row i <- slot base + i), global -> LDS without registers: one instruction moves
 // 4 rows (64 lanes x 16 bytes, lane l to byte 16 l). Complete after s_waitcnt + barrier.
+// K rows are stored swizzled: 16-byte chunk c of row r sits in slot c ^ (r & 15) (lane l
+// loads the chunk that belongs in its slot), so the 16 rows of a matrix-core fragment read
+// at one column hit 16 different bank groups.
+__device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }
+
 __device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t hb, int base, int n) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int r0 = 4 * wid; r0 < n; r0 += 16) {
-        const int r = r0 + (lane >> 4);
+        const int r = r0 + (lane >> 4), sl = lane & 15;
         if (r < n) {
-            const size_t off = hb + (size_t)(base + r) * DH + (lane & 15) * 8;
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + off), (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + off), (LDS_AS void*)&sm.u.kv.v[r0][0], 16, 0, 0);
+            const size_t row = hb + (size_t)(base + r) * DH;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r, sl)),
+                                             (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl), (LDS_AS void*)&sm.u.kv.v[r0][0],
+                                             16, 0, 0);
         }
     }
 }
@@ -378,11 +393,11 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
         const bool with_new = last && k1 == T;
         const int nk = n + (with_new ? 1 : 0);
         if (with_new && tid < 32) {                // the new key / value as staged row n
-            const float* src = tid < 16 ? sm.kn : sm.vn;
-            bf16* dst = tid < 16 ? &sm.u.kv.k[n][0] : &sm.u.kv.v[n][0];
-            const int e0 = 8 * (tid & 15);
+            const int c = tid & 15;
+            const float* src = (tid < 16 ? sm.kn : sm.vn) + 8 * c;
+            bf16* dst = tid < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e0 + e] = f2bf(src[e0 + e]);   // exact: already bf16 values
+            for (int e = 0; e < 8; ++e) dst[e] = f2bf(src[e]);   // exact: already bf16 values
         }
         __syncthreads();
         // scores of 16-key tiles, tile t on wave t % 4
@@ -391,7 +406,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][32 * ks + 8 * quad]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][8 * kslot(col, 4 * ks + quad)]);
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sc, 0, 0, 0);
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sc, 0, 0, 0);
             }
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     __syncthreads();
     pf_qkv(p, sm.layers[0], pf, pre, w);
     int tslot = 0;
-    trace_at(p, tslot++);
+    trace_at(p, sm, tslot++);
 
     for (int layer = 0; layer < p.n_layers; ++layer) {
         const MegaLayer& L = sm.layers[layer];
@@ -575,8 +590,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         __syncthreads();
         if (tid < 32 * B) sm.xg[tid >> 5][tid & 31] = sm.u.s.act[tid >> 5][32 * j + (tid & 31)];
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
+        trace_at(p, sm, tslot++);
         {
             const int r = tid >> 4, sub = tid & 15;
             for (int b = 0; b < B; ++b) {
@@ -585,7 +601,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             }
         }
         pf_oproj(L, pf, g, j);
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
 
         // ---------------- B: attention of kv group g and its O-projection partial
         int Tmax = 0;
@@ -600,8 +616,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
-                if (b == 0) trace_at(p, tslot++);
+                if (b == 0) trace_at(p, sm, tslot++);
                 group_prep(p, sm, pre, layer, b, g, pos, slot, j == 0);
+                if (b == 0) trace_at(p, sm, tslot++);
                 attend(p, sm, hb, 0, T, T);
                 const int h = tid >> 7, dd = tid & 127;
                 sm.o[b][h * DH + dd] = sm.att[h][1] > 0.f ? sm.att[h][2 + dd] / sm.att[h][1] : 0.f;
@@ -623,14 +640,16 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                                  p.err))
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
-                    if (b == 0) trace_at(p, tslot++);
+                    if (b == 0) trace_at(p, sm, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, pos, slot, k1 == T);
+                    if (b == 0) trace_at(p, sm, tslot++);
                     attend(p, sm, hb, k0, k1, T);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
-                    trace_at(p, tslot++);
+                    trace_at(p, sm, tslot++);
+                    trace_at(p, sm, tslot++);
                 }
             }
             // combine: every workgroup of group g merges the group's chunks itself (one
@@ -661,14 +680,15 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 __syncthreads();
             }
         }
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         oproj_partial(sm, pf, P, g, j, B);
         pf_gu(L, pf, pre, w);
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
 
         // ---------------- C: x' = P[0] + ... + P[7] -> RMSNorm -> gate/up of 12 columns -> SwiGLU
         for (int b = 0; b < B; ++b) {
             if (!poll<8>(P + (size_t)b * W_P, W_P, Contig{}, HKV * D / 4, sm.u.s.part, p.err)) return;
+            if (b == 0) trace_at(p, sm, tslot++);
             const int n = 4 * tid;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -680,8 +700,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             __syncthreads();
         }
         if (tid < 4 * B) sm.xr[tid >> 2][tid & 3] = sm.u.s.act[tid >> 2][4 * w + (tid & 3)];
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
+        trace_at(p, sm, tslot++);
         {
             const int rr = tid >> 3, sub = tid & 7;
             for (int b = 0; b < B; ++b) {
@@ -698,12 +719,12 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             }
         }
         pf_down(L, pf, w);
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
 
         // ---------------- D: rows 4w..4w+3 of down + residual
         for (int b = 0; b < B; ++b)
             if (!poll<3>(A + (size_t)b * W_A, W_A, Contig{}, F / 4, sm.u.s.act[b], p.err)) return;
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         {
             const int rr = tid >> 6, sub = tid & 63;
             const int n = 4 * w + rr;
@@ -715,7 +736,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
         else pre.nw = ldf4(p.final_norm + 4 * tid);
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         __syncthreads();
     }
 
@@ -737,7 +758,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         for (int b = 0; b < B; ++b)
             if (!poll<1>(Xl + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
         __syncthreads();
-        trace_at(p, tslot++);
+        trace_at(p, sm, tslot++);
         rmsnorm_act(p, sm, B, pre.nw);
     }
     u64 best[BMAX] = {0ull, 0ull, 0ull, 0ull};
@@ -786,7 +807,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         for (int wv = 1; wv < 4; ++wv) v = wbest[wv][tid] > v ? wbest[wv][tid] : v;
         p.cand[(size_t)tid * NWG + w] = v;
     }
-    trace_at(p, tslot++);
+    trace_at(p, sm, tslot++);
+    trace_flush(p, sm, tslot);
 }
 
 }  // namespace
@@ -797,11 +819,13 @@ size_t decode_mega_exchange_words_per_layer() {
 
 // Tail of a persistent decode step, run after every launch (also one that gave up):
 // blocks b < B: amax[b] = max over the 256 workgroup candidates of row b (packed logit
-// key | ~id) and lens[seq_base + b] += 1; all blocks: the sentinel back into every
+// key | ~id), lens[seq_base + b] += 1 and, when greedy_out is given, the greedy token
+// (Step 8's argmax, lowest id on ties); all blocks: the sentinel back into every
 // exchange word the launch may have written -- per layer, rows < B of x, q/k/v, P and a,
 // and pt_words words of chunk partials per row -- with coherent stores.
 __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
-                            int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words) {
+                            int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words,
+                            int32_t* __restrict__ greedy_out) {
     if ((int)blockIdx.x < B) {
         const int b = blockIdx.x;
         u64 v = cand[(size_t)b * NWG + threadIdx.x];
@@ -816,6 +840,7 @@ __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax
             for (int i = 0; i < 4; ++i) v = r[i] > v ? r[i] : v;
             amax[b] = v;
             lens[seq_base + b] += 1;
+            if (greedy_out) greedy_out[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
         }
     }
     const __amdgpu_buffer_rsrc_t rs =
@@ -845,7 +870,8 @@ __global__ void k_mega_fill(float* ex, size_t words) {
 }
 
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, hipStream_t s) {
+                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, int32_t* greedy_out,
+                            hipStream_t s) {
     if (B < 1 || B > BMAX || n_layers < 1 || ex_layer != decode_mega_exchange_words_per_layer())
         return hipErrorInvalidValue;
     int pt_words = 0;
@@ -855,7 +881,7 @@ hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* 
         pt_words = nch * PT_CHUNK;
     }
     hipLaunchKernelGGL(k_mega_tail, dim3(NWG), dim3(NT), 0, s, cand, amax, lens, seq_base, B, ex, ex_layer, n_layers,
-                       pt_words);
+                       pt_words, greedy_out);
     return hipGetLastError();
 }
 

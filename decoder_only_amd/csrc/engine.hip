@@ -79,6 +79,10 @@ struct q3_engine {
     float* m_ex = nullptr;                   // exchange words, (n_layers + 1) layers
     size_t m_ex_layer = 0;
     unsigned long long* m_cand = nullptr;    // per-workgroup argmax candidates
+    // The tail of the last persistent launch is deferred to the next call, so that a greedy
+    // q3_sample right after it is the same launch.
+    bool tail_pending = false;
+    int tail_B = 0, tail_seq_base = 0, tail_maxT = 0;
     unsigned long long* m_trace = nullptr;   // caller's device buffer for phase timestamps
     int m_trace_n = 0;
 
@@ -301,6 +305,7 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
     if (!(e->logits = (float*)e->alloc((size_t)B * V * 4))) return oom();
     if (!(e->amax = (unsigned long long*)e->alloc((size_t)B * 8))) return oom();
     if (!(e->sample_ws = e->alloc(sample_workspace_bytes(V, B)))) return oom();
+    if (hipMemset(e->sample_ws, 0, sample_workspace_bytes(V, B)) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
     e->attn_ws_T = c.max_seq;
     if (!(e->attn_ws = (float*)e->alloc(attn_decode_workspace_bytes(B, Hkv, c.max_seq)))) return oom();
     // persistent decode kernel: fixed layer shape, bf16 weights and cache, one workgroup per CU
@@ -350,6 +355,16 @@ extern "C" int32_t q3_seq_len(const q3_engine* e, int32_t seq) {
     return e->h_len[seq];
 }
 
+// Launch the deferred tail of the last persistent decode launch (greedy_out: also write the
+// greedy tokens of its rows).
+static q3_status flush_tail(q3_engine* e, int32_t* greedy_out = nullptr) {
+    if (!e->tail_pending) return Q3_OK;
+    e->tail_pending = false;
+    HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, e->tail_seq_base, e->tail_B, e->m_ex, e->m_ex_layer,
+                               e->cfg.n_layers, e->tail_maxT, greedy_out, e->stream));
+    return Q3_OK;
+}
+
 // Algorithmic K/V bytes read by one decode step (all layers): 2 * Hkv * 128 * kv bytes per
 // visible slot and layer.
 static double kv_read_bytes(const q3_engine* e, int seq_base, int B) {
@@ -385,6 +400,7 @@ static double attn_prefill_flops(int M, int t0, int Hq) {
 
 static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* positions,
                             int seq_base, int B, float* logits_out, bool want_logits) {
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;   // the previous launch's tail first
     const q3_config& c = e->cfg;
     const int d = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
     const int wdt = c.weight_dtype == Q3_BF16 ? DT_BF16 : DT_F32;
@@ -427,8 +443,10 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
         HIPCHK(e, launch_decode_mega(mp, e->decode_path != 3, s));
         prof_mark(e, Q3_PROF_DECODE_STEP, false);
-        HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, seq_base, B, e->m_ex, e->m_ex_layer, c.n_layers, maxT,
-                                   s));
+        e->tail_pending = true;
+        e->tail_B = B;
+        e->tail_seq_base = seq_base;
+        e->tail_maxT = maxT;
         e->cur_logits = lg;
         e->cur_rows = B;
         for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;
@@ -534,6 +552,7 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
 
 extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens, int32_t n, float* logits) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
     if (!tokens || n < 1) return e->fail(Q3_ERR_ARG, "tokens is NULL or n < 1");
     if ((int64_t)e->h_len[seq] + n > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
@@ -552,6 +571,7 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
 extern "C" q3_status q3_decode_step(q3_engine* e, const int32_t* tokens, const int32_t* positions,
                                     int32_t batch, float* logits) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (!tokens || batch < 1 || batch > e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "bad tokens or batch");
     for (int b = 0; b < batch; ++b)
         if (e->h_len[b] + 1 > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
@@ -565,6 +585,11 @@ extern "C" q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch,
     if (!(temperature >= 0.f)) return e->fail(Q3_ERR_ARG, "temperature must be >= 0");
     if (temperature > 0.f && !uniforms) return e->fail(Q3_ERR_ARG, "uniforms required when temperature > 0");
     const int V = e->cfg.vocab;
+    if (e->tail_pending && temperature == 0.f && !logits && batch == e->tail_B) {
+        // greedy pick of the persistent launch's rows: fused into its tail
+        return flush_tail(e, tokens_out);
+    }
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (!logits) {
         if (!e->cur_logits || batch > e->cur_rows) return e->fail(Q3_ERR_STATE, "no current logits for that many rows");
         logits = e->cur_logits;
@@ -572,12 +597,13 @@ extern "C" q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch,
         HIPCHK(e, launch_argmax_rows(logits, e->amax, V, batch, e->d_err, e->stream));
     }
     HIPCHK(e, launch_sample(logits, e->amax, V, batch, temperature, top_p, uniforms, tokens_out,
-                            e->sample_ws, e->stream));
+                            e->sample_ws, true, e->stream));
     return Q3_OK;
 }
 
 extern "C" q3_status q3_reset(q3_engine* e, int32_t seq) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
     int32_t zero = 0;
     HIPCHK(e, hipMemcpyAsync(e->d_len + seq, &zero, 4, hipMemcpyHostToDevice, e->stream));
@@ -589,6 +615,7 @@ extern "C" q3_status q3_reset(q3_engine* e, int32_t seq) {
 extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k, const void* v,
                                   int32_t len) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     const q3_config& c = e->cfg;
     if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !k || !v || len < 0)
         return e->fail(Q3_ERR_ARG, "bad kv_import arguments");
@@ -610,6 +637,7 @@ extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, cons
 
 extern "C" q3_status q3_sync(q3_engine* e) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     HIPCHK(e, hipStreamSynchronize(e->stream));
     unsigned flags = 0, zero = 0;
     HIPCHK(e, hipMemcpyAsync(&flags, e->d_err, 4, hipMemcpyDeviceToHost, e->stream));
@@ -627,6 +655,7 @@ extern "C" q3_status q3_sync(q3_engine* e) {
 
 extern "C" q3_status q3_profile_begin(q3_engine* e, int32_t kind) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (kind < Q3_PROF_OFF || kind > Q3_PROF_ATTN_PREFILL) return e->fail(Q3_ERR_ARG, "bad profile kind");
     HIPCHK(e, hipStreamSynchronize(e->stream));
     e->prof.kind = kind;
@@ -639,6 +668,7 @@ extern "C" q3_status q3_profile_begin(q3_engine* e, int32_t kind) {
 extern "C" q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, double* bytes,
                                     double* flops) {
     if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     HIPCHK(e, hipStreamSynchronize(e->stream));
     double ms = 0;
     for (size_t i = 0; i + 1 < e->prof.used; i += 2) {

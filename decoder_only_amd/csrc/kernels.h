@@ -92,9 +92,11 @@ hipError_t decode_mega_prepare();
 // cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s);
 // After each launch: argmax over the per-workgroup candidates, lens[seq_base + b] += 1,
-// and the sentinel back into the exchange words used (Tmax = longest visible length).
+// the sentinel back into the exchange words used (Tmax = longest visible length), and the
+// greedy token of each row into greedy_out when it is not NULL.
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, hipStream_t s);
+                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, int32_t* greedy_out,
+                            hipStream_t s);
 // Sentinel into all `words` exchange words (at load).
 hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);
 size_t decode_mega_exchange_words_per_layer();
@@ -107,8 +109,10 @@ hipError_t launch_argmax_rows(const float* logits, unsigned long long* amax, int
                               unsigned* err, hipStream_t s);
 hipError_t launch_greedy(const unsigned long long* amax, int32_t* out, int B, hipStream_t s);
 size_t sample_workspace_bytes(int V, int B);
+// ws: sample_workspace_bytes; the select kernel leaves it zeroed, so a workspace that was
+// zeroed once and is only used here may pass ws_zeroed = true.
 hipError_t launch_sample(const float* logits, const unsigned long long* amax, int V, int B,
                          float temperature, float top_p, const float* u, int32_t* out, void* ws,
-                         hipStream_t s);
+                         bool ws_zeroed, hipStream_t s);
 
 }  // namespace q3

@@ -105,6 +105,6 @@ extern "C" q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, flo
     void* ws = (char*)sc.p + amax_bytes + 256;
     hipError_t e = hipMemsetAsync(err, 0, 4, s);
     if (e == hipSuccess) e = launch_argmax_rows(logits, amax, V, B, err, s);
-    if (e == hipSuccess) e = launch_sample(logits, amax, V, B, temperature, top_p, uniforms, tokens_out, ws, s);
+    if (e == hipSuccess) e = launch_sample(logits, amax, V, B, temperature, top_p, uniforms, tokens_out, ws, false, s);
     return st(e);
 }

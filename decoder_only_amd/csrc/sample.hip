@@ -191,7 +191,7 @@ __global__ __launch_bounds__(1024) void k_sample_select(const float* __restrict_
                                                         const u64* __restrict__ amax, int V,
                                                         double Td, double scale, float top_p,
                                                         const float* __restrict__ u,
-                                                        const u64* __restrict__ ws,
+                                                        u64* __restrict__ ws,
                                                         int32_t* __restrict__ out) {
     __shared__ u64 scan_lds[16];
     __shared__ u64 h2[256];
@@ -221,6 +221,10 @@ __global__ __launch_bounds__(1024) void k_sample_select(const float* __restrict_
     if (thrB < 1) thrB = 1;
     select_first(l, hist, V, Td, zmax, scale, thrB, scan_lds, h2, &st);
     if (threadIdx.x == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
+    // leave the row's histogram zeroed for the next call
+    __syncthreads();
+    u64* hw = ws + (size_t)b * RowWs::words + RowWs::hist;
+    for (int k = 0; k < 64; ++k) hw[64 * threadIdx.x + k] = 0ull;
 }
 
 }  // namespace
@@ -247,7 +251,7 @@ size_t sample_workspace_bytes(int V, int B) {
 
 hipError_t launch_sample(const float* logits, const unsigned long long* amax, int V, int B,
                          float temperature, float top_p, const float* u, int32_t* out, void* ws,
-                         hipStream_t s) {
+                         bool ws_zeroed, hipStream_t s) {
     if (B <= 0) return hipSuccess;
     if (temperature == 0.f) return launch_greedy(amax, out, B, s);
     int lg = 0;
@@ -255,8 +259,8 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     const double scale = ldexp(1.0, 63 - lg);
     const double Td = (double)temperature;
     u64* w = (u64*)ws;
-    hipError_t e = launch_fill_u64(w, 0ull, (int)(B * RowWs::words), s);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * RowWs::words), s)) != hipSuccess) return e;
     const int nblk = (V + 255) / 256 < 512 ? (V + 255) / 256 : 512;
     hipLaunchKernelGGL(k_sample_hist, dim3(nblk, B), dim3(256), 0, s, logits, amax, V, Td, scale, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
