@@ -54,9 +54,10 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
     lo = __builtin_bit_cast(bf16x8, u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
 }
 
+template <bool PAIR>
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
                                                       const bf16* __restrict__ vc, int t_cap, int M, int t0,
-                                                      int Hq, int Hkv, float* __restrict__ o) {
+                                                      int Hq, int Hkv, void* __restrict__ o) {
     __shared__ u32x4 sK[BKV * 16];
     __shared__ bf16 sVT[128 * BKV];
     const int nqt = (M + BQ - 1) / BQ;
@@ -205,22 +206,44 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         const int row = qbase + c * 16 + l16;
         if (row >= M) continue;
         const float inv = 1.0f / lrow[c];
-        float* orow = o + (size_t)row * Hq * 128 + h * 128;
+        if constexpr (PAIR) {
+            // bf16 pair row: Hq*128 hi parts, then Hq*128 lo parts
+            const size_t HD = (size_t)Hq * 128;
+            bf16* orow = static_cast<bf16*>(o) + (size_t)row * 2 * HD + h * 128;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            *reinterpret_cast<f32x4*>(orow + dt * 16 + lg * 4) =
-                f32x4{oacc[dt][c][0] * inv, oacc[dt][c][1] * inv, oacc[dt][c][2] * inv, oacc[dt][c][3] * inv};
+            for (int dt = 0; dt < 8; ++dt) {
+                unsigned hw[2], lw[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float a0 = oacc[dt][c][2 * e] * inv, a1 = oacc[dt][c][2 * e + 1] * inv;
+                    const bf16 h0 = f2bf(a0), h1 = f2bf(a1);
+                    hw[e] = (unsigned)h0 | ((unsigned)h1 << 16);
+                    lw[e] = (unsigned)f2bf(a0 - bf2f(h0)) | ((unsigned)f2bf(a1 - bf2f(h1)) << 16);
+                }
+                *reinterpret_cast<u32x2*>(orow + dt * 16 + lg * 4) = u32x2{hw[0], hw[1]};
+                *reinterpret_cast<u32x2*>(orow + HD + dt * 16 + lg * 4) = u32x2{lw[0], lw[1]};
+            }
+        } else {
+            float* orow = static_cast<float*>(o) + (size_t)row * Hq * 128 + h * 128;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<f32x4*>(orow + dt * 16 + lg * 4) =
+                    f32x4{oacc[dt][c][0] * inv, oacc[dt][c][1] * inv, oacc[dt][c][2] * inv, oacc[dt][c][3] * inv};
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, float* o, hipStream_t s) {
+                               int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (Hq != 2 * Hkv) return hipErrorInvalidValue;
     dim3 grid((M + BQ - 1) / BQ, Hkv);
-    hipLaunchKernelGGL(k_attn_prefill, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    if (o_pair)
+        hipLaunchKernelGGL(k_attn_prefill<true>, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    else
+        hipLaunchKernelGGL(k_attn_prefill<false>, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
     return hipGetLastError();
 }
 

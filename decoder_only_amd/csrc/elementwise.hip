@@ -34,9 +34,11 @@ hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, in
     return hipGetLastError();
 }
 
-template <typename OT>
+// MODE 0: float32 out [rows][d]; 1: bf16 [rows][d]; 2: bf16 pair rows [rows][2d]
+// (hi = bf16(v) in the first d, lo = bf16(v - hi) in the second d).
+template <int MODE>
 __global__ void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w,
-                          OT* __restrict__ out, int d, float eps) {
+                          void* __restrict__ out, int d, float eps) {
     __shared__ float red[16];
     const int r = blockIdx.x;
     const float* xr = x + (size_t)r * d;
@@ -44,20 +46,28 @@ __global__ void k_rmsnorm(const float* __restrict__ x, const float* __restrict__
     for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
     ss = block_sum(ss, red);
     const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-    OT* o = out + (size_t)r * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
         const float v = (xr[i] * rs) * w[i];
-        if constexpr (sizeof(OT) == 2) o[i] = f2bf(v); else o[i] = v;
+        if constexpr (MODE == 0) {
+            static_cast<float*>(out)[(size_t)r * d + i] = v;
+        } else if constexpr (MODE == 1) {
+            static_cast<bf16*>(out)[(size_t)r * d + i] = f2bf(v);
+        } else {
+            bf16* o = static_cast<bf16*>(out) + (size_t)r * 2 * d;
+            const bf16 h = f2bf(v);
+            o[i] = h;
+            o[d + i] = f2bf(v - bf2f(h));
+        }
     }
 }
 
-hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_bf16, int rows, int d,
+hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_mode, int rows, int d,
                           float eps, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (out_bf16)
-        hipLaunchKernelGGL(k_rmsnorm<bf16>, dim3(rows), dim3(256), 0, s, x, w, (bf16*)out, d, eps);
-    else
-        hipLaunchKernelGGL(k_rmsnorm<float>, dim3(rows), dim3(256), 0, s, x, w, (float*)out, d, eps);
+    if (out_mode == 0) hipLaunchKernelGGL(k_rmsnorm<0>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
+    else if (out_mode == 1) hipLaunchKernelGGL(k_rmsnorm<1>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
+    else if (out_mode == 2) hipLaunchKernelGGL(k_rmsnorm<2>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

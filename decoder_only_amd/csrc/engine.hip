@@ -504,6 +504,7 @@ static q3_status ensure_prefill_ws(q3_engine* e, int M) {
     e->pf_cap = 0;
     if (!(e->pf_x = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
     if (!(e->pf_qkv = (float*)e->alloc((size_t)M * e->qkv_rows() * 4))) return Q3_ERR_OOM;
+    // pf_h, pf_o, pf_a hold bf16 hi/lo pair rows (same bytes as float32)
     if (!(e->pf_h = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
     if (!(e->pf_q = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
     if (!(e->pf_o = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
@@ -525,24 +526,25 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
         const auto& L = e->layers[l];
         uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
         uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 0, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 2, M, d, c.rms_eps, s));
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * e->qkv_rows() * d);
-        HIPCHK(e, launch_gemm(e->pf_h, 1, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d, GEMM_F32, s));
+        HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d,
+                              GEMM_F32, s));
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
                                          e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
         prof_mark(e, Q3_PROF_ATTN_PREFILL, true, 0, attn_prefill_flops(M, t0, Hq));
-        HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, s));
+        HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, 1, s));
         prof_mark(e, Q3_PROF_ATTN_PREFILL, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * Hq * 128);
-        HIPCHK(e, launch_gemm(e->pf_o, 1, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+        HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
         prof_mark(e, Q3_PROF_GEMM, false);
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 0, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 2, M, d, c.rms_eps, s));
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * 2 * F * d);
-        HIPCHK(e, launch_gemm(e->pf_h, 1, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_F32, s));
+        HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_PAIR, s));
         prof_mark(e, Q3_PROF_GEMM, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * F);
-        HIPCHK(e, launch_gemm(e->pf_a, 1, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+        HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
         prof_mark(e, Q3_PROF_GEMM, false);
     }
     HIPCHK(e, launch_len_advance(e->d_len, seq, 1, M, s));

@@ -1,19 +1,21 @@
-// Prefill projections on the matrix cores: C = A W^T with A [M, K] bf16 activations and
+// Prefill projections on the matrix cores: C = A W^T with A [M, K] activations and
 // W [N, K] bf16 weights in the [out, in] layout of the article's projections
 // ("Inside an LLM ...", Step 5 q/k/v/o, Step 6 gate/up/down), float32 accumulation.
 //
-// Block tile 128 x 128 x 64, four waves in a 2 x 2 grid, each wave a 64 x 64 sub-tile of
-// 4 x 4 v_mfma_f32_16x16x32_bf16 tiles. Global -> registers -> LDS with two LDS buffers
-// (one barrier per k-tile). LDS rows are 8 chunks of 16 bytes, chunk c of row r stored at
+// Block tile BM x 128 x 64 (BM = 128, or 64 when 128-row tiles would leave compute units
+// idle), four waves in a 2 x 2 grid, each wave a BM/2 x 64 sub-tile of
+// v_mfma_f32_16x16x32_bf16 tiles. Global -> registers -> LDS with two LDS buffers (one
+// barrier per k-tile). LDS rows are 8 chunks of 16 bytes, chunk c of row r stored at
 // c ^ (r & 7) so the 16-lane fragment reads of one chunk column hit distinct banks.
 //
-// A may be bf16, or float32: then each element is split while staging into
-// hi = bf16(a) and lo = bf16(a - hi) and every tile takes two MFMAs (hi W + lo W). The
-// weights are exactly bf16, so the product keeps ~16 significant bits of the activations
-// (relative error ~2^-17) instead of 8 -- what the float32 reference needs at 28 layers.
+// A is bf16 (one MFMA per tile), or carries ~16 significant bits as a bf16 pair
+// a = hi + lo (two MFMAs per tile, hi W + lo W; the weights are exact bf16, so the product
+// keeps relative error ~2^-17 instead of 2^-9 -- what the float32 reference needs at 28
+// layers). The pair either comes ready-made from the producing kernel (rows of 2K bf16:
+// the K hi parts, then the K lo parts) or is split here from float32 A while staging.
 //
-// Epilogues: float32 store, float32 residual add (x += A W^T), SwiGLU to float32 (W packs
-// 16 gate rows then the 16 matching up rows; a lane holds both), bf16 store.
+// Epilogues: float32 store, float32 residual add (x += A W^T), SwiGLU (W packs 16 gate rows
+// then the 16 matching up rows; a lane holds both) to float32 or to bf16 pair rows, bf16.
 // Requires N % 128 == 0 and K % 64 == 0; rows >= M are masked.
 #include "common.h"
 #include "kernels.h"
@@ -26,7 +28,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BN = 128, BK = 64;
 
 __device__ __forceinline__ int swz(int row, int ck) { return row * 8 + (ck ^ (row & 7)); }
 
@@ -45,51 +47,64 @@ __device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, u32x4& 
     lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
 }
 
-template <typename AT, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm(const AT* __restrict__ A, const bf16* __restrict__ W,
+template <int AM, int EPI, int BM>
+__global__ __launch_bounds__(256, 1) void k_gemm(const void* __restrict__ Av, const bf16* __restrict__ W,
                                                  void* __restrict__ C, int M, int N, int K) {
-    constexpr bool SPLIT = sizeof(AT) == 4;
+    constexpr bool SPLIT = AM != GEMM_A_BF16;
+    constexpr int FM = BM / 32;          // 16-row fragments per wave along M
+    constexpr int AJ = BM * 8 / 256;     // 16-byte A chunks per thread and k-tile
     __shared__ u32x4 sA[2][BM * 8];
     __shared__ u32x4 sL[SPLIT ? 2 : 1][SPLIT ? BM * 8 : 1];
     __shared__ u32x4 sB[2][BN * 8];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const size_t lda = AM == GEMM_A_PAIR ? 2 * (size_t)K : (size_t)K;
 
-    u32x4 ra[4], rl[4], rb[4];
+    u32x4 ra[AJ], rl[AJ], rb[4];
     const u32x4 zero = {0u, 0u, 0u, 0u};
     auto gload = [&](int kt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < AJ; ++j) {
             const int q = tid + 256 * j, row = q >> 3, ck = q & 7;
             const int gm = m0 + row;
-            if constexpr (SPLIT) {
+            if constexpr (AM == GEMM_A_F32) {
                 f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
                 if (gm < M) {
-                    const f32x4* p = reinterpret_cast<const f32x4*>(A + (size_t)gm * K + kt * BK + ck * 8);
+                    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(Av) + gm * lda + kt * BK + ck * 8);
                     x0 = p[0];
                     x1 = p[1];
                 }
                 split8(x0, x1, ra[j], rl[j]);
             } else {
-                ra[j] = gm < M ? *reinterpret_cast<const u32x4*>(A + (size_t)gm * K + kt * BK + ck * 8) : zero;
+                const bf16* A = static_cast<const bf16*>(Av) + gm * lda + kt * BK + ck * 8;
+                ra[j] = gm < M ? *reinterpret_cast<const u32x4*>(A) : zero;
+                if constexpr (AM == GEMM_A_PAIR) rl[j] = gm < M ? *reinterpret_cast<const u32x4*>(A + K) : zero;
             }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = tid + 256 * j, row = q >> 3, ck = q & 7;
             rb[j] = *reinterpret_cast<const u32x4*>(W + (size_t)(n0 + row) * K + kt * BK + ck * 8);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < AJ; ++j) {
             const int q = tid + 256 * j, row = q >> 3, ck = q & 7;
             sA[buf][swz(row, ck)] = ra[j];
             if constexpr (SPLIT) sL[buf][swz(row, ck)] = rl[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = tid + 256 * j, row = q >> 3, ck = q & 7;
             sB[buf][swz(row, ck)] = rb[j];
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[FM][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -102,24 +117,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const AT* __restrict__ A, const
         if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 a[4], b[4];
+            bf16x8 a[FM], b[4];
             const int ck = ks * 4 + (lane >> 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = __builtin_bit_cast(bf16x8, sA[cur][swz(wm * 64 + i * 16 + (lane & 15), ck)]);
-                b[i] = __builtin_bit_cast(bf16x8, sB[cur][swz(wn * 64 + i * 16 + (lane & 15), ck)]);
-            }
+            for (int i = 0; i < FM; ++i)
+                a[i] = __builtin_bit_cast(bf16x8, sA[cur][swz(wm * (BM / 2) + i * 16 + (lane & 15), ck)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                b[j] = __builtin_bit_cast(bf16x8, sB[cur][swz(wn * 64 + j * 16 + (lane & 15), ck)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             if constexpr (SPLIT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = __builtin_bit_cast(bf16x8, sL[cur][swz(wm * 64 + i * 16 + (lane & 15), ck)]);
+                for (int i = 0; i < FM; ++i)
+                    a[i] = __builtin_bit_cast(bf16x8, sL[cur][swz(wm * (BM / 2) + i * 16 + (lane & 15), ck)]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -132,18 +148,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const AT* __restrict__ A, const
     // D layout of 16x16 MFMA: lane holds column (lane & 15), rows 4 * (lane >> 4) + r.
     const int col_l = lane & 15, row_l = 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * 64 + i * 16 + row_l + r;
+            const int row = m0 + wm * (BM / 2) + i * 16 + row_l + r;
             if (row >= M) continue;
-            if (EPI == GEMM_SWIGLU_F32) {
-                float* out = reinterpret_cast<float*>(C) + (size_t)row * (N / 2);
+            if (EPI == GEMM_SWIGLU_F32 || EPI == GEMM_SWIGLU_PAIR) {
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
                     const int col = (n0 + wn * 64 + 32 * p) / 2 + col_l;
-                    out[col] = g / (1.0f + expf(-g)) * u;
+                    const float a = g / (1.0f + expf(-g)) * u;
+                    if (EPI == GEMM_SWIGLU_F32) {
+                        reinterpret_cast<float*>(C)[(size_t)row * (N / 2) + col] = a;
+                    } else {                     // pair row of N bf16: N/2 hi, then N/2 lo
+                        bf16* out = reinterpret_cast<bf16*>(C) + (size_t)row * N;
+                        const bf16 h = f2bf(a);
+                        out[col] = h;
+                        out[N / 2 + col] = f2bf(a - bf2f(h));
+                    }
                 }
             } else {
 #pragma unroll
@@ -161,25 +184,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const AT* __restrict__ A, const
 
 }  // namespace
 
-template <typename AT>
-static hipError_t launch_t(const AT* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
+template <int AM, int BM>
+static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
     dim3 grid(N / BN, (M + BM - 1) / BM);
     switch (epi) {
-        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AT, GEMM_F32>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AT, GEMM_RESID_F32>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AT, GEMM_SWIGLU_F32>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AT, GEMM_BF16>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const void* A, int a_f32, const uint16_t* W, void* C, int M, int N, int K, int epi,
+template <int AM>
+static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
+    // 128-row tiles unless that leaves fewer than two blocks per compute unit
+    const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128);
+    if (blocks128 < 512) return launch_t<AM, 64>(A, W, C, M, N, K, epi, s);
+    return launch_t<AM, 128>(A, W, C, M, N, K, epi, s);
+}
+
+hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
                        hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (N % BN != 0 || K % BK != 0) return hipErrorInvalidValue;
-    if (a_f32) return launch_t<float>((const float*)A, W, C, M, N, K, epi, s);
-    return launch_t<bf16>((const bf16*)A, W, C, M, N, K, epi, s);
+    switch (a_mode) {
+        case GEMM_A_BF16: return launch_bm<GEMM_A_BF16>(A, W, C, M, N, K, epi, s);
+        case GEMM_A_F32: return launch_bm<GEMM_A_F32>(A, W, C, M, N, K, epi, s);
+        case GEMM_A_PAIR: return launch_bm<GEMM_A_PAIR>(A, W, C, M, N, K, epi, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace q3

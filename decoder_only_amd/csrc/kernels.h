@@ -13,8 +13,9 @@ enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
 // x[r, :] = E[tok[r], :] widened to float32. Out-of-range ids set Q3_DEVERR_TOKEN and give a zero row.
 hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
                         int vocab, unsigned* err, hipStream_t s);
-// out[r, :] = rmsnorm(x[r, :]) * w, out float32 or bf16.
-hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_bf16, int rows, int d,
+// out[r, :] = rmsnorm(x[r, :]) * w; out_mode 0 float32, 1 bf16, 2 bf16 pair rows [rows][2d]
+// (d hi parts, then d lo parts).
+hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_mode, int rows, int d,
                           float eps, hipStream_t s);
 // Decode rows: per-head RMSNorm of q and k, RoPE at the row's position, K/V append at
 // slot lens[seq]. qkv: [B][(Hq + 2 Hkv) * 128] float32. q_out: [B][Hq][128] float32.
@@ -52,16 +53,19 @@ hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, in
                               int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s);
 
 // ---- gemm.hip (prefill projections on MFMA: A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
-// A is bf16 (a_f32 = 0) or float32 split into bf16 hi + lo parts (a_f32 = 1, two MFMAs per tile).
-enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3 };
-hipError_t launch_gemm(const void* A, int a_f32, const uint16_t* W, void* C, int M, int N, int K, int epi,
+// a_mode: A bf16 [M][K]; float32 [M][K] split into bf16 hi + lo while staging; or a bf16
+// pair [M][2K] (per row the K hi parts, then the K lo parts). Split / pair: two MFMAs per tile.
+enum GemmAMode { GEMM_A_BF16 = 0, GEMM_A_F32 = 1, GEMM_A_PAIR = 2 };
+// Epilogues; SWIGLU_PAIR writes C as bf16 pair rows [M][N] (N/2 hi, then N/2 lo).
+enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3, GEMM_SWIGLU_PAIR = 4 };
+hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
                        hipStream_t s);
 
 // ---- attn_prefill.hip (causal GQA flash attention on MFMA)
 // q: [Hq][M][128] float32 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16;
-// o: [M][Hq*128] float32.
+// o: [M][Hq*128] float32, or (o_pair) bf16 pair rows [M][2*Hq*128] (hi parts, then lo parts).
 hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, float* o, hipStream_t s);
+                               int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s);
 
 // ---- decode_mega.hip (whole decode step in one cooperative launch; fixed Qwen3-0.6B layer
 // shape: hidden 1024, 16/8 heads of 128, FFN 3072; bf16 weights and KV; 1..4 rows)

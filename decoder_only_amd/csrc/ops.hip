@@ -30,8 +30,10 @@ q3_status st(hipError_t e) { return e == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
 
 extern "C" q3_status q3_op_rmsnorm(const float* x, const float* w, void* out, int32_t out_dtype, int32_t rows,
                                    int32_t d, float eps, void* stream) {
-    if (!x || !w || !out || rows < 0 || d <= 0 || (out_dtype != Q3_F32 && out_dtype != Q3_BF16)) return Q3_ERR_ARG;
-    return st(launch_rmsnorm(x, w, out, out_dtype == Q3_BF16, rows, d, eps, (hipStream_t)stream));
+    if (!x || !w || !out || rows < 0 || d <= 0 || (out_dtype != Q3_F32 && out_dtype != Q3_BF16 && out_dtype != Q3_OP_PAIR))
+        return Q3_ERR_ARG;
+    return st(launch_rmsnorm(x, w, out, out_dtype == Q3_F32 ? 0 : (out_dtype == Q3_BF16 ? 1 : 2), rows, d, eps,
+                             (hipStream_t)stream));
 }
 
 extern "C" q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, int32_t N, int32_t K,
@@ -44,11 +46,12 @@ extern "C" q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, 
 
 extern "C" q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
                                 int32_t K, int32_t epilogue, void* stream) {
-    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 3 ||
-        (a_dtype != Q3_F32 && a_dtype != Q3_BF16))
+    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 4 ||
+        (a_dtype != Q3_F32 && a_dtype != Q3_BF16 && a_dtype != Q3_OP_PAIR))
         return Q3_ERR_ARG;
     if (N % 128 || K % 64) return Q3_ERR_SHAPE;
-    return st(launch_gemm(A, a_dtype == Q3_F32, W, C, M, N, K, epilogue, (hipStream_t)stream));
+    const int mode = a_dtype == Q3_F32 ? GEMM_A_F32 : (a_dtype == Q3_BF16 ? GEMM_A_BF16 : GEMM_A_PAIR);
+    return st(launch_gemm(A, mode, W, C, M, N, K, epilogue, (hipStream_t)stream));
 }
 
 extern "C" q3_status q3_op_qk_norm_rope(const float* qkv, const float* q_norm, const float* k_norm,
@@ -85,10 +88,13 @@ extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, cons
 
 extern "C" q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                         int32_t t_cap, int32_t M, int32_t t0, int32_t n_heads, int32_t n_kv_heads,
-                                        float* o, void* stream) {
-    if (!q || !k_cache || !v_cache || !o || M < 0 || t0 < 0 || t_cap <= 0 || (int64_t)t0 + M > t_cap) return Q3_ERR_ARG;
+                                        void* o, int32_t o_dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !o || M < 0 || t0 < 0 || t_cap <= 0 || (int64_t)t0 + M > t_cap ||
+        (o_dtype != Q3_F32 && o_dtype != Q3_OP_PAIR))
+        return Q3_ERR_ARG;
     if (n_heads != 2 * n_kv_heads) return Q3_ERR_SHAPE;
-    return st(launch_attn_prefill(q, k_cache, v_cache, t_cap, M, t0, n_heads, n_kv_heads, o, (hipStream_t)stream));
+    return st(launch_attn_prefill(q, k_cache, v_cache, t_cap, M, t0, n_heads, n_kv_heads, o, o_dtype == Q3_OP_PAIR,
+                                  (hipStream_t)stream));
 }
 
 extern "C" q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, float temperature, float top_p,

@@ -17,6 +17,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq3.so")
 
 F32, BF16 = 0, 1
+OP_PAIR = 2     # single operations: bf16 pair rows (n hi parts, then n lo parts)
 STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -4: "Q3_ERR_CAPACITY", -5: "Q3_ERR_OOM", -6: "Q3_ERR_HIP", -7: "Q3_ERR_STATE",
           -8: "Q3_ERR_NUMERIC"}
@@ -29,7 +30,7 @@ EXPORTS = [
 ]
 GEMV_STORE, GEMV_RESID, GEMV_SWIGLU = 0, 1, 2
 PROF_DECODE_STEP, PROF_GEMV, PROF_LMHEAD, PROF_ATTN_DECODE, PROF_GEMM, PROF_ATTN_PREFILL = range(6)
-GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_F32, GEMM_BF16 = 0, 1, 2, 3
+GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_F32, GEMM_BF16, GEMM_SWIGLU_PAIR = 0, 1, 2, 3, 4
 
 
 class Q3Error(RuntimeError):
@@ -85,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_op_gemm": ([vp, i32, vp, vp, i32, i32, i32, i32, vp], i32),
         "q3_op_qk_norm_rope": ([vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, i32, i32, vp], i32),
         "q3_op_attn_decode": ([vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, vp, vp], i32),
-        "q3_op_attn_prefill": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, vp], i32),
+        "q3_op_attn_prefill": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp], i32),
         "q3_op_sample": ([vp, i32, i32, f32, f32, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
@@ -231,9 +232,10 @@ class Engine:
 
 # ------------------------------------------------------------------------- op level
 
-def op_rmsnorm(x, w, out, eps: float) -> None:
+def op_rmsnorm(x, w, out, eps: float, pair: bool = False) -> None:
+    """out: float32 or bf16 [rows, d], or (pair) bf16 [rows, 2d]."""
     import torch
-    dt = BF16 if out.dtype == torch.bfloat16 else F32
+    dt = OP_PAIR if pair else (BF16 if out.dtype == torch.bfloat16 else F32)
     rows, d = x.shape
     _check(load_library().q3_op_rmsnorm(_ptr(x, torch.float32), _ptr(w, torch.float32), _ptr(out), dt,
                                         rows, d, eps, _stream()), "q3_op_rmsnorm")
@@ -247,12 +249,14 @@ def op_gemv(W, x, y, epilogue: int = GEMV_STORE) -> None:
                                      x.shape[0], epilogue, _stream()), "q3_op_gemv")
 
 
-def op_gemm(A, W, C, epilogue: int = GEMM_F32) -> None:
-    """A: bf16 or float32 [M, K]; W: bf16 [N, K]."""
+def op_gemm(A, W, C, epilogue: int = GEMM_F32, a_pair: bool = False) -> None:
+    """A: bf16 or float32 [M, K], or (a_pair) bf16 pair rows [M, 2K]; W: bf16 [N, K]."""
     import torch
     M, K = A.shape
     N = W.shape[0]
-    adt = F32 if A.dtype == torch.float32 else BF16
+    if a_pair:
+        K //= 2
+    adt = OP_PAIR if a_pair else (F32 if A.dtype == torch.float32 else BF16)
     _check(load_library().q3_op_gemm(_ptr(A, (torch.bfloat16, torch.float32)), adt, _ptr(W, torch.bfloat16),
                                      _ptr(C), M, N, K, epilogue, _stream()), "q3_op_gemm")
 
@@ -278,13 +282,15 @@ def op_attn_decode(q, k_cache, v_cache, lens, o, max_len: int) -> None:
                                             _ptr(o, torch.float32), _stream()), "q3_op_attn_decode")
 
 
-def op_attn_prefill(q, k_cache, v_cache, t0: int, o) -> None:
+def op_attn_prefill(q, k_cache, v_cache, t0: int, o, pair: bool = False) -> None:
+    """o: float32 [M, Hq*128], or (pair) bf16 pair rows [M, 2*Hq*128]."""
     import torch
     Hq, M, _ = q.shape
     Hkv, t_cap, _ = k_cache.shape
     _check(load_library().q3_op_attn_prefill(_ptr(q, torch.float32), _ptr(k_cache, torch.bfloat16),
                                              _ptr(v_cache, torch.bfloat16), t_cap, M, t0, Hq, Hkv,
-                                             _ptr(o, torch.float32), _stream()), "q3_op_attn_prefill")
+                                             _ptr(o, torch.bfloat16 if pair else torch.float32),
+                                             OP_PAIR if pair else F32, _stream()), "q3_op_attn_prefill")
 
 
 def op_sample(logits, temperature: float, top_p: float, uniforms, out) -> None:

@@ -18,9 +18,15 @@
 extern "C" {
 #endif
 
+/* dtype code of the single operations for "bf16 pair rows": a float32 value a is carried as
+ * hi = bf16(a), lo = bf16(a - hi) (~16 significant bits); a row of width n holds the n hi
+ * parts, then the n lo parts (2n bf16). */
+#define Q3_OP_PAIR 2
+
 /* RMSNorm ("Inside an LLM ...", Step 3) of `rows` rows of width d:
  * out = x * (1 / sqrt(mean(x^2) + eps)) * w.  x: float32 [rows][d]; w: float32 [d];
- * out: float32 (out_dtype Q3_F32) or bf16 (Q3_BF16) [rows][d]. */
+ * out: float32 (out_dtype Q3_F32) or bf16 (Q3_BF16) [rows][d], or bf16 pair rows
+ * (Q3_OP_PAIR) [rows][2d]. */
 q3_status q3_op_rmsnorm(const float* x, const float* w, void* out, int32_t out_dtype, int32_t rows,
                         int32_t d, float eps, void* stream);
 
@@ -35,9 +41,11 @@ q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, i
 /* Prefill projection on the matrix cores: C = A W^T, W bf16 [N][K] (N % 128 == 0,
  * K % 64 == 0), float32 accumulation. A [M][K] is bf16 (a_dtype Q3_BF16), or float32
  * (Q3_F32): then each element enters as a bf16 hi + lo pair, hi = bf16(a),
- * lo = bf16(a - hi), two matrix-core products per tile (~2^-17 relative error).
+ * lo = bf16(a - hi), two matrix-core products per tile (~2^-17 relative error), or
+ * already such pairs (Q3_OP_PAIR, A bf16 [M][2K]).
  * epilogue 0: C float32 [M][N]; 1: C float32 [M][N] += result; 2: SwiGLU (W packed as
- * for q3_op_gemv), C float32 [M][N/2]; 3: C bf16 [M][N]. */
+ * for q3_op_gemv), C float32 [M][N/2]; 3: C bf16 [M][N]; 4: SwiGLU to bf16 pair rows,
+ * C bf16 [M][N] (N/2 hi parts, then N/2 lo parts). */
 q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
                      int32_t K, int32_t epilogue, void* stream);
 
@@ -62,11 +70,12 @@ q3_status q3_op_attn_decode(const float* q, const void* k_cache, const void* v_c
 
 /* Causal prefill attention (Step 5) of M new rows at slots t0 .. t0+M-1 of one sequence:
  * q: float32 [n_heads][M][128] (rotated); k_cache, v_cache: bf16 [n_kv_heads][t_cap][128]
- * with slots 0 .. t0+M-1 filled; row i sees slots j <= t0 + i. o: float32 [M][n_heads * 128].
+ * with slots 0 .. t0+M-1 filled; row i sees slots j <= t0 + i. o: float32 [M][n_heads * 128]
+ * (o_dtype Q3_F32) or bf16 pair rows [M][2 * n_heads * 128] (Q3_OP_PAIR).
  * q and the softmax weights enter the matrix-core products as bf16 hi + lo pairs. */
 q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
                              int32_t t_cap, int32_t M, int32_t t0, int32_t n_heads, int32_t n_kv_heads,
-                             float* o, void* stream);
+                             void* o, int32_t o_dtype, void* stream);
 
 /* Sampling of B rows of float32 logits [B][V] (Step 8), same rule as q3_sample. */
 q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, float temperature, float top_p,

@@ -115,6 +115,8 @@ def test_null_engine_and_op_argument_errors(lib):
     assert lib.q3_op_gemv(fake, 1, fake, fake, 6, 12, 1, 0, None) == -2         # K % 8
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 7, 4, fake, None) == -2
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 8, 17, fake, None) == -1
-    assert lib.q3_op_attn_prefill(fake, fake, fake, 10, 8, 3, 16, 8, fake, None) == -1   # t0+M > t_cap
+    assert lib.q3_op_attn_prefill(fake, fake, fake, 10, 8, 3, 16, 8, fake, 0, None) == -1   # t0+M > t_cap
+    assert lib.q3_op_attn_prefill(fake, fake, fake, 16, 8, 3, 16, 8, fake, 1, None) == -1   # bad o dtype
+    assert lib.q3_op_gemm(fake, 2, fake, fake, 4, 128, 64, 5, None) == -1       # bad epilogue
     assert lib.q3_op_sample(fake, 1, 10, -1.0, 0.9, fake, fake, None) == -1
     assert lib.q3_op_sample(fake, 1, 10, 0.7, 0.9, None, fake, None) == -1

@@ -26,6 +26,18 @@ def _bf16(x):
     return synth.f32_to_bf16_bits(x)
 
 
+def _pair_bits(x):
+    """float32 [rows, n] -> bf16 pair rows [rows, 2n]: hi = bf16(x), lo = bf16(x - hi)."""
+    hi = _bf16(x)
+    lo = _bf16((x - f32_of_bits(hi)).astype(np.float32))
+    return np.concatenate([hi, lo], axis=1)
+
+
+def _pair_value(bits, n):
+    """bf16 pair rows [rows, 2n] (as bf16 tensor bits) -> float64 hi + lo."""
+    return f32_of_bits(bits[:, :n]).astype(np.float64) + f32_of_bits(bits[:, n:]).astype(np.float64)
+
+
 # ------------------------------------------------------------------ RMSNorm
 
 @pytest.mark.parametrize("rows,d", [(1, 1024), (37, 1024), (5, 3072)])
@@ -44,6 +56,12 @@ def test_rmsnorm(q3, rows, d):
     assert np.allclose(out.cpu().numpy(), ref, rtol=2e-6, atol=1e-6)
     gotb = f32_of_bits(bf16_bits(outb))
     assert np.all(np.abs(gotb - ref) <= np.abs(ref) * 2.0**-8 + 1e-30)
+    outp = torch.empty(rows, 2 * d, dtype=torch.bfloat16, device="cuda")
+    q3.op_rmsnorm(xt, wt, outp, 1e-6, pair=True)
+    torch.cuda.synchronize()
+    # the pair carries the float32 result to ~2^-16 of its size
+    f = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(_pair_value(bf16_bits(outp), d) - f) <= np.abs(f) * 2.0**-16 + 1e-30)
 
 
 # ------------------------------------------------------------------ GEMV (decode projections)
@@ -146,6 +164,26 @@ def test_gemm_f32_activations_split(q3, M, N, K):
     assert np.abs(single - ref).max() > 20 * err
 
 
+@pytest.mark.parametrize("M,N,K", [(77, 1024, 2048), (300, 1024, 3072), (2047, 4096, 1024)])
+def test_gemm_pair_activations_equal_split(q3, M, N, K):
+    """A handed over as bf16 pair rows gives exactly the products of float32 A split while
+    staging (same hi / lo parts, same matrix-core sequence); 2047 x 4096 takes 128-row tiles,
+    the others 64-row tiles."""
+    import torch
+    announce("gemm pair-A", M, N, K)
+    A = synth.normal((19, M, K), (M, K))
+    W = bf16_dev(_bf16(synth.normal((11, N, K), (N, K), 0.02)))
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    q3.op_gemm(torch.from_numpy(A).cuda(), W, C, q3.GEMM_F32)
+    Cp = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    q3.op_gemm(bf16_dev(_pair_bits(A)), W, Cp, q3.GEMM_F32, a_pair=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C, Cp)
+    rows = [0, M // 2, M - 1]
+    ref = A[rows].astype(np.float64) @ f32_of_bits(bf16_bits(W)).T.astype(np.float64)
+    assert np.abs(Cp.cpu().numpy()[rows] - ref).max() <= 3e-5 * np.sqrt(K) * 0.02
+
+
 def test_gemm_swiglu(q3):
     import torch
     announce("gemm swiglu")
@@ -155,9 +193,14 @@ def test_gemm_swiglu(q3):
     A = synth.normal((15, M, K), (M, K))
     ref = oracle.silu(A @ g.T) * (A @ u.T)
     C = torch.empty(M, F, dtype=torch.float32, device="cuda")
-    q3.op_gemm(torch.from_numpy(A).cuda(), bf16_dev(_bf16(_pack_gate_up(g, u))), C, q3.GEMM_SWIGLU_F32)
+    Wp = bf16_dev(_bf16(_pack_gate_up(g, u)))
+    q3.op_gemm(torch.from_numpy(A).cuda(), Wp, C, q3.GEMM_SWIGLU_F32)
+    Cp = torch.empty(M, 2 * F, dtype=torch.bfloat16, device="cuda")
+    q3.op_gemm(torch.from_numpy(A).cuda(), Wp, Cp, q3.GEMM_SWIGLU_PAIR)
     torch.cuda.synchronize()
-    assert np.allclose(C.cpu().numpy(), ref, rtol=1e-4, atol=2e-5)
+    f = C.cpu().numpy()
+    assert np.allclose(f, ref, rtol=1e-4, atol=2e-5)
+    assert np.all(np.abs(_pair_value(bf16_bits(Cp), F) - f) <= np.abs(f) * 2.0**-16 + 1e-30)
 
 
 def test_gemm_full_prefill_shape_sampled_rows(q3):
@@ -285,6 +328,12 @@ def test_attn_prefill(q3, M, t0):
     ref = oracle.attend(q, K[:, :t0 + M], V[:, :t0 + M], t0)
     assert np.abs(got - ref).max() <= 1e-4, np.abs(got - ref).max()
     assert rel_l2(got, ref) <= 2e-5, rel_l2(got, ref)
+    op = torch.empty(M, 2 * Hq * 128, dtype=torch.bfloat16, device="cuda")
+    q3.op_attn_prefill(torch.from_numpy(q).cuda(), torch.from_numpy(K).bfloat16().cuda(),
+                       torch.from_numpy(V).bfloat16().cuda(), t0, op, pair=True)
+    torch.cuda.synchronize()
+    f = got.astype(np.float64)
+    assert np.all(np.abs(_pair_value(bf16_bits(op), Hq * 128) - f) <= np.abs(f) * 2.0**-16 + 1e-30)
 
 
 def test_attn_prefill_long_sampled_rows(q3):
