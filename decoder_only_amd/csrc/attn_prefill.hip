@@ -34,24 +34,25 @@ constexpr int BKV = 64;   // keys per tile
 
 // K tile: 64 rows (keys) x 16 chunks of 16 B; chunk c of row r at c ^ (r & 15).
 __device__ __forceinline__ int kidx(int key, int ck) { return key * 16 + (ck ^ (key & 15)); }
-// V^T tile: 128 rows (dims) x 8 chunks of 16 B (64 keys); chunk c of row d at c ^ (d & 7).
+// V^T tile: 128 rows (dims) x 8 chunks of 16 B (64 keys); chunk c of row d at
+// c ^ ((d ^ (d >> 3)) & 7): the fragment reads (16 consecutive dims) and the staging writes
+// (dims 8 apart) both spread over the banks.
 __device__ __forceinline__ int vt_off(int d, int key) {  // offset in bf16 elements
     const int ck = key >> 3;
-    return d * 64 + ((ck ^ (d & 7)) << 3) + (key & 7);
+    return d * 64 + ((ck ^ ((d ^ (d >> 3)) & 7)) << 3) + (key & 7);
 }
 
 __device__ __forceinline__ unsigned int pack2(bf16 a, bf16 b) { return (unsigned)a | ((unsigned)b << 16); }
 
-// 8 float32 -> bf16 hi parts and bf16 lo parts, as two 8-element operands.
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+
+// 8 float32 -> bf16 hi parts and bf16 lo parts, as two 8-element operands (hardware
+// round-to-nearest-even conversions, two values per instruction).
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
-    bf16 h[8], l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h[i] = f2bf(v[i]);
-        l[i] = f2bf(v[i] - bf2f(h[i]));
-    }
-    hi = __builtin_bit_cast(bf16x8, u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
-    lo = __builtin_bit_cast(bf16x8, u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
+    const f32x8 x = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    hi = __builtin_convertvector(x, bf16x8);
+    const f32x8 hf = __builtin_convertvector(hi, f32x8);
+    lo = __builtin_convertvector(x - hf, bf16x8);
 }
 
 template <bool PAIR>
@@ -100,27 +101,44 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     const bf16* kh = kc + (size_t)g * t_cap * 128;
     const bf16* vh = vc + (size_t)g * t_cap * 128;
 
+    // K/V of tile kt + 1 are loaded into registers while tile kt is in use. Thread t takes
+    // 16-byte chunk ck = t % 16 of the key pairs t / 16 and t / 16 + 16.
+    const int ck = tid & 15;
+    u32x4 kreg[2][2], vreg[2][2];
+    auto kv_load = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int key = 2 * ((tid >> 4) + 16 * j) + u;
+                const int slot = kt * BKV + key;
+                kreg[j][u] = u32x4{0u, 0u, 0u, 0u};
+                vreg[j][u] = u32x4{0u, 0u, 0u, 0u};
+                if (slot <= last_slot) {
+                    kreg[j][u] = *reinterpret_cast<const u32x4*>(kh + (size_t)slot * 128 + ck * 8);
+                    vreg[j][u] = *reinterpret_cast<const u32x4*>(vh + (size_t)slot * 128 + ck * 8);
+                }
+            }
+    };
+    kv_load(0);
     for (int kt = 0; kt < ntiles; ++kt) {
         __syncthreads();
-        // stage K (row-major, swizzled) and V^T; slots beyond last_slot are zero-filled
+        // stage K (row-major, swizzled) and V^T (two keys per 32-bit store); slots beyond
+        // last_slot are zero-filled
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int qd = tid + 256 * j, key = qd >> 4, ck = qd & 15;
-            const int slot = kt * BKV + key;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (slot <= last_slot) {
-                kv = *reinterpret_cast<const u32x4*>(kh + (size_t)slot * 128 + ck * 8);
-                vv = *reinterpret_cast<const u32x4*>(vh + (size_t)slot * 128 + ck * 8);
-            }
-            sK[kidx(key, ck)] = kv;
-            const unsigned int w[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int j = 0; j < 2; ++j) {
+            const int key0 = 2 * ((tid >> 4) + 16 * j);
+            sK[kidx(key0, ck)] = kreg[j][0];
+            sK[kidx(key0 + 1, ck)] = kreg[j][1];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVT[vt_off(ck * 8 + 2 * e, key)] = (bf16)(w[e] & 0xFFFFu);
-                sVT[vt_off(ck * 8 + 2 * e + 1, key)] = (bf16)(w[e] >> 16);
+            for (int e = 0; e < 8; ++e) {
+                const unsigned a = (vreg[j][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const unsigned b = (vreg[j][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                *reinterpret_cast<unsigned*>(&sVT[vt_off(ck * 8 + e, key0)]) = a | (b << 16);
             }
         }
         __syncthreads();
+        if (kt + 1 < ntiles) kv_load(kt + 1);
 
         // S^T[key][row] for 4 key tiles x 2 row tiles
         f32x4 s[4][2];
@@ -158,13 +176,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float mnew = fmaxf(mrow[c], mx);
-            const float corr = exp2f(mrow[c] - mnew);   // 0 on the first tile (mrow = -inf)
+            const float corr = __builtin_amdgcn_exp2f(mrow[c] - mnew);   // 0 on the first tile (mrow = -inf)
             float sum = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = exp2f(s[j][c][r] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(s[j][c][r] - mnew);
                     s[j][c][r] = p;
                     sum += p;
                 }

@@ -4,8 +4,8 @@
 //
 // Block tile BM x 128 x 64 (BM = 128, or 64 when 128-row tiles would leave compute units
 // idle), four waves in a 2 x 2 grid, each wave a BM/2 x 64 sub-tile of
-// v_mfma_f32_16x16x32_bf16 tiles. Global -> registers -> LDS with two LDS buffers (one
-// barrier per k-tile). LDS rows are 8 chunks of 16 bytes, chunk c of row r stored at
+// v_mfma_f32_16x16x32_bf16 tiles. Global -> registers (the next k-tile, in flight during
+// the current one's products) -> LDS. LDS rows are 8 chunks of 16 bytes, chunk c of row r stored at
 // c ^ (r & 7) so the 16-lane fragment reads of one chunk column hit distinct banks.
 //
 // A is bf16 (one MFMA per tile), or carries ~16 significant bits as a bf16 pair
@@ -47,15 +47,17 @@ __device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, u32x4& 
     lo = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
 }
 
-template <int AM, int EPI, int BM>
-__global__ __launch_bounds__(256, 1) void k_gemm(const void* __restrict__ Av, const bf16* __restrict__ W,
-                                                 void* __restrict__ C, int M, int N, int K) {
+// NB = LDS buffers: 2 (the next k-tile is stored while the current one is read; one block
+// per compute unit at BM = 128) or 1 (two barriers per k-tile, two blocks per compute unit).
+template <int AM, int EPI, int BM, int NB>
+__global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ Av, const bf16* __restrict__ W,
+                                                      void* __restrict__ C, int M, int N, int K) {
     constexpr bool SPLIT = AM != GEMM_A_BF16;
     constexpr int FM = BM / 32;          // 16-row fragments per wave along M
     constexpr int AJ = BM * 8 / 256;     // 16-byte A chunks per thread and k-tile
-    __shared__ u32x4 sA[2][BM * 8];
-    __shared__ u32x4 sL[SPLIT ? 2 : 1][SPLIT ? BM * 8 : 1];
-    __shared__ u32x4 sB[2][BN * 8];
+    __shared__ u32x4 sA[NB][BM * 8];
+    __shared__ u32x4 sL[SPLIT ? NB : 1][SPLIT ? BM * 8 : 1];
+    __shared__ u32x4 sB[NB][BN * 8];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const void* __restrict__ Av, co
     sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
+        const int cur = NB == 2 ? (kt & 1) : 0;
         if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -141,8 +143,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const void* __restrict__ Av, co
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             }
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
+        if constexpr (NB == 2) {
+            if (kt + 1 < nk) sstore(cur ^ 1);
+            __syncthreads();
+        } else {
+            __syncthreads();
+            if (kt + 1 < nk) {
+                sstore(0);
+                __syncthreads();
+            }
+        }
     }
 
     // D layout of 16x16 MFMA: lane holds column (lane & 15), rows 4 * (lane >> 4) + r.
@@ -184,15 +194,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const void* __restrict__ Av, co
 
 }  // namespace
 
-template <int AM, int BM>
+template <int AM, int BM, int NB>
 static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
     dim3 grid(N / BN, (M + BM - 1) / BM);
     switch (epi) {
-        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -202,8 +212,10 @@ template <int AM>
 static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
     // 128-row tiles unless that leaves fewer than two blocks per compute unit
     const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128);
-    if (blocks128 < 512) return launch_t<AM, 64>(A, W, C, M, N, K, epi, s);
-    return launch_t<AM, 128>(A, W, C, M, N, K, epi, s);
+    // (measured on MI355X at the prefill shapes: 64-row tiles with two LDS buffers, 128-row
+    // tiles with one buffer and two blocks per compute unit)
+    if (blocks128 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, s);
+    return launch_t<AM, 128, 1>(A, W, C, M, N, K, epi, s);
 }
 
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
