@@ -141,9 +141,11 @@ __global__ __launch_bounds__(256) void k_attn_decode_part(
     }
 }
 
+// o_pair: o is bf16 pair rows [B][2 * Hq * 128] (hi parts, then lo parts), else float32.
+template <bool PAIR>
 __global__ __launch_bounds__(128) void k_attn_decode_combine(
     const float* __restrict__ part, const int32_t* __restrict__ lens, int len_extra, int seq_base,
-    int Hq, int Hkv, int nchunk, float* __restrict__ o) {
+    int Hq, int Hkv, int nchunk, void* __restrict__ o) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int g = h / G, hh = h % G;
     const int T = lens[seq_base + b] + len_extra;
@@ -163,7 +165,15 @@ __global__ __launch_bounds__(128) void k_attn_decode_combine(
             A += pp[2 + d] * cf;
         }
     }
-    o[((size_t)b * Hq + h) * 128 + d] = L > 0.f ? A / L : 0.f;
+    const float v = L > 0.f ? A / L : 0.f;
+    if constexpr (PAIR) {
+        bf16* row = static_cast<bf16*>(o) + (size_t)b * 2 * Hq * 128;
+        const bf16 hi = f2bf(v);
+        row[h * 128 + d] = hi;
+        row[(size_t)Hq * 128 + h * 128 + d] = f2bf(v - bf2f(hi));
+    } else {
+        static_cast<float*>(o)[((size_t)b * Hq + h) * 128 + d] = v;
+    }
 }
 
 }  // namespace
@@ -175,7 +185,7 @@ size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T) {
 
 hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
                               int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
-                              int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s) {
+                              int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s) {
     if (B <= 0) return hipSuccess;
     if (Hq != G * Hkv) return hipErrorInvalidValue;
     const int nchunk = (max_T + CHUNK - 1) / CHUNK;
@@ -188,8 +198,12 @@ hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, in
                            (const float*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_decode_combine, dim3(Hq, B), dim3(128), 0, s, ws, lens, len_extra,
-                       seq_base, Hq, Hkv, nchunk, o);
+    if (o_pair)
+        hipLaunchKernelGGL(k_attn_decode_combine<true>, dim3(Hq, B), dim3(128), 0, s, ws, lens, len_extra,
+                           seq_base, Hq, Hkv, nchunk, (void*)o);
+    else
+        hipLaunchKernelGGL(k_attn_decode_combine<false>, dim3(Hq, B), dim3(128), 0, s, ws, lens, len_extra,
+                           seq_base, Hq, Hkv, nchunk, (void*)o);
     return hipGetLastError();
 }
 

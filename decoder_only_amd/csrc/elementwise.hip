@@ -37,14 +37,21 @@ hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, in
 // MODE 0: float32 out [rows][d]; 1: bf16 [rows][d]; 2: bf16 pair rows [rows][2d]
 // (hi = bf16(v) in the first d, lo = bf16(v - hi) in the second d).
 template <int MODE>
-__global__ void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w,
-                          void* __restrict__ out, int d, float eps) {
+__global__ void k_rmsnorm(float* __restrict__ x, const float* __restrict__ w, void* __restrict__ out, int d,
+                          float eps, const float* __restrict__ parts, int nparts, int rows) {
     __shared__ float red[16];
     const int r = blockIdx.x;
-    const float* xr = x + (size_t)r * d;
+    float* xr = x + (size_t)r * d;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
-    ss = block_sum(ss, red);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        float v = xr[i];
+        if (nparts > 0) {
+            for (int p = 0; p < nparts; ++p) v += parts[((size_t)p * rows + r) * d + i];
+            xr[i] = v;
+        }
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);    // (its barriers also order the x write-back before the reads below)
     const float rs = 1.0f / sqrtf(ss / (float)d + eps);
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
         const float v = (xr[i] * rs) * w[i];
@@ -61,12 +68,13 @@ __global__ void k_rmsnorm(const float* __restrict__ x, const float* __restrict__
     }
 }
 
-hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_mode, int rows, int d,
-                          float eps, hipStream_t s) {
+hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int rows, int d,
+                          float eps, hipStream_t s, const float* parts, int nparts) {
     if (rows <= 0) return hipSuccess;
-    if (out_mode == 0) hipLaunchKernelGGL(k_rmsnorm<0>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
-    else if (out_mode == 1) hipLaunchKernelGGL(k_rmsnorm<1>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
-    else if (out_mode == 2) hipLaunchKernelGGL(k_rmsnorm<2>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps);
+    if (nparts < 0 || (nparts > 0 && !parts)) return hipErrorInvalidValue;
+    if (out_mode == 0) hipLaunchKernelGGL(k_rmsnorm<0>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
+    else if (out_mode == 1) hipLaunchKernelGGL(k_rmsnorm<1>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
+    else if (out_mode == 2) hipLaunchKernelGGL(k_rmsnorm<2>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

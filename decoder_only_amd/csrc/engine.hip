@@ -58,6 +58,8 @@ struct q3_engine {
     float* logits = nullptr;
     unsigned long long* amax = nullptr;
     float* attn_ws = nullptr;
+    float* parts = nullptr;        // split-K partial products of the batched decode projections
+    static constexpr int kMaxSplits = 32;
     int attn_ws_T = 0;
     void* sample_ws = nullptr;
     const float* cur_logits = nullptr;
@@ -305,6 +307,7 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
     if (!(e->logits = (float*)e->alloc((size_t)B * V * 4))) return oom();
     if (!(e->amax = (unsigned long long*)e->alloc((size_t)B * 8))) return oom();
     if (!(e->sample_ws = e->alloc(sample_workspace_bytes(V, B)))) return oom();
+    if (B > 8 && !(e->parts = (float*)e->alloc((size_t)q3_engine::kMaxSplits * B * d * 4))) return oom();
     if (hipMemset(e->sample_ws, 0, sample_workspace_bytes(V, B)) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
     e->attn_ws_T = c.max_seq;
     if (!(e->attn_ws = (float*)e->alloc(attn_decode_workspace_bytes(B, Hkv, c.max_seq)))) return oom();
@@ -452,39 +455,82 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;
         return Q3_OK;
     }
+    // More rows than one GEMV pass takes (8): the projections and the LM head run on the
+    // matrix cores, activations handed over as bf16 hi/lo pairs, so every weight is read
+    // once per step instead of once per 8 rows.
+    const int HD = Hq * 128;
+    const bool mm = c.weight_dtype == Q3_BF16 && B > 8 && e->qkv_rows() % 128 == 0 && d % 128 == 0 &&
+                    (2 * F) % 128 == 0 && V % 128 == 0 && d % 64 == 0 && HD % 64 == 0 && F % 64 == 0;
+    const int nmode = mm ? 2 : 0;   // RMSNorm output: bf16 pairs for the matrix cores, else float32
+    // The residual projections (o, down) of few rows are split along K over enough blocks to
+    // fill the GPU; their partials are added to x by the next RMSNorm, in a fixed order.
+    int split = 1, pending = 0;
+    if (mm) {
+        const int mblocks = (B + 63) / 64, nblocks = d / 128;
+        split = std::min(q3_engine::kMaxSplits, std::max(1, (256 + nblocks * mblocks - 1) / (nblocks * mblocks)));
+        split = std::min(split, std::min(HD, F) / 64);
+    }
     prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
     HIPCHK(e, launch_embed(tokens, e->embed, wdt, e->x, B, d, V, e->d_err, s));
     for (int l = 0; l < c.n_layers; ++l) {
         const auto& L = e->layers[l];
         char* kcl = (char*)e->kc + (size_t)l * e->kv_layer_elems * e->kvbytes();
         char* vcl = (char*)e->vc + (size_t)l * e->kv_layer_elems * e->kvbytes();
-        HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, 0, B, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
+        pending = 0;
         prof_mark(e, Q3_PROF_GEMV, true, wb * e->qkv_rows() * d + 4.0 * B * (d + e->qkv_rows()));
-        HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
+        if (mm) HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->qkv, B, e->qkv_rows(), d, GEMM_F32, s));
+        else HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
         prof_mark(e, Q3_PROF_GEMV, false);
         HIPCHK(e, launch_qk_rope_decode(e->qkv, positions, e->d_len, seq_base, B, L.q_norm, L.k_norm,
                                         e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq, Hq, Hkv, s));
         prof_mark(e, Q3_PROF_ATTN_DECODE, true, kv_read_bytes(e, seq_base, B) / c.n_layers);
         HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, e->d_len, 1, seq_base, B, Hq, Hkv,
-                                     maxT, e->attn_ws, e->o, s));
+                                     maxT, e->attn_ws, e->o, mm, s));
         prof_mark(e, Q3_PROF_ATTN_DECODE, false);
-        prof_mark(e, Q3_PROF_GEMV, true, wb * d * Hq * 128 + 4.0 * B * (Hq * 128 + 2 * d));
-        HIPCHK(e, launch_gemv(L.wo, wdt, e->o, e->x, d, Hq * 128, B, GEMV_RESID, s));
+        prof_mark(e, Q3_PROF_GEMV, true, wb * d * HD + 4.0 * B * (HD + 2 * d));
+        if (mm && split > 1) {
+            HIPCHK(e, launch_gemm(e->o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->parts, B, d, HD, GEMM_PARTIAL_F32, s, split));
+            pending = split;
+        } else if (mm) {
+            HIPCHK(e, launch_gemm(e->o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->x, B, d, HD, GEMM_RESID_F32, s));
+        } else {
+            HIPCHK(e, launch_gemv(L.wo, wdt, e->o, e->x, d, HD, B, GEMV_RESID, s));
+        }
         prof_mark(e, Q3_PROF_GEMV, false);
-        HIPCHK(e, launch_rmsnorm(e->x, L.post_norm, e->h, 0, B, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->x, L.post_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
+        pending = 0;
         prof_mark(e, Q3_PROF_GEMV, true, wb * 2.0 * F * d + 4.0 * B * (d + F));
-        HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
+        if (mm) HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->a, B, 2 * F, d, GEMM_SWIGLU_PAIR, s));
+        else HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
         prof_mark(e, Q3_PROF_GEMV, false);
         prof_mark(e, Q3_PROF_GEMV, true, wb * d * F + 4.0 * B * (F + 2 * d));
-        HIPCHK(e, launch_gemv(L.wd, wdt, e->a, e->x, d, F, B, GEMV_RESID, s));
+        if (mm && split > 1) {
+            HIPCHK(e, launch_gemm(e->a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->parts, B, d, F, GEMM_PARTIAL_F32, s, split));
+            pending = split;
+        } else if (mm) {
+            HIPCHK(e, launch_gemm(e->a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->x, B, d, F, GEMM_RESID_F32, s));
+        } else {
+            HIPCHK(e, launch_gemv(L.wd, wdt, e->a, e->x, d, F, B, GEMV_RESID, s));
+        }
         prof_mark(e, Q3_PROF_GEMV, false);
+    }
+    if (pending && !want_logits) {   // x must be complete when the step ends
+        HIPCHK(e, launch_rmsnorm(e->x, e->final_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
+        pending = 0;
     }
     if (want_logits) {
         float* lg = logits_out ? logits_out : e->logits;
-        HIPCHK(e, launch_rmsnorm(e->x, e->final_norm, e->h, 0, B, d, c.rms_eps, s));
-        HIPCHK(e, launch_fill_u64(e->amax, 0ull, B, s));
+        HIPCHK(e, launch_rmsnorm(e->x, e->final_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
+        pending = 0;
         prof_mark(e, Q3_PROF_LMHEAD, true, wb * V * d + 4.0 * B * (d + V));
-        HIPCHK(e, launch_lmhead(e->embed, wdt, e->h, lg, e->amax, V, d, B, e->d_err, s));
+        if (mm) {
+            HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)e->embed, lg, B, V, d, GEMM_F32, s));
+            HIPCHK(e, launch_argmax_rows(lg, e->amax, V, B, e->d_err, s));
+        } else {
+            HIPCHK(e, launch_fill_u64(e->amax, 0ull, B, s));
+            HIPCHK(e, launch_lmhead(e->embed, wdt, e->h, lg, e->amax, V, d, B, e->d_err, s));
+        }
         prof_mark(e, Q3_PROF_LMHEAD, false);
         e->cur_logits = lg;
         e->cur_rows = B;

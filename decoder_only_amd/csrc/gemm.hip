@@ -15,7 +15,9 @@
 // the K hi parts, then the K lo parts) or is split here from float32 A while staging.
 //
 // Epilogues: float32 store, float32 residual add (x += A W^T), SwiGLU (W packs 16 gate rows
-// then the 16 matching up rows; a lane holds both) to float32 or to bf16 pair rows, bf16.
+// then the 16 matching up rows; a lane holds both) to float32 or to bf16 pair rows, bf16,
+// and split-K partials (gridDim.z blocks along K, each writing its float32 partial product,
+// summed by the consumer in a fixed order).
 // Requires N % 128 == 0 and K % 64 == 0; rows >= M are masked.
 #include "common.h"
 #include "kernels.h"
@@ -110,12 +112,14 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-    gload(0);
+    // split-K: block z of gridDim.z takes k-tiles [z nk / S, (z + 1) nk / S)
+    const int nkt = K / BK, S = gridDim.z, z = blockIdx.z;
+    const int kt0 = (int)((long long)nkt * z / S), nk = (int)((long long)nkt * (z + 1) / S);
+    gload(kt0);
     sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = NB == 2 ? (kt & 1) : 0;
+    for (int kt = kt0; kt < nk; ++kt) {
+        const int cur = NB == 2 ? ((kt - kt0) & 1) : 0;
         if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -184,6 +188,8 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
                     const int col = n0 + wn * 64 + j * 16 + col_l;
                     const float v = acc[i][j][r];
                     if (EPI == GEMM_F32) reinterpret_cast<float*>(C)[(size_t)row * N + col] = v;
+                    else if (EPI == GEMM_PARTIAL_F32)
+                        reinterpret_cast<float*>(C)[((size_t)z * M + row) * N + col] = v;
                     else if (EPI == GEMM_RESID_F32) reinterpret_cast<float*>(C)[(size_t)row * N + col] += v;
                     else reinterpret_cast<bf16*>(C)[(size_t)row * N + col] = f2bf(v);
                 }
@@ -195,37 +201,41 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
 }  // namespace
 
 template <int AM, int BM, int NB>
-static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
-    dim3 grid(N / BN, (M + BM - 1) / BM);
+static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
+                           hipStream_t s) {
+    dim3 grid(N / BN, (M + BM - 1) / BM, splits);
     switch (epi) {
         case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_PARTIAL_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_PARTIAL_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <int AM>
-static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, hipStream_t s) {
+static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
+                            hipStream_t s) {
     // 128-row tiles unless that leaves fewer than two blocks per compute unit
     const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128);
     // (measured on MI355X at the prefill shapes: 64-row tiles with two LDS buffers, 128-row
     // tiles with one buffer and two blocks per compute unit)
-    if (blocks128 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, s);
-    return launch_t<AM, 128, 1>(A, W, C, M, N, K, epi, s);
+    if (blocks128 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s);
+    return launch_t<AM, 128, 1>(A, W, C, M, N, K, epi, splits, s);
 }
 
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
-                       hipStream_t s) {
+                       hipStream_t s, int splits) {
     if (M <= 0) return hipSuccess;
-    if (N % BN != 0 || K % BK != 0) return hipErrorInvalidValue;
+    if (N % BN != 0 || K % BK != 0 || splits < 1 || splits > K / BK || (splits > 1 && epi != GEMM_PARTIAL_F32))
+        return hipErrorInvalidValue;
     switch (a_mode) {
-        case GEMM_A_BF16: return launch_bm<GEMM_A_BF16>(A, W, C, M, N, K, epi, s);
-        case GEMM_A_F32: return launch_bm<GEMM_A_F32>(A, W, C, M, N, K, epi, s);
-        case GEMM_A_PAIR: return launch_bm<GEMM_A_PAIR>(A, W, C, M, N, K, epi, s);
+        case GEMM_A_BF16: return launch_bm<GEMM_A_BF16>(A, W, C, M, N, K, epi, splits, s);
+        case GEMM_A_F32: return launch_bm<GEMM_A_F32>(A, W, C, M, N, K, epi, splits, s);
+        case GEMM_A_PAIR: return launch_bm<GEMM_A_PAIR>(A, W, C, M, N, K, epi, splits, s);
         default: return hipErrorInvalidValue;
     }
 }

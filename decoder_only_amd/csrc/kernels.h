@@ -14,9 +14,10 @@ enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
 hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
                         int vocab, unsigned* err, hipStream_t s);
 // out[r, :] = rmsnorm(x[r, :]) * w; out_mode 0 float32, 1 bf16, 2 bf16 pair rows [rows][2d]
-// (d hi parts, then d lo parts).
-hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_mode, int rows, int d,
-                          float eps, hipStream_t s);
+// (d hi parts, then d lo parts). With nparts > 0, first x[r, :] += parts[0][r, :] + ... +
+// parts[nparts-1][r, :] (in that order; parts [nparts][rows][d] float32) and x is written back.
+hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int rows, int d,
+                          float eps, hipStream_t s, const float* parts = nullptr, int nparts = 0);
 // Decode rows: per-head RMSNorm of q and k, RoPE at the row's position, K/V append at
 // slot lens[seq]. qkv: [B][(Hq + 2 Hkv) * 128] float32. q_out: [B][Hq][128] float32.
 // kc/vc: layer base of the cache [S][Hkv][t_cap][128]. positions may be NULL (= slot).
@@ -48,18 +49,21 @@ hipError_t launch_lmhead(const void* E, int wdt, const float* h, float* logits,
 // ---- attn_decode.hip (split-K GQA over the cache, one query row per sequence)
 // Visible keys of row b: slots 0 .. lens[seq_base + b] + len_extra - 1.
 size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T);
+// o: float32 [B][Hq*128], or (o_pair) bf16 pair rows [B][2*Hq*128].
 hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
                               int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
-                              int Hq, int Hkv, int max_T, float* ws, float* o, hipStream_t s);
+                              int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s);
 
 // ---- gemm.hip (prefill projections on MFMA: A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
 // a_mode: A bf16 [M][K]; float32 [M][K] split into bf16 hi + lo while staging; or a bf16
 // pair [M][2K] (per row the K hi parts, then the K lo parts). Split / pair: two MFMAs per tile.
 enum GemmAMode { GEMM_A_BF16 = 0, GEMM_A_F32 = 1, GEMM_A_PAIR = 2 };
-// Epilogues; SWIGLU_PAIR writes C as bf16 pair rows [M][N] (N/2 hi, then N/2 lo).
-enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3, GEMM_SWIGLU_PAIR = 4 };
+// Epilogues; SWIGLU_PAIR writes C as bf16 pair rows [M][N] (N/2 hi, then N/2 lo);
+// PARTIAL_F32 (with splits > 1 blocks along K) writes C[split][M][N] float32 partials.
+enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3, GEMM_SWIGLU_PAIR = 4,
+               GEMM_PARTIAL_F32 = 5 };
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
-                       hipStream_t s);
+                       hipStream_t s, int splits = 1);
 
 // ---- attn_prefill.hip (causal GQA flash attention on MFMA)
 // q: [Hq][M][128] float32 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16;

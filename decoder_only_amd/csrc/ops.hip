@@ -32,7 +32,7 @@ extern "C" q3_status q3_op_rmsnorm(const float* x, const float* w, void* out, in
                                    int32_t d, float eps, void* stream) {
     if (!x || !w || !out || rows < 0 || d <= 0 || (out_dtype != Q3_F32 && out_dtype != Q3_BF16 && out_dtype != Q3_OP_PAIR))
         return Q3_ERR_ARG;
-    return st(launch_rmsnorm(x, w, out, out_dtype == Q3_F32 ? 0 : (out_dtype == Q3_BF16 ? 1 : 2), rows, d, eps,
+    return st(launch_rmsnorm(const_cast<float*>(x), w, out, out_dtype == Q3_F32 ? 0 : (out_dtype == Q3_BF16 ? 1 : 2), rows, d, eps,
                              (hipStream_t)stream));
 }
 
@@ -83,7 +83,7 @@ extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, cons
     Scratch sc(s);
     if (!sc.get(attn_decode_workspace_bytes(B, n_kv_heads, max_len))) return Q3_ERR_OOM;
     return st(launch_attn_decode(q, k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, lens, 0, 0, B, n_heads,
-                                 n_kv_heads, max_len, (float*)sc.p, o, s));
+                                 n_kv_heads, max_len, (float*)sc.p, o, 0, s));
 }
 
 extern "C" q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
