@@ -5,8 +5,9 @@
 //
 // Split-K: the visible slots are cut into chunks of CHUNK keys; a block owns one
 // (sequence, kv head, chunk) and streams that chunk's K and V once for both query
-// heads of the group, keeping a running (max, sum, weighted V) per head. A combine
-// kernel merges the chunks' partial results with the usual max-rescaling.
+// heads of the group, producing (max, sum, weighted V) per head. A combine kernel merges
+// the chunks' partial results with the usual max-rescaling. bf16 caches use the
+// matrix-core kernel below; float32 caches (the toy model) a vector-unit kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -141,6 +142,138 @@ __global__ __launch_bounds__(256) void k_attn_decode_part(
     }
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+// bf16 cache: the same (sequence, kv head, chunk) partial state, computed in two passes.
+// Scores S^T = K q^T on the matrix cores (a wave takes 64 keys as four 16-key tiles whose K
+// rows are loaded straight into A-operand registers; q, split into bf16 hi + lo, is the B
+// operand with the two query heads as columns 0 and 1), then the chunk's max and sum per
+// head through shared memory, then P.V on the vector units (16 lane groups, 8 dims per
+// lane, V rows loaded before the scores are computed) with no per-key rescaling.
+__global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
+    const float* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc, int t_cap,
+    const int32_t* __restrict__ lens, int len_extra, int seq_base, int Hq, int Hkv, int nchunk,
+    float* __restrict__ part) {
+    __shared__ float sp[G][CHUNK];     // scores, then probabilities
+    __shared__ float hs[G][4];         // per-head wave maxima [0..1] and sums [2..3]
+    __shared__ float wm[16][G][128];   // P.V partials of the 16 lane groups
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
+    const int seq = seq_base + b;
+    const int T = min(lens[seq] + len_extra, t_cap);
+    const int k0 = c * CHUNK + wid * 64;             // this wave's first key
+    const size_t head_base = ((size_t)seq * Hkv + g) * t_cap * 128;
+    const float scale = 0.088388346f;                // fl32(128^-0.5)
+
+    // V rows for P.V: lane group (wid, quad) takes keys k0 + quad + 4 i, lane col dims 8 col ..
+    u32x4 vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int key = k0 + quad + 4 * i;
+        vr[i] = key < T ? *reinterpret_cast<const u32x4*>(vc + head_base + (size_t)key * 128 + 8 * col)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    // q^T (B operand): lane holds q[head col][32 ks + 8 quad + e] for col < 2, else zeros
+    bf16x8 qh[4], ql[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        f32x8 x = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (col < G) {
+            const f32x4* qp = reinterpret_cast<const f32x4*>(q + ((size_t)b * Hq + g * G + col) * 128 + 32 * ks + 8 * quad);
+            const f32x4 u0 = qp[0], u1 = qp[1];
+            x = f32x8{u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+        }
+        qh[ks] = __builtin_convertvector(x, bf16x8);
+        ql[ks] = __builtin_convertvector(x - __builtin_convertvector(qh[ks], f32x8), bf16x8);
+    }
+    // K rows (A operand): tile t row col = key k0 + 16 t + col, dims 32 ks + 8 quad ..
+    u32x4 kr[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int key = k0 + 16 * t + col;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kr[t][ks] = key < T ? *reinterpret_cast<const u32x4*>(kc + head_base + (size_t)key * 128 + 32 * ks + 8 * quad)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, kr[t][ks]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sc, 0, 0, 0);
+        }
+        if (col < G) {                               // D[key 4 quad + r][head col]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kl = wid * 64 + 16 * t + 4 * quad + r;
+                sp[col][kl] = c * CHUNK + kl < T ? sc[r] * scale : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+    // chunk max and sum per head: head h = tid / 128 over keys i and i + 128
+    float M, L;
+    {
+        const int h = tid >> 7, i = tid & 127;
+        const float x0 = sp[h][i], x1 = sp[h][i + 128];
+        const float wmx = wave_max(fmaxf(x0, x1));
+        if (lane == 0) hs[h][wid & 1] = wmx;
+        __syncthreads();
+        M = fmaxf(hs[h][0], hs[h][1]);
+        const float p0 = x0 == -INFINITY ? 0.f : __expf(x0 - M);
+        const float p1 = x1 == -INFINITY ? 0.f : __expf(x1 - M);
+        sp[h][i] = p0;
+        sp[h][i + 128] = p1;
+        const float ws = wave_sum(p0 + p1);
+        if (lane == 0) hs[h][2 + (wid & 1)] = ws;
+        __syncthreads();
+        L = hs[h][2] + hs[h][3];
+    }
+    // P.V
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kl = wid * 64 + quad + 4 * i;
+        const float p0 = sp[0][kl], p1 = sp[1][kl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = __uint_as_float(vr[i][e] << 16), v1 = __uint_as_float(vr[i][e] & 0xFFFF0000u);
+            acc[0][2 * e] += p0 * v0;
+            acc[0][2 * e + 1] += p0 * v1;
+            acc[1][2 * e] += p1 * v0;
+            acc[1][2 * e + 1] += p1 * v1;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wm[wid * 4 + quad][h][8 * col + e] = acc[h][e];
+    __syncthreads();
+    {
+        const int h = tid >> 7, d = tid & 127;
+        float a[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = wm[j][h][d];
+#pragma unroll
+        for (int hh = 1; hh < 16; hh <<= 1)
+#pragma unroll
+            for (int j = 0; j + hh < 16; j += 2 * hh) a[j] += a[j + hh];
+        float* pp = part + ((((size_t)b * Hkv + g) * nchunk + c) * G + h) * PART;
+        if (d == 0) { pp[0] = M; pp[1] = L; }     // L == 0 (M = -inf) when the chunk is empty
+        pp[2 + d] = a[0];
+    }
+}
+
 // o_pair: o is bf16 pair rows [B][2 * Hq * 128] (hi parts, then lo parts), else float32.
 template <bool PAIR>
 __global__ __launch_bounds__(128) void k_attn_decode_combine(
@@ -191,7 +324,7 @@ hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, in
     const int nchunk = (max_T + CHUNK - 1) / CHUNK;
     dim3 grid(nchunk, Hkv, B);
     if (kv_bf16)
-        hipLaunchKernelGGL(k_attn_decode_part<bf16>, grid, dim3(256), 0, s, q, (const bf16*)kc,
+        hipLaunchKernelGGL(k_attn_decode_mfma, grid, dim3(256), 0, s, q, (const bf16*)kc,
                            (const bf16*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
     else
         hipLaunchKernelGGL(k_attn_decode_part<float>, grid, dim3(256), 0, s, q, (const float*)kc,
