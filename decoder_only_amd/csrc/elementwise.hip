@@ -46,7 +46,18 @@ __global__ void k_rmsnorm(float* __restrict__ x, const float* __restrict__ w, vo
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
         float v = xr[i];
         if (nparts > 0) {
-            for (int p = 0; p < nparts; ++p) v += parts[((size_t)p * rows + r) * d + i];
+            // partials in batches of 8 loads in flight, added in order p = 0, 1, ...
+            const float* pp = parts + (size_t)r * d + i;
+            const size_t stride = (size_t)rows * d;
+            int p = 0;
+            for (; p + 8 <= nparts; p += 8) {
+                float t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = pp[(size_t)(p + u) * stride];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += t[u];
+            }
+            for (; p < nparts; ++p) v += pp[(size_t)p * stride];
             xr[i] = v;
         }
         ss += v * v;
@@ -104,7 +115,7 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
                                  const float* __restrict__ qn, const float* __restrict__ kn,
                                  const float* __restrict__ inv_freq, float eps,
                                  float* __restrict__ q_out, KT* __restrict__ kc, KT* __restrict__ vc,
-                                 int t_cap, int Hq, int Hkv) {
+                                 int t_cap, int Hq, int Hkv, int nparts) {
     const int b = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
     const int width = (Hq + 2 * Hkv) * 128;
     const float* row = qkv + (size_t)b * width + hd * 128;
@@ -113,6 +124,11 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
     if ((unsigned)slot >= (unsigned)t_cap) return;   // capacity is checked on the host
     const int pos = positions ? positions[b] : slot;
     float x1 = row[i], x2 = row[i + 64];
+    for (int p = 1; p < nparts; ++p) {               // split-K partials, added in order
+        const float* rp = row + (size_t)p * gridDim.x * width;
+        x1 += rp[i];
+        x2 += rp[i + 64];
+    }
     if (hd >= Hq + Hkv) {  // value head: stored as is
         const int g = hd - Hq - Hkv;
         const size_t base = (((size_t)seq * Hkv + g) * t_cap + slot) * 128;
@@ -136,14 +152,45 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
 hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
                                  const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
-                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s) {
+                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s, int nparts) {
+    if (B <= 0) return hipSuccess;
+    if (nparts < 1) return hipErrorInvalidValue;
     dim3 grid(B, Hq + 2 * Hkv);
     if (kv_bf16)
         hipLaunchKernelGGL(k_qk_rope_decode<bf16>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
-                           q_norm, k_norm, inv_freq, eps, q_out, (bf16*)kc, (bf16*)vc, t_cap, Hq, Hkv);
+                           q_norm, k_norm, inv_freq, eps, q_out, (bf16*)kc, (bf16*)vc, t_cap, Hq, Hkv, nparts);
     else
         hipLaunchKernelGGL(k_qk_rope_decode<float>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
-                           q_norm, k_norm, inv_freq, eps, q_out, (float*)kc, (float*)vc, t_cap, Hq, Hkv);
+                           q_norm, k_norm, inv_freq, eps, q_out, (float*)kc, (float*)vc, t_cap, Hq, Hkv, nparts);
+    return hipGetLastError();
+}
+
+// a[b][j] = silu(g) * u with g, u the sums of nparts split-K partials of the packed
+// gate/up projection (blocks of 16 gate rows then the 16 matching up rows), written as
+// bf16 pair rows [B][2F] (F hi parts, then F lo parts).
+__global__ void k_swiglu_parts(const float* __restrict__ parts, int nparts, int B, int F,
+                               bf16* __restrict__ out) {
+    const int b = blockIdx.y, j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= F) return;
+    const int n = 32 * (j >> 4) + (j & 15);
+    const size_t stride = (size_t)B * 2 * F;
+    const float* pg = parts + (size_t)b * 2 * F + n;
+    float g = pg[0], u = pg[16];
+    for (int p = 1; p < nparts; ++p) {
+        g += pg[p * stride];
+        u += pg[p * stride + 16];
+    }
+    const float a = g / (1.0f + expf(-g)) * u;
+    const bf16 h = f2bf(a);
+    out[(size_t)b * 2 * F + j] = h;
+    out[(size_t)b * 2 * F + F + j] = f2bf(a - bf2f(h));
+}
+
+hipError_t launch_swiglu_parts(const float* parts, int nparts, int B, int F, void* out_pair, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    if (nparts < 1 || F % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_swiglu_parts, dim3((F + 255) / 256, B), dim3(256), 0, s, parts, nparts, B, F,
+                       (bf16*)out_pair);
     return hipGetLastError();
 }
 

@@ -464,11 +464,21 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     const int nmode = mm ? 2 : 0;   // RMSNorm output: bf16 pairs for the matrix cores, else float32
     // The residual projections (o, down) of few rows are split along K over enough blocks to
     // fill the GPU; their partials are added to x by the next RMSNorm, in a fixed order.
-    int split = 1, pending = 0;
+    // Split counts: enough blocks (>= 256) along K for each projection, within K / 64 and
+    // the partials workspace (kMaxSplits x rows x hidden floats).
+    int split = 1, split_qkv = 1, split_gu = 1, pending = 0;
     if (mm) {
-        const int mblocks = (B + 63) / 64, nblocks = d / 128;
-        split = std::min(q3_engine::kMaxSplits, std::max(1, (256 + nblocks * mblocks - 1) / (nblocks * mblocks)));
-        split = std::min(split, std::min(HD, F) / 64);
+        const int mblocks = (B + 63) / 64;
+        auto pick = [&](int N, int K) {
+            const int nb = (N / 128) * mblocks;
+            int sp = std::max(1, (256 + nb - 1) / nb);
+            sp = std::min(sp, K / 64);
+            while (sp > 1 && (size_t)sp * N > (size_t)q3_engine::kMaxSplits * d) --sp;
+            return sp;
+        };
+        split = std::min(pick(d, HD), pick(d, F));
+        split_qkv = pick(e->qkv_rows(), d);
+        split_gu = pick(2 * F, d);
     }
     prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
     HIPCHK(e, launch_embed(tokens, e->embed, wdt, e->x, B, d, V, e->d_err, s));
@@ -479,11 +489,18 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
         pending = 0;
         prof_mark(e, Q3_PROF_GEMV, true, wb * e->qkv_rows() * d + 4.0 * B * (d + e->qkv_rows()));
-        if (mm) HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->qkv, B, e->qkv_rows(), d, GEMM_F32, s));
-        else HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
+        if (mm && split_qkv > 1) {
+            HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->parts, B, e->qkv_rows(), d,
+                                  GEMM_PARTIAL_F32, s, split_qkv));
+        } else if (mm) {
+            HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->qkv, B, e->qkv_rows(), d, GEMM_F32, s));
+        } else {
+            HIPCHK(e, launch_gemv(L.wqkv, wdt, e->h, e->qkv, e->qkv_rows(), d, B, GEMV_STORE, s));
+        }
         prof_mark(e, Q3_PROF_GEMV, false);
-        HIPCHK(e, launch_qk_rope_decode(e->qkv, positions, e->d_len, seq_base, B, L.q_norm, L.k_norm,
-                                        e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq, Hq, Hkv, s));
+        HIPCHK(e, launch_qk_rope_decode(mm && split_qkv > 1 ? e->parts : e->qkv, positions, e->d_len, seq_base, B,
+                                        L.q_norm, L.k_norm, e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq,
+                                        Hq, Hkv, s, mm ? split_qkv : 1));
         prof_mark(e, Q3_PROF_ATTN_DECODE, true, kv_read_bytes(e, seq_base, B) / c.n_layers);
         HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, e->d_len, 1, seq_base, B, Hq, Hkv,
                                      maxT, e->attn_ws, e->o, mm, s));
@@ -501,8 +518,15 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         HIPCHK(e, launch_rmsnorm(e->x, L.post_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
         pending = 0;
         prof_mark(e, Q3_PROF_GEMV, true, wb * 2.0 * F * d + 4.0 * B * (d + F));
-        if (mm) HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->a, B, 2 * F, d, GEMM_SWIGLU_PAIR, s));
-        else HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
+        if (mm && split_gu > 1) {
+            HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->parts, B, 2 * F, d, GEMM_PARTIAL_F32, s,
+                                  split_gu));
+            HIPCHK(e, launch_swiglu_parts(e->parts, split_gu, B, F, e->a, s));
+        } else if (mm) {
+            HIPCHK(e, launch_gemm(e->h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->a, B, 2 * F, d, GEMM_SWIGLU_PAIR, s));
+        } else {
+            HIPCHK(e, launch_gemv(L.wgu, wdt, e->h, e->a, 2 * F, d, B, GEMV_SWIGLU, s));
+        }
         prof_mark(e, Q3_PROF_GEMV, false);
         prof_mark(e, Q3_PROF_GEMV, true, wb * d * F + 4.0 * B * (F + 2 * d));
         if (mm && split > 1) {

@@ -21,10 +21,14 @@ hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int
 // Decode rows: per-head RMSNorm of q and k, RoPE at the row's position, K/V append at
 // slot lens[seq]. qkv: [B][(Hq + 2 Hkv) * 128] float32. q_out: [B][Hq][128] float32.
 // kc/vc: layer base of the cache [S][Hkv][t_cap][128]. positions may be NULL (= slot).
+// With nparts > 1, qkv holds nparts split-K partials [nparts][B][...], summed in order.
 hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
                                  const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
-                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s);
+                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s, int nparts = 1);
+// SwiGLU of the summed split-K partials [nparts][B][2F] of the packed gate/up projection,
+// to bf16 pair rows [B][2F].
+hipError_t launch_swiglu_parts(const float* parts, int nparts, int B, int F, void* out_pair, hipStream_t s);
 // Prefill rows of one sequence at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] float32.
 // kc/vc: cache of this (layer, sequence): [Hkv][t_cap][128] bf16.
 hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
