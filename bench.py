@@ -15,8 +15,10 @@ rate on this host (a bounded sample).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,6 +45,9 @@ def main() -> int:
     ap.add_argument("--plain-launch", action="store_true",
                     help="dispatch the persistent decode kernel as an ordinary launch (for tracers "
                          "that cannot follow cooperative launches)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain streaming kernel (torch.neg) over MIB MiB of float32, three "
+                         "times: a known-size reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); "
@@ -56,6 +61,13 @@ def main() -> int:
     from decoder_only_amd import q3
 
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 18, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.workload("bs1_short")
     t = time.time()
     weights = synth.make_weights(w)
@@ -110,7 +122,8 @@ def main() -> int:
     if gemv["launches"] == 0:
         roofline = {"kernel": "k_decode_mega (persistent decode step: all layers, LM head, argmax)",
                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": stored_traffic("k_decode_mega_bs1_traffic.md", MEGA_SOURCES),
                     "avg_launch_us": round(step_us, 3),
                     "bytes_per_launch": round(step["bytes"] / step["launches"])}
     else:
@@ -228,6 +241,31 @@ def bs64_line(eng, w, q3, torch, synth, max_seq):
     log(f"bs64 decode: {B * steps / dt:.0f} tok/s; attention {ag:.0f} GB/s")
     return {"bs64_decode_tok_s": round(B * steps / dt, 1), "bs64_step_ms": round(1e3 * dt / steps, 3),
             "bs64_attn_gbs": round(ag, 1), "bs64_attn_hbm_frac": round(ag / HBM_PEAK_GBS, 4)}
+
+
+def stored_traffic(md_name, sources):
+    """HBM bytes per launch of a kernel as recorded under profiles/ from two hardware-counter
+    passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for a
+    plain streaming kernel of known size. None when the record is missing or was taken on
+    other kernel sources than the ones in this tree."""
+    h = hashlib.sha256()
+    try:
+        for rel in sources:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        with open(os.path.join(ROOT, "profiles", md_name)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"kernel sources sha256: `([0-9a-f]{64})`", text)
+    t = re.search(r"HBM traffic per launch: `(\d+)` bytes", text)
+    if not m or not t or m.group(1) != h.hexdigest():
+        return None
+    return int(t.group(1))
+
+
+MEGA_SOURCES = ("decoder_only_amd/csrc/decode_mega.hip", "decoder_only_amd/csrc/common.h",
+                "decoder_only_amd/csrc/kernels.h")
 
 
 def cpu_baseline(w, weights, budget_s):

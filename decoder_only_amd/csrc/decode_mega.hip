@@ -404,11 +404,14 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
         const int ntile = (nk + 15) >> 4;
         for (int t = wid; t < ntile; t += 4) {
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            bf16x8 a[4];                           // all fragment reads of the tile first
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                a[ks] = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][8 * kslot(col, 4 * ks + quad)]);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][8 * kslot(col, 4 * ks + quad)]);
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qh[ks], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ql[ks], sc, 0, 0, 0);
             }
             if (col < 2) {                         // D[key 4 quad + r][head col]
 #pragma unroll
