@@ -187,56 +187,48 @@ struct Smem {
     float sp[2][STAGE];            // scores, then probabilities, of the staged keys per head
     float hs[2][4];                // per-head softmax statistics of a shot
     float gu[24][BMAX];            // gate/up results
+    float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
     MegaLayer layers[kMegaMaxLayers];
     unsigned long long tr[TRACE_MAX];   // phase timestamps (trace only)
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "shared memory of one CU");
 
 // Per-thread values loaded together with a phase's weight slice: the RMSNorm weights of
-// its 4 elements, and for phase B the QK-norm weights of its RoPE pair and the frequency.
+// its 4 elements, and for phase B the QK-norm weights of its RoPE pair.
 struct Pre {
     f32x4 nw;
-    float qk1, qk2, fr;
+    float qk1, qk2;
 };
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
-}
 
 __device__ __forceinline__ int clamp_tok(const MegaParams& p, int b) {
     const int t = p.tokens[b];
     return (t >= 0 && t < p.vocab) ? t : 0;
 }
 
-// act[b][:] = act[b][:] * rsqrt(mean(act[b]^2) + eps) * w  (act holds x on entry;
-// wv = w[4t .. 4t+3] for thread t)
-__device__ __forceinline__ void rmsnorm_act(const MegaParams& p, Smem& sm, int B, const f32x4 wv) {
+// RMSNorm split in two: thread t owns elements 4t..4t+3 of each row. norm_own replaces
+// them by x * w and hands their sum of squares to the row's per-wave slots (red[b][wave]);
+// after the caller's next barrier, norm_scale gives rsqrt(mean(x^2) + eps), by which the
+// consumers multiply their dot products (so that barrier is the only one of the norm).
+__device__ __forceinline__ void norm_own(Smem& sm, int b, const f32x4 v, const f32x4 wv) {
     const int k = threadIdx.x * 4;
-    for (int b = 0; b < B; ++b) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][k]);
-        float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-        ss = block_sum256(ss, sm.red[b]);
-        const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+    float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.u.s.act[b][k + e] = (v[e] * r) * wv[e];
-    }
-    __syncthreads();
+    for (int e = 0; e < 4; ++e) sm.u.s.act[b][k + e] = v[e] * wv[e];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) sm.red[b][threadIdx.x >> 6] = ss;
+}
+__device__ __forceinline__ float norm_scale(const MegaParams& p, const Smem& sm, int b) {
+    const float ss = (sm.red[b][0] + sm.red[b][1]) + (sm.red[b][2] + sm.red[b][3]);
+    return 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
 }
 
 // QK-norm + RoPE of one 128-wide head held by a wave: lane i owns the pair (i, i + 64).
-__device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, float eps, int pos) {
+__device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, float eps, float c, float sn) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
     x1 = (x1 * r) * pre.qk1;
     x2 = (x2 * r) * pre.qk2;
-    const float ang = __fmul_rn((float)pos, pre.fr);
-    double sd, cd;
-    sincos((double)ang, &sd, &cd);
-    const float c = (float)cd, sn = (float)sd;
     const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, sn));
     const float y2 = __fadd_rn(__fmul_rn(x1, sn), __fmul_rn(x2, c));
     x1 = y1;
@@ -245,12 +237,12 @@ __device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, 
 
 // Polled q/k/v of group g (sm.in[b]) -> rotated q, bf16-rounded new k, v in shared memory;
 // `append` writes k, v into the cache at `slot`.
-__device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const Pre& pre, int layer, int b, int g, int pos,
+__device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const Pre& pre, int layer, int b, int g,
                            int slot, bool append) {
     const int wid = threadIdx.x >> 6, i = threadIdx.x & 63;
     const float* in = sm.in[b];                     // [q0 128 | q1 128 | k 128 | v 128]
     float x1 = in[wid * DH + i], x2 = in[wid * DH + i + 64];
-    if (wid < 3) norm_rope(x1, x2, pre, p.eps, pos);
+    if (wid < 3) norm_rope(x1, x2, pre, p.eps, sm.rc[b][i], sm.rs[b][i]);
     if (wid < 2) {
         sm.q[wid][i] = x1;
         sm.q[wid][i + 64] = x2;
@@ -517,7 +509,6 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
     const float* qk = (threadIdx.x >> 6) < 2 ? L.q_norm : L.k_norm;
     pre.qk1 = ldf(qk + i);
     pre.qk2 = ldf(qk + i + 64);
-    pre.fr = ldf(p.inv_freq + i);
 }
 __device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
     const int rr = threadIdx.x >> 3, sub = threadIdx.x & 7;
@@ -568,6 +559,17 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         const int t = p.tokens[tid];
         if (t < 0 || t >= p.vocab) atomicOr(p.err, Q3_DEVERR_TOKEN);
     }
+    // RoPE factors of this step (the same for every layer): cos / sin of fl32(pos * f_i),
+    // evaluated in double precision and rounded to float
+    if (tid < 64 * B) {
+        const int b = tid >> 6, i = tid & 63;
+        const int pos = p.positions ? p.positions[b] : p.slots[b];
+        const float ang = __fmul_rn((float)pos, ldf(p.inv_freq + i));
+        double sd, cd;
+        sincos((double)ang, &sd, &cd);
+        sm.rc[b][i] = (float)cd;
+        sm.rs[b][i] = (float)sd;
+    }
     __syncthreads();
     pf_qkv(p, sm.layers[0], pf, pre, w);
     int tslot = 0;
@@ -584,22 +586,30 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
         // ---------------- A: x -> RMSNorm -> QKV rows 16w .. 16w+15
         for (int b = 0; b < B; ++b) {
+            f32x4 v;                      // this thread's elements 4 tid .. 4 tid + 3 of x
             if (layer == 0) {
                 const int t = clamp_tok(p, b);
-                for (int k = tid; k < D; k += NT) sm.u.s.act[b][k] = bf2f(p.embed[(size_t)t * D + k]);
-            } else if (!poll<1>(X + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) {
-                return;
+                const unsigned* e = reinterpret_cast<const unsigned*>(p.embed + (size_t)t * D + 4 * tid);
+                const unsigned e0 = *(const GLOBAL_AS unsigned*)e, e1 = *(const GLOBAL_AS unsigned*)(e + 1);
+                v = f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xFFFF0000u), __uint_as_float(e1 << 16),
+                          __uint_as_float(e1 & 0xFFFF0000u)};
+            } else {
+                if (!poll<1>(X + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
+                v = *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][4 * tid]);   // polled by this thread
             }
+            if ((tid >> 3) == j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.xg[b][4 * (tid & 7) + e] = v[e];
+            }
+            norm_own(sm, b, v, pre.nw);
         }
-        __syncthreads();
-        if (tid < 32 * B) sm.xg[tid >> 5][tid & 31] = sm.u.s.act[tid >> 5][32 * j + (tid & 31)];
         trace_at(p, sm, tslot++);
-        rmsnorm_act(p, sm, B, pre.nw);
+        __syncthreads();
         trace_at(p, sm, tslot++);
         {
             const int r = tid >> 4, sub = tid & 15;
             for (int b = 0; b < B; ++b) {
-                const float s = sum16(dot_chunks<8>(pf, sm.u.s.act[b], sub, 16));
+                const float s = sum16(dot_chunks<8>(pf, sm.u.s.act[b], sub, 16)) * norm_scale(p, sm, b);
                 if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s);
             }
         }
@@ -613,14 +623,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         if (Tmax <= SHORT_T) {
             for (int b = 0; b < B; ++b) {
                 const int slot = p.slots[b], T = slot + 1;
-                const int pos = p.positions ? p.positions[b] : slot;
                 const size_t hb = kv_head_base(p, layer, b, g);
                 kv_stage(p, sm, hb, 0, first_shot(0, T, T));   // in flight while q/k/v arrive
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
                 if (b == 0) trace_at(p, sm, tslot++);
-                group_prep(p, sm, pre, layer, b, g, pos, slot, j == 0);
+                group_prep(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
                 attend(p, sm, hb, 0, T, T);
                 const int h = tid >> 7, dd = tid & 127;
@@ -632,7 +641,6 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             const int gg = w & 7, c = w >> 3;
             for (int b = 0; b < B; ++b) {
                 const int slot = p.slots[b], T = slot + 1;
-                const int pos = p.positions ? p.positions[b] : slot;
                 int nch, ch;
                 chunking(T, nch, ch);
                 if (c < nch) {
@@ -644,7 +652,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
                     if (b == 0) trace_at(p, sm, tslot++);
-                    group_prep(p, sm, pre, layer, b, gg, pos, slot, k1 == T);
+                    group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
                     attend(p, sm, hb, k0, k1, T);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
@@ -693,18 +701,22 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             if (!poll<8>(P + (size_t)b * W_P, W_P, Contig{}, HKV * D / 4, sm.u.s.part, p.err)) return;
             if (b == 0) trace_at(p, sm, tslot++);
             const int n = 4 * tid;
+            f32x4 xv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float xv = sm.u.s.part[n + e];
+                float t = sm.u.s.part[n + e];
 #pragma unroll
-                for (int gg = 1; gg < HKV; ++gg) xv += sm.u.s.part[gg * D + n + e];
-                sm.u.s.act[b][n + e] = xv;
+                for (int gg = 1; gg < HKV; ++gg) t += sm.u.s.part[gg * D + n + e];
+                xv[e] = t;
             }
+            if (tid == w) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.xr[b][e] = xv[e];
+            }
+            norm_own(sm, b, xv, pre.nw);
             __syncthreads();
         }
-        if (tid < 4 * B) sm.xr[tid >> 2][tid & 3] = sm.u.s.act[tid >> 2][4 * w + (tid & 3)];
         trace_at(p, sm, tslot++);
-        rmsnorm_act(p, sm, B, pre.nw);
         trace_at(p, sm, tslot++);
         {
             const int rr = tid >> 3, sub = tid & 7;
@@ -712,7 +724,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 float s = 0.f;
                 if (rr < 24) s = dot_chunks<16>(pf, sm.u.s.act[b], sub, 8);
                 s = sum8(s);
-                if (rr < 24 && sub == 0) sm.gu[rr][b] = s;
+                if (rr < 24 && sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b);
             }
             __syncthreads();
             if (tid < 12 * B) {
@@ -758,12 +770,16 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     load_rows(r0 + 16, b1);
     {
         const float* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
-        for (int b = 0; b < B; ++b)
+        for (int b = 0; b < B; ++b) {
             if (!poll<1>(Xl + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
+            norm_own(sm, b, *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][4 * tid]), pre.nw);
+        }
         __syncthreads();
         trace_at(p, sm, tslot++);
-        rmsnorm_act(p, sm, B, pre.nw);
     }
+    float rn[BMAX];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b) rn[b] = b < B ? norm_scale(p, sm, b) : 0.f;
     u64 best[BMAX] = {0ull, 0ull, 0ull, 0ull};
     bool bad = false;
     {
@@ -774,7 +790,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (b >= B) break;
                 float s = 0.f;
                 if (row < r1) s = dot_chunks<8>(wv, sm.u.s.act[b], sub, 16);
-                s = sum16(s);
+                s = sum16(s) * rn[b];
                 if (row < r1 && sub == 0) {
                     p.logits[(size_t)b * p.vocab + row] = s;
                     bad |= !isfinite(s);
