@@ -51,6 +51,8 @@ typedef unsigned long long u64;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // words per (layer, row) in each exchange buffer
 constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_A = F;
@@ -180,12 +182,12 @@ struct Smem {
     float xr[BMAX][4];             // x' at this workgroup's residual rows 4w..4w+3
     float red[BMAX][16];           // block reductions
     float in[BMAX][4 * DH];        // polled group inputs: q (2 x 128), k (128), v (128)
-    float q[2][DH];                // rotated queries of the current group
+    __attribute__((aligned(16))) bf16 qb[2][2][DH];   // rotated queries of the group: bf16 hi, lo parts
     float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
     float o[BMAX][2 * DH];         // attention output of the group, per row
     float att[2][PART];            // merged attention state (max, sum, acc) per head
     float sp[2][STAGE];            // scores, then probabilities, of the staged keys per head
-    float hs[2][4];                // per-head softmax statistics of a shot
+    float hs[2][4], wl[2][4];      // per-wave softmax maximum and sum of each head
     float gu[24][BMAX];            // gate/up results
     float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
     MegaLayer layers[kMegaMaxLayers];
@@ -243,9 +245,15 @@ __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const 
     const float* in = sm.in[b];                     // [q0 128 | q1 128 | k 128 | v 128]
     float x1 = in[wid * DH + i], x2 = in[wid * DH + i + 64];
     if (wid < 3) norm_rope(x1, x2, pre, p.eps, sm.rc[b][i], sm.rs[b][i]);
-    if (wid < 2) {
-        sm.q[wid][i] = x1;
-        sm.q[wid][i + 64] = x2;
+    if (wid < 2) {                                  // q = hi + lo + O(2^-17 q), the MFMA operands
+        // (packed conversions; the halves are taken apart with integer operations)
+        const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x1, x2}, bf16x2));
+        const float r1 = x1 - __uint_as_float(hb << 16), r2 = x2 - __uint_as_float(hb & 0xFFFF0000u);
+        const unsigned lb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r1, r2}, bf16x2));
+        sm.qb[wid][0][i] = (bf16)(hb & 0xFFFFu);
+        sm.qb[wid][0][i + 64] = (bf16)(hb >> 16);
+        sm.qb[wid][1][i] = (bf16)(lb & 0xFFFFu);
+        sm.qb[wid][1][i + 64] = (bf16)(lb >> 16);
     } else {
         const bf16 h1 = f2bf(x1), h2 = f2bf(x2);
         float* dst = wid == 2 ? sm.kn : sm.vn;
@@ -259,22 +267,6 @@ __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const 
         }
     }
     __syncthreads();
-}
-
-__device__ __forceinline__ void merge_state(float& m, float& l, float* a, float m2, float l2, const float* a2) {
-    if (l2 == 0.f) return;
-    if (l == 0.f) {
-        m = m2; l = l2;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = a2[i];
-        return;
-    }
-    const float mn = fmaxf(m, m2);
-    const float c1 = expf(m - mn), c2 = expf(m2 - mn);
-    l = l * c1 + l2 * c2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = a[i] * c1 + a2[i] * c2;
-    m = mn;
 }
 
 // Optional trace: thread 0 of workgroups 0 and NWG-1 records the 100 MHz real-time clock
@@ -304,16 +296,22 @@ __device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, i
 // at one column hit 16 different bank groups.
 __device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }
 
+// Stage cached rows [base, base + n) of one kv head into shared memory: wave w loads the
+// 16-row tiles t = w, w + 4, ... (the tiles it attends), four rows per instruction.
 __device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t hb, int base, int n) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    for (int r0 = 4 * wid; r0 < n; r0 += 16) {
-        const int r = r0 + (lane >> 4), sl = lane & 15;
-        if (r < n) {
-            const size_t row = hb + (size_t)(base + r) * DH;
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r, sl)),
-                                             (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl), (LDS_AS void*)&sm.u.kv.v[r0][0],
-                                             16, 0, 0);
+    for (int t = wid; 16 * t < n; t += 4) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 16 * t + 4 * q4;
+            const int r = r0 + (lane >> 4), sl = lane & 15;
+            if (r < n) {
+                const size_t row = hb + (size_t)(base + r) * DH;
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r, sl)),
+                                                 (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl),
+                                                 (LDS_AS void*)&sm.u.kv.v[r0][0], 16, 0, 0);
+            }
         }
     }
 }
@@ -331,43 +329,35 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
-// float32 x[8] -> bf16 hi and lo parts (x = hi + lo + O(2^-17 x)), as MFMA operands.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-    u32x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
-        const bf16 l0 = f2bf(x[2 * e] - bf2f(h0)), l1 = f2bf(x[2 * e + 1] - bf2f(h1));
-        h[e] = (unsigned)h0 | ((unsigned)h1 << 16);
-        l[e] = (unsigned)l0 | ((unsigned)l1 << 16);
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
 // Attention of both heads of the group for row b over slots [k0, k1) of T visible ones.
-// The caller issued the first shot (kv_stage of first_shot(k0, k1, T) rows at k0) and
-// waited for it; longer ranges are staged here shot by shot (SHOT rows; the new key, kept
-// in shared memory, is appended as the row after the cached ones of the last shot).
-// Per shot: scores S^T = K q^T on the matrix cores (16 keys x 16 columns per tile, columns
-// 0 and 1 the two heads; K rows are exact bf16 operands, q is split into bf16 hi + lo),
-// then the shot's softmax statistics per head, then P.V on the vector units with 16 lane
-// groups of 16 lanes (8 dims per lane), and a rescale of the running state between shots.
-// Leaves the merged per-head state (max, sum, unnormalised acc[128]) in sm.att.
-__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T) {
+// The caller issued the first shot (kv_stage of first_shot(k0, k1, T) rows at k0), waited
+// for it and passed a barrier; longer ranges are staged here shot by shot (SHOT rows; the
+// new key, kept in shared memory, is appended as the row after the cached ones of the
+// last shot). Wave w owns the 16-key tiles t = w, w + 4, ... of every shot: it stages
+// them, computes their scores S^T = K q^T on the matrix cores (columns 0 and 1 the two
+// heads; K rows are exact bf16 operands, q is split into bf16 hi + lo), keeps its own
+// running softmax state per head (max, sum, unnormalised P.V with 16 lanes x 8 dims per
+// key group), so no barrier is needed until the four wave states are merged (Step 6's
+// softmax over all keys, assembled from partial maxima and sums; exponentials in base 2
+// on scores scaled by log2(e)). Writes the normalised output of both heads to o_out, or,
+// when o_out is null, leaves the merged per-head state (base-2 max, sum, unnormalised
+// acc[128]) in sm.att.
+__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, float* o_out) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
-    const float scale = 0.088388346f;   // fl32(128^-0.5)
+    // scores are kept in the base-2 domain: s * log2(e), with s = q.k / sqrt(128)
+    const float scale = 0.088388346f * 1.44269504f;
     bf16x8 qh[4], ql[4];                // B operand: lane holds q[head col][32 ks + 8 quad + i]
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         if (col < 2) {
-            split8(&sm.q[col][32 * ks + 8 * quad], qh[ks], ql[ks]);
+            qh[ks] = *reinterpret_cast<const bf16x8*>(&sm.qb[col][0][32 * ks + 8 * quad]);
+            ql[ks] = *reinterpret_cast<const bf16x8*>(&sm.qb[col][1][32 * ks + 8 * quad]);
         } else {
             qh[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             ql[ks] = qh[ks];
         }
     }
-    float Mh[2] = {-INFINITY, -INFINITY}, Lh[2] = {0.f, 0.f}, acc[2][8];
+    float Mw[2] = {-INFINITY, -INFINITY}, Lw[2] = {0.f, 0.f}, acc[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -375,78 +365,75 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
     const int ce = min(k1, T - 1);                 // end of the cached rows in range
     for (int base = k0;; base += SHOT) {
         const int n = max(0, min(ce, base + SHOT) - base);
-        if (base != k0) {
-            __syncthreads();
+        if (base != k0) {                          // this wave's tiles of the next shot
+            __builtin_amdgcn_s_waitcnt(0);         // (its reads of the previous shot are done)
             kv_stage(p, sm, hb, base, n);
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
         }
         const bool last = base + SHOT >= ce;
         const bool with_new = last && k1 == T;
         const int nk = n + (with_new ? 1 : 0);
-        if (with_new && tid < 32) {                // the new key / value as staged row n
-            const int c = tid & 15;
-            const float* src = (tid < 16 ? sm.kn : sm.vn) + 8 * c;
-            bf16* dst = tid < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c];
+        if (with_new && wid == ((n >> 4) & 3) && lane < 32) {   // the new key / value as row n
+            const int c = lane & 15;
+            const float* src = (lane < 16 ? sm.kn : sm.vn) + 8 * c;
+            bf16* dst = lane < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c];
 #pragma unroll
             for (int e = 0; e < 8; ++e) dst[e] = f2bf(src[e]);   // exact: already bf16 values
         }
-        __syncthreads();
-        // scores of 16-key tiles, tile t on wave t % 4
         const int ntile = (nk + 15) >> 4;
         for (int t = wid; t < ntile; t += 4) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 sh = {0.f, 0.f, 0.f, 0.f}, sl = sh;   // hi and lo products: two chains
             bf16x8 a[4];                           // all fragment reads of the tile first
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 a[ks] = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][8 * kslot(col, 4 * ks + quad)]);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qh[ks], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ql[ks], sc, 0, 0, 0);
+                sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qh[ks], sh, 0, 0, 0);
+                sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ql[ks], sl, 0, 0, 0);
             }
             if (col < 2) {                         // D[key 4 quad + r][head col]
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.sp[col][16 * t + 4 * quad + r] = sc[r] * scale;
+                for (int r = 0; r < 4; ++r) sm.sp[col][16 * t + 4 * quad + r] = (sh[r] + sl[r]) * scale;
             }
         }
-        __syncthreads();
-        // softmax statistics of the shot: head h = tid / 128 over keys i and i + 128;
-        // hs[h][0..1] = maxima of the head's two waves, hs[h][2..3] = their sums
-        {
-            const int h = tid >> 7, i = tid & 127;
-            const float x0 = i < nk ? sm.sp[h][i] : -INFINITY;
-            const float x1 = i + 128 < nk ? sm.sp[h][i + 128] : -INFINITY;
-            const float wmx = wave_max(fmaxf(x0, x1));
-            if (lane == 0) sm.hs[h][wid & 1] = wmx;
-            __syncthreads();
-            const float Mn = fmaxf(Mh[h], fmaxf(sm.hs[h][0], sm.hs[h][1]));
-            const float p0 = i < nk ? expf(x0 - Mn) : 0.f;
-            const float p1 = i + 128 < nk ? expf(x1 - Mn) : 0.f;
-            sm.sp[h][i] = p0;
-            sm.sp[h][i + 128] = p1;
-            const float ws = wave_sum(p0 + p1);
-            if (lane == 0) sm.hs[h][2 + (wid & 1)] = ws;
-            __syncthreads();
+        // this wave's softmax statistics over the shot: lane (tile slot quad, key col)
+        for (int t0 = wid; t0 < ntile; t0 += 16) {
+            const int key = 16 * (t0 + 4 * quad) + col;
+            const bool valid = key < nk;
+            float x[2], mn[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                x[h] = valid ? sm.sp[h][key] : -INFINITY;
+                mn[h] = fmaxf(Mw[h], wave_max(x[h]));
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float pr = valid ? __builtin_amdgcn_exp2f(x[h] - mn[h]) : 0.f;
+                if (valid) sm.sp[h][key] = pr;
+                const float corr = Lw[h] > 0.f ? __builtin_amdgcn_exp2f(Mw[h] - mn[h]) : 0.f;
+                Lw[h] = Lw[h] * corr + wave_sum(pr);
+                Mw[h] = mn[h];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
+            }
         }
+        // P.V of this wave's keys: lane group quad takes keys 16 t + 4 i + quad, lane col
+        // dims 8 col .. 8 col + 7
+        for (int t = wid; t < ntile; t += 4) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float Mn = fmaxf(Mh[h], fmaxf(sm.hs[h][0], sm.hs[h][1]));
-            const float corr = Lh[h] > 0.f ? expf(Mh[h] - Mn) : 0.f;
-            Lh[h] = Lh[h] * corr + (sm.hs[h][2] + sm.hs[h][3]);
-            Mh[h] = Mn;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * t + 4 * i + quad;
+                if (r < nk) {
+                    float v[8];
+                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]), v);
+                    const float p0 = sm.sp[0][r], p1 = sm.sp[1][r];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
-        }
-        // P.V: lane group (wid, quad) takes keys wid*4 + quad + 16 i, lane col dims 8 col ..
-        for (int r = wid * 4 + quad; r < nk; r += 16) {
-            float v[8];
-            unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]), v);
-            const float p0 = sm.sp[0][r], p1 = sm.sp[1][r];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc[0][e] += p0 * v[e];
-                acc[1][e] += p1 * v[e];
+                    for (int e = 0; e < 8; ++e) {
+                        acc[0][e] += p0 * v[e];
+                        acc[1][e] += p1 * v[e];
+                    }
+                }
             }
         }
         if (last) break;
@@ -454,21 +441,39 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
     __syncthreads();                               // the staged rows share memory with wm
     const int slot = wid * 4 + quad;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sm.u.s.wm[slot][h][8 * col + e] = acc[h][e];
+        if (lane == 0) {
+            sm.hs[h][wid] = Mw[h];
+            sm.wl[h][wid] = Lw[h];
+        }
+    }
     __syncthreads();
     {
         const int h = tid >> 7, dd = tid & 127;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, sm.wl[h][w2] > 0.f ? sm.hs[h][w2] : -INFINITY);
+        float cw[4], L = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            cw[w2] = sm.wl[h][w2] > 0.f ? __builtin_amdgcn_exp2f(sm.hs[h][w2] - M) : 0.f;
+            L += sm.wl[h][w2] * cw[w2];
+        }
         float av[16];
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) av[s2] = sm.u.s.wm[s2][h][dd];
+        for (int s2 = 0; s2 < 16; ++s2) av[s2] = sm.u.s.wm[s2][h][dd] * cw[s2 >> 2];
 #pragma unroll
         for (int hh = 1; hh < 16; hh <<= 1)
 #pragma unroll
             for (int s2 = 0; s2 + hh < 16; s2 += 2 * hh) av[s2] += av[s2 + hh];
-        if (dd == 0) { sm.att[h][0] = Mh[h]; sm.att[h][1] = Lh[h]; }
-        sm.att[h][2 + dd] = av[0];
+        if (o_out) {
+            o_out[h * DH + dd] = L > 0.f ? av[0] / L : 0.f;
+        } else {
+            if (dd == 0) { sm.att[h][0] = M; sm.att[h][1] = L; }
+            sm.att[h][2 + dd] = av[0];
+        }
     }
     __syncthreads();
 }
@@ -631,10 +636,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
-                attend(p, sm, hb, 0, T, T);
-                const int h = tid >> 7, dd = tid & 127;
-                sm.o[b][h * DH + dd] = sm.att[h][1] > 0.f ? sm.att[h][2 + dd] / sm.att[h][1] : 0.f;
-                __syncthreads();
+                attend(p, sm, hb, 0, T, T, sm.o[b]);
             }
         } else {
             // B1: unit w = (group w % 8, chunk w / 8) attends its chunk, per row
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
-                    attend(p, sm, hb, k0, k1, T);
+                    attend(p, sm, hb, k0, k1, T, nullptr);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 float Ls = 0.f, Acc = 0.f;
                 for (int c2 = 0; c2 < nch; ++c2) {
                     const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
-                    const float cf = pp[1] > 0.f ? expf(pp[0] - M) : 0.f;
+                    const float cf = pp[1] > 0.f ? __builtin_amdgcn_exp2f(pp[0] - M) : 0.f;
                     Ls += pp[1] * cf;
                     Acc += pp[2 + dd] * cf;
                 }
