@@ -379,9 +379,11 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
         if (with_new && wid == ((n >> 4) & 3) && lane < 32) {   // the new key / value as row n
             const int c = lane & 15;
             const float* src = (lane < 16 ? sm.kn : sm.vn) + 8 * c;
-            bf16* dst = lane < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c];
+            u32x4 u;                               // exact: already bf16 values
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e] = f2bf(src[e]);   // exact: already bf16 values
+            for (int e = 0; e < 4; ++e)
+                u[e] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{src[2 * e], src[2 * e + 1]}, bf16x2));
+            *reinterpret_cast<u32x4*>(lane < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c]) = u;
         }
         const int ntile = (nk + 15) >> 4;
         for (int t = wid; t < ntile; t += 4) {
@@ -395,6 +397,9 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
                 sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qh[ks], sh, 0, 0, 0);
                 sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ql[ks], sl, 0, 0, 0);
             }
+            // keep the four fragment reads ahead of the products (one LDS wait per tile)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             if (col < 2) {                         // D[key 4 quad + r][head col]
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.sp[col][16 * t + 4 * quad + r] = (sh[r] + sl[r]) * scale;
