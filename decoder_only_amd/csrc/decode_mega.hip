@@ -189,7 +189,7 @@ struct Smem {
     float kn[DH], vn[DH];          // new key / value (bf16-rounded values)
     float o[BMAX][2 * DH];         // attention output of the group, per row
     float att[2][PART];            // merged attention state (max, sum, acc) per head
-    float sp[2][STAGE];            // scores, then probabilities, of the staged keys per head
+    __attribute__((aligned(16))) float sp[STAGE][2];   // scores, then probabilities (key, head)
     float hs[2][4], wl[2][4];      // per-wave softmax maximum and sum of each head
     float gu[24][BMAX];            // gate/up results
     float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
@@ -402,7 +402,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             if (col < 2) {                         // D[key 4 quad + r][head col]
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.sp[col][16 * t + 4 * quad + r] = (sh[r] + sl[r]) * scale;
+                for (int r = 0; r < 4; ++r) sm.sp[16 * t + 4 * quad + r][col] = (sh[r] + sl[r]) * scale;
             }
         }
         // this wave's softmax statistics over the shot: lane (tile slot quad, key col)
@@ -412,13 +412,13 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
             float x[2], mn[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                x[h] = valid ? sm.sp[h][key] : -INFINITY;
+                x[h] = valid ? sm.sp[key][h] : -INFINITY;
                 mn[h] = fmaxf(Mw[h], wave_max(x[h]));
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const float pr = valid ? __builtin_amdgcn_exp2f(x[h] - mn[h]) : 0.f;
-                if (valid) sm.sp[h][key] = pr;
+                sm.sp[key][h] = pr;                // 0 past the last key
                 const float corr = Lw[h] > 0.f ? __builtin_amdgcn_exp2f(Mw[h] - mn[h]) : 0.f;
                 Lw[h] = Lw[h] * corr + wave_sum(pr);
                 Mw[h] = mn[h];
@@ -426,21 +426,32 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
                 for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
             }
         }
+        // rows past the last key in its tile: zero values (their probabilities are zero too),
+        // so P.V can run over whole tiles
+        if (wid == ((ntile - 1) & 3)) {
+            for (int r = nk + (lane >> 4); r < 16 * ntile; r += 4)
+                *reinterpret_cast<u32x4*>(&sm.u.kv.v[r][8 * col]) = u32x4{0u, 0u, 0u, 0u};
+        }
         // P.V of this wave's keys: lane group quad takes keys 16 t + 4 i + quad, lane col
         // dims 8 col .. 8 col + 7
         for (int t = wid; t < ntile; t += 4) {
+            u32x4 vv[4];
+            f32x2 pp[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * t + 4 * i + quad;
-                if (r < nk) {
-                    float v[8];
-                    unpack8(*reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]), v);
-                    const float p0 = sm.sp[0][r], p1 = sm.sp[1][r];
+                vv[i] = *reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]);
+                pp[i] = *reinterpret_cast<const f32x2*>(&sm.sp[r][0]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // all reads of the tile first
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        acc[0][e] += p0 * v[e];
-                        acc[1][e] += p1 * v[e];
-                    }
+            for (int i = 0; i < 4; ++i) {
+                float v[8];
+                unpack8(vv[i], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    acc[0][e] += pp[i][0] * v[e];
+                    acc[1][e] += pp[i][1] * v[e];
                 }
             }
         }
