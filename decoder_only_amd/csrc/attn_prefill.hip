@@ -55,26 +55,38 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
     lo = __builtin_convertvector(x - hf, bf16x8);
 }
 
-template <bool PAIR>
+// BAL = false: block (query tile, kv head g) covers both query heads of g, each wave 32 rows
+// of one head (RT = 2 row tiles of 16). BAL = true, for short prompts where one query tile
+// per block would leave the causal work unbalanced (tile i needs i + 1 key tiles): block
+// (b, query head h) takes query tiles nqt-1-b and then b, each wave 16 rows (RT = 1), so
+// every block walks nqt + 1 key tiles.
+template <bool PAIR, bool BAL>
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
                                                       const bf16* __restrict__ vc, int t_cap, int M, int t0,
                                                       int Hq, int Hkv, void* __restrict__ o) {
+    constexpr int RT = BAL ? 1 : 2;
     __shared__ u32x4 sK[BKV * 16];
     __shared__ bf16 sVT[128 * BKV];
     const int nqt = (M + BQ - 1) / BQ;
-    const int qt = nqt - 1 - (int)blockIdx.x;   // heaviest (latest) query tiles first
-    const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int h = g * 2 + (wid >> 1);
-    const int qbase = qt * BQ + (wid & 1) * 32;   // first row of this wave
+    const int h = BAL ? (int)blockIdx.y : (int)blockIdx.y * 2 + (wid >> 1);
+    const int g = BAL ? (int)blockIdx.y >> 1 : (int)blockIdx.y;
     const int l16 = lane & 15, lg = lane >> 4;
     const float scale_log2 = 0.088388346f * 1.4426950408889634f;
+    const bf16* kh = kc + (size_t)g * t_cap * 128;
+    const bf16* vh = vc + (size_t)g * t_cap * 128;
+
+    for (int pass = 0; pass < (BAL ? 2 : 1); ++pass) {
+    // heaviest (latest) query tiles first
+    const int qt = pass == 0 ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (pass == 1 && qt >= nqt - 1 - (int)blockIdx.x) break;   // the middle tile of an odd count
+    const int qbase = qt * BQ + (BAL ? wid * 16 : (wid & 1) * 32);   // first row of this wave
 
     // Q^T as B operand (hi and lo parts): lane holds q row (l16) of q-tile c, dims
     // ks*32 + 8*lg .. +8.
-    bf16x8 qh[2][4], ql[2][4];
+    bf16x8 qh[RT][4], ql[RT][4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < RT; ++c) {
         const int row = qbase + c * 16 + l16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -88,18 +100,21 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
             split8(v, qh[c][ks], ql[c][ks]);
         }
     }
-    f32x4 oacc[8][2];
+    f32x4 oacc[8][RT];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) oacc[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+        for (int c = 0; c < RT; ++c) oacc[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrow[RT], lrow[RT];
+#pragma unroll
+    for (int c = 0; c < RT; ++c) {
+        mrow[c] = -INFINITY;
+        lrow[c] = 0.f;
+    }
 
     const int block_last_row = min(M, (qt + 1) * BQ) - 1;
     const int last_slot = t0 + block_last_row;
     const int ntiles = last_slot / BKV + 1;
-    const bf16* kh = kc + (size_t)g * t_cap * 128;
-    const bf16* vh = vc + (size_t)g * t_cap * 128;
 
     // K/V of tile kt + 1 are loaded into registers while tile kt is in use. Thread t takes
     // 16-byte chunk ck = t % 16 of the key pairs t / 16 and t / 16 + 16.
@@ -140,25 +155,25 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         __syncthreads();
         if (kt + 1 < ntiles) kv_load(kt + 1);
 
-        // S^T[key][row] for 4 key tiles x 2 row tiles
-        f32x4 s[4][2];
+        // S^T[key][row] for 4 key tiles x RT row tiles
+        f32x4 s[4][RT];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            s[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < RT; ++c) s[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 a = __builtin_bit_cast(bf16x8, sK[kidx(j * 16 + l16, ks * 4 + lg)]);
-                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[0][ks], s[j][0], 0, 0, 0);
-                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[1][ks], s[j][1], 0, 0, 0);
-                s[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[0][ks], s[j][0], 0, 0, 0);
-                s[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[1][ks], s[j][1], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < RT; ++c) s[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[c][ks], s[j][c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < RT; ++c) s[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c][ks], s[j][c], 0, 0, 0);
             }
         }
         // scale, causal mask, online softmax (per query row = l16 of tile c)
         const bool diag = (kt + 1) * BKV - 1 > t0 + qbase;   // some key may be after some row
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < RT; ++c) {
             const int qslot = t0 + qbase + c * 16 + l16;
             float mx = -INFINITY;
 #pragma unroll
@@ -197,9 +212,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         // keys {32kb + 4lg + i, 32kb + 16 + 4lg + i : i < 4}; V^T uses the same order.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 ph[2], pl[2];
+            bf16x8 ph[RT], pl[RT];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < RT; ++c) {
                 const float pv[8] = {s[2 * kb][c][0], s[2 * kb][c][1], s[2 * kb][c][2], s[2 * kb][c][3],
                                      s[2 * kb + 1][c][0], s[2 * kb + 1][c][1], s[2 * kb + 1][c][2], s[2 * kb + 1][c][3]};
                 split8(pv, ph[c], pl[c]);
@@ -211,16 +226,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
                 const u32x2 hi = *reinterpret_cast<const u32x2*>(&sVT[vt_off(d, kb * 32 + 16 + lg * 4)]);
                 const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
                 const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[0], oacc[dt][0], 0, 0, 0);
-                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[1], oacc[dt][1], 0, 0, 0);
-                oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[0], oacc[dt][0], 0, 0, 0);
-                oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[1], oacc[dt][1], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < RT; ++c) oacc[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[c], oacc[dt][c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < RT; ++c) oacc[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[c], oacc[dt][c], 0, 0, 0);
             }
         }
     }
     // O^T accumulator: lane holds query row (l16) of tile c, dims dt*16 + 4*lg + r.
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < RT; ++c) {
         const int row = qbase + c * 16 + l16;
         if (row >= M) continue;
         const float inv = 1.0f / lrow[c];
@@ -249,6 +264,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
                     f32x4{oacc[dt][c][0] * inv, oacc[dt][c][1] * inv, oacc[dt][c][2] * inv, oacc[dt][c][3] * inv};
         }
     }
+    }   // pass
 }
 
 }  // namespace
@@ -257,11 +273,18 @@ hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_
                                int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (Hq != 2 * Hkv) return hipErrorInvalidValue;
-    dim3 grid((M + BQ - 1) / BQ, Hkv);
-    if (o_pair)
-        hipLaunchKernelGGL(k_attn_prefill<true>, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-    else
-        hipLaunchKernelGGL(k_attn_prefill<false>, grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    const int nqt = (M + BQ - 1) / BQ;
+    // balanced pairs while one query tile per block would give fewer than 4 blocks per
+    // compute unit (the longest block then sets the time)
+    const bool bal = (long long)nqt * Hkv < 1024;
+    const dim3 grid = bal ? dim3((nqt + 1) / 2, Hq) : dim3(nqt, Hkv);
+    if (bal) {
+        if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+        else hipLaunchKernelGGL((k_attn_prefill<false, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    } else {
+        if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, false>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+        else hipLaunchKernelGGL((k_attn_prefill<false, false>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    }
     return hipGetLastError();
 }
 
