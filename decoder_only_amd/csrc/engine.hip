@@ -28,6 +28,8 @@ using namespace q3;
 
 namespace {
 constexpr int kPrefillMfmaMin = 16;   // prompts shorter than this run row by row
+constexpr int kPrefillSplitRows = 8192;   // prefill below this many rows: split-K O / down projections
+constexpr int kPrefillSplits = 3;         // at most this many K splits there
 }
 
 struct q3_engine {
@@ -90,6 +92,7 @@ struct q3_engine {
 
     // prefill workspace (grown on demand)
     int pf_cap = 0;
+    float* pf_parts = nullptr;     // split-K partials of the prefill O / down projections (short prompts)
     float *pf_x = nullptr, *pf_qkv = nullptr, *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr,
           *pf_a = nullptr;
 
@@ -569,8 +572,10 @@ static q3_status ensure_prefill_ws(q3_engine* e, int M) {
     if (M <= e->pf_cap) return Q3_OK;
     const q3_config& c = e->cfg;
     const int d = c.hidden, F = c.ffn, HD = c.n_heads * c.head_dim;
-    for (void* p : {(void*)e->pf_x, (void*)e->pf_qkv, (void*)e->pf_h, (void*)e->pf_q, (void*)e->pf_o, (void*)e->pf_a})
+    for (void* p : {(void*)e->pf_x, (void*)e->pf_qkv, (void*)e->pf_h, (void*)e->pf_q, (void*)e->pf_o, (void*)e->pf_a,
+                    (void*)e->pf_parts})
         if (p) e->release(p);
+    e->pf_parts = nullptr;
     e->pf_cap = 0;
     if (!(e->pf_x = (float*)e->alloc((size_t)M * d * 4))) return Q3_ERR_OOM;
     if (!(e->pf_qkv = (float*)e->alloc((size_t)M * e->qkv_rows() * 4))) return Q3_ERR_OOM;
@@ -579,11 +584,19 @@ static q3_status ensure_prefill_ws(q3_engine* e, int M) {
     if (!(e->pf_q = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
     if (!(e->pf_o = (float*)e->alloc((size_t)M * HD * 4))) return Q3_ERR_OOM;
     if (!(e->pf_a = (float*)e->alloc((size_t)M * F * 4))) return Q3_ERR_OOM;
+    if (M < kPrefillSplitRows && !(e->pf_parts = (float*)e->alloc((size_t)kPrefillSplits * M * d * 4)))
+        return Q3_ERR_OOM;
     e->pf_cap = M;
     return Q3_OK;
 }
 
 // Rows tokens[0..M) of sequence `seq` at slots t0 .. t0+M-1 through the matrix-core path.
+// These rows only have to leave their K/V in the cache (the caller runs the last prompt
+// row through the decode path for the logits), so the last layer stops after its K/V
+// append: its attention, O projection and FFN feed nothing. Below kPrefillSplitRows rows
+// the two hidden-width projections (N = 1024) would give too few 128-row tiles to fill the
+// chip; they run split-K instead, and the next RMSNorm adds the partials to the residual
+// in a fixed order.
 static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, int M) {
     const q3_config& c = e->cfg;
     const int d = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
@@ -592,29 +605,48 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
     if (st != Q3_OK) return e->fail(st, "prefill workspace allocation failed");
     const int t0 = e->h_len[seq];
     HIPCHK(e, launch_embed(tokens, e->embed, DT_BF16, e->pf_x, M, d, V, e->d_err, s));
+    const bool sk = M < kPrefillSplitRows;
+    const int split_o = sk ? std::min(kPrefillSplits, Hq * 128 / 1024) : 1;
+    const int split_d = sk ? std::min(kPrefillSplits, F / 1024) : 1;
+    int pending = 0;                                   // partials not yet added to pf_x
     for (int l = 0; l < c.n_layers; ++l) {
         const auto& L = e->layers[l];
         uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
         uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 2, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 2, M, d, c.rms_eps, s, e->pf_parts, pending));
+        pending = 0;
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * e->qkv_rows() * d);
         HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d,
                               GEMM_F32, s));
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
                                          e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
+        if (l + 1 == c.n_layers) break;               // the last layer's K/V are written
         prof_mark(e, Q3_PROF_ATTN_PREFILL, true, 0, attn_prefill_flops(M, t0, Hq));
         HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, 1, s));
         prof_mark(e, Q3_PROF_ATTN_PREFILL, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * Hq * 128);
-        HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+        if (split_o > 1) {
+            HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_parts, M, d, Hq * 128,
+                                  GEMM_PARTIAL_F32, s, split_o));
+            pending = split_o;
+        } else {
+            HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+        }
         prof_mark(e, Q3_PROF_GEMM, false);
-        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 2, M, d, c.rms_eps, s));
+        HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 2, M, d, c.rms_eps, s, e->pf_parts, pending));
+        pending = 0;
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * 2 * F * d);
         HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_PAIR, s));
         prof_mark(e, Q3_PROF_GEMM, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * F);
-        HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+        if (split_d > 1) {
+            HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_parts, M, d, F, GEMM_PARTIAL_F32, s,
+                                  split_d));
+            pending = split_d;
+        } else {
+            HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+        }
         prof_mark(e, Q3_PROF_GEMM, false);
     }
     HIPCHK(e, launch_len_advance(e->d_len, seq, 1, M, s));

@@ -220,7 +220,7 @@ template <int AM>
 static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
                             hipStream_t s) {
     // 128-row tiles unless that leaves fewer than two blocks per compute unit
-    const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128);
+    const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128) * splits;
     // (measured on MI355X at the prefill shapes: 64-row tiles with two LDS buffers, 128-row
     // tiles with one buffer and two blocks per compute unit)
     if (blocks128 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s);
