@@ -7,10 +7,11 @@ bench step is one whole generation: prefill a 5-token random prompt, then 128 gr
 decode steps, each followed by on-device sampling whose token feeds the next step.
 value = 128 * steps / (wall time of the timed steps).
 
-Also reported (one JSON line): prefill tokens/s of a 2048-token prompt and batch-64
-decode tokens/s with 4096 pre-filled KV slots per sequence, the roofline of the
-dominant kernel (event-timed on the engine's stream), and the CPU oracle's decode
-rate on this host (a bounded sample).
+Also reported (one JSON line, under "extras"): the 2048-token prompt's prefill tokens/s and
+its 256 sampled decode steps, batch-64 decode tokens/s with 4096 pre-filled KV slots per
+sequence, the 32768-token prefill (GEMM and attention TFLOP/s) and its 512 sampled decode
+steps, each with its roofline fraction; the roofline of the dominant kernel (event-timed
+on the engine's stream), and the CPU oracle's decode rate on this host (a bounded sample).
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill and batch-64 lines")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--plain-launch", action="store_true",
                     help="dispatch the persistent decode kernel as an ordinary launch (for tracers "
@@ -141,6 +142,10 @@ def main() -> int:
         except Exception as ex:  # the main line is still reported
             extras["prefill_error"] = repr(ex)
         try:
+            extras.update(c3_decode_line(eng, q3, torch, synth))
+        except Exception as ex:
+            extras["c3_error"] = repr(ex)
+        try:
             extras.update(bs64_line(eng, w, q3, torch, synth, max_seq))
         except Exception as ex:
             extras["bs64_error"] = repr(ex)
@@ -152,6 +157,11 @@ def main() -> int:
         except Exception as ex:
             cpu = {"error": repr(ex)}
     eng.close()
+    if not args.no_extras:
+        try:
+            extras.update(c5_lines(weights, q3, torch, synth))
+        except Exception as ex:
+            extras["c5_error"] = repr(ex)
 
     out = {
         "metric": "decode tok/s (bs1, bs64) + prefill tok/s, Qwen3-0.6B shape; % of roofline",
@@ -210,6 +220,88 @@ def prefill_line(eng, w, q3, torch, synth):
     return {"prefill2048_tok_s": round(n / dt, 1), "prefill2048_ms": round(1e3 * dt, 3),
             "prefill_gemm_tflops": round(gt, 1), "prefill_gemm_frac": round(gt / BF16_PEAK_TFLOPS, 4),
             "prefill_attn_tflops": round(at, 1)}
+
+
+def decode_loop(eng, q3, torch, tok, steps, temperature, top_p, u):
+    """steps x [decode step + sampling] from the engine's current state; returns (seconds,
+    HIP-event-timed persistent-kernel profile of the same steps)."""
+    torch.cuda.synchronize()
+    eng.profile_begin(q3.PROF_DECODE_STEP)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        eng.decode_step(tok)
+        eng.sample(tok, temperature, top_p, None if u is None else u[i + 1:i + 2])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return dt, eng.profile_end()
+
+
+def c3_decode_line(eng, q3, torch, synth):
+    """The 2048-token workload's decode: prefill the 2048-token prompt, then its 256 steps
+    sampled at T = 0.7, p = 0.9 with the workload's uniforms (2049..2304 cached slots)."""
+    wl = synth.workload("prefill2k")
+    toks = torch.from_numpy(synth.prompt_tokens(wl)).cuda()
+    u = torch.from_numpy(synth.uniforms(wl)).cuda()
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    res = None
+    for _ in range(2):                                  # warm-up, then the timed run
+        eng.reset(0)
+        eng.prefill(0, toks)
+        eng.sample(tok, wl.temperature, wl.top_p, u[0:1])
+        res = decode_loop(eng, q3, torch, tok, wl.decode_steps, wl.temperature, wl.top_p, u)
+    eng.reset(0)
+    dt, prof = res
+    gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
+    log(f"2048-token workload decode: {wl.decode_steps / dt:.0f} tok/s; step kernel {gbs:.0f} GB/s")
+    return {"c3_decode_tok_s": round(wl.decode_steps / dt, 1),
+            "c3_decode_step_us": round(1e3 * prof["ms"] / max(1, prof["launches"]), 2),
+            "c3_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def c5_lines(weights, q3, torch, synth):
+    """The long-context workload on an engine of its own (1 sequence, 33,281 slots): the
+    32768-token prefill (tok/s, GEMM and attention TFLOP/s), then its 512 decode steps
+    sampled at T = 1.0, p = 0.95 (32769..33280 cached slots). Weights: the bs1 workload's
+    synthetic tensors (the timing does not depend on their values)."""
+    wl = synth.workload("prefill32k")
+    eng = q3.Engine(q3.config(wl, 1, wl.prompt_len + wl.decode_steps + 1), weights)
+    try:
+        toks = torch.from_numpy(synth.prompt_tokens(wl)).cuda()
+        u = torch.from_numpy(synth.uniforms(wl)).cuda()
+        tok = torch.empty(1, dtype=torch.int32, device="cuda")
+        eng.prefill(0, toks)                            # warm-up
+        eng.sync()
+        eng.reset(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eng.prefill(0, toks)
+        torch.cuda.synchronize()
+        tp = time.perf_counter() - t0
+        eng.reset(0)
+        eng.profile_begin(q3.PROF_GEMM)
+        eng.prefill(0, toks)
+        g = eng.profile_end()
+        eng.reset(0)
+        eng.profile_begin(q3.PROF_ATTN_PREFILL)
+        eng.prefill(0, toks)
+        a = eng.profile_end()
+        eng.sample(tok, wl.temperature, wl.top_p, u[0:1])
+        dt, prof = decode_loop(eng, q3, torch, tok, wl.decode_steps, wl.temperature, wl.top_p, u)
+        eng.sync()
+    finally:
+        eng.close()
+    n = wl.prompt_len
+    gt = g["flops"] / (g["ms"] / 1e3) / 1e12
+    at = a["flops"] / (a["ms"] / 1e3) / 1e12
+    gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
+    log(f"prefill {n}: {n / tp:.0f} tok/s; GEMM {gt:.0f} TFLOP/s; attention {at:.0f} TFLOP/s; "
+        f"decode {wl.decode_steps / dt:.0f} tok/s, step kernel {gbs:.0f} GB/s")
+    return {"prefill32k_tok_s": round(n / tp, 1), "prefill32k_ms": round(1e3 * tp, 2),
+            "prefill32k_gemm_tflops": round(gt, 1), "prefill32k_gemm_frac": round(gt / BF16_PEAK_TFLOPS, 4),
+            "prefill32k_attn_tflops": round(at, 1),
+            "c5_decode_tok_s": round(wl.decode_steps / dt, 1),
+            "c5_decode_step_us": round(1e3 * prof["ms"] / max(1, prof["launches"]), 2),
+            "c5_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bs64_line(eng, w, q3, torch, synth, max_seq):
@@ -279,20 +371,25 @@ def cpu_baseline(w, weights, budget_s):
     except Exception:
         threads = os.cpu_count()
     model = oracle.Model(oracle.Config.from_workload(w), weights)
-    cache = model.new_cache(w.max_seq)
     prompt = synth.prompt_tokens(w)
-    logits = model.forward(prompt, cache, 0)
-    t0 = time.perf_counter()
-    n = 0
-    while n < 2 or (time.perf_counter() - t0 < budget_s and n < w.decode_steps):
-        nxt = int(np.argmax(logits))
-        logits = model.forward([nxt], cache, w.prompt_len + n)
-        n += 1
-    dt = time.perf_counter() - t0
-    log(f"oracle: {n / dt:.2f} tok/s over {n} steps ({threads} threads)")
+    # whole generations (5-token prefill untimed, then the greedy decode steps, timed),
+    # repeated until the budget is spent; a generation may stop early at the budget
+    n, dt, gens = 0, 0.0, 0
+    while dt < budget_s:
+        cache = model.new_cache(w.max_seq)
+        logits = model.forward(prompt, cache, 0)
+        gens += 1
+        for i in range(w.decode_steps):
+            t0 = time.perf_counter()
+            logits = model.forward([int(np.argmax(logits))], cache, w.prompt_len + i)
+            dt += time.perf_counter() - t0
+            n += 1
+            if dt >= budget_s:
+                break
+    log(f"oracle: {n / dt:.2f} tok/s over {n} steps in {gens} generations ({threads} threads)")
     return {"value": round(n / dt, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch-1 Qwen3-0.6B shape, 5-token prefill then the first {n} greedy decode "
-                      f"steps ({dt:.1f} s)"}
+            "sample": f"batch-1 Qwen3-0.6B shape: {n} greedy decode steps over {gens} generations of "
+                      f"the workload (5-token prompt, up to {w.decode_steps} steps each; {dt:.1f} s of decode)"}
 
 
 if __name__ == "__main__":
