@@ -13,8 +13,12 @@
 //   the drawn token is the first with C >= floor(u * N) + 1, i.e. C > u * N.
 // The search is a radix select on the order-preserving 32-bit key of the logit:
 // a 65536-bucket histogram of masses over the key's upper 16 bits (many blocks,
-// integer atomics), then two 8-bit levels inside the crossing bucket, then the tie
-// group (equal logits, equal masses) resolved by token id.
+// integer atomics); one block finds the bucket where the cumulative mass crosses the
+// threshold; many blocks gather that bucket's members as packed (key, ~id) words; one
+// block sorts them (key descending, id ascending -- independent of the gather order) and
+// walks their masses to the crossing token. A bucket with more members than the sort
+// holds falls back to two 8-bit refinement levels and an id-ordered tie pass over the
+// whole row.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +29,16 @@ namespace {
 constexpr int NB1 = 65536;
 typedef unsigned long long u64;
 
+constexpr int SORT_CAP = 4096;   // bucket members sorted in shared memory
+
 struct RowWs {           // per-row workspace layout (in u64 words)
-    static constexpr size_t hist = 0;          // [NB1]
-    static constexpr size_t words = NB1;
+    static constexpr size_t hist = 0;          // [NB1] masses by upper key half (left zeroed)
+    static constexpr size_t state = NB1;       // [8] selection state (SelWord)
+    static constexpr size_t list = NB1 + 8;    // [V] members of the crossing bucket
+    static size_t words(int V) { return NB1 + 8 + (size_t)V; }
 };
+// state words of a row
+enum SelWord { SW_ABOVE = 0, SW_THR = 1, SW_N = 2, SW_BUCKET = 3, SW_COUNT = 4, SW_S = 5 };
 
 __global__ void k_argmax_rows(const float* __restrict__ logits, u64* __restrict__ amax, int V,
                               unsigned* err) {
@@ -74,10 +84,10 @@ __device__ __forceinline__ double row_zmax(const u64* amax, int b, double T) {
 // Fixed-point masses into the row's 65536-bucket histogram (keyed by the upper 16 bits).
 __global__ __launch_bounds__(256) void k_sample_hist(const float* __restrict__ logits,
                                                      const u64* __restrict__ amax, int V, double Td,
-                                                     double scale, u64* __restrict__ ws) {
+                                                     double scale, u64* __restrict__ ws, size_t row_words) {
     const int b = blockIdx.y;
     const float* l = logits + (size_t)b * V;
-    u64* hist = ws + (size_t)b * RowWs::words + RowWs::hist;
+    u64* hist = ws + (size_t)b * row_words + RowWs::hist;
     const double zmax = row_zmax(amax, b, Td);
     for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x) {
         const float v = l[j];
@@ -115,13 +125,12 @@ struct SelState {
     int32_t id;
 };
 
-// First token in order with C >= thr (1 <= thr <= total mass). Block of 1024 threads.
-__device__ void select_first(const float* __restrict__ l, const u64* __restrict__ hist, int V,
-                             double Td, double zmax, double scale, u64 thr, u64* scan_lds,
-                             u64* h2, SelState* st) {
+// Level 1 of the search: the bucket (upper 16 key bits) where the cumulative mass in
+// order reaches thr, and the mass of all buckets before it. Block of 1024 threads.
+__device__ void select_bucket(const u64* __restrict__ hist, u64 thr, u64* scan_lds, SelState* st) {
     const int tid = threadIdx.x;
     if (tid == 0) { st->found = 0; st->prefix = 0; st->above = 0; }
-    // level 1: thread tid owns buckets 65535 - 64*tid - k, k = 0..63 (descending order)
+    // thread tid owns buckets 65535 - 64*tid - k, k = 0..63 (descending order)
     u64 s = 0;
     for (int k = 0; k < 64; ++k) s += hist[NB1 - 1 - (64 * tid + k)];
     u64 excl;
@@ -136,6 +145,12 @@ __device__ void select_first(const float* __restrict__ l, const u64* __restrict_
         }
     }
     __syncthreads();
+}
+
+// The rest of the search over the whole row, from st->prefix (bucket) and st->above.
+__device__ void select_refine(const float* __restrict__ l, int V, double Td, double zmax, double scale, u64 thr,
+                              u64* scan_lds, u64* h2, SelState* st) {
+    const int tid = threadIdx.x;
     // levels 2 and 3: 8 key bits each, inside the chosen bucket
     for (int lev = 0; lev < 2; ++lev) {
         const int shift = lev == 0 ? 8 : 0;
@@ -187,44 +202,140 @@ __device__ void select_first(const float* __restrict__ l, const u64* __restrict_
     __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void k_sample_select(const float* __restrict__ logits,
-                                                        const u64* __restrict__ amax, int V,
-                                                        double Td, double scale, float top_p,
-                                                        const float* __restrict__ u,
-                                                        u64* __restrict__ ws,
-                                                        int32_t* __restrict__ out) {
+// Stage of a selection: NUC finds the nucleus mass N (top_p < 1), DRAW the drawn token.
+enum { SEL_NUC = 0, SEL_DRAW = 1 };
+
+// One block per row: the threshold of this stage and its crossing bucket.
+template <int STAGE>
+__global__ __launch_bounds__(1024) void k_sel_bucket(u64* __restrict__ ws, size_t row_words, float top_p,
+                                                     const float* __restrict__ u) {
+    __shared__ u64 scan_lds[16];
+    __shared__ SelState st;
+    const int b = blockIdx.x;
+    u64* w = ws + (size_t)b * row_words;
+    const u64* hist = w + RowWs::hist;
+    u64* sw = w + RowWs::state;
+    u64 S;
+    if (STAGE == SEL_NUC || top_p >= 1.0f) {
+        u64 s = 0;
+        for (int k = 0; k < 64; ++k) s += hist[64 * threadIdx.x + k];
+        u64 dummy;
+        S = block_scan_excl(s, scan_lds, dummy);
+    } else {
+        S = sw[SW_S];
+    }
+    u64 thr;
+    if (STAGE == SEL_NUC) {
+        const double tA = ceil((double)top_p * (double)S);
+        thr = tA < 1.0 ? 1ull : (tA >= (double)S ? S : (u64)tA);
+    } else {
+        const u64 N = top_p < 1.0f ? sw[SW_N] : S;
+        const double tB = floor((double)u[b] * (double)N) + 1.0;
+        thr = tB >= (double)N ? N : (u64)tB;
+        if (thr < 1) thr = 1;
+    }
+    select_bucket(hist, thr, scan_lds, &st);
+    if (threadIdx.x == 0) {
+        sw[SW_ABOVE] = st.above;
+        sw[SW_THR] = thr;
+        sw[SW_BUCKET] = st.prefix;
+        sw[SW_COUNT] = 0ull;
+        if (STAGE == SEL_NUC) sw[SW_S] = S;
+    }
+}
+
+// Many blocks: the members of each row's crossing bucket, as (key << 32) | (~id).
+__global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ logits, u64* __restrict__ ws,
+                                                    size_t row_words, int V) {
+    const int b = blockIdx.y;
+    const float* l = logits + (size_t)b * V;
+    u64* w = ws + (size_t)b * row_words;
+    const uint32_t want = (uint32_t)w[RowWs::state + SW_BUCKET];
+    unsigned* count = reinterpret_cast<unsigned*>(w + RowWs::state + SW_COUNT);
+    u64* list = w + RowWs::list;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x) {
+        const uint32_t key = ordered_key(l[j]);
+        if ((key >> 16) == want) {
+            const unsigned i = atomicAdd(count, 1u);
+            if (i < (unsigned)V) list[i] = ((u64)key << 32) | (u64)(0xFFFFFFFFu - (uint32_t)j);
+        }
+    }
+}
+
+// One block per row: sort the bucket's members (descending packed word = key descending,
+// id ascending), walk their masses from SW_ABOVE to the first cumulative mass >= SW_THR.
+// NUC stores that mass as N; DRAW writes the token and zeroes the row's histogram.
+template <int STAGE>
+__global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ logits, const u64* __restrict__ amax,
+                                                    int V, double Td, double scale, u64* __restrict__ ws,
+                                                    size_t row_words, int32_t* __restrict__ out) {
+    __shared__ u64 e[SORT_CAP];
     __shared__ u64 scan_lds[16];
     __shared__ u64 h2[256];
     __shared__ SelState st;
-    if (threadIdx.x == 0) st.id = 0;
+    const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const float* l = logits + (size_t)b * V;
-    const u64* hist = ws + (size_t)b * RowWs::words + RowWs::hist;
+    u64* w = ws + (size_t)b * row_words;
+    u64* sw = w + RowWs::state;
     const double zmax = row_zmax(amax, b, Td);
-    // total mass S (bucket t*64 .. t*64+63 per thread)
-    u64 s = 0;
-    for (int k = 0; k < 64; ++k) s += hist[64 * threadIdx.x + k];
-    u64 dummy;
-    const u64 S = block_scan_excl(s, scan_lds, dummy);
-    // nucleus mass N (the whole vocabulary when top_p >= 1)
-    u64 N = S;
-    if (top_p < 1.0f) {
-        const double tA = ceil((double)top_p * (double)S);
-        const u64 thrA = tA < 1.0 ? 1ull : (tA >= (double)S ? S : (u64)tA);
-        select_first(l, hist, V, Td, zmax, scale, thrA, scan_lds, h2, &st);
-        if (st.found) N = st.cum;
-        __syncthreads();                  // every thread has N before the state is reused
+    const u64 above = sw[SW_ABOVE], thr = sw[SW_THR];
+    const int n = (int)min((u64)V, sw[SW_COUNT] & 0xFFFFFFFFull);
+    if (tid == 0) { st.found = 0; st.id = 0; st.cum = 0; st.above = above; st.prefix = (uint32_t)sw[SW_BUCKET]; }
+    if (n <= SORT_CAP) {
+        int P = 64;
+        while (P < n) P <<= 1;
+        for (int i = tid; i < P; i += blockDim.x) e[i] = i < n ? w[RowWs::list + i] : 0ull;
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1)          // bitonic sort, descending
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < P; i += blockDim.x) {
+                    const int pr = i ^ j;
+                    if (pr > i) {
+                        const u64 a = e[i], c = e[pr];
+                        const bool desc = (i & k) == 0;
+                        if (desc ? a < c : a > c) { e[i] = c; e[pr] = a; }
+                    }
+                }
+                __syncthreads();
+            }
+        // masses in order: thread t takes entries 4t .. 4t+3
+        u64 m[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = 4 * tid + q;
+            m[q] = i < n ? mass_of(key_to_float((uint32_t)(e[i] >> 32)), Td, zmax, scale) : 0ull;
+            sum += m[q];
+        }
+        u64 excl;
+        block_scan_excl(sum, scan_lds, excl);
+        u64 c = above + excl;
+        if (c < thr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = 4 * tid + q;
+                if (i < n && c + m[q] >= thr) {
+                    st.id = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[i] & 0xFFFFFFFFull));
+                    st.cum = c + m[q];
+                    st.found = 1;
+                    break;
+                }
+                c += m[q];
+            }
+        }
+        __syncthreads();
+    } else {
+        __syncthreads();
+        select_refine(l, V, Td, zmax, scale, thr, scan_lds, h2, &st);
     }
-    // draw: first token with C >= floor(u N) + 1
-    double tB = floor((double)u[b] * (double)N) + 1.0;
-    u64 thrB = tB >= (double)N ? N : (u64)tB;
-    if (thrB < 1) thrB = 1;
-    select_first(l, hist, V, Td, zmax, scale, thrB, scan_lds, h2, &st);
-    if (threadIdx.x == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
-    // leave the row's histogram zeroed for the next call
-    __syncthreads();
-    u64* hw = ws + (size_t)b * RowWs::words + RowWs::hist;
-    for (int k = 0; k < 64; ++k) hw[64 * threadIdx.x + k] = 0ull;
+    if (STAGE == SEL_NUC) {
+        if (tid == 0) sw[SW_N] = st.found ? st.cum : sw[SW_S];
+    } else {
+        if (tid == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
+        // leave the row's histogram zeroed for the next call
+        u64* hw = w + RowWs::hist;
+        for (int k = 0; k < 64; ++k) hw[64 * tid + k] = 0ull;
+    }
 }
 
 }  // namespace
@@ -245,8 +356,7 @@ hipError_t launch_greedy(const unsigned long long* amax, int32_t* out, int B, hi
 }
 
 size_t sample_workspace_bytes(int V, int B) {
-    (void)V;
-    return (size_t)B * RowWs::words * sizeof(u64);
+    return (size_t)B * RowWs::words(V) * sizeof(u64);
 }
 
 hipError_t launch_sample(const float* logits, const unsigned long long* amax, int V, int B,
@@ -260,12 +370,20 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     const double Td = (double)temperature;
     u64* w = (u64*)ws;
     hipError_t e = hipSuccess;
-    if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * RowWs::words), s)) != hipSuccess) return e;
+    const size_t rw = RowWs::words(V);
+    if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * rw), s)) != hipSuccess) return e;
     const int nblk = (V + 255) / 256 < 512 ? (V + 255) / 256 : 512;
-    hipLaunchKernelGGL(k_sample_hist, dim3(nblk, B), dim3(256), 0, s, logits, amax, V, Td, scale, w);
+    hipLaunchKernelGGL(k_sample_hist, dim3(nblk, B), dim3(256), 0, s, logits, amax, V, Td, scale, w, rw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sample_select, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, top_p,
-                       u, w, out);
+    if (top_p < 1.0f) {
+        hipLaunchKernelGGL(k_sel_bucket<SEL_NUC>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
+        hipLaunchKernelGGL(k_sel_gather, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V);
+        hipLaunchKernelGGL(k_sel_final<SEL_NUC>, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, w, rw, out);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_sel_bucket<SEL_DRAW>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
+    hipLaunchKernelGGL(k_sel_gather, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V);
+    hipLaunchKernelGGL(k_sel_final<SEL_DRAW>, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, w, rw, out);
     return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ def test_toy_fp32_prefill_and_greedy_decode():
     assert not failures(stats), failures(stats)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_toy_bf16_matrix_core_prefill(path):
     """bf16 weights and cache, 512-token prompt: rows 0..510 take the matrix-core prefill
     path, the last row and the decode steps the float32 decode path -- one launch per
@@ -33,7 +33,7 @@ def test_toy_bf16_matrix_core_prefill(path):
     assert not failures(stats), failures(stats)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_toy_bf16_long_context_decode(path):
     """Decode past one 256-slot attention chunk: the persistent kernel switches to its
     split-K attention with a combine phase."""

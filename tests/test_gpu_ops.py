@@ -392,3 +392,10 @@ def test_sampler_ties_and_degenerate(q3):
     spiky = np.full((2, V), -30.0, np.float32)               # one dominant token
     spiky[:, 1234] = 10.0
     _sampler_case(q3, spiky, 1.0, 0.9, [0.0, 0.9999])
+    # full vocabulary: a crossing bucket of 5000 equal logits (more members than the
+    # sort holds, so the whole-row refinement runs) and one of a few hundred
+    Vf = 151936
+    crowd = (synth.normal((63,), (2, Vf)) * 0.5 - 3.0).astype(np.float32)
+    crowd[0, 1000:6000] = 1.0
+    crowd[1, ::400] = 1.0
+    _sampler_case(q3, crowd, 1.0, 0.9, [0.3, 0.8])

@@ -25,10 +25,11 @@ def _summary(stats):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("path", [2, 1])
+@pytest.mark.parametrize("path", [2, 3, 1])
 def test_bs1_short_prompt_greedy(path):
     """5-token prompt, 128 greedy decode steps: persistent decode kernel (2, the default
-    here) and one launch per operation (1)."""
+    here; 3, the same kernel dispatched as an ordinary launch) and one launch per
+    operation (1)."""
     w = synth.workload("bs1_short")
     stats = run_single(w, w.prompt_len, w.decode_steps, decode_path=path)
     print(_summary(stats))
