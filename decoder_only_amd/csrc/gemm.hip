@@ -2,8 +2,8 @@
 // W [N, K] bf16 weights in the [out, in] layout of the article's projections
 // ("Inside an LLM ...", Step 5 q/k/v/o, Step 6 gate/up/down), float32 accumulation.
 //
-// Block tile BM x 128 x 64 (BM = 128, or 64 when 128-row tiles would leave compute units
-// idle), four waves in a 2 x 2 grid, each wave a BM/2 x 64 sub-tile of
+// Block tile BM x 128 x 64 (BM = 64 at every shape in use; the template also takes 128),
+// four waves in a 2 x 2 grid, each wave a BM/2 x 64 sub-tile of
 // v_mfma_f32_16x16x32_bf16 tiles. Global -> registers (the next k-tile, in flight during
 // the current one's products) -> LDS. LDS rows are 8 chunks of 16 bytes, chunk c of row r stored at
 // c ^ (r & 7) so the 16-lane fragment reads of one chunk column hit distinct banks.
@@ -219,12 +219,13 @@ static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int
 template <int AM>
 static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
                             hipStream_t s) {
-    // 128-row tiles unless that leaves fewer than two blocks per compute unit
-    const long long blocks128 = (long long)(N / BN) * ((M + 127) / 128) * splits;
-    // (measured on MI355X at the prefill shapes: 64-row tiles with two LDS buffers, 128-row
-    // tiles with one buffer and two blocks per compute unit)
-    if (blocks128 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s);
-    return launch_t<AM, 128, 1>(A, W, C, M, N, K, epi, splits, s);
+    // 64-row tiles: with one LDS buffer (two barriers per k-tile) several blocks share a
+    // compute unit and hide each other's loads; with fewer than two blocks per compute unit
+    // the double-buffered variant is faster. (Measured on MI355X at the prefill shapes,
+    // M = 2047 and 32767: 128-row tiles were 5-25% slower everywhere.)
+    const long long blocks64 = (long long)(N / BN) * ((M + 63) / 64) * splits;
+    if (blocks64 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s);
+    return launch_t<AM, 64, 1>(A, W, C, M, N, K, epi, splits, s);
 }
 
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
