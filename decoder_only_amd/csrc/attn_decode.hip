@@ -284,36 +284,33 @@ __global__ __launch_bounds__(128) void k_attn_decode_combine(
     const int T = lens[seq_base + b] + len_extra;
     const int nc = min(nchunk, (T + CHUNK - 1) / CHUNK);
     const float* base = part + (((size_t)b * Hkv + g) * nchunk) * G * PART;
-    // chunk states in batches of 8 (loads in flight together); empty chunks (sum 0) weigh 0
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-        float mv[8], lv[8];
+    // one pass over the chunk states in batches of 16 (loads in flight together), the
+    // running state rescaled to each batch's maximum; empty chunks (sum 0) weigh 0
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 16) {
+        float mv[16], lv[16], av[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float* pp = base + ((size_t)(c0 + u) * G + hh) * PART;
-            mv[u] = c0 + u < nc ? pp[0] : -INFINITY;
-            lv[u] = c0 + u < nc ? pp[1] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) M = fmaxf(M, lv[u] > 0.f ? mv[u] : -INFINITY);
-    }
-    float L = 0.f, A = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-        float mv[8], lv[8], av[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const float* pp = base + ((size_t)(c0 + u) * G + hh) * PART;
             const bool in = c0 + u < nc;
             mv[u] = in ? pp[0] : 0.f;
             lv[u] = in ? pp[1] : 0.f;
             av[u] = in ? pp[2 + d] : 0.f;
         }
+        float bm = M;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float cf = lv[u] > 0.f ? expf(mv[u] - M) : 0.f;
+        for (int u = 0; u < 16; ++u) bm = fmaxf(bm, lv[u] > 0.f ? mv[u] : -INFINITY);
+        if (bm == -INFINITY) continue;             // no keys yet
+        const float cs = L > 0.f ? expf(M - bm) : 0.f;
+        L *= cs;
+        A *= cs;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float cf = lv[u] > 0.f ? expf(mv[u] - bm) : 0.f;
             L += lv[u] * cf;
             A += av[u] * cf;
         }
+        M = bm;
     }
     const float v = L > 0.f ? A / L : 0.f;
     if constexpr (PAIR) {

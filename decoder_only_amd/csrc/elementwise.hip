@@ -83,9 +83,11 @@ hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int
                           float eps, hipStream_t s, const float* parts, int nparts) {
     if (rows <= 0) return hipSuccess;
     if (nparts < 0 || (nparts > 0 && !parts)) return hipErrorInvalidValue;
-    if (out_mode == 0) hipLaunchKernelGGL(k_rmsnorm<0>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
-    else if (out_mode == 1) hipLaunchKernelGGL(k_rmsnorm<1>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
-    else if (out_mode == 2) hipLaunchKernelGGL(k_rmsnorm<2>, dim3(rows), dim3(256), 0, s, x, w, out, d, eps, parts, nparts, rows);
+    // many partials per element (batched decode): a thread per element keeps more loads in flight
+    const dim3 blk(nparts > 8 && d >= 1024 ? 1024 : 256);
+    if (out_mode == 0) hipLaunchKernelGGL(k_rmsnorm<0>, dim3(rows), blk, 0, s, x, w, out, d, eps, parts, nparts, rows);
+    else if (out_mode == 1) hipLaunchKernelGGL(k_rmsnorm<1>, dim3(rows), blk, 0, s, x, w, out, d, eps, parts, nparts, rows);
+    else if (out_mode == 2) hipLaunchKernelGGL(k_rmsnorm<2>, dim3(rows), blk, 0, s, x, w, out, d, eps, parts, nparts, rows);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
