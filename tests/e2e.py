@@ -105,3 +105,39 @@ def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
         eng.decode_step(tok, None, logits)
     eng.close()
     return stats
+
+
+def run_ragged(w: synth.Workload, prompt_lens: List[int], steps: int, decode_path: int = 0) -> List[StepStat]:
+    """Sequences of different lengths decoded together: sequence b is prefilled with a
+    seeded prompt of prompt_lens[b] tokens, then `steps` batched decode steps (row b =
+    sequence b, greedy, teacher-forced with each row's oracle token)."""
+    import torch
+    from decoder_only_amd import q3
+
+    weights = synth.make_weights(w)
+    B = len(prompt_lens)
+    max_seq = max(prompt_lens) + steps + 1
+    model = oracle.Model(oracle.Config.from_workload(w), weights)
+    announce("e2e ragged", w.name, w.weight_dtype, prompt_lens, steps, decode_path)
+    eng = q3.Engine(q3.config(w, B, max_seq), weights)
+    eng.set_decode_path(decode_path)
+    caches, refs = [], []
+    for b, n in enumerate(prompt_lens):
+        prompt = synth.prompt_tokens(w, n, seq=b)
+        cache = model.new_cache(max_seq)
+        refs.append(model.forward(prompt, cache, 0))
+        caches.append(cache)
+        eng.prefill(b, torch.from_numpy(prompt).cuda())
+    logits = torch.empty(B, w.vocab, dtype=torch.float32, device="cuda")
+    toks = torch.empty(B, dtype=torch.int32, device="cuda")
+    stats = []
+    for step in range(steps):
+        nxt = [int(np.argmax(r)) for r in refs]
+        toks.copy_(torch.tensor(nxt, dtype=torch.int32))
+        eng.decode_step(toks, None, logits)
+        refs = [model.forward([nxt[b]], caches[b], prompt_lens[b] + step) for b in range(B)]
+        eng.sync()
+        got = logits.cpu().numpy()
+        stats += [compare(step, b, got[b], refs[b]) for b in range(B)]
+    eng.close()
+    return stats

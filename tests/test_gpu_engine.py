@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from e2e import failures, run_single
+from e2e import failures, run_ragged, run_single
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +76,18 @@ def test_engine_capacity_and_token_errors():
     assert e.value.code == -3
     eng.sync()                                               # the sticky word was cleared
     eng.close()
+
+
+@pytest.mark.parametrize("path,lens", [
+    (2, (5, 17, 100)),            # persistent kernel, every row on the short path
+    (3, (5, 40, 300)),            # persistent kernel, split-K attention with one short row
+    (1, (5, 40, 300)),            # one launch per operation
+    (0, (5, 9, 33, 64, 100, 130, 170, 200, 230, 260, 290, 301)),   # 12 rows: matrix-core batch path
+])
+def test_toy_bf16_ragged_batch(path, lens):
+    """Rows of different cache lengths in one decode step (each row attends its own
+    length; the batch paths take the longest row's launch shape)."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_ragged(w, list(lens), 6, decode_path=path)
+    _report(stats)
+    assert not failures(stats), failures(stats)[:5]
