@@ -168,6 +168,8 @@ struct Contig {   // chunk i at word 4 i
 constexpr int TRACE_MAX = 400;   // phase timestamps kept per traced workgroup
 constexpr int STAGE = 256;       // K/V rows of the staging area
 constexpr int SHOT = 240;        // cached rows staged per shot (the new key follows them)
+constexpr int SHOTD = 120;       // the same with two staging halves of 128 rows (long variant)
+constexpr int LONG_T = 8192;     // contexts above this take the long variant of the kernel
 
 struct Smem {
     union {
@@ -319,9 +321,32 @@ __device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t h
     }
 }
 
+// Long variant: the staging area is two halves of 128 rows; shot s uses half s % 2, so
+// the next shot's rows load while the current one is computed. Wave w stages tile slots
+// w and w + 4 of the half (rows past n repeat row n - 1: every wave issues exactly
+// KV_DB_LOADS loads per shot, so a fixed wait count separates the two shots).
+constexpr int KV_DB_LOADS = 16;
+__device__ __forceinline__ void kv_stage_db(const MegaParams& p, Smem& sm, size_t hb, int base, int n, int half) {
+    if (n <= 0) return;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = 16 * (wid + 4 * st) + 4 * q4;
+            const int r = min(r0 + (lane >> 4), n - 1), sl = lane & 15;
+            const size_t row = hb + (size_t)(base + r) * DH;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r0 + (lane >> 4), sl)),
+                                             (LDS_AS void*)&sm.u.kv.k[128 * half + r0][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl),
+                                             (LDS_AS void*)&sm.u.kv.v[128 * half + r0][0], 16, 0, 0);
+        }
+    }
+}
+
 // cached rows of [k0, k1) in the first shot (slot T-1 is the new key, kept in shared memory)
-__device__ __forceinline__ int first_shot(int k0, int k1, int T) {
-    return max(0, min(min(k1, T - 1), k0 + SHOT) - k0);
+__device__ __forceinline__ int first_shot(int k0, int k1, int T, int shot = SHOT) {
+    return max(0, min(min(k1, T - 1), k0 + shot) - k0);
 }
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
@@ -345,7 +370,9 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // on scores scaled by log2(e)). Writes the normalised output of both heads to o_out, or,
 // when o_out is null, leaves the merged per-head state (base-2 max, sum, unnormalised
 // acc[128]) in sm.att.
+template <bool DB>
 __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, float* o_out) {
+    constexpr int SH = DB ? SHOTD : SHOT;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
     // scores are kept in the base-2 domain: s * log2(e), with s = q.k / sqrt(128)
     const float scale = 0.088388346f * 1.44269504f;
@@ -366,14 +393,23 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     const int ce = min(k1, T - 1);                 // end of the cached rows in range
-    for (int base = k0;; base += SHOT) {
-        const int n = max(0, min(ce, base + SHOT) - base);
-        if (base != k0) {                          // this wave's tiles of the next shot
+    for (int base = k0, shot = 0;; base += SH, ++shot) {
+        const int n = max(0, min(ce, base + SH) - base);
+        const bool last = base + SH >= ce;
+        const int ro = DB ? 128 * (shot & 1) : 0;  // first staging row of this shot
+        if constexpr (DB) {
+            // the next shot into the other half (read two shots ago), then wait for this one:
+            // all but this wave's KV_DB_LOADS newest loads
+            const int nn = last ? 0 : max(0, min(ce, base + 2 * SH) - (base + SH));
+            kv_stage_db(p, sm, hb, base + SH, nn, (shot + 1) & 1);
+            static_assert(KV_DB_LOADS == 16, "the wait below encodes vmcnt(16)");
+            if (nn > 0) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
+            else __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+        } else if (base != k0) {                   // this wave's tiles of the next shot
             __builtin_amdgcn_s_waitcnt(0);         // (its reads of the previous shot are done)
             kv_stage(p, sm, hb, base, n);
             __builtin_amdgcn_s_waitcnt(0);
         }
-        const bool last = base + SHOT >= ce;
         const bool with_new = last && k1 == T;
         const int nk = n + (with_new ? 1 : 0);
         if (with_new && wid == ((n >> 4) & 3) && lane < 32) {   // the new key / value as row n
@@ -383,7 +419,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 u[e] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{src[2 * e], src[2 * e + 1]}, bf16x2));
-            *reinterpret_cast<u32x4*>(lane < 16 ? &sm.u.kv.k[n][8 * kslot(n, c)] : &sm.u.kv.v[n][8 * c]) = u;
+            *reinterpret_cast<u32x4*>(lane < 16 ? &sm.u.kv.k[ro + n][8 * kslot(n, c)] : &sm.u.kv.v[ro + n][8 * c]) = u;
         }
         const int ntile = (nk + 15) >> 4;
         for (int t = wid; t < ntile; t += 4) {
@@ -391,7 +427,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
             bf16x8 a[4];                           // all fragment reads of the tile first
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                a[ks] = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[16 * t + col][8 * kslot(col, 4 * ks + quad)]);
+                a[ks] = *reinterpret_cast<const bf16x8*>(&sm.u.kv.k[ro + 16 * t + col][8 * kslot(col, 4 * ks + quad)]);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qh[ks], sh, 0, 0, 0);
@@ -430,7 +466,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
         // so P.V can run over whole tiles
         if (wid == ((ntile - 1) & 3)) {
             for (int r = nk + (lane >> 4); r < 16 * ntile; r += 4)
-                *reinterpret_cast<u32x4*>(&sm.u.kv.v[r][8 * col]) = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(&sm.u.kv.v[ro + r][8 * col]) = u32x4{0u, 0u, 0u, 0u};
         }
         // P.V of this wave's keys: lane group quad takes keys 16 t + 4 i + quad, lane col
         // dims 8 col .. 8 col + 7
@@ -440,7 +476,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * t + 4 * i + quad;
-                vv[i] = *reinterpret_cast<const u32x4*>(&sm.u.kv.v[r][8 * col]);
+                vv[i] = *reinterpret_cast<const u32x4*>(&sm.u.kv.v[ro + r][8 * col]);
                 pp[i] = *reinterpret_cast<const f32x2*>(&sm.sp[r][0]);
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // all reads of the tile first
@@ -563,6 +599,9 @@ __device__ __forceinline__ size_t group_chunk(int gg, int i) {
                   : (i < 96 ? (size_t)HQ * DH + DH * gg + 4 * (i - 64) : (size_t)(HQ + HKV) * DH + DH * gg + 4 * (i - 96));
 }
 
+// LONG: the long-context instance (split-K attention staged in double-buffered halves);
+// a separate instance so its extra registers do not touch the short-context code.
+template <bool LONG>
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -655,7 +694,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
-                attend(p, sm, hb, 0, T, T, sm.o[b]);
+                attend<false>(p, sm, hb, 0, T, T, sm.o[b]);
             }
         } else {
             // B1: unit w = (group w % 8, chunk w / 8) attends its chunk, per row
@@ -667,7 +706,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (c < nch) {
                     const int k0 = c * ch, k1 = min(T, k0 + ch);
                     const size_t hb = kv_head_base(p, layer, b, gg);
-                    kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
+                    if (LONG) kv_stage_db(p, sm, hb, k0, first_shot(k0, k1, T, SHOTD), 0);
+                    else kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
                     if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(gg, i); }, DH, sm.in[b],
                                  p.err))
                         return;
@@ -675,7 +715,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
-                    attend(p, sm, hb, k0, k1, T, nullptr);
+                    attend<LONG>(p, sm, hb, k0, k1, T, nullptr);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
@@ -933,16 +973,23 @@ hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
 
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s) {
     if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers) return hipErrorInvalidValue;
+    int Tmax = 0;
+    for (int b = 0; b < p.B; ++b) Tmax = std::max(Tmax, p.slots[b] + 1);
+    const void* fn = Tmax > LONG_T ? (const void*)k_decode_mega<true> : (const void*)k_decode_mega<false>;
     if (cooperative) {
         void* args[] = {(void*)&p};
-        return hipLaunchCooperativeKernel((const void*)k_decode_mega, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
+        return hipLaunchCooperativeKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
     }
-    hipLaunchKernelGGL(k_decode_mega, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    if (Tmax > LONG_T) hipLaunchKernelGGL(k_decode_mega<true>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else hipLaunchKernelGGL(k_decode_mega<false>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
     return hipGetLastError();
 }
 
 hipError_t decode_mega_prepare() {
-    return hipFuncSetAttribute((const void*)k_decode_mega, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)k_decode_mega<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(Smem));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)k_decode_mega<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)sizeof(Smem));
 }
 
