@@ -55,13 +55,15 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
     lo = __builtin_convertvector(x - hf, bf16x8);
 }
 
-// BAL = false: block (query tile, kv head g) covers both query heads of g, each wave 32 rows
-// of one head (RT = 2 row tiles of 16). BAL = true, for short prompts where one query tile
-// per block would leave the causal work unbalanced (tile i needs i + 1 key tiles): block
-// (b, query head h) takes query tiles nqt-1-b and then b, each wave 16 rows (RT = 1), so
-// every block walks nqt + 1 key tiles.
+// BAL = true (the launched form): block (b, query head h) takes query tiles nqt-1-b and
+// then b, each wave 16 rows (RT = 1), so every block walks nqt + 1 key tiles (tile i needs
+// i + 1), and the register footprint allows two blocks per compute unit, whose
+// score / softmax / P.V chains then interleave on the matrix cores. BAL = false: block
+// (query tile, kv head g) covers both query heads of g, each wave 32 rows (RT = 2); it
+// halves the K/V staging per product but runs one block per compute unit, and measured
+// 1.1x (2048 rows) to 1.8x (8192 rows) slower.
 template <bool PAIR, bool BAL>
-__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
+__global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
                                                       const bf16* __restrict__ vc, int t_cap, int M, int t0,
                                                       int Hq, int Hkv, void* __restrict__ o) {
     constexpr int RT = BAL ? 1 : 2;
@@ -274,17 +276,9 @@ hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_
     if (M <= 0) return hipSuccess;
     if (Hq != 2 * Hkv) return hipErrorInvalidValue;
     const int nqt = (M + BQ - 1) / BQ;
-    // balanced pairs while one query tile per block would give fewer than 4 blocks per
-    // compute unit (the longest block then sets the time)
-    const bool bal = (long long)nqt * Hkv < 1024;
-    const dim3 grid = bal ? dim3((nqt + 1) / 2, Hq) : dim3(nqt, Hkv);
-    if (bal) {
-        if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-        else hipLaunchKernelGGL((k_attn_prefill<false, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-    } else {
-        if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, false>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-        else hipLaunchKernelGGL((k_attn_prefill<false, false>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-    }
+    const dim3 grid((nqt + 1) / 2, Hq);
+    if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    else hipLaunchKernelGGL((k_attn_prefill<false, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
     return hipGetLastError();
 }
 
