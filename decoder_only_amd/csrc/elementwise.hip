@@ -196,31 +196,46 @@ hipError_t launch_swiglu_parts(const float* parts, int nparts, int B, int F, voi
     return hipGetLastError();
 }
 
-__global__ void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
-                                  const float* __restrict__ qn, const float* __restrict__ kn,
-                                  const float* __restrict__ inv_freq, float eps,
-                                  float* __restrict__ q_out, bf16* __restrict__ kc, bf16* __restrict__ vc,
-                                  int t_cap, int Hq, int Hkv) {
-    const int r = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
-    const int width = (Hq + 2 * Hkv) * 128;
-    const float* row = qkv + (size_t)r * width + hd * 128;
+// One block (four waves) per row: lane i evaluates the RoPE factors of its pair once (the
+// angle depends on the position and i only) and wave w takes heads w, w + 4, ... with the
+// same operations as norm_rope_pair.
+__global__ __launch_bounds__(256) void k_qk_rope_prefill(const float* __restrict__ qkv, int M, int t0,
+                                                         const float* __restrict__ qn, const float* __restrict__ kn,
+                                                         const float* __restrict__ inv_freq, float eps,
+                                                         float* __restrict__ q_out, bf16* __restrict__ kc,
+                                                         bf16* __restrict__ vc, int t_cap, int Hq, int Hkv) {
+    const int r = blockIdx.x, i = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nh = Hq + 2 * Hkv, width = nh * 128;
     const int slot = t0 + r;
-    float x1 = row[i], x2 = row[i + 64];
-    if (hd >= Hq + Hkv) {
-        const size_t base = ((size_t)(hd - Hq - Hkv) * t_cap + slot) * 128;
-        vc[base + i] = f2bf(x1);
-        vc[base + i + 64] = f2bf(x2);
-        return;
-    }
-    norm_rope_pair(x1, x2, hd < Hq ? qn : kn, i, eps, slot, inv_freq);
-    if (hd < Hq) {
-        float* qo = q_out + ((size_t)hd * M + r) * 128;
-        qo[i] = x1;
-        qo[i + 64] = x2;
-    } else {
-        const size_t base = ((size_t)(hd - Hq) * t_cap + slot) * 128;
-        kc[base + i] = f2bf(x1);
-        kc[base + i + 64] = f2bf(x2);
+    const float ang = __fmul_rn((float)slot, inv_freq[i]);
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    for (int hd = wid; hd < nh; hd += 4) {
+        const float* row = qkv + (size_t)r * width + hd * 128;
+        float x1 = row[i], x2 = row[i + 64];
+        if (hd >= Hq + Hkv) {
+            const size_t base = ((size_t)(hd - Hq - Hkv) * t_cap + slot) * 128;
+            vc[base + i] = f2bf(x1);
+            vc[base + i + 64] = f2bf(x2);
+            continue;
+        }
+        const float* w = hd < Hq ? qn : kn;
+        const float ss = wave_sum(x1 * x1 + x2 * x2);
+        const float rr = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+        x1 = (x1 * rr) * w[i];
+        x2 = (x2 * rr) * w[i + 64];
+        const float y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, sn));
+        const float y2 = __fadd_rn(__fmul_rn(x1, sn), __fmul_rn(x2, c));
+        if (hd < Hq) {
+            float* qo = q_out + ((size_t)hd * M + r) * 128;
+            qo[i] = y1;
+            qo[i + 64] = y2;
+        } else {
+            const size_t base = ((size_t)(hd - Hq) * t_cap + slot) * 128;
+            kc[base + i] = f2bf(y1);
+            kc[base + i + 64] = f2bf(y2);
+        }
     }
 }
 
@@ -229,8 +244,8 @@ hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* 
                                   float* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
                                   int Hkv, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_qk_rope_prefill, dim3(M, Hq + 2 * Hkv), dim3(64), 0, s, qkv, M, t0, q_norm,
-                       k_norm, inv_freq, eps, q_out, kc, vc, t_cap, Hq, Hkv);
+    hipLaunchKernelGGL(k_qk_rope_prefill, dim3(M), dim3(256), 0, s, qkv, M, t0, q_norm, k_norm, inv_freq, eps,
+                       q_out, kc, vc, t_cap, Hq, Hkv);
     return hipGetLastError();
 }
 
