@@ -472,14 +472,14 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     int split = 1, split_qkv = 1, split_gu = 1, pending = 0;
     if (mm) {
         const int mblocks = (B + 63) / 64;
-        auto pick = [&](int N, int K) {
+        auto pick = [&](int N, int K, int target = 256) {
             const int nb = (N / 128) * mblocks;
-            int sp = std::max(1, (256 + nb - 1) / nb);
+            int sp = std::max(1, (target + nb - 1) / nb);
             sp = std::min(sp, K / 64);
             while (sp > 1 && (size_t)sp * N > (size_t)q3_engine::kMaxSplits * d) --sp;
             return sp;
         };
-        split = std::min(pick(d, HD), pick(d, F));
+        split = std::min(pick(d, HD, 128), pick(d, F, 128));
         split_qkv = pick(e->qkv_rows(), d);
         split_gu = pick(2 * F, d);
     }
