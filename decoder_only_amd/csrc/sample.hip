@@ -33,9 +33,10 @@ constexpr int SORT_CAP = 4096;   // bucket members sorted in shared memory
 
 struct RowWs {           // per-row workspace layout (in u64 words)
     static constexpr size_t hist = 0;          // [NB1] masses by upper key half (left zeroed)
-    static constexpr size_t state = NB1;       // [8] selection state (SelWord)
-    static constexpr size_t list = NB1 + 8;    // [V] members of the crossing bucket
-    static size_t words(int V) { return NB1 + 8 + (size_t)V; }
+    static constexpr size_t gsum = NB1;        // [256] sums of 256-bucket groups
+    static constexpr size_t state = NB1 + 256; // [8] selection state (SelWord)
+    static constexpr size_t list = NB1 + 264;  // [V] members of the crossing bucket
+    static size_t words(int V) { return NB1 + 264 + (size_t)V; }
 };
 // state words of a row
 enum SelWord { SW_ABOVE = 0, SW_THR = 1, SW_N = 2, SW_BUCKET = 3, SW_COUNT = 4, SW_S = 5 };
@@ -126,25 +127,32 @@ struct SelState {
 };
 
 // Level 1 of the search: the bucket (upper 16 key bits) where the cumulative mass in
-// order reaches thr, and the mass of all buckets before it. Block of 1024 threads.
-__device__ void select_bucket(const u64* __restrict__ hist, u64 thr, u64* scan_lds, SelState* st) {
+// order reaches thr, and the mass of all buckets before it: first over the 256 group sums
+// (descending), then over the 256 buckets of the crossing group. Threads 0..255 of the
+// block scan; all threads return after the result is in *st. Also returns S (the sum of
+// all masses).
+__device__ u64 select_bucket(const u64* __restrict__ hist, const u64* __restrict__ gsum, u64 thr, bool find,
+                             u64* scan_lds, SelState* st) {
     const int tid = threadIdx.x;
-    if (tid == 0) { st->found = 0; st->prefix = 0; st->above = 0; }
-    // thread tid owns buckets 65535 - 64*tid - k, k = 0..63 (descending order)
-    u64 s = 0;
-    for (int k = 0; k < 64; ++k) s += hist[NB1 - 1 - (64 * tid + k)];
+    __shared__ u64 lv[2];                  // crossing group, mass before it
+    if (tid == 0) { st->found = 0; st->prefix = 0; st->above = 0; lv[0] = 0; lv[1] = 0; }
+    const u64 g = tid < 256 ? gsum[255 - tid] : 0ull;
     u64 excl;
-    block_scan_excl(s, scan_lds, excl);   // synchronises
-    if (excl < thr && excl + s >= thr) {
-        u64 r = excl;
-        for (int k = 0; k < 64; ++k) {
-            const int bk = NB1 - 1 - (64 * tid + k);
-            const u64 r2 = r + hist[bk];
-            if (r2 >= thr) { st->prefix = (uint32_t)bk; st->above = r; break; }
-            r = r2;
-        }
+    const u64 S = block_scan_excl(g, scan_lds, excl);   // synchronises
+    if (!find) return S;
+    if (tid < 256 && excl < thr && excl + g >= thr) { lv[0] = 255 - tid; lv[1] = excl; }
+    __syncthreads();
+    const uint32_t G = (uint32_t)lv[0];
+    const u64 above0 = lv[1];
+    const u64 h = tid < 256 ? hist[256 * G + 255 - tid] : 0ull;
+    u64 ex2;
+    block_scan_excl(h, scan_lds, ex2);
+    if (tid < 256 && above0 + ex2 < thr && above0 + ex2 + h >= thr) {
+        st->prefix = 256 * G + 255 - tid;
+        st->above = above0 + ex2;
     }
     __syncthreads();
+    return S;
 }
 
 // The rest of the search over the whole row, from st->prefix (bucket) and st->above.
@@ -202,6 +210,22 @@ __device__ void select_refine(const float* __restrict__ l, int V, double Td, dou
     __syncthreads();
 }
 
+// Sums of the 256-bucket groups of each row's histogram: block g of row b.
+__global__ __launch_bounds__(256) void k_hist_groups(u64* __restrict__ ws, size_t row_words) {
+    __shared__ u64 red[4];
+    u64* w = ws + (size_t)blockIdx.y * row_words;
+    u64 v = w[RowWs::hist + 256 * blockIdx.x + threadIdx.x];
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) w[RowWs::gsum + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Leave each row's histogram zeroed for the next call.
+__global__ __launch_bounds__(256) void k_hist_zero(u64* __restrict__ ws, size_t row_words) {
+    ws[(size_t)blockIdx.y * row_words + RowWs::hist + 256 * blockIdx.x + threadIdx.x] = 0ull;
+}
+
 // Stage of a selection: NUC finds the nucleus mass N (top_p < 1), DRAW the drawn token.
 enum { SEL_NUC = 0, SEL_DRAW = 1 };
 
@@ -214,16 +238,9 @@ __global__ __launch_bounds__(1024) void k_sel_bucket(u64* __restrict__ ws, size_
     const int b = blockIdx.x;
     u64* w = ws + (size_t)b * row_words;
     const u64* hist = w + RowWs::hist;
+    const u64* gs = w + RowWs::gsum;
     u64* sw = w + RowWs::state;
-    u64 S;
-    if (STAGE == SEL_NUC || top_p >= 1.0f) {
-        u64 s = 0;
-        for (int k = 0; k < 64; ++k) s += hist[64 * threadIdx.x + k];
-        u64 dummy;
-        S = block_scan_excl(s, scan_lds, dummy);
-    } else {
-        S = sw[SW_S];
-    }
+    const u64 S = select_bucket(hist, gs, 0, false, scan_lds, &st);
     u64 thr;
     if (STAGE == SEL_NUC) {
         const double tA = ceil((double)top_p * (double)S);
@@ -234,7 +251,7 @@ __global__ __launch_bounds__(1024) void k_sel_bucket(u64* __restrict__ ws, size_
         thr = tB >= (double)N ? N : (u64)tB;
         if (thr < 1) thr = 1;
     }
-    select_bucket(hist, thr, scan_lds, &st);
+    select_bucket(hist, gs, thr, true, scan_lds, &st);
     if (threadIdx.x == 0) {
         sw[SW_ABOVE] = st.above;
         sw[SW_THR] = thr;
@@ -332,9 +349,6 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
         if (tid == 0) sw[SW_N] = st.found ? st.cum : sw[SW_S];
     } else {
         if (tid == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
-        // leave the row's histogram zeroed for the next call
-        u64* hw = w + RowWs::hist;
-        for (int k = 0; k < 64; ++k) hw[64 * tid + k] = 0ull;
     }
 }
 
@@ -374,6 +388,7 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * rw), s)) != hipSuccess) return e;
     const int nblk = (V + 255) / 256 < 512 ? (V + 255) / 256 : 512;
     hipLaunchKernelGGL(k_sample_hist, dim3(nblk, B), dim3(256), 0, s, logits, amax, V, Td, scale, w, rw);
+    hipLaunchKernelGGL(k_hist_groups, dim3(256, B), dim3(256), 0, s, w, rw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (top_p < 1.0f) {
         hipLaunchKernelGGL(k_sel_bucket<SEL_NUC>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
@@ -384,6 +399,7 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     hipLaunchKernelGGL(k_sel_bucket<SEL_DRAW>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
     hipLaunchKernelGGL(k_sel_gather, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V);
     hipLaunchKernelGGL(k_sel_final<SEL_DRAW>, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, w, rw, out);
+    hipLaunchKernelGGL(k_hist_zero, dim3(256, B), dim3(256), 0, s, w, rw);
     return hipGetLastError();
 }
 
