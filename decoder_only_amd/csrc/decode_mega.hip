@@ -13,7 +13,9 @@
 // One memory round trip thus carries both the data and the "it is ready" signal. Each
 // layer has its own buffers, so a word is written once per launch; the small tail kernel
 // that follows every launch puts the sentinel back into every word the launch used (also
-// after a launch that gave up waiting). On MI355X one all-to-all hand-over among 256
+// after a launch that gave up waiting). The one reduction among hand-overs, x' = x + the
+// O-projection partials of the 8 kv groups, is summed in memory instead: 64-bit
+// fixed-point words with device-scope atomic adds, whose top bits count the arrivals. On MI355X one all-to-all hand-over among 256
 // workgroups takes ~2.3 us this way (~1.2 us between two), so the layout below is built
 // around needing only four per layer.
 //
@@ -22,10 +24,10 @@
 //   B  workgroup (g, j), kv group g = query heads 2g, 2g+1, j < 32: poll the group's
 //      q/k/v (512) -> QK-norm + RoPE -> KV append (j == 0) -> attention of both heads,
 //      recomputed by the 32 workgroups of the group (K/V staged through LDS) -> rows
-//      32j..32j+31 of Wo[:, 256g:256g+256] . o, plus x for g = 0         -> P[g] words
+//      32j..32j+31 of Wo[:, 256g:256g+256] . o, plus x for g = 0   -> added to x' sums
 //      (long context: split-K partials per (group, chunk), merged again by every
 //       workgroup of the group, then the same O-projection partial)
-//   C  poll P (8 x 1024): x' = P[0] + ... + P[7] (fixed order) -> RMSNorm -> gate/up
+//   C  poll the x' sums (1024, complete when all 8 groups added) -> RMSNorm -> gate/up
 //      rows of 12 SwiGLU columns                                       -> A words
 //   D  poll a (3072) -> rows 4w..4w+3: x'' = x' + Wd a                  -> next x words
 // then poll x, RMSNorm, 594 rows of the tied LM head per workgroup; each workgroup
@@ -55,7 +57,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // words per (layer, row) in each exchange buffer
-constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)HKV * D, W_A = F;
+constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)2 * D, W_A = F;   // W_P: D 64-bit sums
 constexpr size_t W_PT = (size_t)MAXCH * HKV * 2 * PART;   // [chunk][group][head][PART]
 constexpr int PT_CHUNK = HKV * 2 * PART;                     // words per chunk index
 
@@ -128,8 +130,15 @@ __device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS 
 // barrier joins the workgroup. `words` bounds the buffer (reads past it return zero
 // instead of touching other memory). Returns false after ~0.1 s without completion (the
 // caller then leaves the kernel, and so, through their own waits, do all others).
-template <int K, typename CIDX>
-__device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx, int nch, float* dst, unsigned* err) {
+struct NoSentinel {   // a chunk is complete when none of its words holds the sentinel
+    __device__ __forceinline__ bool operator()(const u32x4 v) const {
+        return v[0] != SENT && v[1] != SENT && v[2] != SENT && v[3] != SENT;
+    }
+};
+
+template <int K, typename CIDX, typename READY = NoSentinel>
+__device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx, int nch, float* dst, unsigned* err,
+                                     READY ready = READY{}) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(words * 4), 0x00020000);
     unsigned todo = 0;
@@ -146,7 +155,7 @@ __device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx,
                 v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cidx(threadIdx.x + NT * k) * 4), 0, SC1);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if ((todo & (1u << k)) && v[k][0] != SENT && v[k][1] != SENT && v[k][2] != SENT && v[k][3] != SENT) {
+            if ((todo & (1u << k)) && ready(v[k])) {
                 *reinterpret_cast<u32x4*>(dst + 4 * (threadIdx.x + NT * k)) = v[k];
                 todo &= ~(1u << k);
             }
@@ -160,6 +169,32 @@ __device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx,
     }
     return __syncthreads_and(ok);
 }
+
+// The O-projection partials of the 8 kv groups are summed in memory: each group adds its
+// value to a 64-bit word with a device-scope atomic add, as an integer, so the sum does not
+// depend on the order of arrival. A contribution is 2^60 (bits 60..63 count the arrived
+// groups) + round(v * 2^30) + 2^52 (bias: every contribution's value field is positive and
+// below 2^53, so 8 of them stay below 2^56). A value that is not finite or has |v| >= 2^22
+// adds 2^56 instead (bits 56..59 then make the sum read as NaN). The words start at zero;
+// a sum is complete when its count field reads 8.
+constexpr int FX_SHIFT = 30;
+constexpr float FX_LIMIT = 4194304.0f;   // 2^22
+__device__ __forceinline__ void fx_add(u64* p, float v) {
+    u64 c = 1ull << 60;
+    if (fabsf(v) < FX_LIMIT) c += (u64)(__float2ll_rn(v * (float)(1 << FX_SHIFT)) + (1ll << 52));
+    else c += 1ull << 56;
+    __hip_atomic_fetch_add(p, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fx_value(u64 s) {
+    if ((s >> 56) & 0xFull) return __uint_as_float(0x7FC00000u);
+    const long long q = (long long)(s & ((1ull << 56) - 1)) - (long long)HKV * (1ll << 52);
+    return (float)((double)q * (1.0 / (double)(1ll << FX_SHIFT)));
+}
+struct FxComplete {   // both 64-bit sums of the chunk have all HKV contributions
+    __device__ __forceinline__ bool operator()(const u32x4 v) const {
+        return (v[1] >> 28) == (unsigned)HKV && (v[3] >> 28) == (unsigned)HKV;
+    }
+};
 
 struct Contig {   // chunk i at word 4 i
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
@@ -533,16 +568,16 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
     __syncthreads();
 }
 
-// P[b][g][32j + r] = Wo[32j + r, 256g:256g+256] . o[b]; thread t: row r = t >> 3,
-// 16-byte chunks sub + 8i (i < 4) of the 32 in the row segment.
-// Group 0's partial also carries the residual x, so x' = P[0] + ... + P[7].
+// x'[b][32j + r] += Wo[32j + r, 256g:256g+256] . o[b] (fixed-point sum over the groups);
+// thread t: row r = t >> 3, 16-byte chunks sub + 8i (i < 4) of the 32 in the row segment.
+// Group 0's contribution also carries the residual x.
 __device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, float* P, int g, int j, int B) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<4>(pf, sm.o[b], sub, 8);
         s = sum8(s);
         if (g == 0) s = sm.xg[b][r] + s;
-        if (sub == 0) put(P + (size_t)b * W_P + (size_t)g * D + 32 * j + r, s);
+        if (sub == 0) fx_add(reinterpret_cast<u64*>(P + (size_t)b * W_P) + 32 * j + r, s);
     }
 }
 
@@ -757,18 +792,15 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         pf_gu(L, pf, pre, w);
         trace_at(p, sm, tslot++);
 
-        // ---------------- C: x' = P[0] + ... + P[7] -> RMSNorm -> gate/up of 12 columns -> SwiGLU
+        // ---------------- C: x' (summed in memory) -> RMSNorm -> gate/up of 12 columns -> SwiGLU
         for (int b = 0; b < B; ++b) {
-            if (!poll<8>(P + (size_t)b * W_P, W_P, Contig{}, HKV * D / 4, sm.u.s.part, p.err)) return;
+            if (!poll<2>(P + (size_t)b * W_P, 2 * D, Contig{}, D / 2, sm.u.s.part, p.err, FxComplete{})) return;
             if (b == 0) trace_at(p, sm, tslot++);
-            const int n = 4 * tid;
             f32x4 xv;
+            {
+                const u64* sums = reinterpret_cast<const u64*>(sm.u.s.part) + 4 * tid;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float t = sm.u.s.part[n + e];
-#pragma unroll
-                for (int gg = 1; gg < HKV; ++gg) t += sm.u.s.part[gg * D + n + e];
-                xv[e] = t;
+                for (int e = 0; e < 4; ++e) xv[e] = fx_value(sums[e]);
             }
             if (tid == w) {
 #pragma unroll
@@ -900,9 +932,9 @@ size_t decode_mega_exchange_words_per_layer() {
 // Tail of a persistent decode step, run after every launch (also one that gave up):
 // blocks b < B: amax[b] = max over the 256 workgroup candidates of row b (packed logit
 // key | ~id), lens[seq_base + b] += 1 and, when greedy_out is given, the greedy token
-// (Step 8's argmax, lowest id on ties); all blocks: the sentinel back into every
-// exchange word the launch may have written -- per layer, rows < B of x, q/k/v, P and a,
-// and pt_words words of chunk partials per row -- with coherent stores.
+// (Step 8's argmax, lowest id on ties); all blocks: the initial state back into every
+// exchange word the launch may have written -- per layer, rows < B of x, q/k/v, the x'
+// sums (zero) and a, and pt_words words of chunk partials per row -- with coherent stores.
 __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
                             int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words,
                             int32_t* __restrict__ greedy_out) {
@@ -925,7 +957,7 @@ __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax
     }
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)ex, (short)0, (int)((size_t)(n_layers + 1) * ex_layer * 4), 0x00020000);
-    const u32x4 sv = {SENT, SENT, SENT, SENT};
+    const u32x4 sv = {SENT, SENT, SENT, SENT}, zv = {0u, 0u, 0u, 0u};
     const int nseg = (n_layers + 1) * 5 * B;
     for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
         const int l = seg / (5 * B), kind = (seg % (5 * B)) / B, b = seg % B;
@@ -934,19 +966,23 @@ __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax
         int cnt;
         if (kind == 0) { off += (size_t)b * W_X; cnt = (int)W_X; }
         else if (kind == 1) { off += BMAX * W_X + (size_t)b * W_QKV; cnt = (int)W_QKV; }
-        else if (kind == 2) { off += BMAX * (W_X + W_QKV) + (size_t)b * W_P; cnt = (int)W_P; }
+        else if (kind == 2) { off += BMAX * (W_X + W_QKV) + (size_t)b * W_P; cnt = 2 * D; }
         else if (kind == 3) { off += BMAX * (W_X + W_QKV + W_P) + (size_t)b * W_A; cnt = (int)W_A; }
         else { off += BMAX * (W_X + W_QKV + W_P + W_A) + (size_t)b * W_PT; cnt = pt_words; }
         for (int i = 4 * threadIdx.x; i < cnt; i += 4 * blockDim.x)
-            __builtin_amdgcn_raw_buffer_store_b128(sv, rs, (int)((off + i) * 4), 0, SC1);
+            __builtin_amdgcn_raw_buffer_store_b128(kind == 2 ? zv : sv, rs, (int)((off + i) * 4), 0, SC1);
     }
 }
 
-__global__ void k_mega_fill(float* ex, size_t words) {
+// Initial state of the exchange words: the sentinel, and zero in the O-projection sums.
+__global__ void k_mega_fill(float* ex, size_t words, size_t ex_layer) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)ex, (short)0, (int)(words * 4), 0x00020000);
-    const u32x4 sv = {SENT, SENT, SENT, SENT};
-    for (size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x); i < words; i += 4 * (size_t)gridDim.x * blockDim.x)
-        __builtin_amdgcn_raw_buffer_store_b128(sv, rs, (int)(i * 4), 0, SC1);
+    const u32x4 sv = {SENT, SENT, SENT, SENT}, zv = {0u, 0u, 0u, 0u};
+    constexpr size_t p0 = BMAX * (W_X + W_QKV), p1 = p0 + BMAX * W_P;
+    for (size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x); i < words; i += 4 * (size_t)gridDim.x * blockDim.x) {
+        const size_t o = i % ex_layer;
+        __builtin_amdgcn_raw_buffer_store_b128(o >= p0 && o < p1 ? zv : sv, rs, (int)(i * 4), 0, SC1);
+    }
 }
 
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
@@ -966,8 +1002,9 @@ hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* 
 }
 
 hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
-    if (words % 4 || words * 4 > 0x7FFFFFF0ull) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_mega_fill, dim3(1024), dim3(256), 0, s, ex, words);
+    const size_t ex_layer = decode_mega_exchange_words_per_layer();
+    if (words % 4 || words % ex_layer || words * 4 > 0x7FFFFFF0ull) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_mega_fill, dim3(1024), dim3(256), 0, s, ex, words, ex_layer);
     return hipGetLastError();
 }
 
