@@ -120,6 +120,23 @@ __device__ __forceinline__ float dot_chunks(const u32x4* w, const float* x, int 
 // then wait for all weight prefetches in flight.
 #define GLOBAL_AS __attribute__((address_space(1)))
 __device__ __forceinline__ u32x4 ldw16(const bf16* p) { return *(const GLOBAL_AS u32x4*)(p); }
+// Lanes 2m and 2m + 1 each hold 4 consecutive elements (lo: elements 8m .. 8m + 3 in lane
+// 2m, hi: 8m + 4 .. 8m + 7 in lane 2m + 1); after pair8 both hold all 8, as (lo, hi).
+__device__ __forceinline__ void pair8(const f32x4 mine, f32x4& lo, f32x4& hi) {
+    f32x4 other;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) other[e] = dpp_mov<kDppQuadXor1>(mine[e]);
+    const bool odd = threadIdx.x & 1;
+    lo = odd ? other : mine;
+    hi = odd ? mine : other;
+}
+// 8 bf16 (one 16-byte chunk) dotted with (lo, hi)
+__device__ __forceinline__ float dot8v(const u32x4 w, const f32x4 lo, const f32x4 hi) {
+    return ((__uint_as_float(w[0] << 16) * lo[0] + __uint_as_float(w[0] & 0xFFFF0000u) * lo[1]) +
+            (__uint_as_float(w[1] << 16) * lo[2] + __uint_as_float(w[1] & 0xFFFF0000u) * lo[3])) +
+           ((__uint_as_float(w[2] << 16) * hi[0] + __uint_as_float(w[2] & 0xFFFF0000u) * hi[1]) +
+            (__uint_as_float(w[3] << 16) * hi[2] + __uint_as_float(w[3] & 0xFFFF0000u) * hi[3]));
+}
 __device__ __forceinline__ f32x4 ldf4(const float* p) { return *(const GLOBAL_AS f32x4*)(p); }
 __device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS float*)(p); }
 
@@ -196,6 +213,41 @@ struct FxComplete {   // both 64-bit sums of the chunk have all HKV contribution
     }
 };
 
+// Like `poll`, but without the closing barrier, and the chunks stay in the polling
+// thread's registers: out[k] = chunk cidx(threadIdx.x + NT k). Returns this thread's
+// success; the caller joins the workgroup with __syncthreads_and of it.
+template <int K, typename CIDX, typename READY = NoSentinel>
+__device__ __forceinline__ bool poll_own(const float* base, size_t words, CIDX cidx, u32x4 (&out)[K], unsigned* err,
+                                         READY ready = READY{}) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(words * 4), 0x00020000);
+    unsigned todo = (1u << K) - 1;
+    int spins = 0;
+    for (;;) {
+        u32x4 v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (todo & (1u << k))
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cidx(threadIdx.x + NT * k) * 4), 0, SC1);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if ((todo & (1u << k)) && ready(v[k])) {
+                out[k] = v[k];
+                todo &= ~(1u << k);
+            }
+        }
+        if (!__any(todo != 0)) return true;
+        if (++spins > (1 << 16)) {
+            atomicOr(err, Q3_DEVERR_SYNC);
+            return false;
+        }
+    }
+}
+
+struct FxPair {   // thread t's chunks k = 0, 1: the sums 4t .. 4t+3 (chunk i = t + NT k)
+    __device__ __forceinline__ size_t operator()(int i) const { return (size_t)8 * (i % NT) + 4 * (i / NT); }
+};
+
 struct Contig {   // chunk i at word 4 i
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
 };
@@ -209,10 +261,13 @@ constexpr int LONG_T = 8192;     // contexts above this take the long variant of
 struct Smem {
     union {
         struct {
-            float act[BMAX][F];            // activations of the current phase (x, h, a)
+            float act[BMAX][D];            // normed x of the LM head
             float part[MAXCH * 2 * PART];  // polled chunk partials (long context combine)
             float wm[16][2][PART];         // attention state per (wave, 16-lane key group)
         } s;
+        struct {
+            float rd[BMAX][24][NT / 2];    // partial dot products of phases A, C, D per lane pair
+        } r;
         struct {                           // attention: staged cache rows of one kv head
             bf16 k[STAGE][DH];
             bf16 v[STAGE][DH];
@@ -259,6 +314,13 @@ __device__ __forceinline__ void norm_own(Smem& sm, int b, const f32x4 v, const f
     for (int e = 0; e < 4; ++e) sm.u.s.act[b][k + e] = v[e] * wv[e];
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) sm.red[b][threadIdx.x >> 6] = ss;
+}
+// The same for a thread that keeps its normed elements in registers: returns x * w.
+__device__ __forceinline__ f32x4 norm_part(Smem& sm, int b, const f32x4 v, const f32x4 wv) {
+    float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) sm.red[b][threadIdx.x >> 6] = ss;
+    return f32x4{v[0] * wv[0], v[1] * wv[1], v[2] * wv[2], v[3] * wv[3]};
 }
 __device__ __forceinline__ float norm_scale(const MegaParams& p, const Smem& sm, int b) {
     const float ss = (sm.red[b][0] + sm.red[b][1]) + (sm.red[b][2] + sm.red[b][3]);
@@ -588,17 +650,20 @@ __device__ __forceinline__ void pf_oproj(const MegaLayer& L, u32x4* pf, int g, i
     for (int i = 0; i < 4; ++i) pf[i] = ldw16(base + (sub + 8 * i) * 8);
 }
 
-// Rows of phase C: thread t < 192 owns row rr = t >> 3 (12 gate rows, then 12 up rows).
+// Rows of phase C: rr < 12 the gate rows of the workgroup's 12 SwiGLU columns, then their
+// 12 up rows.
 __device__ __forceinline__ int gu_row(int w, int rr) {
     const int col = 12 * w + (rr < 12 ? rr : rr - 12);
     return 32 * (col >> 4) + (col & 15) + (rr < 12 ? 0 : 16);
 }
 
+// Phases A, C, D: thread t polls 4 consecutive columns; with its pair lane t ^ 1 it holds
+// the 8 columns 8 (t >> 1) .. + 7 (pair8), and it owns half of the phase's rows
+// (by t & 1) at those columns: one 16-byte chunk per row.
 __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
-    const int r = threadIdx.x >> 4, sub = threadIdx.x & 15;
-    const bf16* base = L.wqkv + (size_t)(16 * w + r) * D;
+    const bf16* base = L.wqkv + (size_t)(16 * w + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pf[i] = ldw16(base + (sub + 16 * i) * 8);
+    for (int i = 0; i < 8; ++i) pf[i] = ldw16(base + (size_t)i * D);
     pre.nw = ldf4(L.in_norm + 4 * threadIdx.x);
     const int i = threadIdx.x & 63;
     const float* qk = (threadIdx.x >> 6) < 2 ? L.q_norm : L.k_norm;
@@ -606,18 +671,19 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
     pre.qk2 = ldf(qk + i + 64);
 }
 __device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
-    const int rr = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const bf16* base = L.wgu + 8 * (threadIdx.x >> 1);
+    const int r0 = 12 * (threadIdx.x & 1);
     pre.nw = ldf4(L.post_norm + 4 * threadIdx.x);
-    if (rr >= 24) return;
-    const bf16* base = L.wgu + (size_t)gu_row(w, rr) * D;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pf[i] = ldw16(base + (sub + 8 * i) * 8);
+    for (int i = 0; i < 12; ++i) pf[i] = ldw16(base + (size_t)gu_row(w, r0 + i) * D);
 }
+// pf[2k + i] = row 4w + 2 (t & 1) + i at columns 1024 k + 8 (t >> 1) .. + 7 (k < 3)
 __device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int w) {
-    const int rr = threadIdx.x >> 6, sub = threadIdx.x & 63;
-    const bf16* base = L.wd + (size_t)(4 * w + rr) * F;
+    const bf16* base = L.wd + (size_t)(4 * w + 2 * (threadIdx.x & 1)) * F + 8 * (threadIdx.x >> 1);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pf[i] = ldw16(base + (sub + 64 * i) * 8);
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pf[2 * k + i] = ldw16(base + (size_t)i * F + 1024 * k);
 }
 
 // long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
@@ -683,6 +749,10 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         float* Xn = X + p.ex_layer;                           // next layer's input
 
         // ---------------- A: x -> RMSNorm -> QKV rows 16w .. 16w+15
+        // Thread t polls x[4t .. 4t+3] and dots them (normed) with the 16 rows' weights at
+        // those columns as soon as they arrive; one barrier, then the 256 partial sums of
+        // each row are added (the same scheme in C and D).
+        bool ok = true;
         for (int b = 0; b < B; ++b) {
             f32x4 v;                      // this thread's elements 4 tid .. 4 tid + 3 of x
             if (layer == 0) {
@@ -692,22 +762,29 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 v = f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xFFFF0000u), __uint_as_float(e1 << 16),
                           __uint_as_float(e1 & 0xFFFF0000u)};
             } else {
-                if (!poll<1>(X + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
-                v = *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][4 * tid]);   // polled by this thread
+                u32x4 c[1];
+                ok = poll_own<1>(X + (size_t)b * W_X, W_X, Contig{}, c, p.err) && ok;
+                v = __builtin_bit_cast(f32x4, c[0]);
             }
             if ((tid >> 3) == j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.xg[b][4 * (tid & 7) + e] = v[e];
             }
-            norm_own(sm, b, v, pre.nw);
+            f32x4 lo, hi;
+            pair8(norm_part(sm, b, v, pre.nw), lo, hi);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm.u.r.rd[b][8 * (tid & 1) + i][tid >> 1] = dot8v(pf[i], lo, hi);
         }
         trace_at(p, sm, tslot++);
-        __syncthreads();
+        if (!__syncthreads_and(ok)) return;
         trace_at(p, sm, tslot++);
         {
             const int r = tid >> 4, sub = tid & 15;
             for (int b = 0; b < B; ++b) {
-                const float s = sum16(dot_chunks<8>(pf, sm.u.s.act[b], sub, 16)) * norm_scale(p, sm, b);
+                const f32x4* src = reinterpret_cast<const f32x4*>(sm.u.r.rd[b][r]);
+                const f32x4 q0 = src[sub], q1 = src[sub + 16];
+                float s = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
+                s = sum16(s) * norm_scale(p, sm, b);
                 if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s);
             }
         }
@@ -793,31 +870,39 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         trace_at(p, sm, tslot++);
 
         // ---------------- C: x' (summed in memory) -> RMSNorm -> gate/up of 12 columns -> SwiGLU
+        bool okc = true;
         for (int b = 0; b < B; ++b) {
-            if (!poll<2>(P + (size_t)b * W_P, 2 * D, Contig{}, D / 2, sm.u.s.part, p.err, FxComplete{})) return;
+            u32x4 c[2];                   // thread t: the sums 4t .. 4t+3
+            okc = poll_own<2>(P + (size_t)b * W_P, 2 * D, FxPair{}, c, p.err, FxComplete{}) && okc;
             if (b == 0) trace_at(p, sm, tslot++);
-            f32x4 xv;
-            {
-                const u64* sums = reinterpret_cast<const u64*>(sm.u.s.part) + 4 * tid;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xv[e] = fx_value(sums[e]);
-            }
+            const f32x4 xv = {fx_value((u64)c[0][1] << 32 | c[0][0]), fx_value((u64)c[0][3] << 32 | c[0][2]),
+                              fx_value((u64)c[1][1] << 32 | c[1][0]), fx_value((u64)c[1][3] << 32 | c[1][2])};
             if (tid == w) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.xr[b][e] = xv[e];
             }
-            norm_own(sm, b, xv, pre.nw);
-            __syncthreads();
+            f32x4 lo, hi;
+            pair8(norm_part(sm, b, xv, pre.nw), lo, hi);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) sm.u.r.rd[b][12 * (tid & 1) + i][tid >> 1] = dot8v(pf[i], lo, hi);
         }
         trace_at(p, sm, tslot++);
+        if (!__syncthreads_and(okc)) return;
         trace_at(p, sm, tslot++);
         {
-            const int rr = tid >> 3, sub = tid & 7;
-            for (int b = 0; b < B; ++b) {
-                float s = 0.f;
-                if (rr < 24) s = dot_chunks<16>(pf, sm.u.s.act[b], sub, 8);
-                s = sum8(s);
-                if (rr < 24 && sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b);
+            if (tid < 192) {              // row rr = t >> 3: 8 threads, then 8 lanes
+                const int rr = tid >> 3, sub = tid & 7;
+                for (int b = 0; b < B; ++b) {
+                    const f32x4* src = reinterpret_cast<const f32x4*>(sm.u.r.rd[b][rr]);
+                    float s = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x4 q = src[sub + 8 * i];
+                        s += (q[0] + q[1]) + (q[2] + q[3]);
+                    }
+                    s = sum8(s);
+                    if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b);
+                }
             }
             __syncthreads();
             if (tid < 12 * B) {
@@ -830,15 +915,29 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         trace_at(p, sm, tslot++);
 
         // ---------------- D: rows 4w..4w+3 of down + residual
-        for (int b = 0; b < B; ++b)
-            if (!poll<3>(A + (size_t)b * W_A, W_A, Contig{}, F / 4, sm.u.s.act[b], p.err)) return;
+        bool okd = true;
+        for (int b = 0; b < B; ++b) {
+            u32x4 c[3];                   // a[1024 k + 4t .. 4t + 3], k < 3
+            okd = poll_own<3>(A + (size_t)b * W_A, W_A, Contig{}, c, p.err) && okd;
+            float s[2] = {0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                f32x4 lo, hi;
+                pair8(__builtin_bit_cast(f32x4, c[k]), lo, hi);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) s[i] += dot8v(pf[2 * k + i], lo, hi);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) sm.u.r.rd[b][2 * (tid & 1) + i][tid >> 1] = s[i];
+        }
+        if (!__syncthreads_and(okd)) return;
         trace_at(p, sm, tslot++);
         {
-            const int rr = tid >> 6, sub = tid & 63;
+            const int rr = tid >> 6, sub = tid & 63;   // wave rr adds row 4w + rr
             const int n = 4 * w + rr;
             for (int b = 0; b < B; ++b) {
-                float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 64);
-                s = wave_sum(s);
+                const f32x2 q = reinterpret_cast<const f32x2*>(sm.u.r.rd[b][rr])[sub];
+                const float s = wave_sum(q[0] + q[1]);
                 if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s);
             }
         }
