@@ -64,6 +64,15 @@ constexpr int PT_CHUNK = HKV * 2 * PART;                     // words per chunk 
 constexpr unsigned SENT = 0x7FC0DEADu;   // "not written yet" (a NaN no computation yields)
 constexpr int SC1 = 16;                  // cache-policy bit of an agent-coherent access
 
+// A poll reads the same address again and again with nothing the compiler sees writing it:
+// every read takes its offset through an empty asm statement, which the compiler must treat
+// as producing a new value, so it can neither hoist the read out of the loop nor merge two
+// reads (it still tracks each read for its wait counters).
+__device__ __forceinline__ int fresh(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 __device__ __forceinline__ void put(float* p, float v) {
     unsigned u = __float_as_uint(v);
     if (u == SENT) u = 0x7FC00000u;      // keep real NaNs distinguishable from "not written"
@@ -169,7 +178,7 @@ __device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx,
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (todo & (1u << k))
-                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cidx(threadIdx.x + NT * k) * 4), 0, SC1);
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, fresh((int)(cidx(threadIdx.x + NT * k) * 4)), 0, SC1);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if ((todo & (1u << k)) && ready(v[k])) {
@@ -221,27 +230,41 @@ __device__ __forceinline__ bool poll_own(const float* base, size_t words, CIDX c
                                          READY ready = READY{}) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(words * 4), 0x00020000);
+    // Two rounds in flight: round n + 1 is issued before round n is checked, so a word
+    // that becomes visible is seen about half a round trip sooner than with one round.
+    // (Every round re-reads all K chunks; a chunk found complete is kept from its round.)
     unsigned todo = (1u << K) - 1;
-    int spins = 0;
-    for (;;) {
-        u32x4 v[K];
+    auto load = [&](int k) {
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, fresh((int)(cidx(threadIdx.x + NT * k) * 4)), 0, SC1);
+    };
+    u32x4 va[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) va[k] = load(k);
+    for (int spins = 0; spins < (1 << 15); ++spins) {
+        u32x4 vb[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) vb[k] = load(k);
+        asm volatile("" ::: "memory");   // keeps the issue of this round before the check
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            if (todo & (1u << k))
-                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(cidx(threadIdx.x + NT * k) * 4), 0, SC1);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if ((todo & (1u << k)) && ready(v[k])) {
-                out[k] = v[k];
+            if ((todo & (1u << k)) && ready(va[k])) {
+                out[k] = va[k];
                 todo &= ~(1u << k);
             }
-        }
         if (!__any(todo != 0)) return true;
-        if (++spins > (1 << 16)) {
-            atomicOr(err, Q3_DEVERR_SYNC);
-            return false;
-        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) va[k] = load(k);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if ((todo & (1u << k)) && ready(vb[k])) {
+                out[k] = vb[k];
+                todo &= ~(1u << k);
+            }
+        if (!__any(todo != 0)) return true;
     }
+    atomicOr(err, Q3_DEVERR_SYNC);
+    return false;
 }
 
 struct FxPair {   // thread t's chunks k = 0, 1: the sums 4t .. 4t+3 (chunk i = t + NT k)
