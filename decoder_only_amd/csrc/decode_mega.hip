@@ -693,12 +693,13 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
     pre.qk1 = ldf(qk + i);
     pre.qk2 = ldf(qk + i + 64);
 }
-__device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
+// gate/up rows i < 12 of the thread into pf[4 + i], in two parts: rows i0 <= i < i1
+template <int I0, int I1>
+__device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, int w) {
     const bf16* base = L.wgu + 8 * (threadIdx.x >> 1);
     const int r0 = 12 * (threadIdx.x & 1);
-    pre.nw = ldf4(L.post_norm + 4 * threadIdx.x);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) pf[i] = ldw16(base + (size_t)gu_row(w, r0 + i) * D);
+    for (int i = I0; i < I1; ++i) pf[4 + i] = ldw16(base + (size_t)gu_row(w, r0 + i) * D);
 }
 // pf[2k + i] = row 4w + 2 (t & 1) + i at columns 1024 k + 8 (t >> 1) .. + 7 (k < 3)
 __device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int w) {
@@ -826,6 +827,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
+                if (b == 0) pf_gu<0, 4>(L, pf, w);              // streams during the attention
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
@@ -889,7 +891,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         trace_at(p, sm, tslot++);
         oproj_partial(sm, pf, P, g, j, B);
-        pf_gu(L, pf, pre, w);
+        if (Tmax > SHORT_T) pf_gu<0, 4>(L, pf, w);
+        pf_gu<4, 12>(L, pf, w);
+        pre.nw = ldf4(L.post_norm + 4 * tid);
         trace_at(p, sm, tslot++);
 
         // ---------------- C: x' (summed in memory) -> RMSNorm -> gate/up of 12 columns -> SwiGLU
@@ -907,7 +911,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             f32x4 lo, hi;
             pair8(norm_part(sm, b, xv, pre.nw), lo, hi);
 #pragma unroll
-            for (int i = 0; i < 12; ++i) sm.u.r.rd[b][12 * (tid & 1) + i][tid >> 1] = dot8v(pf[i], lo, hi);
+            for (int i = 0; i < 12; ++i) sm.u.r.rd[b][12 * (tid & 1) + i][tid >> 1] = dot8v(pf[4 + i], lo, hi);
         }
         trace_at(p, sm, tslot++);
         if (!__syncthreads_and(okc)) return;
