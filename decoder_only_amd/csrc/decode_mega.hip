@@ -724,10 +724,13 @@ __device__ __forceinline__ size_t group_chunk(int gg, int i) {
                   : (i < 96 ? (size_t)HQ * DH + DH * gg + 4 * (i - 64) : (size_t)(HQ + HKV) * DH + DH * gg + 4 * (i - 96));
 }
 
-// LONG: the long-context instance (split-K attention staged in double-buffered halves);
-// a separate instance so its extra registers do not touch the short-context code.
-template <bool LONG>
+// MODE 0: every row has at most SHORT_T visible slots (each workgroup of a kv group attends
+// the whole range); 1: split-K attention over chunks; 2: the same with the chunk rows staged
+// in double-buffered halves (contexts above LONG_T). Separate instances, so the code and
+// registers of one path do not touch the others.
+template <int MODE>
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
+    constexpr bool LONG = MODE == 2;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -816,10 +819,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         trace_at(p, sm, tslot++);
 
         // ---------------- B: attention of kv group g and its O-projection partial
-        int Tmax = 0;
-        for (int b = 0; b < B; ++b) Tmax = max(Tmax, p.slots[b] + 1);
         __syncthreads();                  // act (read above) shares memory with the K/V staging
-        if (Tmax <= SHORT_T) {
+        if constexpr (MODE == 0) {
             for (int b = 0; b < B; ++b) {
                 const int slot = p.slots[b], T = slot + 1;
                 const size_t hb = kv_head_base(p, layer, b, g);
@@ -872,18 +873,37 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     return (size_t)(i / 65) * PT_CHUNK + (size_t)g * 2 * PART + 4 * (i % 65);
                 };
                 if (!poll<9>(PT + (size_t)b * W_PT, W_PT, pidx, nch * 65, sm.u.s.part, p.err)) return;
+                // chunks in batches of 8 whose reads are all issued before their use (a
+                // chunk past nch repeats the last one with zero weight); sums in chunk order
                 const int h = tid >> 7, dd = tid & 127;
                 float M = -INFINITY;
-                for (int c2 = 0; c2 < nch; ++c2) {
-                    const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
-                    M = fmaxf(M, pp[1] > 0.f ? pp[0] : -INFINITY);
+                for (int c0 = 0; c0 < nch; c0 += 8) {
+                    float mv[8], lv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float* pp = sm.u.s.part + ((size_t)min(c0 + u, nch - 1) * 2 + h) * PART;
+                        mv[u] = pp[0];
+                        lv[u] = pp[1];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) M = fmaxf(M, lv[u] > 0.f ? mv[u] : -INFINITY);
                 }
                 float Ls = 0.f, Acc = 0.f;
-                for (int c2 = 0; c2 < nch; ++c2) {
-                    const float* pp = sm.u.s.part + ((size_t)c2 * 2 + h) * PART;
-                    const float cf = pp[1] > 0.f ? __builtin_amdgcn_exp2f(pp[0] - M) : 0.f;
-                    Ls += pp[1] * cf;
-                    Acc += pp[2 + dd] * cf;
+                for (int c0 = 0; c0 < nch; c0 += 8) {
+                    float mv[8], lv[8], av[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float* pp = sm.u.s.part + ((size_t)min(c0 + u, nch - 1) * 2 + h) * PART;
+                        mv[u] = pp[0];
+                        lv[u] = c0 + u < nch ? pp[1] : 0.f;
+                        av[u] = pp[2 + dd];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float cf = lv[u] > 0.f ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
+                        Ls += lv[u] * cf;
+                        Acc += av[u] * cf;
+                    }
                 }
                 sm.o[b][h * DH + dd] = Ls > 0.f ? Acc / Ls : 0.f;
                 __syncthreads();
@@ -891,7 +911,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         trace_at(p, sm, tslot++);
         oproj_partial(sm, pf, P, g, j, B);
-        if (Tmax > SHORT_T) pf_gu<0, 4>(L, pf, w);
+        if constexpr (MODE != 0) pf_gu<0, 4>(L, pf, w);
         pf_gu<4, 12>(L, pf, w);
         pre.nw = ldf4(L.post_norm + 4 * tid);
         trace_at(p, sm, tslot++);
@@ -1138,22 +1158,25 @@ hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t
     if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers) return hipErrorInvalidValue;
     int Tmax = 0;
     for (int b = 0; b < p.B; ++b) Tmax = std::max(Tmax, p.slots[b] + 1);
-    const void* fn = Tmax > LONG_T ? (const void*)k_decode_mega<true> : (const void*)k_decode_mega<false>;
+    const int mode = Tmax <= SHORT_T ? 0 : Tmax <= LONG_T ? 1 : 2;
+    const void* fn = mode == 0 ? (const void*)k_decode_mega<0>
+                     : mode == 1 ? (const void*)k_decode_mega<1> : (const void*)k_decode_mega<2>;
     if (cooperative) {
         void* args[] = {(void*)&p};
         return hipLaunchCooperativeKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
     }
-    if (Tmax > LONG_T) hipLaunchKernelGGL(k_decode_mega<true>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else hipLaunchKernelGGL(k_decode_mega<false>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    if (mode == 0) hipLaunchKernelGGL(k_decode_mega<0>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else if (mode == 1) hipLaunchKernelGGL(k_decode_mega<1>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else hipLaunchKernelGGL(k_decode_mega<2>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
     return hipGetLastError();
 }
 
 hipError_t decode_mega_prepare() {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decode_mega<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(Smem));
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)k_decode_mega<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)sizeof(Smem));
+    for (const void* fn : {(const void*)k_decode_mega<0>, (const void*)k_decode_mega<1>, (const void*)k_decode_mega<2>}) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q3
