@@ -1131,17 +1131,26 @@ __global__ void k_mega_fill(float* ex, size_t words, size_t ex_layer) {
     }
 }
 
-hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, int32_t* greedy_out,
-                            hipStream_t s) {
-    if (B < 1 || B > BMAX || n_layers < 1 || ex_layer != decode_mega_exchange_words_per_layer())
-        return hipErrorInvalidValue;
-    int pt_words = 0;
-    if (Tmax > SHORT_T) {
+int decode_mega_chunks(const int* T, int B) {
+    int Tmax = 0;
+    for (int b = 0; b < B; ++b) Tmax = std::max(Tmax, T[b]);
+    if (Tmax <= SHORT_T) return 0;                 // no split-K attention in this launch
+    int m = 0;                                     // (a shorter row can have more chunks)
+    for (int b = 0; b < B; ++b) {
         int nch, ch;
-        chunking(Tmax, nch, ch);
-        pt_words = nch * PT_CHUNK;
+        chunking(T[b], nch, ch);
+        m = std::max(m, nch);
     }
+    return m;
+}
+
+hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
+                            int B, float* ex, size_t ex_layer, int n_layers, int pt_chunks, int32_t* greedy_out,
+                            hipStream_t s) {
+    if (B < 1 || B > BMAX || n_layers < 1 || ex_layer != decode_mega_exchange_words_per_layer() || pt_chunks < 0 ||
+        pt_chunks > MAXCH)
+        return hipErrorInvalidValue;
+    const int pt_words = pt_chunks * PT_CHUNK;
     hipLaunchKernelGGL(k_mega_tail, dim3(NWG), dim3(NT), 0, s, cand, amax, lens, seq_base, B, ex, ex_layer, n_layers,
                        pt_words, greedy_out);
     return hipGetLastError();

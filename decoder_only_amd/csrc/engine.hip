@@ -86,7 +86,7 @@ struct q3_engine {
     // The tail of the last persistent launch is deferred to the next call, so that a greedy
     // q3_sample right after it is the same launch.
     bool tail_pending = false;
-    int tail_B = 0, tail_seq_base = 0, tail_maxT = 0;
+    int tail_B = 0, tail_seq_base = 0, tail_chunks = 0;
     unsigned long long* m_trace = nullptr;   // caller's device buffer for phase timestamps
     int m_trace_n = 0;
 
@@ -367,7 +367,7 @@ static q3_status flush_tail(q3_engine* e, int32_t* greedy_out = nullptr) {
     if (!e->tail_pending) return Q3_OK;
     e->tail_pending = false;
     HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, e->tail_seq_base, e->tail_B, e->m_ex, e->m_ex_layer,
-                               e->cfg.n_layers, e->tail_maxT, greedy_out, e->stream));
+                               e->cfg.n_layers, e->tail_chunks, greedy_out, e->stream));
     return Q3_OK;
 }
 
@@ -452,7 +452,11 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         e->tail_pending = true;
         e->tail_B = B;
         e->tail_seq_base = seq_base;
-        e->tail_maxT = maxT;
+        {
+            int vis[kMegaMaxRows];
+            for (int b = 0; b < B; ++b) vis[b] = mp.slots[b] + 1;
+            e->tail_chunks = decode_mega_chunks(vis, B);
+        }
         e->cur_logits = lg;
         e->cur_rows = B;
         for (int b = 0; b < B; ++b) e->h_len[seq_base + b] += 1;

@@ -103,11 +103,14 @@ struct MegaParams {
 hipError_t decode_mega_prepare();
 // cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s);
+// Attention chunks whose partials a launch over rows of visible lengths T[0..B) writes per
+// row (the largest count over the rows; 0 without split-K attention).
+int decode_mega_chunks(const int* T, int B);
 // After each launch: argmax over the per-workgroup candidates, lens[seq_base + b] += 1,
-// the sentinel back into the exchange words used (Tmax = longest visible length), and the
-// greedy token of each row into greedy_out when it is not NULL.
+// the initial state back into the exchange words used (pt_chunks from decode_mega_chunks),
+// and the greedy token of each row into greedy_out when it is not NULL.
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, float* ex, size_t ex_layer, int n_layers, int Tmax, int32_t* greedy_out,
+                            int B, float* ex, size_t ex_layer, int n_layers, int pt_chunks, int32_t* greedy_out,
                             hipStream_t s);
 // Sentinel into all `words` exchange words (at load).
 hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);

@@ -81,6 +81,7 @@ def test_engine_capacity_and_token_errors():
 @pytest.mark.parametrize("path,lens", [
     (2, (5, 17, 100)),            # persistent kernel, every row on the short path
     (3, (5, 40, 300)),            # persistent kernel, split-K attention with one short row
+    (3, (1990, 2100)),            # split-K: the shorter row has more chunks (32 of 64 keys) than the longer (17 of 128)
     (1, (5, 40, 300)),            # one launch per operation
     (0, (5, 9, 33, 64, 100, 130, 170, 200, 230, 260, 290, 301)),   # 12 rows: matrix-core batch path
 ])
