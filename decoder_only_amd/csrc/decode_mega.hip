@@ -850,6 +850,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                                  p.err))
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
+                    if (b == 0) pf_gu<0, 4>(L, pf, w);          // streams during the attention
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
@@ -858,6 +859,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
+                    pf_gu<0, 4>(L, pf, w);
                     trace_at(p, sm, tslot++);
                     trace_at(p, sm, tslot++);
                 }
@@ -911,7 +913,6 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         trace_at(p, sm, tslot++);
         oproj_partial(sm, pf, P, g, j, B);
-        if constexpr (MODE != 0) pf_gu<0, 4>(L, pf, w);
         pf_gu<4, 12>(L, pf, w);
         pre.nw = ldf4(L.post_norm + 4 * tid);
         trace_at(p, sm, tslot++);
