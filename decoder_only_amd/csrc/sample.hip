@@ -83,18 +83,39 @@ __device__ __forceinline__ double row_zmax(const u64* amax, int b, double T) {
 }
 
 // Fixed-point masses into the row's 65536-bucket histogram (keyed by the upper 16 bits).
-__global__ __launch_bounds__(256) void k_sample_hist(const float* __restrict__ logits,
-                                                     const u64* __restrict__ amax, int V, double Td,
-                                                     double scale, u64* __restrict__ ws, size_t row_words) {
+// Each block first sums its tokens' masses per bucket in shared memory (a direct-mapped
+// table of HIST_SLOTS buckets, slot = bucket mod HIST_SLOTS; a bucket whose slot another
+// bucket holds goes straight to memory), then adds its non-empty slots to the row's
+// histogram: the memory-side atomics drop from one per token to about one per bucket and
+// block. Integer sums: the histogram does not depend on the order of the additions.
+constexpr int HIST_SLOTS = 8192, HIST_THREADS = 1024, HIST_BLOCKS = 32;
+constexpr unsigned HIST_EMPTY = 0xFFFFFFFFu;
+__global__ __launch_bounds__(HIST_THREADS) void k_sample_hist(const float* __restrict__ logits,
+                                                              const u64* __restrict__ amax, int V, double Td,
+                                                              double scale, u64* __restrict__ ws, size_t row_words) {
+    __shared__ unsigned lkey[HIST_SLOTS];
+    __shared__ u64 lmass[HIST_SLOTS];
     const int b = blockIdx.y;
     const float* l = logits + (size_t)b * V;
     u64* hist = ws + (size_t)b * row_words + RowWs::hist;
+    for (int i = threadIdx.x; i < HIST_SLOTS; i += HIST_THREADS) {
+        lkey[i] = HIST_EMPTY;
+        lmass[i] = 0ull;
+    }
+    __syncthreads();
     const double zmax = row_zmax(amax, b, Td);
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x) {
+    for (int j = blockIdx.x * HIST_THREADS + threadIdx.x; j < V; j += gridDim.x * HIST_THREADS) {
         const float v = l[j];
         const u64 m = mass_of(v, Td, zmax, scale);
-        if (m) atomicAdd(hist + (ordered_key(v) >> 16), m);
+        if (!m) continue;
+        const unsigned k = ordered_key(v) >> 16, slot = k % HIST_SLOTS;
+        const unsigned old = atomicCAS(&lkey[slot], HIST_EMPTY, k);
+        if (old == HIST_EMPTY || old == k) atomicAdd(&lmass[slot], m);
+        else atomicAdd(hist + k, m);
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < HIST_SLOTS; i += HIST_THREADS)
+        if (lkey[i] != HIST_EMPTY) atomicAdd(hist + lkey[i], lmass[i]);
 }
 
 // Exclusive prefix sum of one u64 per thread over a 1024-thread block; returns the total.
@@ -387,7 +408,7 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     const size_t rw = RowWs::words(V);
     if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * rw), s)) != hipSuccess) return e;
     const int nblk = (V + 255) / 256 < 512 ? (V + 255) / 256 : 512;
-    hipLaunchKernelGGL(k_sample_hist, dim3(nblk, B), dim3(256), 0, s, logits, amax, V, Td, scale, w, rw);
+    hipLaunchKernelGGL(k_sample_hist, dim3(HIST_BLOCKS, B), dim3(HIST_THREADS), 0, s, logits, amax, V, Td, scale, w, rw);
     hipLaunchKernelGGL(k_hist_groups, dim3(256, B), dim3(256), 0, s, w, rw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (top_p < 1.0f) {
