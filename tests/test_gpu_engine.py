@@ -92,3 +92,30 @@ def test_toy_bf16_ragged_batch(path, lens):
     stats = run_ragged(w, list(lens), 6, decode_path=path)
     _report(stats)
     assert not failures(stats), failures(stats)[:5]
+
+
+@pytest.mark.parametrize("path", [1, 3])
+def test_nonfinite_weight_raises_numeric_error(path):
+    """A +inf in one O-projection row makes the residual non-finite: both decode paths
+    must report non-finite logits (the persistent kernel carries the O-projection sum as
+    fixed-point words, where a non-finite contribution marks the sum as NaN)."""
+    import torch
+    from decoder_only_amd import q3
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16", n_layers=1)
+    ws = dict(synth.make_weights(w))
+    name = "model.layers.0.self_attn.o_proj.weight"
+    wo = ws[name].copy()
+    wo[0, :] = 0x7F80                                        # bf16 +inf
+    ws[name] = wo
+    eng = q3.Engine(q3.config(w, 1, 16), ws)
+    eng.set_decode_path(path)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(q3.Q3Error) as e:
+        eng.prefill(0, torch.from_numpy(synth.prompt_tokens(w, 3)).cuda())
+        eng.sample(tok, 0.0)
+        for _ in range(2):
+            eng.decode_step(tok)
+            eng.sample(tok, 0.0)
+        eng.sync()
+    assert e.value.code == -8
+    eng.close()
