@@ -13,14 +13,15 @@
 // One memory round trip thus carries both the data and the "it is ready" signal. Each
 // layer has its own buffers, so a word is written once per launch; the small tail kernel
 // that follows every launch puts the sentinel back into every word the launch used (also
-// after a launch that gave up waiting). The one reduction among hand-overs, x' = x + the
-// O-projection partials of the 8 kv groups, is summed in memory instead: 64-bit
-// fixed-point words with device-scope atomic adds, whose top bits count the arrivals. On MI355X one all-to-all hand-over among 256
-// workgroups takes ~2.3 us this way (~1.2 us between two), so the layout below is built
-// around needing only four per layer.
+// after a launch that gave up waiting). The two reductions among hand-overs, x' = x + the
+// O-projection partials of the 8 kv groups and x'' = x' + the down-projection partials of
+// 8 column blocks, are summed in memory instead: 64-bit fixed-point words with
+// device-scope atomic adds, whose top bits count the arrivals. On MI355X one all-to-all
+// hand-over among 256 workgroups takes ~2 us this way (~1 us within a group of 32), so the
+// layout below is built around four per layer, one of them group-local.
 //
 // Per layer, for each row b (hand-overs marked ->):
-//   A  poll x (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]                -> QKV words
+//   A  poll the x sums (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]       -> QKV words
 //   B  workgroup (g, j), kv group g = query heads 2g, 2g+1, j < 32: poll the group's
 //      q/k/v (512) -> QK-norm + RoPE -> KV append (j == 0) -> attention of both heads,
 //      recomputed by the 32 workgroups of the group (K/V staged through LDS) -> rows
@@ -29,7 +30,9 @@
 //       workgroup of the group, then the same O-projection partial)
 //   C  poll the x' sums (1024, complete when all 8 groups added) -> RMSNorm -> gate/up
 //      rows of 12 SwiGLU columns                                       -> A words
-//   D  poll a (3072) -> rows 4w..4w+3: x'' = x' + Wd a                  -> next x words
+//   D  workgroup (g, j): poll a[384g .. 384g+383] (written by the 32 workgroups of group
+//      g in C) -> rows 32j..32j+31 of Wd[:, 384g:384g+384] . a, plus x' for g = 0
+//                                                                     -> added to x'' sums
 // then poll x, RMSNorm, 594 rows of the tied LM head per workgroup; each workgroup
 // writes its packed (logit, id) maximum per row, reduced by a small tail kernel. Each
 // workgroup issues the loads of its next weight slice right after finishing a phase, so
@@ -57,7 +60,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // words per (layer, row) in each exchange buffer
-constexpr size_t W_X = D, W_QKV = NQKV, W_P = (size_t)2 * D, W_A = F;   // W_P: D 64-bit sums
+constexpr size_t W_X = (size_t)2 * D, W_QKV = NQKV, W_P = (size_t)2 * D, W_A = F;   // W_X, W_P: D 64-bit sums
+constexpr int DCOLS = F / HKV;    // columns of a per down-projection block (phase D)
+static_assert(DCOLS == 6 * 8 * 8, "phase D: 8 lanes per row, 6 chunks of 8 columns each");
 constexpr size_t W_PT = (size_t)MAXCH * HKV * 2 * PART;   // [chunk][group][head][PART]
 constexpr int PT_CHUNK = HKV * 2 * PART;                     // words per chunk index
 
@@ -148,6 +153,15 @@ __device__ __forceinline__ float dot8v(const u32x4 w, const f32x4 lo, const f32x
 }
 __device__ __forceinline__ f32x4 ldf4(const float* p) { return *(const GLOBAL_AS f32x4*)(p); }
 __device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS float*)(p); }
+// A pointer every lane holds alike, moved into scalar registers here (the empty asm keeps
+// the read at this point of the program).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const unsigned long long v = (unsigned long long)p;
+    unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    return (T*)((unsigned long long)hi << 32 | lo);
+}
 
 // Poll the 16-byte chunks cidx(i), i < nch (nch <= K * 256; cidx = word offset of the
 // chunk's first word from `base`, a multiple of 4), into dst[4 i .. 4 i + 3] until none of
@@ -196,7 +210,8 @@ __device__ __forceinline__ bool poll(const float* base, size_t words, CIDX cidx,
     return __syncthreads_and(ok);
 }
 
-// The O-projection partials of the 8 kv groups are summed in memory: each group adds its
+// The O-projection partials of the 8 kv groups (and the down-projection partials of the 8
+// column blocks) are summed in memory: each group adds its
 // value to a 64-bit word with a device-scope atomic add, as an integer, so the sum does not
 // depend on the order of arrival. A contribution is 2^60 (bits 60..63 count the arrived
 // groups) + round(v * 2^30) + 2^52 (bias: every contribution's value field is positive and
@@ -221,6 +236,11 @@ struct FxComplete {   // both 64-bit sums of the chunk have all HKV contribution
         return (v[1] >> 28) == (unsigned)HKV && (v[3] >> 28) == (unsigned)HKV;
     }
 };
+// the four sums of a thread's two polled chunks (FxPair) as floats
+__device__ __forceinline__ f32x4 fx_vec4(const u32x4 (&c)[2]) {
+    return f32x4{fx_value((u64)c[0][1] << 32 | c[0][0]), fx_value((u64)c[0][3] << 32 | c[0][2]),
+                 fx_value((u64)c[1][1] << 32 | c[1][0]), fx_value((u64)c[1][3] << 32 | c[1][2])};
+}
 
 // Like `poll`, but without the closing barrier, and the chunks stay in the polling
 // thread's registers: out[k] = chunk cidx(threadIdx.x + NT k). Returns this thread's
@@ -298,7 +318,7 @@ struct Smem {
         } kv;
     } u;
     float xg[BMAX][32];            // layer input x at rows 32j..32j+31 (phase-B row block)
-    float xr[BMAX][4];             // x' at this workgroup's residual rows 4w..4w+3
+    float xr[BMAX][32];            // x' at rows 32j..32j+31 (residual of the phase-D row block)
     float red[BMAX][16];           // block reductions
     float in[BMAX][4 * DH];        // polled group inputs: q (2 x 128), k (128), v (128)
     __attribute__((aligned(16))) bf16 qb[2][2][DH];   // rotated queries of the group: bf16 hi, lo parts
@@ -386,7 +406,9 @@ __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const 
         dst[i] = bf2f(h1);
         dst[i + 64] = bf2f(h2);
         if (append) {
-            bf16* cache = (wid == 2 ? p.kc : p.vc) + (size_t)layer * p.kv_layer_elems +
+            // (a wave-uniform choice: a per-lane one reads the pointer with a vector load and
+            // then waits for every outstanding load, the weight prefetch included)
+            bf16* cache = (__builtin_amdgcn_readfirstlane(wid) == 2 ? p.kc : p.vc) + (size_t)layer * p.kv_layer_elems +
                           (size_t)(p.seq_base + b) * p.kv_seq_elems + ((size_t)g * p.t_cap + slot) * DH;
             cache[i] = h1;
             cache[i + 64] = h2;
@@ -667,6 +689,19 @@ __device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, float* 
     }
 }
 
+// x''[b][32j + r] += Wd[32j + r, DCOLS g : DCOLS (g + 1)] . a[b] (fixed-point sum over the
+// column blocks; block 0's contribution also carries the residual x'); thread t: row
+// r = t >> 3, 16-byte chunks sub + 8 i (i < 6) of the 48 in the row segment.
+__device__ __forceinline__ void down_partial(Smem& sm, const u32x4* pf, float* Xn, int g, int j, int B) {
+    const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    for (int b = 0; b < B; ++b) {
+        float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 8);
+        s = sum8(s);
+        if (g == 0) s = sm.xr[b][r] + s;
+        if (sub == 0) fx_add(reinterpret_cast<u64*>(Xn + (size_t)b * W_X) + 32 * j + r, s);
+    }
+}
+
 __device__ __forceinline__ void pf_oproj(const MegaLayer& L, u32x4* pf, int g, int j) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     const bf16* base = L.wo + (size_t)(32 * j + r) * (HQ * DH) + 256 * g;
@@ -696,19 +731,17 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
 }
 // gate/up rows i < 12 of the thread into pf[4 + i], in two parts: rows i0 <= i < i1
 template <int I0, int I1>
-__device__ __forceinline__ void pf_gu(const MegaLayer& L, u32x4* pf, int w) {
-    const bf16* base = L.wgu + 8 * (threadIdx.x >> 1);
+__device__ __forceinline__ void pf_gu(const bf16* wgu, u32x4* pf, int w) {
+    const bf16* base = wgu + 8 * (threadIdx.x >> 1);
     const int r0 = 12 * (threadIdx.x & 1);
 #pragma unroll
     for (int i = I0; i < I1; ++i) pf[4 + i] = ldw16(base + (size_t)gu_row(w, r0 + i) * D);
 }
-// pf[2k + i] = row 4w + 2 (t & 1) + i at columns 1024 k + 8 (t >> 1) .. + 7 (k < 3)
-__device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int w) {
-    const bf16* base = L.wd + (size_t)(4 * w + 2 * (threadIdx.x & 1)) * F + 8 * (threadIdx.x >> 1);
+// pf[i] = row 32j + (t >> 3) of Wd at columns DCOLS g + 8 ((t & 7) + 8 i) .. + 7 (i < 6)
+__device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int g, int j) {
+    const bf16* base = L.wd + (size_t)(32 * j + (threadIdx.x >> 3)) * F + DCOLS * g + 8 * (threadIdx.x & 7);
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) pf[2 * k + i] = ldw16(base + (size_t)i * F + 1024 * k);
+    for (int i = 0; i < 6; ++i) pf[i] = ldw16(base + 64 * i);
 }
 
 // long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
@@ -790,9 +823,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 v = f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xFFFF0000u), __uint_as_float(e1 << 16),
                           __uint_as_float(e1 & 0xFFFF0000u)};
             } else {
-                u32x4 c[1];
-                ok = poll_own<1>(X + (size_t)b * W_X, W_X, Contig{}, c, p.err) && ok;
-                v = __builtin_bit_cast(f32x4, c[0]);
+                u32x4 c[2];
+                ok = poll_own<2>(X + (size_t)b * W_X, W_X, FxPair{}, c, p.err, FxComplete{}) && ok;
+                v = fx_vec4(c);
             }
             if ((tid >> 3) == j) {
 #pragma unroll
@@ -829,7 +862,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
-                if (b == 0) pf_gu<0, 4>(L, pf, w);              // streams during the attention
+                if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);              // streams during the attention
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
@@ -851,7 +884,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                                  p.err))
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
-                    if (b == 0) pf_gu<0, 4>(L, pf, w);          // streams during the attention
+                    if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);          // streams during the attention
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
@@ -860,7 +893,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
-                    pf_gu<0, 4>(L, pf, w);
+                    pf_gu<0, 4>(L.wgu, pf, w);
                     trace_at(p, sm, tslot++);
                     trace_at(p, sm, tslot++);
                 }
@@ -913,9 +946,16 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             }
         }
         trace_at(p, sm, tslot++);
-        oproj_partial(sm, pf, P, g, j, B);
-        pf_gu<4, 12>(L, pf, w);
-        pre.nw = ldf4(L.post_norm + 4 * tid);
+        {
+            // phase C's weight pointers are taken from the layer table before the atomics of
+            // the O projection: read after them, the compiler waits for every outstanding
+            // memory operation (the atomics' round trip included) before the table read
+            const bf16* wgu = uniform_ptr(L.wgu);
+            const float* pnorm = uniform_ptr(L.post_norm);
+            oproj_partial(sm, pf, P, g, j, B);
+            pf_gu<4, 12>(wgu, pf, w);
+            pre.nw = ldf4(pnorm + 4 * tid);
+        }
         trace_at(p, sm, tslot++);
 
         // ---------------- C: x' (summed in memory) -> RMSNorm -> gate/up of 12 columns -> SwiGLU
@@ -924,11 +964,10 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             u32x4 c[2];                   // thread t: the sums 4t .. 4t+3
             okc = poll_own<2>(P + (size_t)b * W_P, 2 * D, FxPair{}, c, p.err, FxComplete{}) && okc;
             if (b == 0) trace_at(p, sm, tslot++);
-            const f32x4 xv = {fx_value((u64)c[0][1] << 32 | c[0][0]), fx_value((u64)c[0][3] << 32 | c[0][2]),
-                              fx_value((u64)c[1][1] << 32 | c[1][0]), fx_value((u64)c[1][3] << 32 | c[1][2])};
-            if (tid == w) {
+            const f32x4 xv = fx_vec4(c);
+            if ((tid >> 3) == j) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.xr[b][e] = xv[e];
+                for (int e = 0; e < 4; ++e) sm.xr[b][4 * (tid & 7) + e] = xv[e];
             }
             f32x4 lo, hi;
             pair8(norm_part(sm, b, xv, pre.nw), lo, hi);
@@ -960,36 +999,18 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 put(A + (size_t)b * W_A + 12 * w + c, gt / (1.0f + expf(-gt)) * up);
             }
         }
-        pf_down(L, pf, w);
+        pf_down(L, pf, g, j);
         trace_at(p, sm, tslot++);
 
-        // ---------------- D: rows 4w..4w+3 of down + residual
-        bool okd = true;
+        // ---------------- D: rows 32j..32j+31 of Wd[:, DCOLS g : DCOLS (g + 1)] . a (plus x' for
+        // g = 0) -> added to the sums of x''; only the group's own slice of a is polled
         for (int b = 0; b < B; ++b) {
-            u32x4 c[3];                   // a[1024 k + 4t .. 4t + 3], k < 3
-            okd = poll_own<3>(A + (size_t)b * W_A, W_A, Contig{}, c, p.err) && okd;
-            float s[2] = {0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                f32x4 lo, hi;
-                pair8(__builtin_bit_cast(f32x4, c[k]), lo, hi);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) s[i] += dot8v(pf[2 * k + i], lo, hi);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) sm.u.r.rd[b][2 * (tid & 1) + i][tid >> 1] = s[i];
+            if (!poll<1>(A + (size_t)b * W_A, W_A, [&](int i) { return (size_t)DCOLS * g + 4 * i; }, DCOLS / 4,
+                         sm.u.s.act[b], p.err))
+                return;
         }
-        if (!__syncthreads_and(okd)) return;
         trace_at(p, sm, tslot++);
-        {
-            const int rr = tid >> 6, sub = tid & 63;   // wave rr adds row 4w + rr
-            const int n = 4 * w + rr;
-            for (int b = 0; b < B; ++b) {
-                const f32x2 q = reinterpret_cast<const f32x2*>(sm.u.r.rd[b][rr])[sub];
-                const float s = wave_sum(q[0] + q[1]);
-                if (sub == 0) put(Xn + (size_t)b * W_X + n, sm.xr[b][rr] + s);
-            }
-        }
+        down_partial(sm, pf, Xn, g, j, B);
         if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
         else pre.nw = ldf4(p.final_norm + 4 * tid);
         trace_at(p, sm, tslot++);
@@ -1011,11 +1032,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     load_rows(r0 + 16, b1);
     {
         const float* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
+        bool okl = true;
         for (int b = 0; b < B; ++b) {
-            if (!poll<1>(Xl + (size_t)b * W_X, W_X, Contig{}, D / 4, sm.u.s.act[b], p.err)) return;
-            norm_own(sm, b, *reinterpret_cast<const f32x4*>(&sm.u.s.act[b][4 * tid]), pre.nw);
+            u32x4 c[2];
+            okl = poll_own<2>(Xl + (size_t)b * W_X, W_X, FxPair{}, c, p.err, FxComplete{}) && okl;
+            norm_own(sm, b, fx_vec4(c), pre.nw);
         }
-        __syncthreads();
+        if (!__syncthreads_and(okl)) return;
         trace_at(p, sm, tslot++);
     }
     float rn[BMAX];
@@ -1081,8 +1104,8 @@ size_t decode_mega_exchange_words_per_layer() {
 // blocks b < B: amax[b] = max over the 256 workgroup candidates of row b (packed logit
 // key | ~id), lens[seq_base + b] += 1 and, when greedy_out is given, the greedy token
 // (Step 8's argmax, lowest id on ties); all blocks: the initial state back into every
-// exchange word the launch may have written -- per layer, rows < B of x, q/k/v, the x'
-// sums (zero) and a, and pt_words words of chunk partials per row -- with coherent stores.
+// exchange word the launch may have written -- per layer, rows < B of the x and x' sums
+// (zero), q/k/v and a, and pt_words words of chunk partials per row -- with coherent stores.
 __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
                             int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words,
                             int32_t* __restrict__ greedy_out) {
@@ -1118,18 +1141,18 @@ __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax
         else if (kind == 3) { off += BMAX * (W_X + W_QKV + W_P) + (size_t)b * W_A; cnt = (int)W_A; }
         else { off += BMAX * (W_X + W_QKV + W_P + W_A) + (size_t)b * W_PT; cnt = pt_words; }
         for (int i = 4 * threadIdx.x; i < cnt; i += 4 * blockDim.x)
-            __builtin_amdgcn_raw_buffer_store_b128(kind == 2 ? zv : sv, rs, (int)((off + i) * 4), 0, SC1);
+            __builtin_amdgcn_raw_buffer_store_b128(kind == 0 || kind == 2 ? zv : sv, rs, (int)((off + i) * 4), 0, SC1);
     }
 }
 
-// Initial state of the exchange words: the sentinel, and zero in the O-projection sums.
+// Initial state of the exchange words: the sentinel, and zero in the x and x' sums.
 __global__ void k_mega_fill(float* ex, size_t words, size_t ex_layer) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)ex, (short)0, (int)(words * 4), 0x00020000);
     const u32x4 sv = {SENT, SENT, SENT, SENT}, zv = {0u, 0u, 0u, 0u};
     constexpr size_t p0 = BMAX * (W_X + W_QKV), p1 = p0 + BMAX * W_P;
     for (size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x); i < words; i += 4 * (size_t)gridDim.x * blockDim.x) {
         const size_t o = i % ex_layer;
-        __builtin_amdgcn_raw_buffer_store_b128(o >= p0 && o < p1 ? zv : sv, rs, (int)(i * 4), 0, SC1);
+        __builtin_amdgcn_raw_buffer_store_b128(o < BMAX * W_X || (o >= p0 && o < p1) ? zv : sv, rs, (int)(i * 4), 0, SC1);
     }
 }
 
