@@ -326,7 +326,8 @@ struct Smem {
     float o[BMAX][2 * DH];         // attention output of the group, per row
     float att[2][PART];            // merged attention state (max, sum, acc) per head
     __attribute__((aligned(16))) float sp[STAGE][2];   // scores, then probabilities (key, head)
-    float hs[2][4], wl[2][4];      // per-wave softmax maximum and sum of each head
+    __attribute__((aligned(16))) float hs[2][4];   // per-wave softmax maximum of each head
+    __attribute__((aligned(16))) float wl[2][4];   // per-wave softmax sum of each head
     float gu[24][BMAX];            // gate/up results
     float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
     MegaLayer layers[kMegaMaxLayers];
@@ -650,14 +651,19 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
     __syncthreads();
     {
         const int h = tid >> 7, dd = tid & 127;
+        // the four waves' states read at once (read one by one under their conditions, they
+        // were a chain of dependent shared-memory round trips)
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(sm.hs[h]);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(sm.wl[h]);
         float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, sm.wl[h][w2] > 0.f ? sm.hs[h][w2] : -INFINITY);
+        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, lv[w2] > 0.f ? hv[w2] : -INFINITY);
         float cw[4], L = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
-            cw[w2] = sm.wl[h][w2] > 0.f ? __builtin_amdgcn_exp2f(sm.hs[h][w2] - M) : 0.f;
-            L += sm.wl[h][w2] * cw[w2];
+            const float e = __builtin_amdgcn_exp2f(hv[w2] - M);   // 0 for a wave without keys
+            cw[w2] = lv[w2] > 0.f ? e : 0.f;
+            L += lv[w2] * cw[w2];
         }
         float av[16];
 #pragma unroll
