@@ -109,6 +109,9 @@ __device__ __forceinline__ float dot_chunks(const u32x4* w, const float* x, int 
         a[2 * i] = src[0];
         a[2 * i + 1] = src[1];
     }
+    // (left to itself the scheduler pairs the reads with their products, one round trip per
+    // pair)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * N, 0);
     float part[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -988,12 +991,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 const int rr = tid >> 3, sub = tid & 7;
                 for (int b = 0; b < B; ++b) {
                     const f32x4* src = reinterpret_cast<const f32x4*>(sm.u.r.rd[b][rr]);
+                    f32x4 q[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) q[i] = src[sub + 8 * i];
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // all four reads first
                     float s = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const f32x4 q = src[sub + 8 * i];
-                        s += (q[0] + q[1]) + (q[2] + q[3]);
-                    }
+                    for (int i = 0; i < 4; ++i) s += (q[i][0] + q[i][1]) + (q[i][2] + q[i][3]);
                     s = sum8(s);
                     if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b);
                 }
