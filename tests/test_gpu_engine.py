@@ -119,3 +119,27 @@ def test_nonfinite_weight_raises_numeric_error(path):
         eng.sync()
     assert e.value.code == -8
     eng.close()
+
+
+@pytest.mark.parametrize("path", [1, 3])
+@pytest.mark.parametrize("name", ["model.layers.0.self_attn.o_proj.weight", "model.layers.0.mlp.down_proj.weight"])
+def test_nonfinite_projection_in_decode(path, name):
+    """The same through the decode step alone (no prefill, so nothing else can report it
+    first): a +inf row in the O projection or in the down projection -- the two sums the
+    persistent kernel carries as fixed-point words -- must surface as non-finite logits."""
+    import torch
+    from decoder_only_amd import q3
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16", n_layers=1)
+    ws = dict(synth.make_weights(w))
+    wt = ws[name].copy()
+    wt[0, :] = 0x7F80                                        # bf16 +inf
+    ws[name] = wt
+    eng = q3.Engine(q3.config(w, 1, 16), ws)
+    eng.set_decode_path(path)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(q3.Q3Error) as e:
+        eng.decode_step(tok)
+        eng.sample(tok, 0.0)
+        eng.sync()
+    assert e.value.code == -8
+    eng.close()
