@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from e2e import failures, run_ragged, run_single
+from e2e import failures, run_continuous, run_ragged, run_single
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,17 @@ def test_toy_bf16_ragged_batch(path, lens):
     w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
     stats = run_ragged(w, list(lens), 6, decode_path=path)
     _report(stats)
+    assert not failures(stats), failures(stats)[:5]
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_toy_bf16_continuous_batching(path):
+    """Sequences retired and admitted between decode steps, prompts prefilled in two calls
+    (the second into a non-empty cache), each slot checked against its own oracle run."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_continuous(w, 8, decode_path=path)
+    _report(stats)
+    assert len(stats) == 3 + 1 + 8 * 3
     assert not failures(stats), failures(stats)[:5]
 
 
