@@ -143,20 +143,22 @@ def run_ragged(w: synth.Workload, prompt_lens: List[int], steps: int, decode_pat
     return stats
 
 
-def run_continuous(w: synth.Workload, steps: int, decode_path: int = 0) -> List[StepStat]:
+def run_continuous(w: synth.Workload, steps: int, decode_path: int = 0, scale: int = 1) -> List[StepStat]:
     """Continuous batching on three sequence slots decoded together (greedy, teacher-forced):
     slot 0 holds a 7-token prompt; slot 2 an 11-token prompt prefilled in two calls (4 then
     7 tokens, the second one into a non-empty cache); slot 1 a 3-token prompt that is
     retired after 3 decode steps (q3_reset), its slot then admitting a new 5-token prompt,
     again prefilled in two calls (2 + 3), while the other slots keep decoding. Every slot's
     logits -- after each prefill and at every step -- are compared with an oracle run of
-    that sequence alone, its prompt in one call."""
+    that sequence alone, its prompt in one call. `scale` multiplies every prompt length and
+    split point (at 40 and more, the prompts take the matrix-core prefill path, the second
+    call of a split one attending to the first call's cache)."""
     import torch
     from decoder_only_amd import q3
 
     weights = synth.make_weights(w)
     B, retire_at = 3, 3
-    max_seq = 11 + steps + 1
+    max_seq = 11 * scale + steps + 1
     model = oracle.Model(oracle.Config.from_workload(w), weights)
     announce("e2e continuous", w.name, w.weight_dtype, steps, decode_path)
     eng = q3.Engine(q3.config(w, B, max_seq), weights)
@@ -175,16 +177,17 @@ def run_continuous(w: synth.Workload, steps: int, decode_path: int = 0) -> List[
         stats.append(compare(tag, slot, one[0].cpu().numpy(), ref))
         return cache, ref, len(prompt)
 
-    state = [admit(0, synth.prompt_tokens(w, 7, seq=0), 0, -1),
-             admit(1, synth.prompt_tokens(w, 3, seq=1), 0, -1),
-             admit(2, synth.prompt_tokens(w, 11, seq=2), 4, -1)]
+    k = scale
+    state = [admit(0, synth.prompt_tokens(w, 7 * k, seq=0), 0, -1),
+             admit(1, synth.prompt_tokens(w, 3 * k, seq=1), 0, -1),
+             admit(2, synth.prompt_tokens(w, 11 * k, seq=2), 4 * k, -1)]
     logits = torch.empty(B, w.vocab, dtype=torch.float32, device="cuda")
     toks = torch.empty(B, dtype=torch.int32, device="cuda")
     for step in range(steps):
         if step == retire_at:
             eng.reset(1)
             assert eng.seq_len(1) == 0
-            state[1] = admit(1, synth.prompt_tokens(w, 5, seq=3), 2, step)
+            state[1] = admit(1, synth.prompt_tokens(w, 5 * k, seq=3), 2 * k, step)
         nxt = [int(np.argmax(ref)) for _, ref, _ in state]
         toks.copy_(torch.tensor(nxt, dtype=torch.int32))
         eng.decode_step(toks, None, logits)

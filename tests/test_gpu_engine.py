@@ -94,12 +94,13 @@ def test_toy_bf16_ragged_batch(path, lens):
     assert not failures(stats), failures(stats)[:5]
 
 
-@pytest.mark.parametrize("path", [1, 2, 3])
-def test_toy_bf16_continuous_batching(path):
+@pytest.mark.parametrize("path,scale", [(1, 1), (2, 1), (3, 1), (3, 40)])
+def test_toy_bf16_continuous_batching(path, scale):
     """Sequences retired and admitted between decode steps, prompts prefilled in two calls
-    (the second into a non-empty cache), each slot checked against its own oracle run."""
+    (the second into a non-empty cache), each slot checked against its own oracle run;
+    scale 40: prompts of 80 to 440 tokens on the matrix-core prefill path."""
     w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
-    stats = run_continuous(w, 8, decode_path=path)
+    stats = run_continuous(w, 8, decode_path=path, scale=scale)
     _report(stats)
     assert len(stats) == 3 + 1 + 8 * 3
     assert not failures(stats), failures(stats)[:5]
