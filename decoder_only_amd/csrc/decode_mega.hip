@@ -308,7 +308,7 @@ constexpr int LONG_T = 8192;     // contexts above this take the long variant of
 struct Smem {
     union {
         struct {
-            float act[BMAX][D];            // normed x of the LM head
+            float act[BMAX][D];            // normed x of the LM head; phase D: the polled slice of a
             float part[MAXCH * 2 * PART];  // polled chunk partials (long context combine)
             float wm[16][2][PART];         // attention state per (wave, 16-lane key group)
         } s;
