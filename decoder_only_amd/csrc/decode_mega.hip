@@ -295,10 +295,6 @@ struct FxPair {   // thread t's chunks k = 0, 1: the sums 4t .. 4t+3 (chunk i = 
     __device__ __forceinline__ size_t operator()(int i) const { return (size_t)8 * (i % NT) + 4 * (i / NT); }
 };
 
-struct Contig {   // chunk i at word 4 i
-    __device__ __forceinline__ size_t operator()(int i) const { return (size_t)4 * i; }
-};
-
 constexpr int TRACE_MAX = 400;   // phase timestamps kept per traced workgroup
 constexpr int STAGE = 256;       // K/V rows of the staging area
 constexpr int SHOT = 240;        // cached rows staged per shot (the new key follows them)
