@@ -1010,15 +1010,24 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 
         // ---------------- D: rows 32j..32j+31 of Wd[:, DCOLS g : DCOLS (g + 1)] . a (plus x' for
         // g = 0) -> added to the sums of x''; only the group's own slice of a is polled
-        bool okd = true;
-        for (int b = 0; b < B; ++b) {
+        if constexpr (MODE == 0) {
             // two reads in flight per chunk; threads past the 96 chunks poll duplicates
-            u32x4 c[1];
-            okd = poll_own<1>(A + (size_t)b * W_A, W_A,
-                              [&](int i) { return (size_t)DCOLS * g + 4 * (i % (DCOLS / 4)); }, c, p.err) && okd;
-            if (tid < DCOLS / 4) *reinterpret_cast<u32x4*>(&sm.u.s.act[b][4 * tid]) = c[0];
+            // (measured faster here, slower in the split-K instances)
+            bool okd = true;
+            for (int b = 0; b < B; ++b) {
+                u32x4 c[1];
+                okd = poll_own<1>(A + (size_t)b * W_A, W_A,
+                                  [&](int i) { return (size_t)DCOLS * g + 4 * (i % (DCOLS / 4)); }, c, p.err) && okd;
+                if (tid < DCOLS / 4) *reinterpret_cast<u32x4*>(&sm.u.s.act[b][4 * tid]) = c[0];
+            }
+            if (!__syncthreads_and(okd)) return;
+        } else {
+            for (int b = 0; b < B; ++b) {
+                if (!poll<1>(A + (size_t)b * W_A, W_A, [&](int i) { return (size_t)DCOLS * g + 4 * i; }, DCOLS / 4,
+                             sm.u.s.act[b], p.err))
+                    return;
+            }
         }
-        if (!__syncthreads_and(okd)) return;
         trace_at(p, sm, tslot++);
         down_partial(sm, pf, Xn, g, j, B);
         if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
