@@ -5,7 +5,9 @@
   residuals, QK-norm before RoPE and per head, GQA map, tied head, SwiGLU);
   run with non-unit RMSNorm weights so a dropped or swapped norm weight shows;
 * invariants: KV-cached decode equals full recomputation; causal prefix
-  invariance; batched independent rows equal single-sequence runs.
+  invariance; batched independent rows equal single-sequence runs, and the
+  batched decode (``forward_batch``, the oracle of the batched workload) equals the
+  pinned single-sequence ``forward`` row by row.
 """
 import numpy as np
 import pytest
@@ -136,3 +138,44 @@ def test_embedding_row_and_tied_head():
     got = model.forward([tok], model.new_cache(1), 0)
     h = E[tok] / np.sqrt(np.mean(E[tok] ** 2) + 1e-6)
     assert np.allclose(got, E @ h, rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("kv_bf16", [False, True])
+def test_forward_batch_equals_forward_per_sequence(kv_bf16):
+    """forward_batch writes its own block loop; pin it to forward() (pinned above against
+    the transformers model) on identical caches. Non-unit norm weights (a dropped or
+    swapped norm weight shows) and positions unequal to the cache lengths (a position
+    taken from the length, or from another row, shows)."""
+    w, cfg = _toy(kv_bf16=kv_bf16)
+    weights = _random_norm_weights(synth.make_weights(w), seed=5)
+    model = oracle.Model(cfg, weights)
+    prompts = [synth.prompt_tokens(w, n, seq=b) for b, n in enumerate((4, 7, 2, 5))]
+    nxt = np.array([5, 4000, 123, 8191])
+    pos = np.array([len(p) for p in prompts]) + np.array([3, 0, 250, 41])
+    batch_caches, single_caches = [], []
+    for p in prompts:
+        for lst in (batch_caches, single_caches):
+            c = model.new_cache(16)
+            model.forward(p, c, 0)
+            lst.append(c)
+    got = model.forward_batch(nxt, batch_caches, pos)
+    for b in range(len(prompts)):
+        want = model.forward([int(nxt[b])], single_caches[b], int(pos[b]))
+        rel = np.linalg.norm(got[b] - want) / np.linalg.norm(want)
+        # fp32 cache: summation order only (~1e-6); bf16 cache: plus rare 1-ulp rounding flips
+        # of K/V entries (one ulp is 2^-6 at magnitudes in [2, 4))
+        assert rel <= (1e-5 if not kv_bf16 else 1e-3), (b, rel)
+        n = batch_caches[b].length
+        for a, c in ((batch_caches[b].K, single_caches[b].K), (batch_caches[b].V, single_caches[b].V)):
+            assert np.allclose(a[:, :, :n], c[:, :, :n], rtol=0, atol=2e-5 if not kv_bf16 else 2.0 ** -6)
+        assert batch_caches[b].length == single_caches[b].length
+    # the same rows with the positions of two rows swapped must differ (positions reach RoPE)
+    swapped = pos.copy()
+    swapped[[0, 2]] = swapped[[2, 0]]
+    caches2 = []
+    for p in prompts:
+        c = model.new_cache(16)
+        model.forward(p, c, 0)
+        caches2.append(c)
+    other = model.forward_batch(nxt, caches2, swapped)
+    assert np.linalg.norm(other[0] - got[0]) > 1e-3 * np.linalg.norm(got[0])
