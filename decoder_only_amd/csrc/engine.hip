@@ -752,8 +752,10 @@ extern "C" q3_status q3_sync(q3_engine* e) {
     HIPCHK(e, hipMemcpyAsync(e->d_err, &zero, 4, hipMemcpyHostToDevice, e->stream));
     HIPCHK(e, hipStreamSynchronize(e->stream));
     if (flags & Q3_DEVERR_SYNC) {
-        // a wait timed out and every workgroup left the kernel; later launches carry new tags,
-        // so nothing needs resetting
+        // a wait timed out and every workgroup left the kernel. The tail kernel that follows
+        // every launch has put the sentinel / zero back into the hand-over words, so later
+        // launches start clean; the rows of that step are not: their lengths advanced while
+        // the layers after the wait never appended K/V (q3.h asks the caller to reset them)
         return e->fail(Q3_ERR_HIP, "persistent decode kernel: a cross-workgroup wait timed out");
     }
     if (flags & Q3_DEVERR_TOKEN) return e->fail(Q3_ERR_TOKEN, "a token id outside [0, vocab) reached the device");

@@ -90,7 +90,7 @@ typedef struct {
 q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int32_t n_weights,
                   void* stream, q3_engine** out);
 
-/* Prefill (Step 9, "process all input tokens at once"): append the n tokens
+/* Prefill (Step 9: every prompt token in one call): append the n tokens
  * `tokens` (device int32 [n]) to sequence slot `seq`, at positions
  * len(seq) .. len(seq)+n-1 where len(seq) is the slot's current cache length,
  * running every layer and writing their K/V. If `logits` is not NULL it receives
@@ -102,8 +102,8 @@ q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens, int32_t n
 
 /* One decode step (Step 9's loop body) for `batch` independent sequences: row b
  * is sequence slot b, fed the token tokens[b] (device int32 [batch]) at RoPE
- * position positions[b] (device int32 [batch]; NULL: each slot's current length,
- * the article's pos = len(ids) - 1). The new K/V are written at slot index
+ * position positions[b] (device int32 [batch]; NULL: each slot's current length, which
+ * is Step 9's position rule for the newest token). The new K/V are written at slot index
  * len(b), which then grows by one. Logits of all rows go to `logits` (device
  * float32 [batch, vocab]) if not NULL, and are kept as the engine's current logits.
  * Errors: Q3_ERR_ARG (batch outside [1, max_batch]), Q3_ERR_CAPACITY. */
@@ -137,7 +137,13 @@ q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k,
 int32_t q3_seq_len(const q3_engine* e, int32_t seq);
 
 /* Wait for the engine's stream; report (and clear) the sticky device error word:
- * Q3_ERR_TOKEN or Q3_ERR_NUMERIC, else Q3_OK (or Q3_ERR_HIP on a runtime error). */
+ * Q3_ERR_TOKEN or Q3_ERR_NUMERIC, else Q3_OK (or Q3_ERR_HIP on a runtime error).
+ * Q3_ERR_HIP with the text "a cross-workgroup wait timed out" means a persistent decode
+ * launch gave up waiting (its workgroups were not all resident, e.g. under an ordinary
+ * launch on a shared GPU): the layers after the wait did not run, yet the lengths of the
+ * rows of that step advanced, so the KV cache of every sequence decoded since the
+ * previous successful q3_sync is undefined and must be q3_reset before reuse. The
+ * engine itself (its hand-over words) is restored and stays usable. */
 q3_status q3_sync(q3_engine* e);
 
 /* Text describing the last error on this engine (never NULL). */
@@ -166,7 +172,9 @@ q3_status q3_profile_end(q3_engine* e, double* total_ms, int64_t* launches, doub
 /* How decode rows run ("The pipeline at a glance": one forward pass per new token).
  * 0 (default): one cooperative launch per decode step (every layer, the LM head and the
  * argmax in a single persistent kernel whose 256 workgroups hand values to each other
- * through tagged words in device memory) when the model has the Qwen3-0.6B layer shape
+ * through device-memory words that hold a "not written" sentinel until their producer
+ * stores them, and through fixed-point sums whose top bits count the arrived
+ * contributions; a small tail kernel after every launch restores those words) when the model has the Qwen3-0.6B layer shape
  * (hidden 1024, 16/8 heads of 128, FFN 3072) with bf16 weights and cache, the GPU has
  * 256 compute units and the step has at most 4 rows; else one launch per operation.
  * 1: always one launch per operation. 2: always the persistent kernel (Q3_ERR_STATE if
