@@ -1,5 +1,6 @@
 // Op-level C ABI (include/q3_ops.h): one kernel family per call, on caller buffers.
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -111,6 +112,69 @@ extern "C" q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, flo
     void* ws = (char*)sc.p + amax_bytes + 256;
     hipError_t e = hipMemsetAsync(err, 0, 4, s);
     if (e == hipSuccess) e = launch_argmax_rows(logits, amax, V, B, err, s);
+    if (e == hipSuccess) e = launch_sample(logits, amax, V, B, temperature, top_p, uniforms, tokens_out, ws, false, s);
+    return st(e);
+}
+
+// ---------------------------------------------------------------------------------
+// Sampling without allocation: the same kernels as q3_op_sample, with their scratch
+// (per-row argmax words, an error word, the per-row selection workspace) in a file-scope
+// device array instead of memory allocated per call. Each GPU the library runs on holds
+// its own copy of the array, at its own address, until the process ends.
+// ---------------------------------------------------------------------------------
+namespace {
+
+constexpr int kNoAllocRows = Q3_SAMPLE_NOALLOC_MAX_ROWS;
+constexpr int kNoAllocVocab = Q3_SAMPLE_NOALLOC_MAX_VOCAB;
+constexpr size_t kNoAllocHeader = 256;   // [0, 32): argmax word per row; [32, 40): error word
+// Selection workspace per row: a 65,536-bucket histogram, 264 words of group sums and state,
+// and one word per vocabulary entry (the sampler's layout; checked against
+// sample_workspace_bytes at every call).
+constexpr size_t kNoAllocWsBytes = (size_t)kNoAllocRows * (65536 + 264 + (size_t)kNoAllocVocab) * 8;
+constexpr size_t kNoAllocBytes = kNoAllocHeader + kNoAllocWsBytes;
+static_assert(kNoAllocRows * 8 <= 32, "argmax words fit the header");
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` on each device
+
+// Device address of this device's copy of `scratch`; looked up once per device, with that
+// device current (in host code the array's name is only a stand-in, never an address).
+q3_status scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q3_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return Q3_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return Q3_OK;
+}
+
+}  // namespace
+
+extern "C" q3_status q3_op_sample_noalloc(const float* logits, int32_t B, int32_t V, float temperature, float top_p,
+                                          const float* uniforms, int32_t* tokens_out, void* stream) {
+    if (!logits || !tokens_out || B < 0 || V <= 0 || !(temperature >= 0.f)) return Q3_ERR_ARG;
+    if (temperature > 0.f && !uniforms) return Q3_ERR_ARG;
+    if (B > kNoAllocRows || V > kNoAllocVocab || sample_workspace_bytes(V, B) > kNoAllocWsBytes)
+        return Q3_ERR_SHAPE;
+    if (B == 0) return Q3_OK;
+    void* base = nullptr;
+    if (q3_status s0 = scratch_address(&base); s0 != Q3_OK) return s0;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned long long* amax = (unsigned long long*)base;
+    unsigned long long* err = (unsigned long long*)((char*)base + 32);
+    void* ws = (char*)base + kNoAllocHeader;
+    // the error word starts at zero (a fill kernel, not a memset: safe under graph capture);
+    // the selection workspace is cleared by launch_sample itself (ws_zeroed = false), and
+    // launch_argmax_rows clears the argmax words
+    hipError_t e = launch_fill_u64(err, 0ull, 1, s);
+    if (e == hipSuccess) e = launch_argmax_rows(logits, amax, V, B, (unsigned*)err, s);
     if (e == hipSuccess) e = launch_sample(logits, amax, V, B, temperature, top_p, uniforms, tokens_out, ws, false, s);
     return st(e);
 }

@@ -26,7 +26,7 @@ EXPORTS = [
     "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
-    "q3_op_attn_prefill", "q3_op_sample",
+    "q3_op_attn_prefill", "q3_op_sample", "q3_op_sample_noalloc",
 ]
 GEMV_STORE, GEMV_RESID, GEMV_SWIGLU = 0, 1, 2
 PROF_DECODE_STEP, PROF_GEMV, PROF_LMHEAD, PROF_ATTN_DECODE, PROF_GEMM, PROF_ATTN_PREFILL = range(6)
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_op_attn_decode": ([vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, vp, vp], i32),
         "q3_op_attn_prefill": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp], i32),
         "q3_op_sample": ([vp, i32, i32, f32, f32, vp, vp, vp], i32),
+        "q3_op_sample_noalloc": ([vp, i32, i32, f32, f32, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -299,3 +300,12 @@ def op_sample(logits, temperature: float, top_p: float, uniforms, out) -> None:
     _check(load_library().q3_op_sample(_ptr(logits, torch.float32), B, V, float(temperature), float(top_p),
                                        _ptr(uniforms, torch.float32), _ptr(out, torch.int32), _stream()),
            "q3_op_sample")
+
+
+def op_sample_noalloc(logits, temperature: float, top_p: float, uniforms, out) -> None:
+    """q3_op_sample without allocation (library-owned scratch; at most 4 rows of 262144)."""
+    import torch
+    B, V = logits.shape
+    _check(load_library().q3_op_sample_noalloc(_ptr(logits, torch.float32), B, V, float(temperature),
+                                               float(top_p), _ptr(uniforms, torch.float32),
+                                               _ptr(out, torch.int32), _stream()), "q3_op_sample_noalloc")

@@ -81,6 +81,19 @@ q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache, const uint
 q3_status q3_op_sample(const float* logits, int32_t B, int32_t V, float temperature, float top_p,
                        const float* uniforms, int32_t* tokens_out, void* stream);
 
+/* The same sampling with no memory allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no hipMalloc, hipFree or allocating library call is made. The scratch
+ * memory lives in a fixed device array of the library (about 10.5 MB, held on each GPU
+ * the library runs on until the process ends), so B <= Q3_SAMPLE_NOALLOC_MAX_ROWS and
+ * V <= Q3_SAMPLE_NOALLOC_MAX_VOCAB; larger calls return Q3_ERR_SHAPE before anything is
+ * enqueued. Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (other streams, other threads) race and must be serialised by the caller. */
+#define Q3_SAMPLE_NOALLOC_MAX_ROWS 4
+#define Q3_SAMPLE_NOALLOC_MAX_VOCAB 262144
+q3_status q3_op_sample_noalloc(const float* logits, int32_t B, int32_t V, float temperature, float top_p,
+                               const float* uniforms, int32_t* tokens_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
