@@ -18,10 +18,14 @@
 // 8 column blocks, are summed in memory instead: 64-bit fixed-point words with
 // device-scope atomic adds, whose top bits count the arrivals. On MI355X one all-to-all
 // hand-over among 256 workgroups takes ~2 us this way (~1 us within a group of 32), so the
-// layout below is built around four per layer, one of them group-local.
+// layout below is built around four per layer, two of them group-local. Workgroup w is
+// (g, j) = (w % 8, w / 8): the dispatcher places workgroup w on XCD w % 8, so each kv
+// group's 32 workgroups share one XCD and its L2, and the group-local words are stored
+// with workgroup scope (they stay in that L2) instead of being written through to memory.
 //
 // Per layer, for each row b (hand-overs marked ->):
-//   A  poll the x sums (1024) -> RMSNorm -> 16 rows of [Wq;Wk;Wv]       -> QKV words
+//   A  poll the x sums (1024) -> RMSNorm -> 16 of the 512 rows of [Wq;Wk;Wv] that kv
+//      group g needs                                                  -> QKV words
 //   B  workgroup (g, j), kv group g = query heads 2g, 2g+1, j < 32: poll the group's
 //      q/k/v (512) -> QK-norm + RoPE -> KV append (j == 0) -> attention of both heads,
 //      recomputed by the 32 workgroups of the group (K/V staged through LDS) -> rows
@@ -29,7 +33,7 @@
 //      (long context: split-K partials per (group, chunk), merged again by every
 //       workgroup of the group, then the same O-projection partial)
 //   C  poll the x' sums (1024, complete when all 8 groups added) -> RMSNorm -> gate/up
-//      rows of 12 SwiGLU columns                                       -> A words
+//      rows of 12 SwiGLU columns in group g's block 384g .. 384g+383   -> A words
 //   D  workgroup (g, j): poll a[384g .. 384g+383] (written by the 32 workgroups of group
 //      g in C) -> rows 32j..32j+31 of Wd[:, 384g:384g+384] . a, plus x' for g = 0
 //                                                                     -> added to x'' sums
@@ -78,13 +82,18 @@ __device__ __forceinline__ int fresh(int v) {
     return v;
 }
 
-__device__ __forceinline__ void put(float* p, float v) {
+// A hand-over word whose consumers all run on the producer's XCD (workgroups w with the
+// same w % 8 share one XCD and its L2): a workgroup-scope store stays in that L2, where the
+// consumers' agent-coherent loads find it; it is invisible to other XCDs. Measured on
+// MI355X: a round trip between two workgroups of one XCD takes ~0.93 us this way against
+// ~1.32 us with agent-scope stores, which write through to memory. Issued as a plain vector
+// store: the compiler's own store would make it wait for the store to complete before the
+// data register is reused (a memory round trip per hand-over); the hardware reads a dword
+// store's data at issue.
+__device__ __forceinline__ void put_xcd(float* p, float v) {
     unsigned u = __float_as_uint(v);
     if (u == SENT) u = 0x7FC00000u;      // keep real NaNs distinguishable from "not written"
-    // Issued as a plain agent-coherent vector store: the compiler's own store would make it
-    // wait for the store to complete before the data register is reused (a full memory
-    // round trip per hand-over); the hardware reads a dword store's data at issue.
-    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(u) : "memory");
+    asm volatile("global_store_dword %0, %1, off sc0" ::"v"(p), "v"(u) : "memory");
 }
 
 // 8 bf16 (one 16-byte chunk) dotted with 8 floats.
@@ -716,16 +725,25 @@ __device__ __forceinline__ void pf_oproj(const MegaLayer& L, u32x4* pf, int g, i
 
 // Rows of phase C: rr < 12 the gate rows of the workgroup's 12 SwiGLU columns, then their
 // 12 up rows.
+__device__ __forceinline__ int gu_col0(int w) { return DCOLS * (w & 7) + 12 * (w >> 3); }
 __device__ __forceinline__ int gu_row(int w, int rr) {
-    const int col = 12 * w + (rr < 12 ? rr : rr - 12);
+    const int col = gu_col0(w) + (rr < 12 ? rr : rr - 12);
     return 32 * (col >> 4) + (col & 15) + (rr < 12 ? 0 : 16);
+}
+
+// First of the 16 rows of [Wq;Wk;Wv] that workgroup w projects in phase A: rows 16j ..
+// 16j + 15 of its kv group g's 512 (query heads 2g, 2g + 1, key head g, value head g), so
+// the q/k/v hand-over stays among the 32 workgroups of the group, on one XCD.
+__device__ __forceinline__ int qkv_row0(int w) {
+    const int g = w & 7, r = 16 * (w >> 3);
+    return r < 2 * DH ? 2 * DH * g + r : (r < 3 * DH ? HQ * DH + DH * g + (r - 2 * DH) : (HQ + HKV) * DH + DH * g + (r - 3 * DH));
 }
 
 // Phases A, C, D: thread t polls 4 consecutive columns; with its pair lane t ^ 1 it holds
 // the 8 columns 8 (t >> 1) .. + 7 (pair8), and it owns half of the phase's rows
 // (by t & 1) at those columns: one 16-byte chunk per row.
 __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
-    const bf16* base = L.wqkv + (size_t)(16 * w + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
+    const bf16* base = L.wqkv + (size_t)(qkv_row0(w) + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) pf[i] = ldw16(base + (size_t)i * D);
     pre.nw = ldf4(L.in_norm + 4 * threadIdx.x);
@@ -776,7 +794,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     const int B = p.B;
     u32x4 pf[16];
     Pre pre;
-    const int g = w >> 5, j = w & 31;       // kv group and row block of phase B
+    // kv group and row block: the 32 workgroups of group g are those with w % 8 == g, which
+    // the dispatcher places on XCD g (workgroup w runs on XCD w % 8)
+    const int g = w & 7, j = w >> 3;
 
     // layer table into shared memory (scalar loads would hold up every later LDS wait)
     {
@@ -851,7 +871,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 const f32x4 q0 = src[sub], q1 = src[sub + 16];
                 float s = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
                 s = sum16(s) * norm_scale(p, sm, b);
-                if (sub == 0) put(QKV + (size_t)b * W_QKV + 16 * w + r, s);
+                if (sub == 0) put_xcd(QKV + (size_t)b * W_QKV + qkv_row0(w) + r, s);
             }
         }
         pf_oproj(L, pf, g, j);
@@ -895,7 +915,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     if (b == 0) trace_at(p, sm, tslot++);
                     attend<LONG>(p, sm, hb, k0, k1, T, nullptr);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
-                    for (int e = tid; e < 2 * PART; e += NT) put(pt + e, sm.att[e / PART][e % PART]);
+                    for (int e = tid; e < 2 * PART; e += NT) put_xcd(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
                     pf_gu<0, 4>(L.wgu, pf, w);
@@ -1002,7 +1022,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             if (tid < 12 * B) {
                 const int c = tid % 12, b = tid / 12;
                 const float gt = sm.gu[c][b], up = sm.gu[12 + c][b];
-                put(A + (size_t)b * W_A + 12 * w + c, gt / (1.0f + expf(-gt)) * up);
+                put_xcd(A + (size_t)b * W_A + gu_col0(w) + c, gt / (1.0f + expf(-gt)) * up);
             }
         }
         pf_down(L, pf, g, j);
