@@ -743,6 +743,25 @@ extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, cons
     return Q3_OK;
 }
 
+extern "C" q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void* k, void* v, int32_t len) {
+    if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
+    const q3_config& c = e->cfg;
+    if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !k || !v || len < 0)
+        return e->fail(Q3_ERR_ARG, "bad kv_export arguments");
+    if (len > e->h_len[seq]) return e->fail(Q3_ERR_ARG, "kv_export beyond the sequence's length");
+    const size_t eb = e->kvbytes(), row = (size_t)c.head_dim * eb;
+    for (int g = 0; g < c.n_kv_heads && len > 0; ++g) {
+        const size_t src = ((size_t)layer * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems +
+                            (size_t)g * c.max_seq * c.head_dim) * eb;
+        const size_t dst = (size_t)g * len * row;
+        HIPCHK(e, hipMemcpyAsync((char*)k + dst, (const char*)e->kc + src, len * row, hipMemcpyDefault, e->stream));
+        HIPCHK(e, hipMemcpyAsync((char*)v + dst, (const char*)e->vc + src, len * row, hipMemcpyDefault, e->stream));
+    }
+    HIPCHK(e, hipStreamSynchronize(e->stream));
+    return Q3_OK;
+}
+
 extern "C" q3_status q3_sync(q3_engine* e) {
     if (!e) return Q3_ERR_ARG;
     if (q3_status st = flush_tail(e); st != Q3_OK) return st;

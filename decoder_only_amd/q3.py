@@ -22,7 +22,7 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -4: "Q3_ERR_CAPACITY", -5: "Q3_ERR_OOM", -6: "Q3_ERR_HIP", -7: "Q3_ERR_STATE",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
-    "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import",
+    "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export",
     "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_sample": ([vp, vp, i32, f32, f32, vp, vp], i32),
         "q3_reset": ([vp, i32], i32),
         "q3_kv_import": ([vp, i32, i32, vp, vp, i32], i32),
+        "q3_kv_export": ([vp, i32, i32, vp, vp, i32], i32),
         "q3_seq_len": ([vp, i32], i32),
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
@@ -202,6 +203,17 @@ class Engine:
         kk = np.ascontiguousarray(k) if isinstance(k, np.ndarray) else k
         vv = np.ascontiguousarray(v) if isinstance(v, np.ndarray) else v
         _check(load_library().q3_kv_import(self._h, seq, layer, p(kk), p(vv), length), "q3_kv_import", self._h)
+
+    def kv_export(self, seq: int, layer: int, length: int):
+        """Slots 0 .. length-1 of one (sequence, layer) of the cache as two host arrays
+        [n_kv_heads, length, head_dim] (uint16 bf16 bit patterns, or float32)."""
+        c = self._cfg
+        dt = np.uint16 if c.kv_dtype == BF16 else np.float32
+        k = np.empty((c.n_kv_heads, length, c.head_dim), dtype=dt)
+        v = np.empty_like(k)
+        _check(load_library().q3_kv_export(self._h, seq, layer, k.ctypes.data, v.ctypes.data, length),
+               "q3_kv_export", self._h)
+        return k, v
 
     def seq_len(self, seq: int) -> int:
         return load_library().q3_seq_len(self._h, seq)

@@ -133,6 +133,13 @@ q3_status q3_reset(q3_engine* e, int32_t seq);
 q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k,
                        const void* v, int32_t len);
 
+/* Copy slots 0 .. len-1 of one (sequence, layer) of the KV cache out to k and v (host or
+ * device, kv_dtype, layout [n_kv_heads][len][head_dim]; caller-owned), the inverse of
+ * q3_kv_import: the keys as stored (after QK-norm and RoPE, Step 5) and the values.
+ * Waits for the engine's stream before returning. Errors: Q3_ERR_ARG (bad slot, layer or
+ * pointer, or len above the sequence's current length). */
+q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void* k, void* v, int32_t len);
+
 /* Current cache length of a sequence slot, as tracked by the host (-1 on error). */
 int32_t q3_seq_len(const q3_engine* e, int32_t seq);
 
