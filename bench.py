@@ -10,8 +10,9 @@ value = 128 * steps / (wall time of the timed steps).
 Also reported (one JSON line, under "extras"): the 2048-token prompt's prefill tokens/s and
 its 256 sampled decode steps, batch-64 decode tokens/s with 4096 pre-filled KV slots per
 sequence, the 32768-token prefill (GEMM and attention TFLOP/s) and its 512 sampled decode
-steps, each with its roofline fraction; the roofline of the dominant kernel (event-timed
-on the engine's stream), and the CPU oracle's decode rate on this host (a bounded sample).
+steps, each with its roofline fraction; a 262,136-token prefill and decode at ~262K cached
+slots; the roofline of the dominant kernel (event-timed on the engine's stream), and the CPU
+oracle on this host (a bounded sample of decode steps and one 2048-token prefill).
 """
 from __future__ import annotations
 
@@ -43,7 +44,8 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill and batch-64 lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-long", action="store_true", help="skip the 32768-token workload's engine")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 32768-token workload's engine and the 262K-context engine")
     ap.add_argument("--cooperative", action="store_true",
                     help="dispatch the persistent decode kernel as a cooperative launch (the engine's "
                          "default); by default the bench, which has the GPU to itself, uses an "
@@ -77,7 +79,7 @@ def main() -> int:
     t = time.time()
     weights = synth.make_weights(w)
     log(f"weights generated in {time.time() - t:.1f}s")
-    max_batch, max_seq = 64, 4160
+    max_batch, max_seq = 64, 4168      # batch-64 line: 4096 pre-filled + 2 warm-up + 64 timed + 2 profiled steps
     eng = q3.Engine(q3.config(w, max_batch, max_seq), weights)
     if not args.cooperative:
         eng.set_decode_path(3)
@@ -109,6 +111,19 @@ def main() -> int:
     value = n_dec * args.steps / elapsed
     ms_per_step = 1000.0 * elapsed / args.steps
     log(f"bs1 decode: {value:.1f} tok/s, {ms_per_step:.2f} ms per generation")
+    # the same generations with the other launch mode of the persistent kernel, for comparison
+    eng.set_decode_path(0 if not args.cooperative else 3)
+    generation()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        generation()
+    torch.cuda.synchronize()
+    other = n_dec * args.steps / (time.perf_counter() - t0)
+    eng.set_decode_path(3 if not args.cooperative else 0)
+    launch_mode = "cooperative" if args.cooperative else "ordinary"
+    other_mode = "ordinary" if args.cooperative else "cooperative"
+    log(f"bs1 decode with the {other_mode} launch: {other:.1f} tok/s")
 
     # Roofline of the dominant kernel, event-timed on the engine's stream over a second pass
     # of the same steps. With the persistent decode kernel (one launch per decode step) that
@@ -123,7 +138,8 @@ def main() -> int:
     gemv = eng.profile_end()
     step_gbs = step["bytes"] / (step["ms"] / 1e3) / 1e9
     step_us = 1e3 * step["ms"] / step["launches"]
-    extras = {"decode_step_us": round(step_us, 2), "decode_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)}
+    extras = {"decode_step_us": round(step_us, 2), "decode_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+              "bs1_launch": launch_mode, f"bs1_decode_tok_s_{other_mode}_launch": round(other, 2)}
     if gemv["launches"] == 0:
         roofline = {"kernel": "k_decode_mega (persistent decode step: all layers, LM head, argmax)",
                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -166,6 +182,10 @@ def main() -> int:
             extras.update(c5_lines(weights, q3, torch, synth))
         except Exception as ex:
             extras["c5_error"] = repr(ex)
+        try:
+            extras.update(ctx262k_lines(weights, q3, torch, synth))
+        except Exception as ex:
+            extras["ctx262k_error"] = repr(ex)
 
     out = {
         "metric": "decode tok/s (bs1, bs64) + prefill tok/s, Qwen3-0.6B shape; % of roofline",
@@ -308,17 +328,58 @@ def c5_lines(weights, q3, torch, synth):
             "c5_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def ctx262k_lines(weights, q3, torch, synth):
+    """Context toward 262K on an engine of its own (1 sequence, 262,160 slots; weights of the
+    bs1 workload): a prefill of 262,136 seeded random tokens timed once (the kernels are warm
+    from the 32768-token line), then 8 greedy decode steps at 262,139 .. 262,146 cached
+    slots (after 2 untimed ones) with the persistent kernel's HBM fraction."""
+    w = synth.workload("bs1_short")
+    n = 262136
+    eng = q3.Engine(q3.config(w, 1, 262160), weights)
+    try:
+        eng.set_decode_path(3)
+        toks = torch.from_numpy(synth.prompt_tokens(w.with_(seed=1006), n)).cuda()
+        tok = torch.empty(1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eng.prefill(0, toks)
+        torch.cuda.synchronize()
+        tp = time.perf_counter() - t0
+        eng.sample(tok, 0.0)
+        for _ in range(2):
+            eng.decode_step(tok)
+            eng.sample(tok, 0.0)
+        eng.sync()
+        dt, prof = decode_loop(eng, q3, torch, tok, 8, 0.0, 1.0, None)
+        eng.sync()
+    finally:
+        eng.close()
+    flops = 2.0 * (n - 1) * 440401920 + 512.0 * 16 * 27 * (n - 1) * n / 2.0   # GEMMs + 27 layers' causal attention
+    gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
+    log(f"prefill {n}: {n / tp:.0f} tok/s ({flops / tp / 1e12:.0f} TFLOP/s); decode at 262K slots "
+        f"{8 / dt:.1f} tok/s, step kernel {gbs:.0f} GB/s")
+    return {"prefill262k_tok_s": round(n / tp, 1), "prefill262k_s": round(tp, 2),
+            "prefill262k_tflops": round(flops / tp / 1e12, 1),
+            "ctx262k_decode_tok_s": round(8 / dt, 2),
+            "ctx262k_decode_step_us": round(1e3 * prof["ms"] / max(1, prof["launches"]), 1),
+            "ctx262k_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bs64_line(eng, w, q3, torch, synth, max_seq):
-    """64 sequences with 4096 pre-filled K/V slots each (synthetic N(0,1) bf16), greedy."""
-    B, T0, steps = 64, 4096, 8
+    """64 sequences with 4096 pre-filled K/V slots each (synthetic N(0,1) bf16), 64 greedy
+    steps timed (after two untimed ones: 4099 .. 4162 cached slots)."""
+    B, T0, steps = 64, 4096, 64
     gen = torch.Generator(device="cuda").manual_seed(1004)
     for b in range(B):
         for layer in range(w.n_layers):
             kv = torch.randn(2, w.n_kv_heads, T0, w.head_dim, generator=gen, device="cuda").bfloat16()
             eng.kv_import(b, layer, kv[0].contiguous(), kv[1].contiguous(), T0)
     toks = torch.from_numpy(synth.batch_first_tokens(w.with_(seed=1004, batch=B))).cuda()
-    eng.decode_step(toks)
-    eng.sample(toks, 0.0)
+    # two untimed warm-up steps (the batch path's kernels load on first use), then the
+    # workload's 64 greedy steps at 4099 .. 4162 cached slots
+    for _ in range(2):
+        eng.decode_step(toks)
+        eng.sample(toks, 0.0)
     eng.sync()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -331,12 +392,18 @@ def bs64_line(eng, w, q3, torch, synth, max_seq):
     eng.decode_step(toks)
     eng.sample(toks, 0.0)
     a = eng.profile_end()
+    eng.profile_begin(q3.PROF_DECODE_STEP)              # the whole step, all its kernels
+    eng.decode_step(toks)
+    eng.sample(toks, 0.0)
+    st = eng.profile_end()
     for b in range(B):
         eng.reset(b)
     ag = a["bytes"] / (a["ms"] / 1e3) / 1e9
-    log(f"bs64 decode: {B * steps / dt:.0f} tok/s; attention {ag:.0f} GB/s")
+    sg = st["bytes"] / (st["ms"] / 1e3) / 1e9
+    log(f"bs64 decode: {B * steps / dt:.0f} tok/s; attention {ag:.0f} GB/s; whole step {sg:.0f} GB/s")
     return {"bs64_decode_tok_s": round(B * steps / dt, 1), "bs64_step_ms": round(1e3 * dt / steps, 3),
-            "bs64_attn_gbs": round(ag, 1), "bs64_attn_hbm_frac": round(ag / HBM_PEAK_GBS, 4)}
+            "bs64_attn_gbs": round(ag, 1), "bs64_attn_hbm_frac": round(ag / HBM_PEAK_GBS, 4),
+            "bs64_step_hbm_frac": round(sg / HBM_PEAK_GBS, 4)}
 
 
 def stored_traffic(md_name, sources):
@@ -364,8 +431,35 @@ MEGA_SOURCES = ("decoder_only_amd/csrc/decode_mega.hip", "decoder_only_amd/csrc/
                 "decoder_only_amd/csrc/kernels.h")
 
 
+def host_cpu():
+    """CPU model, physical cores and logical CPUs this process may use."""
+    cpus = sorted(os.sched_getaffinity(0))
+    model, cores = "unknown", set()
+    try:
+        info, cur = {}, {}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if not line.strip():
+                    if "processor" in cur:
+                        info[int(cur["processor"])] = cur
+                    cur = {}
+                    continue
+                k, _, v = line.partition(":")
+                cur[k.strip()] = v.strip()
+        if "processor" in cur:
+            info[int(cur["processor"])] = cur
+        for c in cpus:
+            d = info.get(c, {})
+            model = d.get("model name", model)
+            cores.add((d.get("physical id", "0"), d.get("core id", str(c))))
+    except OSError:
+        pass
+    return model, len(cores) or len(cpus), len(cpus)
+
+
 def cpu_baseline(w, weights, budget_s):
-    """The oracle (NumPy) on this host: 5-token prefill, then decode steps until the budget."""
+    """The oracle (NumPy) on this host: greedy decode steps of the bs1 workload until the
+    budget is spent, and one 2048-token prefill of the long-prompt workload's shape."""
     import numpy as np
     import oracle
     import synth
@@ -374,6 +468,7 @@ def cpu_baseline(w, weights, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
+    model_name, phys, logical = host_cpu()
     model = oracle.Model(oracle.Config.from_workload(w), weights)
     prompt = synth.prompt_tokens(w)
     # whole generations (5-token prefill untimed, then the greedy decode steps, timed),
@@ -390,10 +485,18 @@ def cpu_baseline(w, weights, budget_s):
             n += 1
             if dt >= budget_s:
                 break
-    log(f"oracle: {n / dt:.2f} tok/s over {n} steps in {gens} generations ({threads} threads)")
+    long_prompt = synth.prompt_tokens(w.with_(seed=1003), 2048)
+    t0 = time.perf_counter()
+    model.forward(long_prompt, model.new_cache(2048), 0)
+    tp = time.perf_counter() - t0
+    log(f"oracle: {n / dt:.2f} tok/s over {n} steps in {gens} generations; 2048-token prefill {tp:.1f} s "
+        f"({threads} BLAS threads; {phys} physical cores, {logical} logical CPUs; {model_name})")
     return {"value": round(n / dt, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"batch-1 Qwen3-0.6B shape: {n} greedy decode steps over {gens} generations of "
-                      f"the workload (5-token prompt, up to {w.decode_steps} steps each; {dt:.1f} s of decode)"}
+                      f"the workload (5-token prompt, up to {w.decode_steps} steps each; {dt:.1f} s of decode)",
+            "cpu_model": model_name, "physical_cores": phys, "logical_cpus": logical,
+            "prefill2048_s": round(tp, 2), "prefill2048_tok_s": round(2048 / tp, 1),
+            "decode_s_per_step": round(dt / n, 4)}
 
 
 if __name__ == "__main__":
