@@ -259,6 +259,30 @@ hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStr
     return hipGetLastError();
 }
 
+// Prefix reuse: slots 0 .. len-1 of sequence src copied into sequence dst for every
+// (layer, kv head) of K and V; blockIdx.y = (layer * Hkv + head) * 2 + (0: K, 1: V), one
+// 16-byte unit per thread. Block (0, 0) also sets dst's length.
+__global__ void k_kv_copy(uint4* __restrict__ kc, uint4* __restrict__ vc, size_t layer_u, size_t seq_u,
+                          size_t head_u, int Hkv, int src, int dst, size_t n_u, int32_t* lens, int len) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lg = (int)blockIdx.y >> 1, l = lg / Hkv, g = lg % Hkv;
+    uint4* base = ((int)blockIdx.y & 1) ? vc : kc;
+    const size_t off = (size_t)l * layer_u + (size_t)g * head_u;
+    if (i < n_u) base[off + (size_t)dst * seq_u + i] = base[off + (size_t)src * seq_u + i];
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens[dst] = len;
+}
+
+hipError_t launch_kv_copy(void* kc, void* vc, size_t kv_layer_elems, size_t kv_seq_elems, int t_cap, int n_layers,
+                          int Hkv, int kv_bytes, int src, int dst, int len, int32_t* lens, hipStream_t s) {
+    if (n_layers <= 0 || len < 0 || (128 * kv_bytes) % 16) return hipErrorInvalidValue;
+    const size_t u = 16 / kv_bytes;     // elements per 16-byte unit
+    const size_t n_u = (size_t)len * 128 / u;
+    const dim3 grid((unsigned)((n_u + 255) / 256 > 0 ? (n_u + 255) / 256 : 1), (unsigned)(n_layers * Hkv * 2));
+    hipLaunchKernelGGL(k_kv_copy, grid, dim3(256), 0, s, (uint4*)kc, (uint4*)vc, kv_layer_elems / u, kv_seq_elems / u,
+                       (size_t)t_cap * 128 / u, Hkv, src, dst, n_u, lens, len);
+    return hipGetLastError();
+}
+
 __global__ void k_fill_u64(unsigned long long* dst, unsigned long long v, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = v;

@@ -743,6 +743,20 @@ extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, cons
     return Q3_OK;
 }
 
+extern "C" q3_status q3_kv_fork(q3_engine* e, int32_t src, int32_t dst, int32_t len) {
+    if (!e) return Q3_ERR_ARG;
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
+    const q3_config& c = e->cfg;
+    if (src < 0 || src >= c.max_batch || dst < 0 || dst >= c.max_batch || src == dst || len < 0)
+        return e->fail(Q3_ERR_ARG, "bad kv_fork arguments");
+    if (len > e->h_len[src]) return e->fail(Q3_ERR_ARG, "kv_fork beyond the source sequence's length");
+    if (c.n_layers > 0)
+        HIPCHK(e, launch_kv_copy(e->kc, e->vc, e->kv_layer_elems, e->kv_seq_elems, c.max_seq, c.n_layers,
+                                 c.n_kv_heads, (int)e->kvbytes(), src, dst, len, e->d_len, e->stream));
+    e->h_len[dst] = len;
+    return Q3_OK;
+}
+
 extern "C" q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void* k, void* v, int32_t len) {
     if (!e) return Q3_ERR_ARG;
     if (q3_status st = flush_tail(e); st != Q3_OK) return st;

@@ -37,6 +37,10 @@ hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* 
                                   int Hkv, hipStream_t s);
 // lens[seq_base + b] += by for b < B.
 hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s);
+// Slots 0 .. len-1 of sequence src into sequence dst for every layer and kv head of the K
+// and V caches ([L][S][Hkv][t_cap][128], kv_bytes per element); lens[dst] = len.
+hipError_t launch_kv_copy(void* kc, void* vc, size_t kv_layer_elems, size_t kv_seq_elems, int t_cap, int n_layers,
+                          int Hkv, int kv_bytes, int src, int dst, int len, int32_t* lens, hipStream_t s);
 // dst[i] = v for i < n (64-bit words); graph-safe replacement for a memset.
 hipError_t launch_fill_u64(unsigned long long* dst, unsigned long long v, int n, hipStream_t s);
 

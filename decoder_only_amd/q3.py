@@ -22,7 +22,7 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -4: "Q3_ERR_CAPACITY", -5: "Q3_ERR_OOM", -6: "Q3_ERR_HIP", -7: "Q3_ERR_STATE",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
-    "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export",
+    "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export", "q3_kv_fork",
     "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_reset": ([vp, i32], i32),
         "q3_kv_import": ([vp, i32, i32, vp, vp, i32], i32),
         "q3_kv_export": ([vp, i32, i32, vp, vp, i32], i32),
+        "q3_kv_fork": ([vp, i32, i32, i32], i32),
         "q3_seq_len": ([vp, i32], i32),
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
@@ -203,6 +204,10 @@ class Engine:
         kk = np.ascontiguousarray(k) if isinstance(k, np.ndarray) else k
         vv = np.ascontiguousarray(v) if isinstance(v, np.ndarray) else v
         _check(load_library().q3_kv_import(self._h, seq, layer, p(kk), p(vv), length), "q3_kv_import", self._h)
+
+    def kv_fork(self, src: int, dst: int, length: int) -> None:
+        """Slot dst becomes a copy of the first `length` cached tokens of slot src."""
+        _check(load_library().q3_kv_fork(self._h, src, dst, length), "q3_kv_fork", self._h)
 
     def kv_export(self, seq: int, layer: int, length: int):
         """Slots 0 .. length-1 of one (sequence, layer) of the cache as two host arrays

@@ -133,6 +133,16 @@ q3_status q3_reset(q3_engine* e, int32_t seq);
 q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k,
                        const void* v, int32_t len);
 
+/* Prefix reuse: sequence slot dst becomes a copy of the first len cached tokens of slot src
+ * (every layer's K and V; len <= src's length) and its length becomes len, so a prompt
+ * prefix shared by several sequences is prefilled once and each copy continues with its
+ * own tokens (q3_prefill / q3_decode_step append after slot len-1). Whatever dst held is
+ * replaced; src is unchanged. One device copy on the engine's stream (no host wait).
+ * The result equals prefilling the prefix into dst itself (Step 5's cache holds only the
+ * prefix's K/V, which depend on nothing after it). Errors: Q3_ERR_ARG (bad slots, src ==
+ * dst, len above src's length). */
+q3_status q3_kv_fork(q3_engine* e, int32_t src, int32_t dst, int32_t len);
+
 /* Copy slots 0 .. len-1 of one (sequence, layer) of the KV cache out to k and v (host or
  * device, kv_dtype, layout [n_kv_heads][len][head_dim]; caller-owned), the inverse of
  * q3_kv_import: the keys as stored (after QK-norm and RoPE, Step 5) and the values.
