@@ -55,7 +55,7 @@ constexpr int NWG = 256, NT = 256;
 constexpr int BMAX = 4;
 constexpr int PART = 2 + DH;     // (max, sum, acc[128]) per (chunk, head)
 constexpr int MAXCH = 32;        // attention chunks per kv group (long context)
-constexpr int SHORT_T = 240;     // visible slots up to which every group workgroup attends itself
+constexpr int SHORT_T = kMegaShortSlots;   // visible slots up to which every group workgroup attends itself
 typedef unsigned long long u64;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -340,8 +340,11 @@ struct Smem {
     float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
     MegaLayer layers[kMegaMaxLayers];
     unsigned long long tr[TRACE_MAX];   // phase timestamps (trace only)
+    __attribute__((aligned(16))) bf16 knc[BMAX][DH];   // causal rows: every row's new key / value
+    __attribute__((aligned(16))) bf16 vnc[BMAX][DH];   // (bf16: the values are bf16-rounded already)
 };
-static_assert(sizeof(Smem) <= 160 * 1024, "shared memory of one CU");
+constexpr size_t kStaticShared = 4 * BMAX * sizeof(unsigned long long);   // wbest of the LM head
+static_assert(sizeof(Smem) + kStaticShared <= 160 * 1024, "shared memory of one CU");
 
 // Per-thread values loaded together with a phase's weight slice: the RMSNorm weights of
 // its 4 elements, and for phase B the QK-norm weights of its RoPE pair.
@@ -392,8 +395,13 @@ __device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, 
     x2 = y2;
 }
 
+// Sequence slot of row b.
+template <bool CAUSAL>
+__device__ __forceinline__ int row_seq(const MegaParams& p, int b) { return p.seq_base + (CAUSAL ? 0 : b); }
+
 // Polled q/k/v of group g (sm.in[b]) -> rotated q, bf16-rounded new k, v in shared memory;
 // `append` writes k, v into the cache at `slot`.
+template <bool CAUSAL>
 __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const Pre& pre, int layer, int b, int g,
                            int slot, bool append) {
     const int wid = threadIdx.x >> 6, i = threadIdx.x & 63;
@@ -411,14 +419,22 @@ __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const 
         sm.qb[wid][1][i + 64] = (bf16)(lb >> 16);
     } else {
         const bf16 h1 = f2bf(x1), h2 = f2bf(x2);
-        float* dst = wid == 2 ? sm.kn : sm.vn;
-        dst[i] = bf2f(h1);
-        dst[i + 64] = bf2f(h2);
+        // (causal rows keep every row's new key / value for the rows after it; otherwise one
+        // buffer serves each row in turn)
+        if constexpr (CAUSAL) {
+            bf16* dc = wid == 2 ? sm.knc[b] : sm.vnc[b];
+            dc[i] = h1;
+            dc[i + 64] = h2;
+        } else {
+            float* dst = wid == 2 ? sm.kn : sm.vn;
+            dst[i] = bf2f(h1);
+            dst[i + 64] = bf2f(h2);
+        }
         if (append) {
             // (a wave-uniform choice: a per-lane one reads the pointer with a vector load and
             // then waits for every outstanding load, the weight prefetch included)
             bf16* cache = (__builtin_amdgcn_readfirstlane(wid) == 2 ? p.kc : p.vc) + (size_t)layer * p.kv_layer_elems +
-                          (size_t)(p.seq_base + b) * p.kv_seq_elems + ((size_t)g * p.t_cap + slot) * DH;
+                          (size_t)row_seq<CAUSAL>(p, b) * p.kv_seq_elems + ((size_t)g * p.t_cap + slot) * DH;
             cache[i] = h1;
             cache[i + 64] = h2;
         }
@@ -439,8 +455,9 @@ __device__ __forceinline__ void trace_flush(const MegaParams& p, const Smem& sm,
             p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + i] = sm.tr[i];
 }
 
+template <bool CAUSAL>
 __device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, int b, int g) {
-    return (size_t)layer * p.kv_layer_elems + (size_t)(p.seq_base + b) * p.kv_seq_elems + (size_t)g * p.t_cap * DH;
+    return (size_t)layer * p.kv_layer_elems + (size_t)row_seq<CAUSAL>(p, b) * p.kv_seq_elems + (size_t)g * p.t_cap * DH;
 }
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -509,11 +526,12 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
-// Attention of both heads of the group for row b over slots [k0, k1) of T visible ones.
-// The caller issued the first shot (kv_stage of first_shot(k0, k1, T) rows at k0), waited
-// for it and passed a barrier; longer ranges are staged here shot by shot (SHOT rows; the
-// new key, kept in shared memory, is appended as the row after the cached ones of the
-// last shot). Wave w owns the 16-key tiles t = w, w + 4, ... of every shot: it stages
+// Attention of both heads of the group for row b over slots [k0, k1) of T visible ones,
+// the last nnew of which are new in this launch (rows b - nnew + 1 .. b, kept in shared
+// memory). The caller issued the first shot (kv_stage of the cached rows in range, up to
+// SHOT of them, at k0), waited for it and passed a barrier; longer ranges are staged here
+// shot by shot (SHOT rows; the new keys are appended as the rows after the cached ones of
+// the last shot). Wave w owns the 16-key tiles t = w, w + 4, ... of every shot: it stages
 // them, computes their scores S^T = K q^T on the matrix cores (columns 0 and 1 the two
 // heads; K rows are exact bf16 operands, q is split into bf16 hi + lo), keeps its own
 // running softmax state per head (max, sum, unnormalised P.V with 16 lanes x 8 dims per
@@ -522,8 +540,10 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // on scores scaled by log2(e)). Writes the normalised output of both heads to o_out, or,
 // when o_out is null, leaves the merged per-head state (base-2 max, sum, unnormalised
 // acc[128]) in sm.att.
-template <bool DB>
-__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, float* o_out) {
+template <bool DB, bool CAUSAL>
+__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, float* o_out,
+                                       int b, int nnew_rt) {
+    const int nnew = CAUSAL ? nnew_rt : 1;
     constexpr int SH = DB ? SHOTD : SHOT;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
     // scores are kept in the base-2 domain: s * log2(e), with s = q.k / sqrt(128)
@@ -544,7 +564,7 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    const int ce = min(k1, T - 1);                 // end of the cached rows in range
+    const int ce = min(k1, T - nnew);              // end of the cached rows in range
     for (int base = k0, shot = 0;; base += SH, ++shot) {
         const int n = max(0, min(ce, base + SH) - base);
         const bool last = base + SH >= ce;
@@ -563,8 +583,19 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
             __builtin_amdgcn_s_waitcnt(0);
         }
         const bool with_new = last && k1 == T;
-        const int nk = n + (with_new ? 1 : 0);
-        if (with_new && wid == ((n >> 4) & 3) && lane < 32) {   // the new key / value as row n
+        const int nk = n + (with_new ? nnew : 0);
+        if constexpr (CAUSAL) {
+            if (with_new && lane < 32) {           // the new keys / values as rows n .. n + nnew - 1
+                for (int i = 0; i < nnew; ++i) {
+                    const int r = n + i;
+                    if (wid != ((r >> 4) & 3)) continue;   // the wave that owns the row's tile writes it
+                    const int c = lane & 15;
+                    const u32x4 u = *reinterpret_cast<const u32x4*>(
+                        (lane < 16 ? sm.knc[b - nnew + 1 + i] : sm.vnc[b - nnew + 1 + i]) + 8 * c);
+                    *reinterpret_cast<u32x4*>(lane < 16 ? &sm.u.kv.k[ro + r][8 * kslot(r, c)] : &sm.u.kv.v[ro + r][8 * c]) = u;
+                }
+            }
+        } else if (with_new && wid == ((n >> 4) & 3) && lane < 32) {   // the new key / value as row n
             const int c = lane & 15;
             const float* src = (lane < 16 ? sm.kn : sm.vn) + 8 * c;
             u32x4 u;                               // exact: already bf16 values
@@ -785,9 +816,10 @@ __device__ __forceinline__ size_t group_chunk(int gg, int i) {
 // the whole range); 1: split-K attention over chunks; 2: the same with the chunk rows staged
 // in double-buffered halves (contexts above LONG_T). Separate instances, so the code and
 // registers of one path do not touch the others.
-template <int MODE>
+template <int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     constexpr bool LONG = MODE == 2;
+    static_assert(!CAUSAL || MODE == 0, "causal rows run in the short-context instance only");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -882,16 +914,19 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         if constexpr (MODE == 0) {
             for (int b = 0; b < B; ++b) {
                 const int slot = p.slots[b], T = slot + 1;
-                const size_t hb = kv_head_base(p, layer, b, g);
-                kv_stage(p, sm, hb, 0, first_shot(0, T, T));   // in flight while q/k/v arrive
+                // new keys of this launch that row b sees (held in shared memory, not read back
+                // from the cache, which other workgroups of this launch are still writing)
+                const int nnew = CAUSAL ? b + 1 : 1;
+                const size_t hb = kv_head_base<CAUSAL>(p, layer, b, g);
+                kv_stage(p, sm, hb, 0, first_shot(0, T, T - nnew + 1));   // in flight while q/k/v arrive
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
                 if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);              // streams during the attention
                 if (b == 0) trace_at(p, sm, tslot++);
-                group_prep(p, sm, pre, layer, b, g, slot, j == 0);
+                group_prep<CAUSAL>(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
-                attend<false>(p, sm, hb, 0, T, T, sm.o[b]);
+                attend<false, CAUSAL>(p, sm, hb, 0, T, T, sm.o[b], b, nnew);
             }
         } else {
             // B1: unit w = (group w % 8, chunk w / 8) attends its chunk, per row
@@ -902,7 +937,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 chunking(T, nch, ch);
                 if (c < nch) {
                     const int k0 = c * ch, k1 = min(T, k0 + ch);
-                    const size_t hb = kv_head_base(p, layer, b, gg);
+                    const size_t hb = kv_head_base<false>(p, layer, b, gg);
                     if (LONG) kv_stage_db(p, sm, hb, k0, first_shot(k0, k1, T, SHOTD), 0);
                     else kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
                     if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(gg, i); }, DH, sm.in[b],
@@ -911,9 +946,9 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     __builtin_amdgcn_s_waitcnt(0);
                     if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);          // streams during the attention
                     if (b == 0) trace_at(p, sm, tslot++);
-                    group_prep(p, sm, pre, layer, b, gg, slot, k1 == T);
+                    group_prep<false>(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
-                    attend<LONG>(p, sm, hb, k0, k1, T, nullptr);
+                    attend<LONG, false>(p, sm, hb, k0, k1, T, nullptr, b, 1);
                     float* pt = PT + (size_t)b * W_PT + (size_t)c * PT_CHUNK + (size_t)gg * 2 * PART;
                     for (int e = tid; e < 2 * PART; e += NT) put_xcd(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
@@ -1056,7 +1091,13 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         __syncthreads();
     }
 
-    // ---------------- final RMSNorm + LM head rows [r0, r1) + per-workgroup argmax
+    // ---------------- final RMSNorm + LM head rows [r0, r1) + per-workgroup argmax, for the
+    // rows b >= head_first (a chunk of a prompt whose logits nobody reads has none)
+    const int hf = CAUSAL ? p.head_first : 0;
+    if (CAUSAL && hf >= B) {
+        trace_flush(p, sm, tslot);
+        return;
+    }
     const int r0 = (int)((long long)p.vocab * w / NWG), r1 = (int)((long long)p.vocab * (w + 1) / NWG);
     const int rsub = tid >> 4, sub = tid & 15;   // 16 rows per pass, 16 lanes per row
     u32x4 b0[8], b1[8], b2[8];                     // three passes: two loads in flight
@@ -1072,7 +1113,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     {
         const float* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
         bool okl = true;
-        for (int b = 0; b < B; ++b) {
+        for (int b = hf; b < B; ++b) {
             u32x4 c[2];
             okl = poll_own<2>(Xl + (size_t)b * W_X, W_X, FxPair{}, c, p.err, FxComplete{}) && okl;
             norm_own(sm, b, fx_vec4(c), pre.nw);
@@ -1082,7 +1123,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     }
     float rn[BMAX];
 #pragma unroll
-    for (int b = 0; b < BMAX; ++b) rn[b] = b < B ? norm_scale(p, sm, b) : 0.f;
+    for (int b = 0; b < BMAX; ++b) rn[b] = b >= hf && b < B ? norm_scale(p, sm, b) : 0.f;
     u64 best[BMAX] = {0ull, 0ull, 0ull, 0ull};
     bool bad = false;
     {
@@ -1091,11 +1132,12 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 if (b >= B) break;
+                if (b < hf) continue;
                 float s = 0.f;
                 if (row < r1) s = dot_chunks<8>(wv, sm.u.s.act[b], sub, 16);
                 s = sum16(s) * rn[b];
                 if (row < r1 && sub == 0) {
-                    p.logits[(size_t)b * p.vocab + row] = s;
+                    p.logits[(size_t)(b - hf) * p.vocab + row] = s;
                     bad |= !isfinite(s);
                     const u64 key = pack_argmax(s, (uint32_t)row);
                     best[b] = key > best[b] ? key : best[b];
@@ -1116,6 +1158,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
         if (b >= B) break;
+        if (b < hf) continue;
         u64 v = best[b];
         for (int o = 32; o >= 1; o >>= 1) {
             const u64 t = __shfl_xor(v, o, 64);
@@ -1124,10 +1167,10 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         if (lane == 0) wbest[tid >> 6][b] = v;
     }
     __syncthreads();
-    if (tid < B) {
+    if (tid >= hf && tid < B) {
         u64 v = wbest[0][tid];
         for (int wv = 1; wv < 4; ++wv) v = wbest[wv][tid] > v ? wbest[wv][tid] : v;
-        p.cand[(size_t)tid * NWG + w] = v;
+        p.cand[(size_t)(tid - hf) * NWG + w] = v;
     }
     trace_at(p, sm, tslot++);
     trace_flush(p, sm, tslot);
@@ -1140,15 +1183,24 @@ size_t decode_mega_exchange_words_per_layer() {
 }
 
 // Tail of a persistent decode step, run after every launch (also one that gave up):
-// blocks b < B: amax[b] = max over the 256 workgroup candidates of row b (packed logit
-// key | ~id), lens[seq_base + b] += 1 and, when greedy_out is given, the greedy token
-// (Step 8's argmax, lowest id on ties); all blocks: the initial state back into every
-// exchange word the launch may have written -- per layer, rows < B of the x and x' sums
-// (zero), q/k/v and a, and pt_words words of chunk partials per row -- with coherent stores.
+// lengths advanced (lens[seq_base + b] += 1 per row, or lens[seq_base] += B for causal
+// rows of one sequence); blocks b < nout (the rows that had the LM head): amax[b] = max
+// over the 256 workgroup candidates of output row b (packed logit key | ~id) and, when
+// greedy_out is given, the greedy token (Step 8's argmax, lowest id on ties); all blocks:
+// the initial state back into every exchange word the launch may have written -- per
+// layer, rows < B of the x and x' sums (zero), q/k/v and a, and pt_words words of chunk
+// partials per row -- with coherent stores.
 __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax, int* __restrict__ lens,
                             int seq_base, int B, float* ex, size_t ex_layer, int n_layers, int pt_words,
-                            int32_t* __restrict__ greedy_out) {
-    if ((int)blockIdx.x < B) {
+                            int32_t* __restrict__ greedy_out, int nout, int causal) {
+    if (threadIdx.x == 0) {
+        if (causal) {
+            if (blockIdx.x == 0) lens[seq_base] += B;
+        } else if ((int)blockIdx.x < B) {
+            lens[seq_base + blockIdx.x] += 1;
+        }
+    }
+    if ((int)blockIdx.x < nout) {
         const int b = blockIdx.x;
         u64 v = cand[(size_t)b * NWG + threadIdx.x];
         for (int o = 32; o >= 1; o >>= 1) {
@@ -1161,7 +1213,6 @@ __global__ void k_mega_tail(const u64* __restrict__ cand, u64* __restrict__ amax
         if (threadIdx.x == 0) {
             for (int i = 0; i < 4; ++i) v = r[i] > v ? r[i] : v;
             amax[b] = v;
-            lens[seq_base + b] += 1;
             if (greedy_out) greedy_out[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
         }
     }
@@ -1210,13 +1261,13 @@ int decode_mega_chunks(const int* T, int B) {
 
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
                             int B, float* ex, size_t ex_layer, int n_layers, int pt_chunks, int32_t* greedy_out,
-                            hipStream_t s) {
+                            hipStream_t s, int nout, int causal) {
     if (B < 1 || B > BMAX || n_layers < 1 || ex_layer != decode_mega_exchange_words_per_layer() || pt_chunks < 0 ||
-        pt_chunks > MAXCH)
+        pt_chunks > MAXCH || nout < 0 || nout > B)
         return hipErrorInvalidValue;
     const int pt_words = pt_chunks * PT_CHUNK;
     hipLaunchKernelGGL(k_mega_tail, dim3(NWG), dim3(NT), 0, s, cand, amax, lens, seq_base, B, ex, ex_layer, n_layers,
-                       pt_words, greedy_out);
+                       pt_words, greedy_out, nout, causal);
     return hipGetLastError();
 }
 
@@ -1228,24 +1279,35 @@ hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
 }
 
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s) {
-    if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers) return hipErrorInvalidValue;
+    if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers || p.head_first < 0 ||
+        p.head_first > p.B)
+        return hipErrorInvalidValue;
     int Tmax = 0;
     for (int b = 0; b < p.B; ++b) Tmax = std::max(Tmax, p.slots[b] + 1);
-    const int mode = Tmax <= SHORT_T ? 0 : Tmax <= LONG_T ? 1 : 2;
-    const void* fn = mode == 0 ? (const void*)k_decode_mega<0>
-                     : mode == 1 ? (const void*)k_decode_mega<1> : (const void*)k_decode_mega<2>;
+    if (p.causal) {                  // consecutive slots of one sequence, short instance only
+        for (int b = 1; b < p.B; ++b)
+            if (p.slots[b] != p.slots[0] + b) return hipErrorInvalidValue;
+        if (Tmax > SHORT_T) return hipErrorInvalidValue;
+    }
+    if (!p.causal && p.head_first != 0) return hipErrorInvalidValue;
+    const int mode = p.causal ? 3 : Tmax <= SHORT_T ? 0 : Tmax <= LONG_T ? 1 : 2;
+    const void* fn = mode == 0 ? (const void*)k_decode_mega<0, false>
+                     : mode == 1 ? (const void*)k_decode_mega<1, false>
+                     : mode == 2 ? (const void*)k_decode_mega<2, false> : (const void*)k_decode_mega<0, true>;
     if (cooperative) {
         void* args[] = {(void*)&p};
         return hipLaunchCooperativeKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
     }
-    if (mode == 0) hipLaunchKernelGGL(k_decode_mega<0>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else if (mode == 1) hipLaunchKernelGGL(k_decode_mega<1>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else hipLaunchKernelGGL(k_decode_mega<2>, dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    if (mode == 0) hipLaunchKernelGGL((k_decode_mega<0, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else if (mode == 1) hipLaunchKernelGGL((k_decode_mega<1, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else if (mode == 2) hipLaunchKernelGGL((k_decode_mega<2, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
+    else hipLaunchKernelGGL((k_decode_mega<0, true>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
     return hipGetLastError();
 }
 
 hipError_t decode_mega_prepare() {
-    for (const void* fn : {(const void*)k_decode_mega<0>, (const void*)k_decode_mega<1>, (const void*)k_decode_mega<2>}) {
+    for (const void* fn : {(const void*)k_decode_mega<0, false>, (const void*)k_decode_mega<1, false>,
+                           (const void*)k_decode_mega<2, false>, (const void*)k_decode_mega<0, true>}) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
         if (e != hipSuccess) return e;
     }

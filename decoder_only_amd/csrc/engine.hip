@@ -87,6 +87,7 @@ struct q3_engine {
     // q3_sample right after it is the same launch.
     bool tail_pending = false;
     int tail_B = 0, tail_seq_base = 0, tail_chunks = 0;
+    int tail_nout = 0, tail_causal = 0;      // rows with the LM head; rows of one sequence
     unsigned long long* m_trace = nullptr;   // caller's device buffer for phase timestamps
     int m_trace_n = 0;
 
@@ -320,9 +321,9 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         int occ = 0;
         const bool shape = d == 1024 && Hq == 16 && Hkv == 8 && dh == 128 && F == 3072 &&
                            c.weight_dtype == Q3_BF16 && c.kv_dtype == Q3_BF16 && c.n_layers > 0 && c.n_layers <= kMegaMaxLayers;
-        if (shape && hipGetDeviceProperties(&prop, e->device) == hipSuccess && prop.multiProcessorCount == 256 &&
-            decode_mega_prepare() == hipSuccess) {
-            e->mega_ok = true;
+        if (shape && hipGetDeviceProperties(&prop, e->device) == hipSuccess && prop.multiProcessorCount == 256) {
+            if (decode_mega_prepare() == hipSuccess) e->mega_ok = true;
+            else (void)hipGetLastError();   // not usable here: clear the error, use the per-operation path
         }
         (void)occ;
         if (e->mega_ok) {
@@ -367,7 +368,7 @@ static q3_status flush_tail(q3_engine* e, int32_t* greedy_out = nullptr) {
     if (!e->tail_pending) return Q3_OK;
     e->tail_pending = false;
     HIPCHK(e, launch_mega_tail(e->m_cand, e->amax, e->d_len, e->tail_seq_base, e->tail_B, e->m_ex, e->m_ex_layer,
-                               e->cfg.n_layers, e->tail_chunks, greedy_out, e->stream));
+                               e->cfg.n_layers, e->tail_chunks, greedy_out, e->stream, e->tail_nout, e->tail_causal));
     return Q3_OK;
 }
 
@@ -404,6 +405,67 @@ static double attn_prefill_flops(int M, int t0, int Hq) {
 // decode rows (also the tail of a prefill)
 // ---------------------------------------------------------------------------------
 
+// Persistent-kernel parameters shared by every launch (rows' slots left to the caller).
+static MegaParams mega_params(const q3_engine* e, const int32_t* tokens, const int32_t* positions, int seq_base,
+                              int B, float* logits) {
+    const q3_config& c = e->cfg;
+    MegaParams mp{};
+    mp.n_layers = c.n_layers;
+    mp.vocab = c.vocab;
+    mp.B = B;
+    mp.seq_base = seq_base;
+    mp.t_cap = c.max_seq;
+    mp.causal = 0;
+    mp.head_first = 0;
+    mp.eps = c.rms_eps;
+    mp.layers = e->d_layers;
+    mp.embed = (const uint16_t*)e->embed;
+    mp.final_norm = e->final_norm;
+    mp.inv_freq = e->inv_freq;
+    mp.kc = (uint16_t*)e->kc;
+    mp.vc = (uint16_t*)e->vc;
+    mp.kv_layer_elems = e->kv_layer_elems;
+    mp.kv_seq_elems = e->kv_seq_elems;
+    mp.tokens = tokens;
+    mp.positions = positions;
+    mp.ex = e->m_ex;
+    mp.ex_layer = e->m_ex_layer;
+    mp.logits = logits;
+    mp.cand = e->m_cand;
+    mp.err = e->d_err;
+    mp.trace = e->m_trace;
+    mp.trace_n = e->m_trace_n;
+    return mp;
+}
+
+// A short prompt through the persistent kernel: up to kMegaMaxRows consecutive tokens of
+// sequence `seq` in one launch, row b at slot len + b, each row attending the rows before
+// it in the launch as well as the cache (Step 5's causal mask). With want_logits, the last
+// row's logits go to logits_out (or the engine's buffer); otherwise the launch has no LM
+// head at all.
+static q3_status run_prefill_mega(q3_engine* e, int seq, const int32_t* tokens, int n, float* logits_out,
+                                  bool want_logits) {
+    if (q3_status st = flush_tail(e); st != Q3_OK) return st;
+    float* lg = logits_out ? logits_out : e->logits;
+    MegaParams mp = mega_params(e, tokens, nullptr, seq, n, lg);
+    mp.causal = 1;
+    mp.head_first = want_logits ? n - 1 : n;
+    for (int b = 0; b < n; ++b) mp.slots[b] = e->h_len[seq] + b;
+    HIPCHK(e, launch_decode_mega(mp, e->decode_path != 3, e->stream));
+    e->tail_pending = true;
+    e->tail_B = n;
+    e->tail_nout = want_logits ? 1 : 0;
+    e->tail_causal = 1;
+    e->tail_seq_base = seq;
+    e->tail_chunks = 0;                 // the short-context instance writes no chunk partials
+    if (want_logits) {
+        e->cur_logits = lg;
+        e->cur_rows = 1;
+    }
+    e->h_len[seq] += n;
+    return Q3_OK;
+}
+
 static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* positions,
                             int seq_base, int B, float* logits_out, bool want_logits) {
     if (q3_status st = flush_tail(e); st != Q3_OK) return st;   // the previous launch's tail first
@@ -420,37 +482,16 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     const bool use_mega = e->mega_ok && B <= kMegaMaxRows && e->decode_path != 1;
     if (!use_mega && e->decode_path == 2) return e->fail(Q3_ERR_STATE, "persistent decode kernel not usable here");
     if (use_mega) {
-        MegaParams mp{};
-        mp.n_layers = c.n_layers;
-        mp.vocab = V;
-        mp.B = B;
-        mp.seq_base = seq_base;
-        mp.t_cap = c.max_seq;
-        for (int b = 0; b < B; ++b) mp.slots[b] = e->h_len[seq_base + b];
-        mp.eps = c.rms_eps;
-        mp.layers = e->d_layers;
-        mp.embed = (const uint16_t*)e->embed;
-        mp.final_norm = e->final_norm;
-        mp.inv_freq = e->inv_freq;
-        mp.kc = (uint16_t*)e->kc;
-        mp.vc = (uint16_t*)e->vc;
-        mp.kv_layer_elems = e->kv_layer_elems;
-        mp.kv_seq_elems = e->kv_seq_elems;
-        mp.tokens = tokens;
-        mp.positions = positions;
-        mp.ex = e->m_ex;
-        mp.ex_layer = e->m_ex_layer;
         float* lg = logits_out ? logits_out : e->logits;
-        mp.logits = lg;
-        mp.cand = e->m_cand;
-        mp.err = e->d_err;
-        mp.trace = e->m_trace;
-        mp.trace_n = e->m_trace_n;
+        MegaParams mp = mega_params(e, tokens, positions, seq_base, B, lg);
+        for (int b = 0; b < B; ++b) mp.slots[b] = e->h_len[seq_base + b];
         prof_mark(e, Q3_PROF_DECODE_STEP, true, step_bytes(e, seq_base, B), 0);
         HIPCHK(e, launch_decode_mega(mp, e->decode_path != 3, s));
         prof_mark(e, Q3_PROF_DECODE_STEP, false);
         e->tail_pending = true;
         e->tail_B = B;
+        e->tail_nout = B;
+        e->tail_causal = 0;
         e->tail_seq_base = seq_base;
         {
             int vis[kMegaMaxRows];
@@ -666,6 +707,15 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
     if ((int64_t)e->h_len[seq] + n > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
     q3_status st;
     int done = 0;
+    if (e->mega_ok && e->decode_path != 1 && n < kPrefillMfmaMin && e->h_len[seq] + n <= kMegaShortSlots) {
+        // a short prompt: causal chunks of up to kMegaMaxRows rows per persistent launch, the
+        // LM head only in the last one
+        for (int i = 0; i < n; i += kMegaMaxRows) {
+            const int cnt = std::min(kMegaMaxRows, n - i);
+            if ((st = run_prefill_mega(e, seq, tokens + i, cnt, logits, i + cnt == n)) != Q3_OK) return st;
+        }
+        return Q3_OK;
+    }
     if (e->cfg.weight_dtype == Q3_BF16 && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
         if ((st = run_prefill_mfma(e, seq, tokens, n - 1)) != Q3_OK) return st;
         done = n - 1;
@@ -693,7 +743,7 @@ extern "C" q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch,
     if (!(temperature >= 0.f)) return e->fail(Q3_ERR_ARG, "temperature must be >= 0");
     if (temperature > 0.f && !uniforms) return e->fail(Q3_ERR_ARG, "uniforms required when temperature > 0");
     const int V = e->cfg.vocab;
-    if (e->tail_pending && temperature == 0.f && !logits && batch == e->tail_B) {
+    if (e->tail_pending && temperature == 0.f && !logits && batch == e->tail_nout) {
         // greedy pick of the persistent launch's rows: fused into its tail
         return flush_tail(e, tokens_out);
     }

@@ -88,6 +88,11 @@ struct MegaLayer {
 struct MegaParams {
     int n_layers, vocab, B, seq_base, t_cap;
     int slots[4];                   // cache slot (= current length) of each row
+    int causal;                     // 0: row b is sequence seq_base + b; 1: every row is sequence
+                                    // seq_base at consecutive slots, and row b also attends the
+                                    // rows before it in this launch (a short prompt)
+    int head_first;                 // rows b >= head_first get the LM head: logits row b - head_first
+                                    // and argmax candidates; B: no LM head at all
     float eps;
     const MegaLayer* layers;        // device array [n_layers]
     const uint16_t* embed;
@@ -110,16 +115,19 @@ hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t
 // Attention chunks whose partials a launch over rows of visible lengths T[0..B) writes per
 // row (the largest count over the rows; 0 without split-K attention).
 int decode_mega_chunks(const int* T, int B);
-// After each launch: argmax over the per-workgroup candidates, lens[seq_base + b] += 1,
+// After each launch: argmax over the per-workgroup candidates of the nout rows that had the
+// LM head, the lengths advanced (lens[seq_base + b] += 1 per row; causal: lens[seq_base] += B),
 // the initial state back into the exchange words used (pt_chunks from decode_mega_chunks),
-// and the greedy token of each row into greedy_out when it is not NULL.
+// and the greedy token of each output row into greedy_out when it is not NULL.
 hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
                             int B, float* ex, size_t ex_layer, int n_layers, int pt_chunks, int32_t* greedy_out,
-                            hipStream_t s);
+                            hipStream_t s, int nout, int causal);
 // Sentinel into all `words` exchange words (at load).
 hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);
 size_t decode_mega_exchange_words_per_layer();
 constexpr int kMegaMaxRows = 4;
+constexpr int kMegaShortSlots = 240;   // launches whose rows see at most this many slots run the
+                                       // short-context instance (the only one that takes causal rows)
 constexpr int kMegaMaxLayers = 64;
 constexpr int kMegaWorkgroups = 256;
 

@@ -155,3 +155,48 @@ def test_nonfinite_projection_in_decode(path, name):
         eng.sync()
     assert e.value.code == -8
     eng.close()
+
+
+@pytest.mark.parametrize("path", [0, 3])
+def test_toy_bf16_short_prompts_in_causal_chunks(path):
+    """Prompts under 16 tokens run through the persistent kernel in causal chunks of up to 4
+    rows (row b of a chunk attends the chunk's earlier rows from shared memory and the
+    cache), the LM head only in the last chunk. Prompts of 1..15 tokens into an empty
+    cache and after earlier tokens (230 + 10 fills the 240-slot short instance exactly;
+    231 + 10 goes row by row), each followed by 3 decode steps that read every cache entry
+    the chunks wrote; logits against the oracle run of the whole token sequence."""
+    import torch
+    from decoder_only_amd import q3
+    import oracle
+    from e2e import compare, failures
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    weights = synth.make_weights(w)
+    model = oracle.Model(oracle.Config.from_workload(w), weights)
+    eng = q3.Engine(q3.config(w, 1, 260), weights)
+    eng.set_decode_path(path)
+    logits = torch.empty(1, w.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    stats = []
+    cases = [(0, n) for n in (1, 2, 3, 4, 5, 8, 9, 15)] + [(7, 6), (3, 13), (230, 10), (231, 10)]
+    for t0, n in cases:
+        base = synth.prompt_tokens(w, t0, seq=1) if t0 else np.zeros(0, np.int32)
+        new = synth.prompt_tokens(w, n, seq=2)
+        eng.reset(0)
+        if t0:
+            eng.prefill(0, torch.from_numpy(base).cuda())
+        eng.prefill(0, torch.from_numpy(new).cuda(), logits)
+        eng.sample(tok, 0.0)
+        cache = model.new_cache(260)
+        ref = model.forward(np.concatenate([base, new]), cache, 0)
+        for step in range(4):
+            eng.sync()
+            stats.append(compare(step, 1000 * t0 + n, logits[0].cpu().numpy(), ref))
+            if step == 3:
+                break
+            nxt = int(np.argmax(ref))
+            eng.decode_step(torch.tensor([nxt], dtype=torch.int32, device="cuda"), None, logits)
+            ref = model.forward([nxt], cache, t0 + n + step)
+        assert eng.seq_len(0) == t0 + n + 3
+    eng.close()
+    _report(stats)
+    assert not failures(stats), failures(stats)[:5]
