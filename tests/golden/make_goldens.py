@@ -12,7 +12,8 @@ s >= 1 the decode steps), under teacher forcing with the oracle's own sampled to
   argmax[s], gap[s], norm[s]    argmax, top-2 logit gap, L2 norm of the logits
   top_ids[s], top_vals[s]       the 32 largest logits
   probe_vals[s]   logits at the fixed ids probe_ids (seeded, shared by all steps)
-and full_logits for step 0.
+and the whole logit row at the steps full_steps (step 0, the last step and N_FULL seeded
+steps in between): full_logits[i] belongs to step full_steps[i] (full_logits0 = step 0).
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ import synth  # noqa: E402
 
 N_TOP = 32
 N_PROBE = 256
+N_FULL = 10
 
 
 def main() -> int:
@@ -51,6 +53,10 @@ def main() -> int:
     T = float(np.float32(w.temperature))
     p = float(np.float32(w.top_p))
     probe_ids = np.sort(np.random.default_rng([w.seed, 7]).choice(w.vocab, N_PROBE, replace=False))
+    inner = np.random.default_rng([w.seed, 8]).choice(np.arange(1, steps), min(N_FULL, max(0, steps - 1)),
+                                                      replace=False)
+    full_steps = np.unique(np.concatenate([[0, steps], inner])).astype(np.int32)
+    full_rows = []
     print(f"[{time.time() - t0:.0f}s] prefill {len(prompt)}", flush=True)
     logits = model.forward(prompt, cache, 0)
     rec = {k: [] for k in ("tokens", "u", "margin", "argmax", "gap", "norm", "top_ids", "top_vals", "probe_vals")}
@@ -69,6 +75,8 @@ def main() -> int:
         rec["top_ids"].append(order.astype(np.int32))
         rec["top_vals"].append(logits[order])
         rec["probe_vals"].append(logits[probe_ids])
+        if s in full_steps:
+            full_rows.append(logits.copy())
         if s == steps:
             break
         logits = model.forward([tok], cache, len(prompt) + s)
@@ -78,6 +86,7 @@ def main() -> int:
     np.savez_compressed(
         out, workload=w.name, temperature=np.float32(w.temperature), top_p=np.float32(w.top_p),
         prompt_len=len(prompt), probe_ids=probe_ids.astype(np.int32), full_logits0=full0,
+        full_steps=full_steps, full_logits=np.stack(full_rows),
         tokens=np.array(rec["tokens"], np.int32), u=np.array(rec["u"], np.float32),
         margin=np.array(rec["margin"]), argmax=np.array(rec["argmax"], np.int32),
         gap=np.array(rec["gap"]), norm=np.array(rec["norm"]), top_ids=np.stack(rec["top_ids"]),
