@@ -163,6 +163,53 @@ __device__ __forceinline__ float dot8v(const u32x4 w, const f32x4 lo, const f32x
            ((__uint_as_float(w[2] << 16) * hi[0] + __uint_as_float(w[2] & 0xFFFF0000u) * hi[1]) +
             (__uint_as_float(w[3] << 16) * hi[2] + __uint_as_float(w[3] & 0xFFFF0000u) * hi[3]));
 }
+// Weight-only int8: codes q in [-127, 127], one byte each; a code becomes a float exactly
+// (sign-extending bit extract, then int to float) and multiplies x without cancellation
+// (an offset-binary code u = q + 128 would save the extract but sum terms ~3x the size of
+// the result: measured 2e-3 relative L2 on the 28-layer logits against ~5e-4). The row's
+// scale multiplies the finished row sum. A chunk is 8 codes (8 bytes), at the same columns
+// as a bf16 chunk of 16 bytes.
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+template <bool W8> struct WChunk { typedef u32x4 T; };
+template <> struct WChunk<true> { typedef u32x2 T; };
+__device__ __forceinline__ u32x2 ldw8(const uint8_t* p) { return *(const GLOBAL_AS u32x2*)(p); }
+template <bool W8>
+__device__ __forceinline__ typename WChunk<W8>::T ldwc(const void* base, size_t e) {
+    if constexpr (W8) return ldw8(static_cast<const uint8_t*>(base) + e);
+    else return ldw16(static_cast<const bf16*>(base) + e);
+}
+// int8 matrix buffer: codes [rows][cols] (n_codes bytes), then the rows' float32 scales
+__device__ __forceinline__ const float* row_scales(const void* m, size_t n_codes) {
+    return reinterpret_cast<const float*>(static_cast<const uint8_t*>(m) + n_codes);
+}
+__device__ __forceinline__ float sb(unsigned w, int k) { return (float)((int)(w << (24 - 8 * k)) >> 24); }
+// 8 codes dotted with (lo, hi)
+__device__ __forceinline__ float dot8v(const u32x2 w, const f32x4 lo, const f32x4 hi) {
+    return ((sb(w[0], 0) * lo[0] + sb(w[0], 1) * lo[1]) + (sb(w[0], 2) * lo[2] + sb(w[0], 3) * lo[3])) +
+           ((sb(w[1], 0) * hi[0] + sb(w[1], 1) * hi[1]) + (sb(w[1], 2) * hi[2] + sb(w[1], 3) * hi[3]));
+}
+// sum over i < N of chunk i of codes dotted with x[(first + step i) * 8 ...], as the bf16
+// dot_chunks: every shared-memory read first, one accumulator per chunk
+template <int N>
+__device__ __forceinline__ float dot_chunks(const u32x2* w, const float* x, int first, int step) {
+    f32x4 a[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(x + (first + step * i) * 8);
+        a[2 * i] = src[0];
+        a[2 * i + 1] = src[1];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * N, 0);
+    float part[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) part[i] = dot8v(w[i], a[2 * i], a[2 * i + 1]);
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+        for (int i = 0; i + h < N; i += 2 * h) part[i] += part[i + h];
+    return part[0];
+}
+
 __device__ __forceinline__ f32x4 ldf4(const float* p) { return *(const GLOBAL_AS f32x4*)(p); }
 __device__ __forceinline__ float ldf(const float* p) { return *(const GLOBAL_AS float*)(p); }
 // A pointer every lane holds alike, moved into scalar registers here (the empty asm keeps
@@ -351,6 +398,7 @@ static_assert(sizeof(Smem) + kStaticShared <= 160 * 1024, "shared memory of one 
 struct Pre {
     f32x4 nw;
     float qk1, qk2;
+    float sa, so, sg, sd;   // int8 weights: scale of the row this thread finishes in phase A, B, C, D
 };
 
 
@@ -724,11 +772,13 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb,
 // x'[b][32j + r] += Wo[32j + r, 256g:256g+256] . o[b] (fixed-point sum over the groups);
 // thread t: row r = t >> 3, 16-byte chunks sub + 8i (i < 4) of the 32 in the row segment.
 // Group 0's contribution also carries the residual x.
-__device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, float* P, int g, int j, int B) {
+template <typename WT>
+__device__ __forceinline__ void oproj_partial(Smem& sm, const WT* pf, float* P, int g, int j, int B, float sc) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<4>(pf, sm.o[b], sub, 8);
         s = sum8(s);
+        if constexpr (sizeof(WT) == 8) s *= sc;   // int8 row scale
         if (g == 0) s = sm.xg[b][r] + s;
         if (sub == 0) fx_add(reinterpret_cast<u64*>(P + (size_t)b * W_P) + 32 * j + r, s);
     }
@@ -737,21 +787,25 @@ __device__ __forceinline__ void oproj_partial(Smem& sm, const u32x4* pf, float* 
 // x''[b][32j + r] += Wd[32j + r, DCOLS g : DCOLS (g + 1)] . a[b] (fixed-point sum over the
 // column blocks; block 0's contribution also carries the residual x'); thread t: row
 // r = t >> 3, 16-byte chunks sub + 8 i (i < 6) of the 48 in the row segment.
-__device__ __forceinline__ void down_partial(Smem& sm, const u32x4* pf, float* Xn, int g, int j, int B) {
+template <typename WT>
+__device__ __forceinline__ void down_partial(Smem& sm, const WT* pf, float* Xn, int g, int j, int B, float sc) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 8);
         s = sum8(s);
+        if constexpr (sizeof(WT) == 8) s *= sc;   // int8 row scale
         if (g == 0) s = sm.xr[b][r] + s;
         if (sub == 0) fx_add(reinterpret_cast<u64*>(Xn + (size_t)b * W_X) + 32 * j + r, s);
     }
 }
 
-__device__ __forceinline__ void pf_oproj(const MegaLayer& L, u32x4* pf, int g, int j) {
+template <bool W8>
+__device__ __forceinline__ void pf_oproj(const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre, int g, int j) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
-    const bf16* base = L.wo + (size_t)(32 * j + r) * (HQ * DH) + 256 * g;
+    const size_t base = (size_t)(32 * j + r) * (HQ * DH) + 256 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = ldw16(base + (sub + 8 * i) * 8);
+    for (int i = 0; i < 4; ++i) pf[i] = ldwc<W8>(L.wo, base + (sub + 8 * i) * 8);
+    if constexpr (W8) pre.so = ldf(row_scales(L.wo, (size_t)D * HQ * DH) + 32 * j + r);
 }
 
 // Rows of phase C: rr < 12 the gate rows of the workgroup's 12 SwiGLU columns, then their
@@ -773,10 +827,14 @@ __device__ __forceinline__ int qkv_row0(int w) {
 // Phases A, C, D: thread t polls 4 consecutive columns; with its pair lane t ^ 1 it holds
 // the 8 columns 8 (t >> 1) .. + 7 (pair8), and it owns half of the phase's rows
 // (by t & 1) at those columns: one 16-byte chunk per row.
-__device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, u32x4* pf, Pre& pre, int w) {
-    const bf16* base = L.wqkv + (size_t)(qkv_row0(w) + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
+template <bool W8>
+__device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre,
+                                       int w) {
+    const size_t base = (size_t)(qkv_row0(w) + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pf[i] = ldw16(base + (size_t)i * D);
+    for (int i = 0; i < 8; ++i)
+        pf[i] = ldwc<W8>(L.wqkv, base + (size_t)i * D);
+    if constexpr (W8) pre.sa = ldf(row_scales(L.wqkv, (size_t)NQKV * D) + qkv_row0(w) + (threadIdx.x >> 4));
     pre.nw = ldf4(L.in_norm + 4 * threadIdx.x);
     const int i = threadIdx.x & 63;
     const float* qk = (threadIdx.x >> 6) < 2 ? L.q_norm : L.k_norm;
@@ -784,18 +842,24 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
     pre.qk2 = ldf(qk + i + 64);
 }
 // gate/up rows i < 12 of the thread into pf[4 + i], in two parts: rows i0 <= i < i1
-template <int I0, int I1>
-__device__ __forceinline__ void pf_gu(const bf16* wgu, u32x4* pf, int w) {
-    const bf16* base = wgu + 8 * (threadIdx.x >> 1);
+// (int8: the second part also loads the scale of the row this thread finishes in phase C)
+template <bool W8, int I0, int I1>
+__device__ __forceinline__ void pf_gu(const void* wgu, typename WChunk<W8>::T* pf, Pre& pre, int w) {
+    const size_t base = 8 * (threadIdx.x >> 1);
     const int r0 = 12 * (threadIdx.x & 1);
 #pragma unroll
-    for (int i = I0; i < I1; ++i) pf[4 + i] = ldw16(base + (size_t)gu_row(w, r0 + i) * D);
+    for (int i = I0; i < I1; ++i) pf[4 + i] = ldwc<W8>(wgu, base + (size_t)gu_row(w, r0 + i) * D);
+    if constexpr (W8 && I1 == 12) {
+        if (threadIdx.x < 192) pre.sg = ldf(row_scales(wgu, (size_t)2 * F * D) + gu_row(w, threadIdx.x >> 3));
+    }
 }
 // pf[i] = row 32j + (t >> 3) of Wd at columns DCOLS g + 8 ((t & 7) + 8 i) .. + 7 (i < 6)
-__device__ __forceinline__ void pf_down(const MegaLayer& L, u32x4* pf, int g, int j) {
-    const bf16* base = L.wd + (size_t)(32 * j + (threadIdx.x >> 3)) * F + DCOLS * g + 8 * (threadIdx.x & 7);
+template <bool W8>
+__device__ __forceinline__ void pf_down(const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre, int g, int j) {
+    const size_t base = (size_t)(32 * j + (threadIdx.x >> 3)) * F + DCOLS * g + 8 * (threadIdx.x & 7);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pf[i] = ldw16(base + 64 * i);
+    for (int i = 0; i < 6; ++i) pf[i] = ldwc<W8>(L.wd, base + 64 * i);
+    if constexpr (W8) pre.sd = ldf(row_scales(L.wd, (size_t)D * F) + 32 * j + (threadIdx.x >> 3));
 }
 
 // long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
@@ -816,7 +880,7 @@ __device__ __forceinline__ size_t group_chunk(int gg, int i) {
 // the whole range); 1: split-K attention over chunks; 2: the same with the chunk rows staged
 // in double-buffered halves (contexts above LONG_T). Separate instances, so the code and
 // registers of one path do not touch the others.
-template <int MODE, bool CAUSAL>
+template <int MODE, bool CAUSAL, bool W8>
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     constexpr bool LONG = MODE == 2;
     static_assert(!CAUSAL || MODE == 0, "causal rows run in the short-context instance only");
@@ -824,7 +888,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int B = p.B;
-    u32x4 pf[16];
+    typedef typename WChunk<W8>::T WT;   // one weight chunk: 8 bf16, or 8 int8 codes
+    WT pf[16];
     Pre pre;
     // kv group and row block: the 32 workgroups of group g are those with w % 8 == g, which
     // the dispatcher places on XCD g (workgroup w runs on XCD w % 8)
@@ -853,7 +918,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         sm.rs[b][i] = (float)sd;
     }
     __syncthreads();
-    pf_qkv(p, sm.layers[0], pf, pre, w);
+    pf_qkv<W8>(p, sm.layers[0], pf, pre, w);
     int tslot = 0;
     trace_at(p, sm, tslot++);
 
@@ -875,10 +940,17 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             f32x4 v;                      // this thread's elements 4 tid .. 4 tid + 3 of x
             if (layer == 0) {
                 const int t = clamp_tok(p, b);
-                const unsigned* e = reinterpret_cast<const unsigned*>(p.embed + (size_t)t * D + 4 * tid);
-                const unsigned e0 = *(const GLOBAL_AS unsigned*)e, e1 = *(const GLOBAL_AS unsigned*)(e + 1);
-                v = f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xFFFF0000u), __uint_as_float(e1 << 16),
-                          __uint_as_float(e1 & 0xFFFF0000u)};
+                if constexpr (W8) {     // row t of the embedding: codes times the row's scale
+                    const uint8_t* e8p = reinterpret_cast<const uint8_t*>(p.embed);
+                    const unsigned e8 = *(const GLOBAL_AS unsigned*)(e8p + (size_t)t * D + 4 * tid);
+                    const float es = ldf(row_scales(p.embed, (size_t)p.vocab * D) + t);
+                    v = f32x4{sb(e8, 0) * es, sb(e8, 1) * es, sb(e8, 2) * es, sb(e8, 3) * es};
+                } else {
+                    const unsigned* e = reinterpret_cast<const unsigned*>(p.embed + (size_t)t * D + 4 * tid);
+                    const unsigned e0 = *(const GLOBAL_AS unsigned*)e, e1 = *(const GLOBAL_AS unsigned*)(e + 1);
+                    v = f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xFFFF0000u), __uint_as_float(e1 << 16),
+                              __uint_as_float(e1 & 0xFFFF0000u)};
+                }
             } else {
                 u32x4 c[2];
                 ok = poll_own<2>(X + (size_t)b * W_X, W_X, FxPair{}, c, p.err, FxComplete{}) && ok;
@@ -903,10 +975,11 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 const f32x4 q0 = src[sub], q1 = src[sub + 16];
                 float s = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
                 s = sum16(s) * norm_scale(p, sm, b);
+                if constexpr (W8) s *= pre.sa;
                 if (sub == 0) put_xcd(QKV + (size_t)b * W_QKV + qkv_row0(w) + r, s);
             }
         }
-        pf_oproj(L, pf, g, j);
+        pf_oproj<W8>(L, pf, pre, g, j);
         trace_at(p, sm, tslot++);
 
         // ---------------- B: attention of kv group g and its O-projection partial
@@ -922,7 +995,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
-                if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);              // streams during the attention
+                if (b == 0) pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep<CAUSAL>(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
@@ -944,7 +1017,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                                  p.err))
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
-                    if (b == 0) pf_gu<0, 4>(L.wgu, pf, w);          // streams during the attention
+                    if (b == 0) pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep<false>(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
@@ -953,7 +1026,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     for (int e = tid; e < 2 * PART; e += NT) put_xcd(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
-                    pf_gu<0, 4>(L.wgu, pf, w);
+                    pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
                     trace_at(p, sm, tslot++);
                     trace_at(p, sm, tslot++);
                 }
@@ -1012,8 +1085,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             // memory operation (the atomics' round trip included) before the table read
             const bf16* wgu = uniform_ptr(L.wgu);
             const float* pnorm = uniform_ptr(L.post_norm);
-            oproj_partial(sm, pf, P, g, j, B);
-            pf_gu<4, 12>(wgu, pf, w);
+            oproj_partial(sm, pf, P, g, j, B, pre.so);
+            pf_gu<W8, 4, 12>(wgu, pf, pre, w);
             pre.nw = ldf4(pnorm + 4 * tid);
         }
         trace_at(p, sm, tslot++);
@@ -1050,7 +1123,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) s += (q[i][0] + q[i][1]) + (q[i][2] + q[i][3]);
                     s = sum8(s);
-                    if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b);
+                    if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b) * (W8 ? pre.sg : 1.0f);
                 }
             }
             __syncthreads();
@@ -1060,7 +1133,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 put_xcd(A + (size_t)b * W_A + gu_col0(w) + c, gt / (1.0f + expf(-gt)) * up);
             }
         }
-        pf_down(L, pf, g, j);
+        pf_down<W8>(L, pf, pre, g, j);
         trace_at(p, sm, tslot++);
 
         // ---------------- D: rows 32j..32j+31 of Wd[:, DCOLS g : DCOLS (g + 1)] . a (plus x' for
@@ -1084,8 +1157,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             }
         }
         trace_at(p, sm, tslot++);
-        down_partial(sm, pf, Xn, g, j, B);
-        if (layer + 1 < p.n_layers) pf_qkv(p, sm.layers[layer + 1], pf, pre, w);
+        down_partial(sm, pf, Xn, g, j, B, pre.sd);
+        if (layer + 1 < p.n_layers) pf_qkv<W8>(p, sm.layers[layer + 1], pf, pre, w);
         else pre.nw = ldf4(p.final_norm + 4 * tid);
         trace_at(p, sm, tslot++);
         __syncthreads();
@@ -1100,16 +1173,18 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     }
     const int r0 = (int)((long long)p.vocab * w / NWG), r1 = (int)((long long)p.vocab * (w + 1) / NWG);
     const int rsub = tid >> 4, sub = tid & 15;   // 16 rows per pass, 16 lanes per row
-    u32x4 b0[8], b1[8], b2[8];                     // three passes: two loads in flight
-    auto load_rows = [&](int base, u32x4* dst) {
+    WT b0[8], b1[8], b2[8];                        // three passes: two loads in flight
+    float s0 = 1.f, s1 = 1.f, s2 = 1.f;            // int8: the rows' scales
+    auto load_rows = [&](int base, WT* dst, float& sc) {
         const int row = base + rsub;
         if (row < r1) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = ldw16(p.embed + (size_t)row * D + (sub + 16 * i) * 8);
+            for (int i = 0; i < 8; ++i) dst[i] = ldwc<W8>(p.embed, (size_t)row * D + (sub + 16 * i) * 8);
+            if constexpr (W8) sc = ldf(row_scales(p.embed, (size_t)p.vocab * D) + row);
         }
     };
-    load_rows(r0, b0);                             // in flight while the last layer finishes
-    load_rows(r0 + 16, b1);
+    load_rows(r0, b0, s0);                         // in flight while the last layer finishes
+    load_rows(r0 + 16, b1, s1);
     {
         const float* Xl = p.ex + (size_t)p.n_layers * p.ex_layer;
         bool okl = true;
@@ -1127,7 +1202,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     u64 best[BMAX] = {0ull, 0ull, 0ull, 0ull};
     bool bad = false;
     {
-        auto rows_dot = [&](int base, const u32x4* wv) {
+        auto rows_dot = [&](int base, const WT* wv, float sc) {
             const int row = base + rsub;
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
@@ -1136,6 +1211,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 float s = 0.f;
                 if (row < r1) s = dot_chunks<8>(wv, sm.u.s.act[b], sub, 16);
                 s = sum16(s) * rn[b];
+                if constexpr (W8) s *= sc;
                 if (row < r1 && sub == 0) {
                     p.logits[(size_t)(b - hf) * p.vocab + row] = s;
                     bad |= !isfinite(s);
@@ -1145,12 +1221,12 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             }
         };
         for (int base = r0; base < r1; base += 48) {
-            load_rows(base + 32, b2);
-            rows_dot(base, b0);
-            load_rows(base + 48, b0);
-            rows_dot(base + 16, b1);
-            load_rows(base + 64, b1);
-            rows_dot(base + 32, b2);
+            load_rows(base + 32, b2, s2);
+            rows_dot(base, b0, s0);
+            load_rows(base + 48, b0, s0);
+            rows_dot(base + 16, b1, s1);
+            load_rows(base + 64, b1, s1);
+            rows_dot(base + 32, b2, s2);
         }
     }
     if (bad) atomicOr(p.err, Q3_DEVERR_NONFINITE);
@@ -1278,6 +1354,13 @@ hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
     return hipGetLastError();
 }
 
+// [bf16 / int8 weights][short, split-K, split-K double-buffered, short with causal rows]
+static const void* const kInstances[2][4] = {
+    {(const void*)k_decode_mega<0, false, false>, (const void*)k_decode_mega<1, false, false>,
+     (const void*)k_decode_mega<2, false, false>, (const void*)k_decode_mega<0, true, false>},
+    {(const void*)k_decode_mega<0, false, true>, (const void*)k_decode_mega<1, false, true>,
+     (const void*)k_decode_mega<2, false, true>, (const void*)k_decode_mega<0, true, true>}};
+
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s) {
     if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers || p.head_first < 0 ||
         p.head_first > p.B)
@@ -1291,25 +1374,21 @@ hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t
     }
     if (!p.causal && p.head_first != 0) return hipErrorInvalidValue;
     const int mode = p.causal ? 3 : Tmax <= SHORT_T ? 0 : Tmax <= LONG_T ? 1 : 2;
-    const void* fn = mode == 0 ? (const void*)k_decode_mega<0, false>
-                     : mode == 1 ? (const void*)k_decode_mega<1, false>
-                     : mode == 2 ? (const void*)k_decode_mega<2, false> : (const void*)k_decode_mega<0, true>;
+    const void* fn = kInstances[p.w8 ? 1 : 0][mode];
     if (cooperative) {
         void* args[] = {(void*)&p};
         return hipLaunchCooperativeKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
     }
-    if (mode == 0) hipLaunchKernelGGL((k_decode_mega<0, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else if (mode == 1) hipLaunchKernelGGL((k_decode_mega<1, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else if (mode == 2) hipLaunchKernelGGL((k_decode_mega<2, false>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    else hipLaunchKernelGGL((k_decode_mega<0, true>), dim3(NWG), dim3(NT), sizeof(Smem), s, p);
-    return hipGetLastError();
+    void* args[] = {(void*)&p};
+    return hipLaunchKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
 }
 
 hipError_t decode_mega_prepare() {
-    for (const void* fn : {(const void*)k_decode_mega<0, false>, (const void*)k_decode_mega<1, false>,
-                           (const void*)k_decode_mega<2, false>, (const void*)k_decode_mega<0, true>}) {
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
-        if (e != hipSuccess) return e;
+    for (int w8 = 0; w8 < 2; ++w8) {
+        for (const void* fn : kInstances[w8]) {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -14,23 +14,26 @@ namespace q3 {
 
 template <typename WT>
 __global__ void k_embed(const int32_t* __restrict__ tok, const WT* __restrict__ E,
-                        float* __restrict__ x, int d, int vocab, unsigned* err) {
+                        float* __restrict__ x, int d, int vocab, unsigned* err, const float* __restrict__ rowscale) {
     const int r = blockIdx.x;
     int t = tok[r];
     const bool ok = (t >= 0) && (t < vocab);
     if (!ok && threadIdx.x == 0) atomicOr(err, Q3_DEVERR_TOKEN);
     const WT* src = E + (size_t)(ok ? t : 0) * d;
     float* dst = x + (size_t)r * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = ok ? ldw(src, i) : 0.f;
+    const float sc = rowscale && ok ? rowscale[t] : 1.f;   // int8 codes: the row's scale
+    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = ok ? (rowscale ? ldw(src, i) * sc : ldw(src, i)) : 0.f;
 }
 
 hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
-                        int vocab, unsigned* err, hipStream_t s) {
+                        int vocab, unsigned* err, hipStream_t s, const float* rowscale) {
     if (rows <= 0) return hipSuccess;
     if (wdt == DT_BF16)
-        hipLaunchKernelGGL(k_embed<bf16>, dim3(rows), dim3(256), 0, s, tok, (const bf16*)E, x, d, vocab, err);
+        hipLaunchKernelGGL(k_embed<bf16>, dim3(rows), dim3(256), 0, s, tok, (const bf16*)E, x, d, vocab, err,
+                           rowscale);
     else
-        hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, x, d, vocab, err);
+        hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(256), 0, s, tok, (const float*)E, x, d, vocab, err,
+                           rowscale);
     return hipGetLastError();
 }
 

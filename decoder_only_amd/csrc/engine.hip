@@ -13,6 +13,7 @@
 // keeps ~16 significant bits where a single bf16 rounding would cost ~5e-3 relative
 // error in the logits. The last row then goes through the float32 decode path, which
 // gives the same result as a full prefill by causality (a row only sees earlier slots).
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -40,10 +41,14 @@ struct q3_engine {
     std::vector<void*> allocs;
 
     struct Layer {
-        void *wqkv, *wo, *wgu, *wd;
+        void *wqkv, *wo, *wgu, *wd;       // bf16 (or float32) matrices; int8 engines: the codes as bf16
         float *in_norm, *post_norm, *q_norm, *k_norm;
+        uint8_t *wqkv8 = nullptr, *wo8 = nullptr, *wgu8 = nullptr, *wd8 = nullptr;   // int8: the codes
+        float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;          // int8: row scales
     };
     void* embed = nullptr;
+    uint8_t* embed8 = nullptr;     // int8: embedding codes and row scales
+    float* escale = nullptr;
     std::vector<Layer> layers;
     float* final_norm = nullptr;
     float* inv_freq = nullptr;
@@ -97,7 +102,9 @@ struct q3_engine {
     float *pf_x = nullptr, *pf_qkv = nullptr, *pf_h = nullptr, *pf_q = nullptr, *pf_o = nullptr,
           *pf_a = nullptr;
 
-    size_t wbytes() const { return cfg.weight_dtype == Q3_BF16 ? 2 : 4; }
+    bool i8() const { return cfg.weight_dtype == Q3_I8; }
+    // bytes per weight a decode step streams (int8: the codes; their row scales are counted apart)
+    size_t wbytes() const { return cfg.weight_dtype == Q3_F32 ? 4 : (cfg.weight_dtype == Q3_BF16 ? 2 : 1); }
     size_t kvbytes() const { return cfg.kv_dtype == Q3_BF16 ? 2 : 4; }
     int qkv_rows() const { return (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim; }
 
@@ -174,6 +181,39 @@ std::vector<float> to_f32(const q3_tensor& t) {
 
 }  // namespace
 
+// Weight-only int8 rule of one row (q3_quantize_i8): s = fl32(max |w| / 127), q = round half
+// to even of fl32(w / s), clamped to [-127, 127]; an all-zero row gives s = 0, q = 0. Every
+// step is one IEEE float32 operation (no contraction), so any implementation agrees.
+static void quantize_row_i8(const float* w, int64_t n, int8_t* q, float* s) {
+    float amax = 0.f;
+    for (int64_t k = 0; k < n; ++k) amax = std::max(amax, std::fabs(w[k]));
+    const float sc = amax / 127.0f;
+    *s = sc;
+    for (int64_t k = 0; k < n; ++k) {
+        float r = sc > 0.f ? std::nearbyint(w[k] / sc) : 0.f;
+        r = std::min(127.f, std::max(-127.f, r));
+        q[k] = (int8_t)r;
+    }
+}
+
+extern "C" q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q,
+                                    float* scale) {
+    if (!w || !q || !scale || rows < 0 || cols <= 0 || (dtype != Q3_F32 && dtype != Q3_BF16)) return Q3_ERR_ARG;
+    std::vector<float> row((size_t)cols);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < cols; ++k) {
+            if (dtype == Q3_F32) {
+                row[k] = ((const float*)w)[r * cols + k];
+            } else {
+                const uint32_t bits = (uint32_t)((const uint16_t*)w)[r * cols + k] << 16;
+                memcpy(&row[k], &bits, 4);
+            }
+        }
+        quantize_row_i8(row.data(), cols, q + r * cols, scale + r);
+    }
+    return Q3_OK;
+}
+
 static q3_status validate_config(const q3_config* c, std::string& why) {
     if (!c) { why = "config is NULL"; return Q3_ERR_ARG; }
     if (c->n_layers < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->ffn <= 0 ||
@@ -183,7 +223,14 @@ static q3_status validate_config(const q3_config* c, std::string& why) {
     if (c->hidden % 128 || c->ffn % 128 || (c->n_heads * 128) % 128) { why = "hidden and ffn must be multiples of 128"; return Q3_ERR_ARG; }
     if (c->vocab % 2) { why = "vocab must be even"; return Q3_ERR_ARG; }
     if (c->tie_embeddings != 1) { why = "only a tied LM head is supported"; return Q3_ERR_ARG; }
-    if ((c->weight_dtype != Q3_F32 && c->weight_dtype != Q3_BF16) || (c->kv_dtype != Q3_F32 && c->kv_dtype != Q3_BF16)) { why = "bad dtype"; return Q3_ERR_ARG; }
+    if ((c->weight_dtype != Q3_F32 && c->weight_dtype != Q3_BF16 && c->weight_dtype != Q3_I8) ||
+        (c->kv_dtype != Q3_F32 && c->kv_dtype != Q3_BF16)) { why = "bad dtype"; return Q3_ERR_ARG; }
+    if (c->weight_dtype == Q3_I8 && (c->kv_dtype != Q3_BF16 || c->hidden != 1024 || c->n_heads != 16 ||
+                                     c->n_kv_heads != 8 || c->ffn != 3072 || c->n_layers < 1 ||
+                                     c->n_layers > kMegaMaxLayers || c->max_batch > kMegaMaxRows)) {
+        why = "int8 weights need the Qwen3-0.6B layer shape, a bf16 cache and at most 4 sequence slots";
+        return Q3_ERR_ARG;
+    }
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) { why = "bad rms_eps or rope_theta"; return Q3_ERR_ARG; }
     return Q3_OK;
 }
@@ -203,13 +250,15 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         byname[weights[i].name] = &weights[i];
     }
     const int d = c.hidden, dh = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
-    const size_t wb = c.weight_dtype == Q3_BF16 ? 2 : 4;
+    const bool i8 = c.weight_dtype == Q3_I8;
+    const size_t wb = c.weight_dtype == Q3_F32 ? 4 : 2;   // bytes per element of L.wqkv etc.
 
     auto need = [&](const std::string& name, int64_t numel, bool norm, const q3_tensor** t) -> q3_status {
         auto it = byname.find(name);
         if (it == byname.end()) return Q3_ERR_SHAPE;
         if (it->second->numel != numel) return Q3_ERR_SHAPE;
-        if (!norm && it->second->dtype != c.weight_dtype) return Q3_ERR_SHAPE;
+        if (!norm && !i8 && it->second->dtype != c.weight_dtype) return Q3_ERR_SHAPE;
+        if (!norm && i8 && it->second->dtype != Q3_F32 && it->second->dtype != Q3_BF16) return Q3_ERR_SHAPE;
         if (norm && it->second->dtype != Q3_F32 && it->second->dtype != Q3_BF16) return Q3_ERR_SHAPE;
         *t = it->second;
         return Q3_OK;
@@ -252,14 +301,87 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         return (float*)upload(f.data(), f.size() * 4);
     };
 
-    e->embed = upload(byname["model.embed_tokens.weight"]->data, (size_t)V * d * wb);
-    if (!e->embed) return oom();
+    // int8 weights: each matrix, its rows in the engine's packed order, quantised row by row;
+    // uploaded as the codes (the persistent decode kernel), as the codes in bf16 (exact:
+    // |q| <= 127; the prefill GEMMs, which apply the scale per output column) and the scales
+    auto quant_upload = [&](const std::vector<std::pair<const q3_tensor*, int64_t>>& rows, int cols, void** bf16q,
+                            uint8_t** u8, float** sc) -> bool {
+        const size_t R = rows.size();
+        std::vector<uint16_t> hq(R * cols);
+        std::vector<uint8_t> hu(R * cols);
+        std::vector<float> hs(R), rowf(cols);
+        std::vector<int8_t> qrow(cols);
+        for (size_t r = 0; r < R; ++r) {
+            const q3_tensor* t = rows[r].first;
+            const int64_t src = rows[r].second * cols;
+            for (int k = 0; k < cols; ++k) {
+                if (t->dtype == Q3_F32) {
+                    rowf[k] = ((const float*)t->data)[src + k];
+                } else {
+                    const uint32_t bits = (uint32_t)((const uint16_t*)t->data)[src + k] << 16;
+                    memcpy(&rowf[k], &bits, 4);
+                }
+            }
+            quantize_row_i8(rowf.data(), cols, qrow.data(), &hs[r]);
+            for (int k = 0; k < cols; ++k) {
+                const float f = (float)qrow[k];
+                uint32_t b;
+                memcpy(&b, &f, 4);
+                hq[r * cols + k] = (uint16_t)(b >> 16);
+                hu[r * cols + k] = (uint8_t)qrow[k];
+            }
+        }
+        // the persistent kernel's buffer: the codes, then the scales (it finds them at a fixed offset)
+        hu.resize(R * cols + 4 * R);
+        memcpy(hu.data() + R * cols, hs.data(), 4 * R);
+        if (!(*bf16q = upload(hq.data(), hq.size() * 2)) || !(*u8 = (uint8_t*)upload(hu.data(), hu.size())))
+            return false;
+        *sc = (float*)(*u8 + R * cols);
+        return true;
+    };
+    auto rows_of = [&](std::vector<std::pair<const q3_tensor*, int64_t>>& v, const std::string& name, int64_t r0,
+                       int64_t n) {
+        const q3_tensor* t = byname[name];
+        for (int64_t r = r0; r < r0 + n; ++r) v.emplace_back(t, r);
+    };
+    if (i8) {
+        std::vector<std::pair<const q3_tensor*, int64_t>> rows;
+        rows_of(rows, "model.embed_tokens.weight", 0, V);
+        if (!quant_upload(rows, d, &e->embed, &e->embed8, &e->escale)) return oom();
+    } else {
+        e->embed = upload(byname["model.embed_tokens.weight"]->data, (size_t)V * d * wb);
+        if (!e->embed) return oom();
+    }
     if (!(e->final_norm = upload_norm("model.norm.weight"))) return oom();
     e->layers.resize(c.n_layers);
     std::vector<uint8_t> buf;
     for (int l = 0; l < c.n_layers; ++l) {
         const std::string p = "model.layers." + std::to_string(l) + ".";
         auto& L = e->layers[l];
+        if (i8) {
+            std::vector<std::pair<const q3_tensor*, int64_t>> r;
+            rows_of(r, p + "self_attn.q_proj.weight", 0, (int64_t)Hq * dh);
+            rows_of(r, p + "self_attn.k_proj.weight", 0, (int64_t)Hkv * dh);
+            rows_of(r, p + "self_attn.v_proj.weight", 0, (int64_t)Hkv * dh);
+            if (!quant_upload(r, d, &L.wqkv, &L.wqkv8, &L.sqkv)) return oom();
+            r.clear();
+            rows_of(r, p + "self_attn.o_proj.weight", 0, d);
+            if (!quant_upload(r, Hq * dh, &L.wo, &L.wo8, &L.so)) return oom();
+            r.clear();
+            for (int j = 0; j < F / 16; ++j) {          // gate/up packed as for bf16 weights
+                rows_of(r, p + "mlp.gate_proj.weight", 16 * j, 16);
+                rows_of(r, p + "mlp.up_proj.weight", 16 * j, 16);
+            }
+            if (!quant_upload(r, d, &L.wgu, &L.wgu8, &L.sgu)) return oom();
+            r.clear();
+            rows_of(r, p + "mlp.down_proj.weight", 0, d);
+            if (!quant_upload(r, F, &L.wd, &L.wd8, &L.sd)) return oom();
+            if (!(L.in_norm = upload_norm(p + "input_layernorm.weight"))) return oom();
+            if (!(L.post_norm = upload_norm(p + "post_attention_layernorm.weight"))) return oom();
+            if (!(L.q_norm = upload_norm(p + "self_attn.q_norm.weight"))) return oom();
+            if (!(L.k_norm = upload_norm(p + "self_attn.k_norm.weight"))) return oom();
+            continue;
+        }
         // QKV packed as [q rows; k rows; v rows]
         const size_t qb = (size_t)Hq * dh * d * wb, kb = (size_t)Hkv * dh * d * wb;
         buf.resize(qb + 2 * kb);
@@ -320,18 +442,26 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         hipDeviceProp_t prop;
         int occ = 0;
         const bool shape = d == 1024 && Hq == 16 && Hkv == 8 && dh == 128 && F == 3072 &&
-                           c.weight_dtype == Q3_BF16 && c.kv_dtype == Q3_BF16 && c.n_layers > 0 && c.n_layers <= kMegaMaxLayers;
+                           (c.weight_dtype == Q3_BF16 || i8) && c.kv_dtype == Q3_BF16 && c.n_layers > 0 &&
+                           c.n_layers <= kMegaMaxLayers;
         if (shape && hipGetDeviceProperties(&prop, e->device) == hipSuccess && prop.multiProcessorCount == 256) {
             if (decode_mega_prepare() == hipSuccess) e->mega_ok = true;
             else (void)hipGetLastError();   // not usable here: clear the error, use the per-operation path
         }
         (void)occ;
+        if (i8 && !e->mega_ok) {
+            q3_free(e);
+            return Q3_ERR_HIP;     // int8 decode runs only in the persistent kernel (a 256-CU GPU)
+        }
         if (e->mega_ok) {
             std::vector<MegaLayer> hl(c.n_layers);
             for (int l = 0; l < c.n_layers; ++l) {
                 const auto& L = e->layers[l];
-                hl[l] = MegaLayer{(const uint16_t*)L.wqkv, (const uint16_t*)L.wo, (const uint16_t*)L.wgu,
-                                  (const uint16_t*)L.wd, L.in_norm, L.post_norm, L.q_norm, L.k_norm};
+                // (int8: the matrix buffers of codes + scales)
+                hl[l] = i8 ? MegaLayer{(const uint16_t*)L.wqkv8, (const uint16_t*)L.wo8, (const uint16_t*)L.wgu8,
+                                       (const uint16_t*)L.wd8, L.in_norm, L.post_norm, L.q_norm, L.k_norm}
+                           : MegaLayer{(const uint16_t*)L.wqkv, (const uint16_t*)L.wo, (const uint16_t*)L.wgu,
+                                       (const uint16_t*)L.wd, L.in_norm, L.post_norm, L.q_norm, L.k_norm};
             }
             if (!(e->d_layers = (MegaLayer*)upload(hl.data(), hl.size() * sizeof(MegaLayer)))) return oom();
             e->m_ex_layer = decode_mega_exchange_words_per_layer();
@@ -388,7 +518,9 @@ static double step_bytes(const q3_engine* e, int seq_base, int B) {
     const double wb = (double)e->wbytes();
     const double per_layer = (double)e->qkv_rows() * c.hidden + (double)c.hidden * c.n_heads * c.head_dim +
                              3.0 * c.ffn * c.hidden;
-    const double weights = wb * (per_layer * c.n_layers + (double)c.vocab * c.hidden);
+    double weights = wb * (per_layer * c.n_layers + (double)c.vocab * c.hidden);
+    if (e->i8())                // the row scales (float32) of every matrix
+        weights += 4.0 * ((double)(e->qkv_rows() + c.hidden + 2 * c.ffn + c.hidden) * c.n_layers + c.vocab);
     const double norms = 4.0 * (c.n_layers * (2.0 * c.hidden + 2.0 * c.head_dim) + c.hidden);
     const double kv_write = (double)B * c.n_layers * 2.0 * c.n_kv_heads * c.head_dim * e->kvbytes();
     const double rows = (double)B * (c.hidden * wb + 4.0 * c.vocab);
@@ -419,7 +551,8 @@ static MegaParams mega_params(const q3_engine* e, const int32_t* tokens, const i
     mp.head_first = 0;
     mp.eps = c.rms_eps;
     mp.layers = e->d_layers;
-    mp.embed = (const uint16_t*)e->embed;
+    mp.embed = e->i8() ? (const uint16_t*)e->embed8 : (const uint16_t*)e->embed;
+    mp.w8 = e->i8() ? 1 : 0;
     mp.final_norm = e->final_norm;
     mp.inv_freq = e->inv_freq;
     mp.kc = (uint16_t*)e->kc;
@@ -481,6 +614,8 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     // caller does not want them)
     const bool use_mega = e->mega_ok && B <= kMegaMaxRows && e->decode_path != 1;
     if (!use_mega && e->decode_path == 2) return e->fail(Q3_ERR_STATE, "persistent decode kernel not usable here");
+    if (!use_mega && e->i8())
+        return e->fail(Q3_ERR_STATE, "int8 weights: decode runs only in the persistent kernel (at most 4 rows)");
     if (use_mega) {
         float* lg = logits_out ? logits_out : e->logits;
         MegaParams mp = mega_params(e, tokens, positions, seq_base, B, lg);
@@ -649,7 +784,7 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
     q3_status st = ensure_prefill_ws(e, M);
     if (st != Q3_OK) return e->fail(st, "prefill workspace allocation failed");
     const int t0 = e->h_len[seq];
-    HIPCHK(e, launch_embed(tokens, e->embed, DT_BF16, e->pf_x, M, d, V, e->d_err, s));
+    HIPCHK(e, launch_embed(tokens, e->embed, DT_BF16, e->pf_x, M, d, V, e->d_err, s, e->escale));
     const bool sk = M < kPrefillSplitRows;
     const int split_o = sk ? std::min(kPrefillSplits, Hq * 128 / 1024) : 1;
     const int split_d = sk ? std::min(kPrefillSplits, F / 1024) : 1;
@@ -662,7 +797,7 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
         pending = 0;
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * e->qkv_rows() * d);
         HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wqkv, e->pf_qkv, M, e->qkv_rows(), d,
-                              GEMM_F32, s));
+                              GEMM_F32, s, 1, L.sqkv));
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
                                          e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
@@ -673,24 +808,27 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * Hq * 128);
         if (split_o > 1) {
             HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_parts, M, d, Hq * 128,
-                                  GEMM_PARTIAL_F32, s, split_o));
+                                  GEMM_PARTIAL_F32, s, split_o, L.so));
             pending = split_o;
         } else {
-            HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s));
+            HIPCHK(e, launch_gemm(e->pf_o, GEMM_A_PAIR, (const uint16_t*)L.wo, e->pf_x, M, d, Hq * 128, GEMM_RESID_F32, s,
+                                  1, L.so));
         }
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_rmsnorm(e->pf_x, L.post_norm, e->pf_h, 2, M, d, c.rms_eps, s, e->pf_parts, pending));
         pending = 0;
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * 2 * F * d);
-        HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_PAIR, s));
+        HIPCHK(e, launch_gemm(e->pf_h, GEMM_A_PAIR, (const uint16_t*)L.wgu, e->pf_a, M, 2 * F, d, GEMM_SWIGLU_PAIR, s,
+                              1, L.sgu));
         prof_mark(e, Q3_PROF_GEMM, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * F);
         if (split_d > 1) {
             HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_parts, M, d, F, GEMM_PARTIAL_F32, s,
-                                  split_d));
+                                  split_d, L.sd));
             pending = split_d;
         } else {
-            HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s));
+            HIPCHK(e, launch_gemm(e->pf_a, GEMM_A_PAIR, (const uint16_t*)L.wd, e->pf_x, M, d, F, GEMM_RESID_F32, s, 1,
+                                  L.sd));
         }
         prof_mark(e, Q3_PROF_GEMM, false);
     }
@@ -716,7 +854,7 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
         }
         return Q3_OK;
     }
-    if (e->cfg.weight_dtype == Q3_BF16 && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+    if ((e->cfg.weight_dtype == Q3_BF16 || e->i8()) && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
         if ((st = run_prefill_mfma(e, seq, tokens, n - 1)) != Q3_OK) return st;
         done = n - 1;
     }
@@ -882,6 +1020,7 @@ extern "C" q3_status q3_set_decode_path(q3_engine* e, int32_t path) {
     if (!e) return Q3_ERR_ARG;
     if (path < 0 || path > 3) return e->fail(Q3_ERR_ARG, "decode path must be 0, 1, 2 or 3");
     if (path == 2 && !e->mega_ok) return e->fail(Q3_ERR_STATE, "persistent decode kernel not available for this model/GPU");
+    if (path == 1 && e->i8()) return e->fail(Q3_ERR_STATE, "int8 weights: no per-operation decode path");
     e->decode_path = path;
     return Q3_OK;
 }

@@ -53,7 +53,8 @@ __device__ __forceinline__ void split8(const f32x4& x0, const f32x4& x1, u32x4& 
 // per compute unit at BM = 128) or 1 (two barriers per k-tile, two blocks per compute unit).
 template <int AM, int EPI, int BM, int NB>
 __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ Av, const bf16* __restrict__ W,
-                                                      void* __restrict__ C, int M, int N, int K) {
+                                                      void* __restrict__ C, int M, int N, int K,
+                                                      const float* __restrict__ cs) {
     constexpr bool SPLIT = AM != GEMM_A_BF16;
     constexpr int FM = BM / 32;          // 16-row fragments per wave along M
     constexpr int AJ = BM * 8 / 256;     // 16-byte A chunks per thread and k-tile
@@ -161,6 +162,14 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
 
     // D layout of 16x16 MFMA: lane holds column (lane & 15), rows 4 * (lane >> 4) + r.
     const int col_l = lane & 15, row_l = 4 * (lane >> 4);
+    if (cs) {                          // int8 weights: each output column times its row scale
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float c = cs[n0 + wn * 64 + j * 16 + col_l];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][j] *= c;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -202,15 +211,15 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
 
 template <int AM, int BM, int NB>
 static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
-                           hipStream_t s) {
+                           hipStream_t s, const float* cs) {
     dim3 grid(N / BN, (M + BM - 1) / BM, splits);
     switch (epi) {
-        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
-        case GEMM_PARTIAL_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_PARTIAL_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K); break;
+        case GEMM_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
+        case GEMM_RESID_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_RESID_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
+        case GEMM_SWIGLU_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
+        case GEMM_BF16: hipLaunchKernelGGL((k_gemm<AM, GEMM_BF16, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
+        case GEMM_SWIGLU_PAIR: hipLaunchKernelGGL((k_gemm<AM, GEMM_SWIGLU_PAIR, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
+        case GEMM_PARTIAL_F32: hipLaunchKernelGGL((k_gemm<AM, GEMM_PARTIAL_F32, BM, NB>), grid, dim3(256), 0, s, A, W, C, M, N, K, cs); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -218,25 +227,25 @@ static hipError_t launch_t(const void* A, const uint16_t* W, void* C, int M, int
 
 template <int AM>
 static hipError_t launch_bm(const void* A, const uint16_t* W, void* C, int M, int N, int K, int epi, int splits,
-                            hipStream_t s) {
+                            hipStream_t s, const float* cs) {
     // 64-row tiles: with one LDS buffer (two barriers per k-tile) several blocks share a
     // compute unit and hide each other's loads; with fewer than two blocks per compute unit
     // the double-buffered variant is faster. (Measured on MI355X at the prefill shapes,
     // M = 2047 and 32767: 128-row tiles were 5-25% slower everywhere.)
     const long long blocks64 = (long long)(N / BN) * ((M + 63) / 64) * splits;
-    if (blocks64 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s);
-    return launch_t<AM, 64, 1>(A, W, C, M, N, K, epi, splits, s);
+    if (blocks64 < 512) return launch_t<AM, 64, 2>(A, W, C, M, N, K, epi, splits, s, cs);
+    return launch_t<AM, 64, 1>(A, W, C, M, N, K, epi, splits, s, cs);
 }
 
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
-                       hipStream_t s, int splits) {
+                       hipStream_t s, int splits, const float* cs) {
     if (M <= 0) return hipSuccess;
     if (N % BN != 0 || K % BK != 0 || splits < 1 || splits > K / BK || (splits > 1 && epi != GEMM_PARTIAL_F32))
         return hipErrorInvalidValue;
     switch (a_mode) {
-        case GEMM_A_BF16: return launch_bm<GEMM_A_BF16>(A, W, C, M, N, K, epi, splits, s);
-        case GEMM_A_F32: return launch_bm<GEMM_A_F32>(A, W, C, M, N, K, epi, splits, s);
-        case GEMM_A_PAIR: return launch_bm<GEMM_A_PAIR>(A, W, C, M, N, K, epi, splits, s);
+        case GEMM_A_BF16: return launch_bm<GEMM_A_BF16>(A, W, C, M, N, K, epi, splits, s, cs);
+        case GEMM_A_F32: return launch_bm<GEMM_A_F32>(A, W, C, M, N, K, epi, splits, s, cs);
+        case GEMM_A_PAIR: return launch_bm<GEMM_A_PAIR>(A, W, C, M, N, K, epi, splits, s, cs);
         default: return hipErrorInvalidValue;
     }
 }

@@ -10,9 +10,10 @@ namespace q3 {
 enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
 
 // ---- elementwise.hip
-// x[r, :] = E[tok[r], :] widened to float32. Out-of-range ids set Q3_DEVERR_TOKEN and give a zero row.
+// x[r, :] = E[tok[r], :] widened to float32 (times rowscale[tok[r]] when given: int8 codes held
+// as bf16). Out-of-range ids set Q3_DEVERR_TOKEN and give a zero row.
 hipError_t launch_embed(const int32_t* tok, const void* E, int wdt, float* x, int rows, int d,
-                        int vocab, unsigned* err, hipStream_t s);
+                        int vocab, unsigned* err, hipStream_t s, const float* rowscale = nullptr);
 // out[r, :] = rmsnorm(x[r, :]) * w; out_mode 0 float32, 1 bf16, 2 bf16 pair rows [rows][2d]
 // (d hi parts, then d lo parts). With nparts > 0, first x[r, :] += parts[0][r, :] + ... +
 // parts[nparts-1][r, :] (in that order; parts [nparts][rows][d] float32) and x is written back.
@@ -70,8 +71,10 @@ enum GemmAMode { GEMM_A_BF16 = 0, GEMM_A_F32 = 1, GEMM_A_PAIR = 2 };
 // PARTIAL_F32 (with splits > 1 blocks along K) writes C[split][M][N] float32 partials.
 enum GemmEpi { GEMM_F32 = 0, GEMM_RESID_F32 = 1, GEMM_SWIGLU_F32 = 2, GEMM_BF16 = 3, GEMM_SWIGLU_PAIR = 4,
                GEMM_PARTIAL_F32 = 5 };
+// colscale (int8 weights: W holds the codes in bf16): output column n is multiplied by
+// colscale[n] before the epilogue (for SwiGLU, the gate and up columns by their own scales).
 hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, int M, int N, int K, int epi,
-                       hipStream_t s, int splits = 1);
+                       hipStream_t s, int splits = 1, const float* colscale = nullptr);
 
 // ---- attn_prefill.hip (causal GQA flash attention on MFMA)
 // q: [Hq][M][128] float32 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16;
@@ -81,6 +84,8 @@ hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_
 
 // ---- decode_mega.hip (whole decode step in one cooperative launch; fixed Qwen3-0.6B layer
 // shape: hidden 1024, 16/8 heads of 128, FFN 3072; bf16 weights and KV; 1..4 rows)
+// Matrices of one layer: bf16 weights, or (int8 weights) one buffer per matrix holding the
+// int8 codes [rows][cols] followed by the rows' float32 scales [rows].
 struct MegaLayer {
     const uint16_t *wqkv, *wo, *wgu, *wd;
     const float *in_norm, *post_norm, *q_norm, *k_norm;
@@ -95,7 +100,7 @@ struct MegaParams {
                                     // and argmax candidates; B: no LM head at all
     float eps;
     const MegaLayer* layers;        // device array [n_layers]
-    const uint16_t* embed;
+    const uint16_t* embed;          // bf16 [vocab][hidden], or int8 codes followed by the row scales
     const float *final_norm, *inv_freq;
     uint16_t *kc, *vc;
     size_t kv_layer_elems, kv_seq_elems;
@@ -108,6 +113,7 @@ struct MegaParams {
     unsigned* err;
     unsigned long long* trace;      // optional phase timestamps [2][trace_n] (NULL: off)
     int trace_n;
+    int w8;                         // 1: every matrix (and the embedding) is int8 codes + row scales
 };
 hipError_t decode_mega_prepare();
 // cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.

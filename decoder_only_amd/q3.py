@@ -16,14 +16,14 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq3.so")
 
-F32, BF16 = 0, 1
+F32, BF16, I8 = 0, 1, 2
 OP_PAIR = 2     # single operations: bf16 pair rows (n hi parts, then n lo parts)
 STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -4: "Q3_ERR_CAPACITY", -5: "Q3_ERR_OOM", -6: "Q3_ERR_HIP", -7: "Q3_ERR_STATE",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
     "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export", "q3_kv_fork",
-    "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end",
+    "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end", "q3_quantize_i8",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
     "q3_op_attn_prefill", "q3_op_sample", "q3_op_sample_noalloc",
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_kv_export": ([vp, i32, i32, vp, vp, i32], i32),
         "q3_kv_fork": ([vp, i32, i32, i32], i32),
         "q3_seq_len": ([vp, i32], i32),
+        "q3_quantize_i8": ([vp, i32, c_int64, c_int64, vp, vp], i32),
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
         "q3_free": ([vp], None),
@@ -124,12 +125,13 @@ def _check(code: int, what: str = "", eng=None) -> None:
         raise Q3Error(code, msg)
 
 
-def config(w, max_batch: int, max_seq: int) -> Q3Config:
-    """q3_config of a model description with the synth.Workload fields."""
+def config(w, max_batch: int, max_seq: int, int8: bool = False) -> Q3Config:
+    """q3_config of a model description with the synth.Workload fields; int8: weight-only
+    int8 (the engine quantises the given weights at load)."""
     return Q3Config(n_layers=w.n_layers, hidden=w.hidden, n_heads=w.n_heads,
                     n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn, vocab=w.vocab,
                     rms_eps=w.rms_eps, rope_theta=w.rope_theta, tie_embeddings=1,
-                    weight_dtype=BF16 if w.weight_dtype == "bf16" else F32,
+                    weight_dtype=I8 if int8 else (BF16 if w.weight_dtype == "bf16" else F32),
                     kv_dtype=BF16 if w.kv_dtype == "bf16" else F32,
                     max_batch=max_batch, max_seq=max_seq)
 

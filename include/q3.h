@@ -42,7 +42,7 @@ typedef enum {
     Q3_ERR_NUMERIC = -8    /* a non-finite logit was produced (sticky) */
 } q3_status;
 
-typedef enum { Q3_F32 = 0, Q3_BF16 = 1 } q3_dtype;
+typedef enum { Q3_F32 = 0, Q3_BF16 = 1, Q3_I8 = 2 } q3_dtype;
 
 /* Model and capacity. Only the Qwen3 block structure is supported: head_dim 128,
  * n_heads a multiple of n_kv_heads, hidden and ffn multiples of 128, a tied LM
@@ -59,7 +59,11 @@ typedef struct {
     float rms_eps;         /* 1e-6 */
     float rope_theta;      /* 1e6 */
     int32_t tie_embeddings;/* must be 1: the LM head is the embedding matrix */
-    int32_t weight_dtype;  /* q3_dtype of the matrices: Q3_BF16, or Q3_F32 */
+    int32_t weight_dtype;  /* q3_dtype of the matrices: Q3_BF16, Q3_F32, or Q3_I8 (weight-only int8:
+                              the engine quantises the given bf16 / float32 matrices at load
+                              with the rule of q3_quantize_i8 and computes with scale * code;
+                              needs the Qwen3-0.6B layer shape, a bf16 cache, decode batches of at
+                              most 4 rows and the persistent decode kernel) */
     int32_t kv_dtype;      /* q3_dtype of the KV cache */
     int32_t max_batch;     /* number of sequence slots (rows of a decode step) */
     int32_t max_seq;       /* KV-cache capacity per sequence, in tokens */
@@ -72,7 +76,8 @@ typedef struct {
  * model.layers.{i}.self_attn.{q,k}_norm.weight [head_dim],
  * model.layers.{i}.post_attention_layernorm.weight [hidden],
  * model.layers.{i}.mlp.{gate,up,down}_proj.weight; and model.norm.weight.
- * Matrices must have dtype == weight_dtype; norm weights may be Q3_F32 or Q3_BF16.
+ * Matrices must have dtype == weight_dtype (Q3_BF16 or Q3_F32 when weight_dtype is Q3_I8);
+ * norm weights may be Q3_F32 or Q3_BF16.
  * lm_head.weight, if given, is ignored (tied head). */
 typedef struct {
     const char* name;
@@ -121,6 +126,14 @@ q3_status q3_decode_step(q3_engine* e, const int32_t* tokens, const int32_t* pos
  * Errors: Q3_ERR_ARG (batch, temperature < 0, missing uniforms). */
 q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch, float temperature,
                     float top_p, const float* uniforms, int32_t* tokens_out);
+
+/* Weight-only int8 codes of a [rows, cols] matrix (host memory, dtype Q3_BF16 or Q3_F32),
+ * one scale per row ("What the script leaves out": production weights in 8 bits; the
+ * article gives no scheme, so the plainest symmetric one): s = fl32(max_k |w_k| / 127),
+ * q_k = round-half-even(fl32(w_k / s)) clamped to [-127, 127], q = 0 for an all-zero row;
+ * the quantised weight is s * q. q: host int8 [rows, cols]; scale: host float [rows].
+ * Host code only (no GPU). This is the rule q3_load applies for Q3_I8. Errors: Q3_ERR_ARG. */
+q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q, float* scale);
 
 /* Empty sequence slot `seq` (its cache length becomes 0). */
 q3_status q3_reset(q3_engine* e, int32_t seq);
