@@ -11,7 +11,7 @@ Also reported (one JSON line, under "extras"): the 2048-token prompt's prefill t
 its 256 sampled decode steps, batch-64 decode tokens/s with 4096 pre-filled KV slots per
 sequence, the 32768-token prefill (GEMM and attention TFLOP/s) and its 512 sampled decode
 steps, each with its roofline fraction; a 262,136-token prefill and decode at ~262K cached
-slots; the roofline of the dominant kernel (event-timed on the engine's stream), and the CPU
+slots; the bs1 workload on weight-only int8 weights; the roofline of the dominant kernel (event-timed on the engine's stream), and the CPU
 oracle on this host (a bounded sample of decode steps and one 2048-token prefill).
 """
 from __future__ import annotations
@@ -170,6 +170,12 @@ def main() -> int:
         except Exception as ex:
             extras["bs64_error"] = repr(ex)
 
+    if not args.no_extras:
+        try:
+            extras.update(int8_line(weights, q3, torch, synth, args.steps))
+        except Exception as ex:
+            extras["int8_error"] = repr(ex)
+
     cpu = None
     if not args.no_cpu:
         try:
@@ -326,6 +332,50 @@ def c5_lines(weights, q3, torch, synth):
             "c5_decode_tok_s": round(wl.decode_steps / dt, 1),
             "c5_decode_step_us": round(1e3 * prof["ms"] / max(1, prof["launches"]), 2),
             "c5_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def int8_line(weights, q3, torch, synth, steps):
+    """The bs1 workload (5-token prompt, 128 greedy steps per generation) on an engine whose
+    weights are quantised to int8 at load (one byte per weight plus a float scale per row):
+    decode tok/s over whole generations, and the persistent kernel's HBM fraction against
+    the int8 step's algorithmic bytes."""
+    w = synth.workload("bs1_short")
+    eng = q3.Engine(q3.config(w, 1, w.max_seq + 1, int8=True), weights)
+    try:
+        eng.set_decode_path(3)
+        prompt = torch.from_numpy(synth.prompt_tokens(w)).cuda()
+        tok = torch.empty(1, dtype=torch.int32, device="cuda")
+
+        def generation():
+            eng.reset(0)
+            eng.prefill(0, prompt)
+            eng.sample(tok, 0.0)
+            for _ in range(w.decode_steps):
+                eng.decode_step(tok)
+                eng.sample(tok, 0.0)
+
+        generation()
+        eng.sync()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            generation()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        eng.profile_begin(q3.PROF_DECODE_STEP)
+        for _ in range(steps):
+            generation()
+        prof = eng.profile_end()
+        eng.sync()
+    finally:
+        eng.close()
+    gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
+    us = 1e3 * prof["ms"] / prof["launches"]
+    log(f"int8 bs1 decode: {w.decode_steps * steps / dt:.0f} tok/s; step {us:.1f} us "
+        f"({prof['bytes'] / prof['launches'] / 1e9:.3f} GB, {gbs:.0f} GB/s)")
+    return {"int8_bs1_decode_tok_s": round(w.decode_steps * steps / dt, 2), "int8_decode_step_us": round(us, 2),
+            "int8_step_bytes": round(prof["bytes"] / prof["launches"]),
+            "int8_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def ctx262k_lines(weights, q3, torch, synth):
