@@ -2,8 +2,9 @@
 
 The oracle's own token is fed to both sides at every step, so a single near-tie in
 the argmax cannot make the two runs diverge. Per step and row the comparison reports
-max-abs and relative-L2 logit error, whether the argmax agrees, and the oracle's
-top-2 logit gap.
+max-abs and relative-L2 logit error, whether the greedy pick agrees (the oracle's argmax,
+or a token whose oracle logit is within near_tie() of it: logits fixed only to a
+tolerance cannot order two tokens closer than that), and the oracle's top-2 logit gap.
 """
 from __future__ import annotations
 
@@ -35,9 +36,17 @@ def top2_gap(l: np.ndarray) -> float:
     return float(abs(t[1] - t[0]))
 
 
+def near_tie(ref: np.ndarray) -> float:
+    """Greedy picks within this much of the oracle's largest logit are all correct: twice
+    the per-element deviation that the relative-L2 bar allows on average (REL_L2 times the
+    row's rms logit). Above it the engine must pick the oracle's argmax."""
+    return 2.0 * REL_L2 * float(np.sqrt(np.mean(np.square(ref.astype(np.float64)))))
+
+
 def compare(step: int, row: int, got: np.ndarray, ref: np.ndarray) -> StepStat:
-    return StepStat(step, row, float(np.abs(got - ref).max()), rel_l2(got, ref),
-                    int(np.argmax(got)) == int(np.argmax(ref)), top2_gap(ref))
+    ga, ra = int(np.argmax(got)), int(np.argmax(ref))
+    ok = ga == ra or float(ref[ra]) - float(ref[ga]) < near_tie(ref)
+    return StepStat(step, row, float(np.abs(got - ref).max()), rel_l2(got, ref), ok, top2_gap(ref))
 
 
 def failures(stats: List[StepStat], greedy: bool = True) -> List[StepStat]:
