@@ -15,7 +15,8 @@ namespace q3 {
 
 namespace {
 
-constexpr int CHUNK = 256;     // keys per block (64 per wave)
+constexpr int CHUNK = 256;     // keys per block (64 per wave): one page of a paged cache
+static_assert(CHUNK == kKvPage, "a decode chunk is one cache page");
 constexpr int G = 2;           // query heads per kv head
 constexpr int PART = 2 + 128;  // (max, sum, acc[128]) per (chunk, head)
 
@@ -54,7 +55,7 @@ __device__ __forceinline__ void merge(float& m, float& l, float* a, float m2, fl
 
 template <typename KT>
 __global__ __launch_bounds__(256) void k_attn_decode_part(
-    const float* __restrict__ q, const KT* __restrict__ kc, const KT* __restrict__ vc, int t_cap,
+    const float* __restrict__ q, const KT* __restrict__ kc, const KT* __restrict__ vc, int t_cap, KvLayout lay,
     const int32_t* __restrict__ lens, int len_extra, int seq_base, int Hq, int Hkv, int nchunk,
     float* __restrict__ part) {
     __shared__ float sm[4][G][PART];
@@ -79,13 +80,14 @@ __global__ __launch_bounds__(256) void k_attn_decode_part(
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
-    const size_t head_base = ((size_t)seq * Hkv + g) * t_cap * 128;
     const int kbeg = c * CHUNK + wid * 64;
     const int kend = min(kbeg + 64, T);
+    // the chunk is one page (CHUNK == kKvPage): its keys are one strided run
+    const size_t chunk_base = kbeg < kend ? lay.off(seq, g, c * CHUNK) : 0;
     for (int kk = kbeg + grp; kk < kend; kk += 4) {
         float kv[8], vv[8];
-        ld8(kc + head_base + (size_t)kk * 128 + sub * 8, kv);
-        ld8(vc + head_base + (size_t)kk * 128 + sub * 8, vv);
+        ld8(kc + chunk_base + (size_t)(kk - c * CHUNK) * 128 + sub * 8, kv);
+        ld8(vc + chunk_base + (size_t)(kk - c * CHUNK) * 128 + sub * 8, vv);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float d = 0.f;
@@ -154,7 +156,7 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 // head through shared memory, then P.V on the vector units (16 lane groups, 8 dims per
 // lane, V rows loaded before the scores are computed) with no per-key rescaling.
 __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
-    const float* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc, int t_cap,
+    const float* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc, int t_cap, KvLayout lay,
     const int32_t* __restrict__ lens, int len_extra, int seq_base, int Hq, int Hkv, int nchunk,
     float* __restrict__ part) {
     __shared__ float sp[G][CHUNK];     // scores, then probabilities
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
     const int seq = seq_base + b;
     const int T = min(lens[seq] + len_extra, t_cap);
     const int k0 = c * CHUNK + wid * 64;             // this wave's first key
-    const size_t head_base = ((size_t)seq * Hkv + g) * t_cap * 128;
+    // the chunk is one page (CHUNK == kKvPage): keys key, offset head_base + key * 128
+    const size_t head_base = c * CHUNK < T ? lay.off(seq, g, c * CHUNK) - (size_t)c * CHUNK * 128 : 0;
     const float scale = 0.088388346f;                // fl32(128^-0.5)
 
     // V rows for P.V: lane group (wid, quad) takes keys k0 + quad + 4 i, lane col dims 8 col ..
@@ -331,18 +334,18 @@ size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T) {
 }
 
 hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
-                              int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
-                              int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s) {
+                              int t_cap, const KvLayout& lay, const int32_t* lens, int len_extra, int seq_base,
+                              int B, int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s) {
     if (B <= 0) return hipSuccess;
     if (Hq != G * Hkv) return hipErrorInvalidValue;
     const int nchunk = (max_T + CHUNK - 1) / CHUNK;
     dim3 grid(nchunk, Hkv, B);
     if (kv_bf16)
         hipLaunchKernelGGL(k_attn_decode_mfma, grid, dim3(256), 0, s, q, (const bf16*)kc,
-                           (const bf16*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
+                           (const bf16*)vc, t_cap, lay, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
     else
         hipLaunchKernelGGL(k_attn_decode_part<float>, grid, dim3(256), 0, s, q, (const float*)kc,
-                           (const float*)vc, t_cap, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
+                           (const float*)vc, t_cap, lay, lens, len_extra, seq_base, Hq, Hkv, nchunk, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (o_pair)

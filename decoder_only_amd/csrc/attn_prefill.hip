@@ -64,8 +64,8 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 // 1.1x (2048 rows) to 1.8x (8192 rows) slower.
 template <bool PAIR, bool BAL>
 __global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* __restrict__ q, const bf16* __restrict__ kc,
-                                                      const bf16* __restrict__ vc, int t_cap, int M, int t0,
-                                                      int Hq, int Hkv, void* __restrict__ o) {
+                                                      const bf16* __restrict__ vc, KvLayout lay, int seq, int M,
+                                                      int t0, int Hq, int Hkv, void* __restrict__ o) {
     constexpr int RT = BAL ? 1 : 2;
     __shared__ u32x4 sK[BKV * 16];
     __shared__ bf16 sVT[128 * BKV];
@@ -75,8 +75,6 @@ __global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* 
     const int g = BAL ? (int)blockIdx.y >> 1 : (int)blockIdx.y;
     const int l16 = lane & 15, lg = lane >> 4;
     const float scale_log2 = 0.088388346f * 1.4426950408889634f;
-    const bf16* kh = kc + (size_t)g * t_cap * 128;
-    const bf16* vh = vc + (size_t)g * t_cap * 128;
 
     for (int pass = 0; pass < (BAL ? 2 : 1); ++pass) {
     // heaviest (latest) query tiles first
@@ -123,6 +121,8 @@ __global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* 
     const int ck = tid & 15;
     u32x4 kreg[2][2], vreg[2][2];
     auto kv_load = [&](int kt) {
+        // a 64-key tile lies within one page: one strided run from the tile's first slot
+        const size_t tb = lay.off(seq, g, kt * BKV);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* 
                 kreg[j][u] = u32x4{0u, 0u, 0u, 0u};
                 vreg[j][u] = u32x4{0u, 0u, 0u, 0u};
                 if (slot <= last_slot) {
-                    kreg[j][u] = *reinterpret_cast<const u32x4*>(kh + (size_t)slot * 128 + ck * 8);
-                    vreg[j][u] = *reinterpret_cast<const u32x4*>(vh + (size_t)slot * 128 + ck * 8);
+                    kreg[j][u] = *reinterpret_cast<const u32x4*>(kc + tb + (size_t)key * 128 + ck * 8);
+                    vreg[j][u] = *reinterpret_cast<const u32x4*>(vc + tb + (size_t)key * 128 + ck * 8);
                 }
             }
     };
@@ -271,14 +271,17 @@ __global__ __launch_bounds__(256, BAL ? 2 : 1) void k_attn_prefill(const float* 
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s) {
+hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, const KvLayout& lay,
+                               int seq, int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s) {
+    static_assert(kKvPage % BKV == 0, "a key tile lies within one cache page");
     if (M <= 0) return hipSuccess;
     if (Hq != 2 * Hkv) return hipErrorInvalidValue;
     const int nqt = (M + BQ - 1) / BQ;
     const dim3 grid((nqt + 1) / 2, Hq);
-    if (o_pair) hipLaunchKernelGGL((k_attn_prefill<true, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
-    else hipLaunchKernelGGL((k_attn_prefill<false, true>), grid, dim3(256), 0, s, q, kc, vc, t_cap, M, t0, Hq, Hkv, o);
+    if (o_pair)
+        hipLaunchKernelGGL((k_attn_prefill<true, true>), grid, dim3(256), 0, s, q, kc, vc, lay, seq, M, t0, Hq, Hkv, o);
+    else
+        hipLaunchKernelGGL((k_attn_prefill<false, true>), grid, dim3(256), 0, s, q, kc, vc, lay, seq, M, t0, Hq, Hkv, o);
     return hipGetLastError();
 }
 

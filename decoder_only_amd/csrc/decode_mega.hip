@@ -352,6 +352,7 @@ struct FxPair {   // thread t's chunks k = 0, 1: the sums 4t .. 4t+3 (chunk i = 
 };
 
 constexpr int TRACE_MAX = 400;   // phase timestamps kept per traced workgroup
+constexpr int PGMAX = kMegaPageIds;   // cache page ids per row held in shared memory
 constexpr int STAGE = 256;       // K/V rows of the staging area
 constexpr int SHOT = 240;        // cached rows staged per shot (the new key follows them)
 constexpr int SHOTD = 120;       // the same with two staging halves of 128 rows (long variant)
@@ -387,6 +388,8 @@ struct Smem {
     float rc[BMAX][64], rs[BMAX][64];   // cos / sin of the row's position times frequency i
     MegaLayer layers[kMegaMaxLayers];
     unsigned long long tr[TRACE_MAX];   // phase timestamps (trace only)
+    int pg[BMAX][PGMAX];           // cache page ids of this workgroup's attention range, per row
+    int pg0[BMAX];                 // (the range's first page)
     __attribute__((aligned(16))) bf16 knc[BMAX][DH];   // causal rows: every row's new key / value
     __attribute__((aligned(16))) bf16 vnc[BMAX][DH];   // (bf16: the values are bf16-rounded already)
 };
@@ -447,6 +450,24 @@ __device__ __forceinline__ void norm_rope(float& x1, float& x2, const Pre& pre, 
 template <bool CAUSAL>
 __device__ __forceinline__ int row_seq(const MegaParams& p, int b) { return p.seq_base + (CAUSAL ? 0 : b); }
 
+// One kv head of one row in one layer: the head's base within every cache page, and the row
+// whose page ids (sm.pg) locate the slots.
+struct KvHead {
+    size_t lb;
+    int b;
+};
+__device__ __forceinline__ KvHead kv_head(const MegaParams& p, int layer, int b, int g) {
+    return KvHead{(size_t)layer * p.kv_layer_elems + (size_t)g * p.kv.head_stride, b};
+}
+// element offset of a slot (in the row's prefetched page range) of a kv head
+__device__ __forceinline__ size_t kv_page_base(const MegaParams& p, const Smem& sm, const KvHead& kh, int page) {
+    return kh.lb + (size_t)sm.pg[kh.b][page - sm.pg0[kh.b]] * p.kv.page_stride;
+}
+__device__ __forceinline__ size_t kv_slot(const MegaParams& p, const Smem& sm, const KvHead& kh, int slot) {
+    return kv_page_base(p, sm, kh, slot >> 8) + (size_t)(slot & (kKvPage - 1)) * DH;
+}
+
+
 // Polled q/k/v of group g (sm.in[b]) -> rotated q, bf16-rounded new k, v in shared memory;
 // `append` writes k, v into the cache at `slot`.
 template <bool CAUSAL>
@@ -481,8 +502,8 @@ __device__ __forceinline__ void group_prep(const MegaParams& p, Smem& sm, const 
         if (append) {
             // (a wave-uniform choice: a per-lane one reads the pointer with a vector load and
             // then waits for every outstanding load, the weight prefetch included)
-            bf16* cache = (__builtin_amdgcn_readfirstlane(wid) == 2 ? p.kc : p.vc) + (size_t)layer * p.kv_layer_elems +
-                          (size_t)row_seq<CAUSAL>(p, b) * p.kv_seq_elems + ((size_t)g * p.t_cap + slot) * DH;
+            bf16* cache = (__builtin_amdgcn_readfirstlane(wid) == 2 ? p.kc : p.vc) +
+                          kv_slot(p, sm, kv_head(p, layer, b, g), slot);
             cache[i] = h1;
             cache[i + 64] = h2;
         }
@@ -503,11 +524,6 @@ __device__ __forceinline__ void trace_flush(const MegaParams& p, const Smem& sm,
             p.trace[(blockIdx.x == 0 ? 0 : p.trace_n) + i] = sm.tr[i];
 }
 
-template <bool CAUSAL>
-__device__ __forceinline__ size_t kv_head_base(const MegaParams& p, int layer, int b, int g) {
-    return (size_t)layer * p.kv_layer_elems + (size_t)row_seq<CAUSAL>(p, b) * p.kv_seq_elems + (size_t)g * p.t_cap * DH;
-}
-
 #define LDS_AS __attribute__((address_space(3)))
 
 // Issue asynchronous copies of cache rows base .. base+n-1 (n <= STAGE) of one kv head into
@@ -520,15 +536,21 @@ __device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }
 
 // Stage cached rows [base, base + n) of one kv head into shared memory: wave w loads the
 // 16-row tiles t = w, w + 4, ... (the tiles it attends), four rows per instruction.
-__device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t hb, int base, int n) {
+// (A shot of at most 240 rows spans at most two cache pages: their bases are read once.)
+__device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, const KvHead& kh, int base, int n) {
+    if (n <= 0) return;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int pa = base >> 8;
+    const size_t offa = kv_page_base(p, sm, kh, pa);
+    const size_t offb = ((base + n - 1) >> 8) != pa ? kv_page_base(p, sm, kh, pa + 1) : offa;
     for (int t = wid; 16 * t < n; t += 4) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int r0 = 16 * t + 4 * q4;
             const int r = r0 + (lane >> 4), sl = lane & 15;
             if (r < n) {
-                const size_t row = hb + (size_t)(base + r) * DH;
+                const int slot = base + r;
+                const size_t row = ((slot >> 8) == pa ? offa : offb) + (size_t)(slot & (kKvPage - 1)) * DH;
                 __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r, sl)),
                                                  (LDS_AS void*)&sm.u.kv.k[r0][0], 16, 0, 0);
                 __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl),
@@ -543,16 +565,21 @@ __device__ __forceinline__ void kv_stage(const MegaParams& p, Smem& sm, size_t h
 // w and w + 4 of the half (rows past n repeat row n - 1: every wave issues exactly
 // KV_DB_LOADS loads per shot, so a fixed wait count separates the two shots).
 constexpr int KV_DB_LOADS = 16;
-__device__ __forceinline__ void kv_stage_db(const MegaParams& p, Smem& sm, size_t hb, int base, int n, int half) {
+__device__ __forceinline__ void kv_stage_db(const MegaParams& p, Smem& sm, const KvHead& kh, int base, int n,
+                                            int half) {
     if (n <= 0) return;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int pa = base >> 8;
+    const size_t offa = kv_page_base(p, sm, kh, pa);
+    const size_t offb = ((base + n - 1) >> 8) != pa ? kv_page_base(p, sm, kh, pa + 1) : offa;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int r0 = 16 * (wid + 4 * st) + 4 * q4;
             const int r = min(r0 + (lane >> 4), n - 1), sl = lane & 15;
-            const size_t row = hb + (size_t)(base + r) * DH;
+            const int slot = base + r;
+            const size_t row = ((slot >> 8) == pa ? offa : offb) + (size_t)(slot & (kKvPage - 1)) * DH;
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r0 + (lane >> 4), sl)),
                                              (LDS_AS void*)&sm.u.kv.k[128 * half + r0][0], 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl),
@@ -589,7 +616,7 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // when o_out is null, leaves the merged per-head state (base-2 max, sum, unnormalised
 // acc[128]) in sm.att.
 template <bool DB, bool CAUSAL>
-__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, size_t hb, int k0, int k1, int T, float* o_out,
+__device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, const KvHead& hb, int k0, int k1, int T, float* o_out,
                                        int b, int nnew_rt) {
     const int nnew = CAUSAL ? nnew_rt : 1;
     constexpr int SH = DB ? SHOTD : SHOT;
@@ -862,6 +889,7 @@ __device__ __forceinline__ void pf_down(const MegaLayer& L, typename WChunk<W8>:
     if constexpr (W8) pre.sd = ldf(row_scales(L.wd, (size_t)D * F) + 32 * j + (threadIdx.x >> 3));
 }
 
+static_assert(MAXCH == 32, "kMegaMaxSlots assumes 32 chunks");
 // long-context attention split: number of chunks (<= 32) and keys per chunk (multiple of 64)
 __host__ __device__ __forceinline__ void chunking(int T, int& nch, int& ch) {
     nch = min(MAXCH, (T + 63) / 64);
@@ -905,6 +933,24 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     if (w == 0 && tid < B) {
         const int t = p.tokens[tid];
         if (t < 0 || t >= p.vocab) atomicOr(p.err, Q3_DEVERR_TOKEN);
+    }
+    // cache page ids of the slots this workgroup stages or appends, per row: MODE 0 the
+    // row's whole range [0, T); the split-K instances the workgroup's chunk of it
+    if (tid < B * PGMAX) {
+        const int b = tid / PGMAX, i = tid % PGMAX;
+        const int T = p.slots[b] + 1;
+        int k0 = 0, k1 = T;
+        if constexpr (MODE != 0) {
+            int nch, ch;
+            chunking(T, nch, ch);
+            const int c = w >> 3;
+            k0 = c < nch ? c * ch : 0;
+            k1 = c < nch ? min(T, k0 + ch) : 0;
+        }
+        const int first = k0 >> 8, last = k1 > k0 ? (k1 - 1) >> 8 : first - 1;
+        if (i == 0) sm.pg0[b] = first;
+        if (first + i <= last)
+            sm.pg[b][i] = p.kv.pt[(size_t)row_seq<CAUSAL>(p, b) * p.kv.max_pages + first + i];
     }
     // RoPE factors of this step (the same for every layer): cos / sin of fl32(pos * f_i),
     // evaluated in double precision and rounded to float
@@ -990,7 +1036,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 // new keys of this launch that row b sees (held in shared memory, not read back
                 // from the cache, which other workgroups of this launch are still writing)
                 const int nnew = CAUSAL ? b + 1 : 1;
-                const size_t hb = kv_head_base<CAUSAL>(p, layer, b, g);
+                const KvHead hb = kv_head(p, layer, b, g);
                 kv_stage(p, sm, hb, 0, first_shot(0, T, T - nnew + 1));   // in flight while q/k/v arrive
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
@@ -1010,7 +1056,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 chunking(T, nch, ch);
                 if (c < nch) {
                     const int k0 = c * ch, k1 = min(T, k0 + ch);
-                    const size_t hb = kv_head_base<false>(p, layer, b, gg);
+                    const KvHead hb = kv_head(p, layer, b, gg);
                     if (LONG) kv_stage_db(p, sm, hb, k0, first_shot(k0, k1, T, SHOTD), 0);
                     else kv_stage(p, sm, hb, k0, first_shot(k0, k1, T));
                     if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(gg, i); }, DH, sm.in[b],

@@ -120,7 +120,7 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
                                  const float* __restrict__ qn, const float* __restrict__ kn,
                                  const float* __restrict__ inv_freq, float eps,
                                  float* __restrict__ q_out, KT* __restrict__ kc, KT* __restrict__ vc,
-                                 int t_cap, int Hq, int Hkv, int nparts) {
+                                 int t_cap, KvLayout lay, int Hq, int Hkv, int nparts) {
     const int b = blockIdx.x, hd = blockIdx.y, i = threadIdx.x;
     const int width = (Hq + 2 * Hkv) * 128;
     const float* row = qkv + (size_t)b * width + hd * 128;
@@ -136,7 +136,7 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
     }
     if (hd >= Hq + Hkv) {  // value head: stored as is
         const int g = hd - Hq - Hkv;
-        const size_t base = (((size_t)seq * Hkv + g) * t_cap + slot) * 128;
+        const size_t base = lay.off(seq, g, slot);
         stkv(vc, base + i, x1);
         stkv(vc, base + i + 64, x2);
         return;
@@ -148,7 +148,7 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
         qo[i + 64] = x2;
     } else {
         const int g = hd - Hq;
-        const size_t base = (((size_t)seq * Hkv + g) * t_cap + slot) * 128;
+        const size_t base = lay.off(seq, g, slot);
         stkv(kc, base + i, x1);
         stkv(kc, base + i + 64, x2);
     }
@@ -157,16 +157,18 @@ __global__ void k_qk_rope_decode(const float* __restrict__ qkv, const int32_t* _
 hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
                                  const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
-                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s, int nparts) {
+                                 int kv_bf16, int t_cap, const KvLayout& lay, int Hq, int Hkv, hipStream_t s,
+                                 int nparts) {
     if (B <= 0) return hipSuccess;
     if (nparts < 1) return hipErrorInvalidValue;
     dim3 grid(B, Hq + 2 * Hkv);
     if (kv_bf16)
         hipLaunchKernelGGL(k_qk_rope_decode<bf16>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
-                           q_norm, k_norm, inv_freq, eps, q_out, (bf16*)kc, (bf16*)vc, t_cap, Hq, Hkv, nparts);
+                           q_norm, k_norm, inv_freq, eps, q_out, (bf16*)kc, (bf16*)vc, t_cap, lay, Hq, Hkv, nparts);
     else
         hipLaunchKernelGGL(k_qk_rope_decode<float>, grid, dim3(64), 0, s, qkv, positions, lens, seq_base,
-                           q_norm, k_norm, inv_freq, eps, q_out, (float*)kc, (float*)vc, t_cap, Hq, Hkv, nparts);
+                           q_norm, k_norm, inv_freq, eps, q_out, (float*)kc, (float*)vc, t_cap, lay, Hq, Hkv,
+                           nparts);
     return hipGetLastError();
 }
 
@@ -206,7 +208,8 @@ __global__ __launch_bounds__(256) void k_qk_rope_prefill(const float* __restrict
                                                          const float* __restrict__ qn, const float* __restrict__ kn,
                                                          const float* __restrict__ inv_freq, float eps,
                                                          float* __restrict__ q_out, bf16* __restrict__ kc,
-                                                         bf16* __restrict__ vc, int t_cap, int Hq, int Hkv) {
+                                                         bf16* __restrict__ vc, KvLayout lay, int seq, int Hq,
+                                                         int Hkv) {
     const int r = blockIdx.x, i = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nh = Hq + 2 * Hkv, width = nh * 128;
     const int slot = t0 + r;
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void k_qk_rope_prefill(const float* __restrict
         const float* row = qkv + (size_t)r * width + hd * 128;
         float x1 = row[i], x2 = row[i + 64];
         if (hd >= Hq + Hkv) {
-            const size_t base = ((size_t)(hd - Hq - Hkv) * t_cap + slot) * 128;
+            const size_t base = lay.off(seq, hd - Hq - Hkv, slot);
             vc[base + i] = f2bf(x1);
             vc[base + i + 64] = f2bf(x2);
             continue;
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(256) void k_qk_rope_prefill(const float* __restrict
             qo[i] = y1;
             qo[i + 64] = y2;
         } else {
-            const size_t base = ((size_t)(hd - Hq) * t_cap + slot) * 128;
+            const size_t base = lay.off(seq, hd - Hq, slot);
             kc[base + i] = f2bf(y1);
             kc[base + i + 64] = f2bf(y2);
         }
@@ -244,11 +247,11 @@ __global__ __launch_bounds__(256) void k_qk_rope_prefill(const float* __restrict
 
 hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
                                   const float* k_norm, const float* inv_freq, float eps,
-                                  float* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  float* q_out, uint16_t* kc, uint16_t* vc, const KvLayout& lay, int seq, int Hq,
                                   int Hkv, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_qk_rope_prefill, dim3(M), dim3(256), 0, s, qkv, M, t0, q_norm, k_norm, inv_freq, eps,
-                       q_out, kc, vc, t_cap, Hq, Hkv);
+                       q_out, kc, vc, lay, seq, Hq, Hkv);
     return hipGetLastError();
 }
 
@@ -262,27 +265,77 @@ hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStr
     return hipGetLastError();
 }
 
-// Prefix reuse: slots 0 .. len-1 of sequence src copied into sequence dst for every
-// (layer, kv head) of K and V; blockIdx.y = (layer * Hkv + head) * 2 + (0: K, 1: V), one
-// 16-byte unit per thread. Block (0, 0) also sets dst's length.
-__global__ void k_kv_copy(uint4* __restrict__ kc, uint4* __restrict__ vc, size_t layer_u, size_t seq_u,
-                          size_t head_u, int Hkv, int src, int dst, size_t n_u, int32_t* lens, int len) {
+// Page copy (prefix reuse): slots 0 .. n-1 of page src into page dst, for every (layer,
+// kv head) run of a page ([layer][head][kKvPage][128]) in the K and V pools; blockIdx.y =
+// (layer * Hkv + head) * 2 + (0: K, 1: V), one 16-byte unit per thread.
+__global__ void k_kv_page_copy(uint4* __restrict__ kc, uint4* __restrict__ vc, size_t page_u, int Hkv, int src,
+                               int dst, size_t run_u, size_t n_u) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int lg = (int)blockIdx.y >> 1, l = lg / Hkv, g = lg % Hkv;
     uint4* base = ((int)blockIdx.y & 1) ? vc : kc;
-    const size_t off = (size_t)l * layer_u + (size_t)g * head_u;
-    if (i < n_u) base[off + (size_t)dst * seq_u + i] = base[off + (size_t)src * seq_u + i];
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens[dst] = len;
+    const size_t off = (size_t)((int)blockIdx.y >> 1) * run_u + i;
+    if (i < n_u) base[(size_t)dst * page_u + off] = base[(size_t)src * page_u + off];
 }
 
-hipError_t launch_kv_copy(void* kc, void* vc, size_t kv_layer_elems, size_t kv_seq_elems, int t_cap, int n_layers,
-                          int Hkv, int kv_bytes, int src, int dst, int len, int32_t* lens, hipStream_t s) {
-    if (n_layers <= 0 || len < 0 || (128 * kv_bytes) % 16) return hipErrorInvalidValue;
+hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, int n_layers, int Hkv, int kv_bytes,
+                               int src_page, int dst_page, int n, hipStream_t s) {
+    if (n_layers <= 0 || n <= 0) return hipSuccess;
+    if (n > kKvPage || (128 * kv_bytes) % 16) return hipErrorInvalidValue;
     const size_t u = 16 / kv_bytes;     // elements per 16-byte unit
-    const size_t n_u = (size_t)len * 128 / u;
-    const dim3 grid((unsigned)((n_u + 255) / 256 > 0 ? (n_u + 255) / 256 : 1), (unsigned)(n_layers * Hkv * 2));
-    hipLaunchKernelGGL(k_kv_copy, grid, dim3(256), 0, s, (uint4*)kc, (uint4*)vc, kv_layer_elems / u, kv_seq_elems / u,
-                       (size_t)t_cap * 128 / u, Hkv, src, dst, n_u, lens, len);
+    const size_t n_u = (size_t)n * 128 / u;
+    const dim3 grid((unsigned)((n_u + 255) / 256), (unsigned)(n_layers * Hkv * 2));
+    hipLaunchKernelGGL(k_kv_page_copy, grid, dim3(256), 0, s, (uint4*)kc, (uint4*)vc, page_elems / u, Hkv, src_page,
+                       dst_page, (size_t)kKvPage * 128 / u, n_u);
+    return hipGetLastError();
+}
+
+// Dense [Hkv][len][128] buffer <-> the cache slots 0 .. len-1 of one (sequence, layer):
+// thread = one 16-byte unit of one row; blockIdx.y = head * 2 + (0: K, 1: V).
+__global__ void k_kv_dense(uint4* __restrict__ kc, uint4* __restrict__ vc, KvLayout lay, int seq, uint4* dk,
+                           uint4* dv, int len, int units_per_row, int to_cache) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int g = (int)blockIdx.y >> 1;
+    const bool isv = blockIdx.y & 1;
+    if (i >= (size_t)len * units_per_row) return;
+    const int slot = (int)(i / units_per_row), u = (int)(i % units_per_row);
+    // the layout's element offsets become unit offsets (a row of 128 elements is units_per_row units)
+    const size_t c = lay.off(seq, g, slot) / (128 / units_per_row) + u;
+    const size_t d = ((size_t)g * len + slot) * units_per_row + u;
+    uint4* cache = isv ? vc : kc;
+    uint4* dense = isv ? dv : dk;
+    if (to_cache) cache[c] = dense[d];
+    else dense[d] = cache[c];
+}
+
+hipError_t launch_kv_dense(void* kc_layer, void* vc_layer, const KvLayout& lay, int seq, int Hkv, int kv_bytes,
+                           void* dk, void* dv, int len, bool to_cache, hipStream_t s) {
+    if (len <= 0) return hipSuccess;
+    if ((128 * kv_bytes) % 16) return hipErrorInvalidValue;
+    const int upr = 128 * kv_bytes / 16;
+    const size_t n = (size_t)len * upr;
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)(Hkv * 2));
+    hipLaunchKernelGGL(k_kv_dense, grid, dim3(256), 0, s, (uint4*)kc_layer, (uint4*)vc_layer, lay, seq, (uint4*)dk,
+                       (uint4*)dv, len, upr, to_cache ? 1 : 0);
+    return hipGetLastError();
+}
+
+// Page-table entries and a length set on the stream (a kernel, so the update is ordered
+// with the launches around it and safe under graph capture).
+struct PageSet {
+    int32_t p[64];
+};
+__global__ void k_set_pages(int32_t* pt, int max_pages, int seq, int first, PageSet v, int n, int32_t* lens,
+                            int len) {
+    const int i = threadIdx.x;
+    if (i < n) pt[(size_t)seq * max_pages + first + i] = v.p[i];
+    if (i == 0 && len >= 0) lens[seq] = len;
+}
+
+hipError_t launch_set_pages(int32_t* pt, int max_pages, int seq, int first, const int32_t* pages, int n,
+                            int32_t* lens, int len, hipStream_t s) {
+    if (n < 0 || n > 64) return hipErrorInvalidValue;
+    PageSet v{};
+    for (int i = 0; i < n; ++i) v.p[i] = pages[i];
+    hipLaunchKernelGGL(k_set_pages, dim3(1), dim3(64), 0, s, pt, max_pages, seq, first, v, n, lens, len);
     return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@
 // error in the logits. The last row then goes through the float32 decode path, which
 // gives the same result as a full prefill by causality (a row only sees earlier slots).
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -53,9 +54,23 @@ struct q3_engine {
     float* final_norm = nullptr;
     float* inv_freq = nullptr;
 
+    // KV cache: a pool of pages, page = kKvPage token slots of every layer and kv head,
+    // [page][layer][kv head][slot][head_dim] in each of kc, vc. A sequence's page table row
+    // lists its pages in slot order; a page held by several sequences (q3_kv_fork) is copied
+    // by the first one that writes into it.
     void* kc = nullptr;
     void* vc = nullptr;
-    size_t kv_layer_elems = 0, kv_seq_elems = 0;
+    size_t kv_layer_elems = 0;     // one layer's run within a page
+    size_t page_elems = 0;         // one page (every layer)
+    int n_pages = 0, max_pages = 0;                // pool size; table entries per sequence
+    int32_t* d_pt = nullptr;                       // page table [max_batch][max_pages]
+    std::vector<int32_t> h_pt;                     // its host copy
+    std::vector<int32_t> h_npages;                 // pages each sequence holds
+    std::vector<int32_t> refs;                     // sequences holding each page
+    std::vector<int32_t> free_pages;
+    void* kv_dense = nullptr;                      // staging for q3_kv_import / q3_kv_export
+    size_t kv_dense_bytes = 0;
+    KvLayout layout() const { return KvLayout{d_pt, max_pages, page_elems, (size_t)kKvPage * 128}; }
     int32_t* d_len = nullptr;
     std::vector<int32_t> h_len;
     unsigned* d_err = nullptr;
@@ -214,6 +229,7 @@ extern "C" q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, 
     return Q3_OK;
 }
 
+static_assert(kMegaMaxSlots == 270336, "the int8 limit quoted below");
 static q3_status validate_config(const q3_config* c, std::string& why) {
     if (!c) { why = "config is NULL"; return Q3_ERR_ARG; }
     if (c->n_layers < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->ffn <= 0 ||
@@ -227,8 +243,15 @@ static q3_status validate_config(const q3_config* c, std::string& why) {
         (c->kv_dtype != Q3_F32 && c->kv_dtype != Q3_BF16)) { why = "bad dtype"; return Q3_ERR_ARG; }
     if (c->weight_dtype == Q3_I8 && (c->kv_dtype != Q3_BF16 || c->hidden != 1024 || c->n_heads != 16 ||
                                      c->n_kv_heads != 8 || c->ffn != 3072 || c->n_layers < 1 ||
-                                     c->n_layers > kMegaMaxLayers || c->max_batch > kMegaMaxRows)) {
-        why = "int8 weights need the Qwen3-0.6B layer shape, a bf16 cache and at most 4 sequence slots";
+                                     c->n_layers > kMegaMaxLayers || c->max_batch > kMegaMaxRows ||
+                                     c->max_seq > kMegaMaxSlots)) {
+        why = "int8 weights need the Qwen3-0.6B layer shape, a bf16 cache, at most 4 sequence slots and "
+              "max_seq <= 270336";
+        return Q3_ERR_ARG;
+    }
+    if (c->kv_pages < 0) { why = "kv_pages must be >= 0"; return Q3_ERR_ARG; }
+    if ((int64_t)c->max_batch * ((c->max_seq + kKvPage - 1) / kKvPage) > INT32_MAX) {
+        why = "max_batch * max_seq too large";
         return Q3_ERR_ARG;
     }
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) { why = "bad rms_eps or rope_theta"; return Q3_ERR_ARG; }
@@ -412,11 +435,20 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         for (int i = 0; i < dh / 2; ++i) f[i] = (float)std::pow((double)c.rope_theta, -(double)i / (dh / 2));
         if (!(e->inv_freq = (float*)upload(f.data(), f.size() * 4))) return oom();
     }
-    // KV cache [L][S][Hkv][max_seq][dh]
-    e->kv_seq_elems = (size_t)Hkv * c.max_seq * dh;
-    e->kv_layer_elems = e->kv_seq_elems * c.max_batch;
-    const size_t kvb = e->kv_layer_elems * (size_t)(c.n_layers > 0 ? c.n_layers : 1) * e->kvbytes();
+    // KV-cache page pool and page table
+    e->max_pages = (c.max_seq + kKvPage - 1) / kKvPage;
+    e->n_pages = c.kv_pages > 0 ? c.kv_pages : c.max_batch * e->max_pages;
+    e->kv_layer_elems = (size_t)Hkv * kKvPage * dh;
+    e->page_elems = e->kv_layer_elems * (size_t)(c.n_layers > 0 ? c.n_layers : 1);
+    const size_t kvb = e->page_elems * (size_t)e->n_pages * e->kvbytes();
     if (!(e->kc = e->alloc(kvb)) || !(e->vc = e->alloc(kvb))) return oom();
+    const size_t ptn = (size_t)c.max_batch * e->max_pages;
+    e->h_pt.assign(ptn, 0);       // entry 0 until a sequence holds the page: never read
+    if (!(e->d_pt = (int32_t*)upload(e->h_pt.data(), ptn * 4))) return oom();
+    e->h_npages.assign(c.max_batch, 0);
+    e->refs.assign(e->n_pages, 0);
+    e->free_pages.resize(e->n_pages);
+    for (int i = 0; i < e->n_pages; ++i) e->free_pages[i] = e->n_pages - 1 - i;   // page 0 handed out first
     if (!(e->d_len = (int32_t*)e->alloc(sizeof(int32_t) * c.max_batch))) return oom();
     if (hipMemset(e->d_len, 0, sizeof(int32_t) * c.max_batch) != hipSuccess) { q3_free(e); return Q3_ERR_HIP; }
     e->h_len.assign(c.max_batch, 0);
@@ -534,6 +566,91 @@ static double attn_prefill_flops(int M, int t0, int Hq) {
 }
 
 // ---------------------------------------------------------------------------------
+// KV-cache pages
+// ---------------------------------------------------------------------------------
+
+// Page-table entries [first, first + n) of sequence seq (from the host copy) to the device,
+// and the sequence's device length when len >= 0, in stream order (kernels, not copies).
+static q3_status push_pages(q3_engine* e, int seq, int first, int n, int len = -1) {
+    if (n <= 0 && len < 0) return Q3_OK;
+    do {
+        const int k = std::min(n, 64);
+        HIPCHK(e, launch_set_pages(e->d_pt, e->max_pages, seq, first,
+                                   e->h_pt.data() + (size_t)seq * e->max_pages + first, std::max(k, 0), e->d_len,
+                                   len, e->stream));
+        first += k;
+        n -= k;
+        len = -1;
+    } while (n > 0);
+    return Q3_OK;
+}
+
+// Slots of page p that sequence seq has written.
+static int page_valid(const q3_engine* e, int seq, int p) {
+    return std::max(0, std::min(kKvPage, e->h_len[seq] - p * kKvPage));
+}
+
+// Pages taken from the pool to make slots [slot0, slot0 + n) of seq writable.
+static size_t pages_needed(const q3_engine* e, int seq, int slot0, int n) {
+    if (n <= 0) return 0;
+    const int32_t* row = e->h_pt.data() + (size_t)seq * e->max_pages;
+    size_t need = 0;
+    for (int p = std::min(slot0 / kKvPage, e->h_npages[seq]); p <= (slot0 + n - 1) / kKvPage; ++p)
+        need += p >= e->h_npages[seq] || e->refs[row[p]] > 1;
+    return need;
+}
+
+// Pages of seq from index `keep` on back to the pool (a page another sequence still holds
+// stays with it).
+static void release_pages(q3_engine* e, int seq, int keep) {
+    const int32_t* row = e->h_pt.data() + (size_t)seq * e->max_pages;
+    for (int p = keep; p < e->h_npages[seq]; ++p)
+        if (--e->refs[row[p]] == 0) e->free_pages.push_back(row[p]);
+    e->h_npages[seq] = std::min(e->h_npages[seq], keep);
+}
+
+// Make the pages of slots [slot0, slot0 + n) of seq present and held by seq alone: a missing
+// page comes from the pool, a shared one is first copied (the slots seq has written, every
+// layer) into a page of its own. All of them or none (Q3_ERR_CAPACITY).
+static q3_status claim_pages(q3_engine* e, int seq, int slot0, int n) {
+    if (n <= 0) return Q3_OK;
+    if (pages_needed(e, seq, slot0, n) > e->free_pages.size())
+        return e->fail(Q3_ERR_CAPACITY, "KV cache full: no free page in the pool");
+    int32_t* row = e->h_pt.data() + (size_t)seq * e->max_pages;
+    const int p1 = (slot0 + n - 1) / kKvPage;
+    int lo = -1, hi = -1;
+    for (int p = std::min(slot0 / kKvPage, e->h_npages[seq]); p <= p1; ++p) {
+        const bool missing = p >= e->h_npages[seq];
+        if (!missing && e->refs[row[p]] == 1) continue;
+        const int32_t pg = e->free_pages.back();
+        e->free_pages.pop_back();
+        e->refs[pg] = 1;
+        if (!missing) {      // copy on write
+            --e->refs[row[p]];
+            HIPCHK(e, launch_kv_page_copy(e->kc, e->vc, e->page_elems, e->cfg.n_layers, e->cfg.n_kv_heads,
+                                          (int)e->kvbytes(), row[p], pg, page_valid(e, seq, p), e->stream));
+        }
+        row[p] = pg;
+        if (lo < 0) lo = p;
+        hi = p;
+    }
+    e->h_npages[seq] = std::max(e->h_npages[seq], p1 + 1);
+    return lo < 0 ? Q3_OK : push_pages(e, seq, lo, hi - lo + 1);
+}
+
+static q3_status ensure_kv_dense(q3_engine* e, size_t bytes) {
+    if (bytes <= e->kv_dense_bytes) return Q3_OK;
+    if (e->kv_dense) e->release(e->kv_dense);
+    e->kv_dense = nullptr;
+    e->kv_dense_bytes = 0;
+    if (!(e->kv_dense = e->alloc(bytes))) return e->fail(Q3_ERR_OOM, "KV staging buffer allocation failed");
+    e->kv_dense_bytes = bytes;
+    return Q3_OK;
+}
+
+extern "C" int32_t q3_kv_free_pages(const q3_engine* e) { return e ? (int32_t)e->free_pages.size() : -1; }
+
+// ---------------------------------------------------------------------------------
 // decode rows (also the tail of a prefill)
 // ---------------------------------------------------------------------------------
 
@@ -558,7 +675,7 @@ static MegaParams mega_params(const q3_engine* e, const int32_t* tokens, const i
     mp.kc = (uint16_t*)e->kc;
     mp.vc = (uint16_t*)e->vc;
     mp.kv_layer_elems = e->kv_layer_elems;
-    mp.kv_seq_elems = e->kv_seq_elems;
+    mp.kv = e->layout();
     mp.tokens = tokens;
     mp.positions = positions;
     mp.ex = e->m_ex;
@@ -612,7 +729,7 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     const double wb = (double)e->wbytes();
     // the persistent kernel always computes the logits (into the engine's buffer when the
     // caller does not want them)
-    const bool use_mega = e->mega_ok && B <= kMegaMaxRows && e->decode_path != 1;
+    const bool use_mega = e->mega_ok && B <= kMegaMaxRows && maxT <= kMegaMaxSlots && e->decode_path != 1;
     if (!use_mega && e->decode_path == 2) return e->fail(Q3_ERR_STATE, "persistent decode kernel not usable here");
     if (!use_mega && e->i8())
         return e->fail(Q3_ERR_STATE, "int8 weights: decode runs only in the persistent kernel (at most 4 rows)");
@@ -669,6 +786,7 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         const auto& L = e->layers[l];
         char* kcl = (char*)e->kc + (size_t)l * e->kv_layer_elems * e->kvbytes();
         char* vcl = (char*)e->vc + (size_t)l * e->kv_layer_elems * e->kvbytes();
+        const KvLayout lay = e->layout();
         HIPCHK(e, launch_rmsnorm(e->x, L.in_norm, e->h, nmode, B, d, c.rms_eps, s, e->parts, pending));
         pending = 0;
         prof_mark(e, Q3_PROF_GEMV, true, wb * e->qkv_rows() * d + 4.0 * B * (d + e->qkv_rows()));
@@ -683,9 +801,9 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
         prof_mark(e, Q3_PROF_GEMV, false);
         HIPCHK(e, launch_qk_rope_decode(mm && split_qkv > 1 ? e->parts : e->qkv, positions, e->d_len, seq_base, B,
                                         L.q_norm, L.k_norm, e->inv_freq, c.rms_eps, e->q, kcl, vcl, kvbf, c.max_seq,
-                                        Hq, Hkv, s, mm ? split_qkv : 1));
+                                        lay, Hq, Hkv, s, mm ? split_qkv : 1));
         prof_mark(e, Q3_PROF_ATTN_DECODE, true, kv_read_bytes(e, seq_base, B) / c.n_layers);
-        HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, e->d_len, 1, seq_base, B, Hq, Hkv,
+        HIPCHK(e, launch_attn_decode(e->q, kcl, vcl, kvbf, c.max_seq, lay, e->d_len, 1, seq_base, B, Hq, Hkv,
                                      maxT, e->attn_ws, e->o, mm, s));
         prof_mark(e, Q3_PROF_ATTN_DECODE, false);
         prof_mark(e, Q3_PROF_GEMV, true, wb * d * HD + 4.0 * B * (HD + 2 * d));
@@ -791,8 +909,9 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
     int pending = 0;                                   // partials not yet added to pf_x
     for (int l = 0; l < c.n_layers; ++l) {
         const auto& L = e->layers[l];
-        uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
-        uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems;
+        uint16_t* kcs = (uint16_t*)e->kc + (size_t)l * e->kv_layer_elems;
+        uint16_t* vcs = (uint16_t*)e->vc + (size_t)l * e->kv_layer_elems;
+        const KvLayout lay = e->layout();
         HIPCHK(e, launch_rmsnorm(e->pf_x, L.in_norm, e->pf_h, 2, M, d, c.rms_eps, s, e->pf_parts, pending));
         pending = 0;
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * e->qkv_rows() * d);
@@ -800,10 +919,10 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
                               GEMM_F32, s, 1, L.sqkv));
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
-                                         e->pf_q, kcs, vcs, c.max_seq, Hq, Hkv, s));
+                                         e->pf_q, kcs, vcs, lay, seq, Hq, Hkv, s));
         if (l + 1 == c.n_layers) break;               // the last layer's K/V are written
         prof_mark(e, Q3_PROF_ATTN_PREFILL, true, 0, attn_prefill_flops(M, t0, Hq));
-        HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, c.max_seq, M, t0, Hq, Hkv, e->pf_o, 1, s));
+        HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, lay, seq, M, t0, Hq, Hkv, e->pf_o, 1, s));
         prof_mark(e, Q3_PROF_ATTN_PREFILL, false);
         prof_mark(e, Q3_PROF_GEMM, true, 0, 2.0 * M * d * Hq * 128);
         if (split_o > 1) {
@@ -843,7 +962,8 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
     if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
     if (!tokens || n < 1) return e->fail(Q3_ERR_ARG, "tokens is NULL or n < 1");
     if ((int64_t)e->h_len[seq] + n > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
-    q3_status st;
+    q3_status st = claim_pages(e, seq, e->h_len[seq], n);
+    if (st != Q3_OK) return st;
     int done = 0;
     if (e->mega_ok && e->decode_path != 1 && n < kPrefillMfmaMin && e->h_len[seq] + n <= kMegaShortSlots) {
         // a short prompt: causal chunks of up to kMegaMaxRows rows per persistent launch, the
@@ -869,8 +989,14 @@ extern "C" q3_status q3_decode_step(q3_engine* e, const int32_t* tokens, const i
     if (!e) return Q3_ERR_ARG;
     if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (!tokens || batch < 1 || batch > e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "bad tokens or batch");
-    for (int b = 0; b < batch; ++b)
+    size_t need = 0;
+    for (int b = 0; b < batch; ++b) {
         if (e->h_len[b] + 1 > e->cfg.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
+        need += pages_needed(e, b, e->h_len[b], 1);
+    }
+    if (need > e->free_pages.size()) return e->fail(Q3_ERR_CAPACITY, "KV cache full: no free page in the pool");
+    for (int b = 0; b < batch; ++b)
+        if (q3_status st = claim_pages(e, b, e->h_len[b], 1); st != Q3_OK) return st;
     return run_decode(e, tokens, positions, 0, batch, logits, true);
 }
 
@@ -901,11 +1027,9 @@ extern "C" q3_status q3_reset(q3_engine* e, int32_t seq) {
     if (!e) return Q3_ERR_ARG;
     if (q3_status st = flush_tail(e); st != Q3_OK) return st;
     if (seq < 0 || seq >= e->cfg.max_batch) return e->fail(Q3_ERR_ARG, "seq out of range");
-    int32_t zero = 0;
-    HIPCHK(e, hipMemcpyAsync(e->d_len + seq, &zero, 4, hipMemcpyHostToDevice, e->stream));
-    HIPCHK(e, hipStreamSynchronize(e->stream));
+    release_pages(e, seq, 0);
     e->h_len[seq] = 0;
-    return Q3_OK;
+    return push_pages(e, seq, 0, 0, 0);
 }
 
 extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k, const void* v,
@@ -916,18 +1040,24 @@ extern "C" q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, cons
     if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !k || !v || len < 0)
         return e->fail(Q3_ERR_ARG, "bad kv_import arguments");
     if (len > c.max_seq) return e->fail(Q3_ERR_CAPACITY, "KV cache full");
-    const size_t eb = e->kvbytes(), row = (size_t)c.head_dim * eb;
-    for (int g = 0; g < c.n_kv_heads; ++g) {
-        const size_t dst = ((size_t)layer * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems +
-                            (size_t)g * c.max_seq * c.head_dim) * eb;
-        const size_t src = (size_t)g * len * row;
-        if (len == 0) break;
-        HIPCHK(e, hipMemcpyAsync((char*)e->kc + dst, (const char*)k + src, len * row, hipMemcpyDefault, e->stream));
-        HIPCHK(e, hipMemcpyAsync((char*)e->vc + dst, (const char*)v + src, len * row, hipMemcpyDefault, e->stream));
+    const int keep = (len + kKvPage - 1) / kKvPage;
+    if (pages_needed(e, seq, 0, len) > e->free_pages.size())
+        return e->fail(Q3_ERR_CAPACITY, "KV cache full: no free page in the pool");
+    const size_t bytes = (size_t)c.n_kv_heads * len * c.head_dim * e->kvbytes();
+    if (q3_status st = ensure_kv_dense(e, 2 * bytes); st != Q3_OK) return st;
+    release_pages(e, seq, keep);
+    if (q3_status st = claim_pages(e, seq, 0, len); st != Q3_OK) return st;
+    char* dk = (char*)e->kv_dense;
+    if (len > 0) {
+        HIPCHK(e, hipMemcpyAsync(dk, k, bytes, hipMemcpyDefault, e->stream));
+        HIPCHK(e, hipMemcpyAsync(dk + bytes, v, bytes, hipMemcpyDefault, e->stream));
+        const size_t lo = (size_t)layer * e->kv_layer_elems * e->kvbytes();
+        HIPCHK(e, launch_kv_dense((char*)e->kc + lo, (char*)e->vc + lo, e->layout(), seq, c.n_kv_heads,
+                                  (int)e->kvbytes(), dk, dk + bytes, len, true, e->stream));
     }
-    HIPCHK(e, hipMemcpyAsync(e->d_len + seq, &len, 4, hipMemcpyHostToDevice, e->stream));
-    HIPCHK(e, hipStreamSynchronize(e->stream));
     e->h_len[seq] = len;
+    if (q3_status st = push_pages(e, seq, 0, 0, len); st != Q3_OK) return st;
+    HIPCHK(e, hipStreamSynchronize(e->stream));
     return Q3_OK;
 }
 
@@ -938,11 +1068,16 @@ extern "C" q3_status q3_kv_fork(q3_engine* e, int32_t src, int32_t dst, int32_t 
     if (src < 0 || src >= c.max_batch || dst < 0 || dst >= c.max_batch || src == dst || len < 0)
         return e->fail(Q3_ERR_ARG, "bad kv_fork arguments");
     if (len > e->h_len[src]) return e->fail(Q3_ERR_ARG, "kv_fork beyond the source sequence's length");
-    if (c.n_layers > 0)
-        HIPCHK(e, launch_kv_copy(e->kc, e->vc, e->kv_layer_elems, e->kv_seq_elems, c.max_seq, c.n_layers,
-                                 c.n_kv_heads, (int)e->kvbytes(), src, dst, len, e->d_len, e->stream));
+    release_pages(e, dst, 0);
+    const int np = (len + kKvPage - 1) / kKvPage;
+    for (int p = 0; p < np; ++p) {
+        const int32_t pg = e->h_pt[(size_t)src * e->max_pages + p];
+        e->h_pt[(size_t)dst * e->max_pages + p] = pg;
+        ++e->refs[pg];
+    }
+    e->h_npages[dst] = np;
     e->h_len[dst] = len;
-    return Q3_OK;
+    return push_pages(e, dst, 0, np, len);
 }
 
 extern "C" q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void* k, void* v, int32_t len) {
@@ -952,14 +1087,15 @@ extern "C" q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void
     if (seq < 0 || seq >= c.max_batch || layer < 0 || layer >= c.n_layers || !k || !v || len < 0)
         return e->fail(Q3_ERR_ARG, "bad kv_export arguments");
     if (len > e->h_len[seq]) return e->fail(Q3_ERR_ARG, "kv_export beyond the sequence's length");
-    const size_t eb = e->kvbytes(), row = (size_t)c.head_dim * eb;
-    for (int g = 0; g < c.n_kv_heads && len > 0; ++g) {
-        const size_t src = ((size_t)layer * e->kv_layer_elems + (size_t)seq * e->kv_seq_elems +
-                            (size_t)g * c.max_seq * c.head_dim) * eb;
-        const size_t dst = (size_t)g * len * row;
-        HIPCHK(e, hipMemcpyAsync((char*)k + dst, (const char*)e->kc + src, len * row, hipMemcpyDefault, e->stream));
-        HIPCHK(e, hipMemcpyAsync((char*)v + dst, (const char*)e->vc + src, len * row, hipMemcpyDefault, e->stream));
-    }
+    if (len == 0) return Q3_OK;
+    const size_t bytes = (size_t)c.n_kv_heads * len * c.head_dim * e->kvbytes();
+    if (q3_status st = ensure_kv_dense(e, 2 * bytes); st != Q3_OK) return st;
+    char* dk = (char*)e->kv_dense;
+    const size_t lo = (size_t)layer * e->kv_layer_elems * e->kvbytes();
+    HIPCHK(e, launch_kv_dense((char*)e->kc + lo, (char*)e->vc + lo, e->layout(), seq, c.n_kv_heads,
+                              (int)e->kvbytes(), dk, dk + bytes, len, false, e->stream));
+    HIPCHK(e, hipMemcpyAsync(k, dk, bytes, hipMemcpyDefault, e->stream));
+    HIPCHK(e, hipMemcpyAsync(v, dk + bytes, bytes, hipMemcpyDefault, e->stream));
     HIPCHK(e, hipStreamSynchronize(e->stream));
     return Q3_OK;
 }

@@ -9,6 +9,35 @@ namespace q3 {
 
 enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
 
+// Where the K (or V) cache keeps slot `slot` of kv head g of sequence `seq`, as an element
+// offset from the cache's base for the layer in question.
+//   paged (pt != NULL): a page holds kKvPage consecutive slots of one sequence, for every
+//     layer and kv head ([layer][head][kKvPage][128]); pt[seq][slot / kKvPage] is the page
+//     id; page_stride = elements per page, head_stride = kKvPage * 128 (the layer's base
+//     already points at its part of page 0);
+//   contiguous (pt == NULL): [seq][head][t_cap][128] from the layer's base; page_stride =
+//     elements per sequence, head_stride = t_cap * 128.
+// Within one page (or one contiguous run) consecutive slots of a head are 128 elements
+// apart, so a range that does not cross a page boundary is one strided run.
+constexpr int kKvPage = 256;
+struct KvLayout {
+    const int32_t* pt;
+    int max_pages;          // page-table entries per sequence
+    size_t page_stride, head_stride;
+#ifdef __HIPCC__
+    __host__ __device__ __forceinline__ size_t off(int seq, int g, int slot) const {
+        if (pt)
+            return (size_t)pt[(size_t)seq * max_pages + (slot >> 8)] * page_stride + (size_t)g * head_stride +
+                   (size_t)(slot & (kKvPage - 1)) * 128;
+        return (size_t)seq * page_stride + (size_t)g * head_stride + (size_t)slot * 128;
+    }
+#endif
+};
+static_assert(kKvPage == 256, "KvLayout::off divides by shifting");
+inline KvLayout kv_contiguous(int Hkv, int t_cap) {
+    return KvLayout{nullptr, 0, (size_t)Hkv * t_cap * 128, (size_t)t_cap * 128};
+}
+
 // ---- elementwise.hip
 // x[r, :] = E[tok[r], :] widened to float32 (times rowscale[tok[r]] when given: int8 codes held
 // as bf16). Out-of-range ids set Q3_DEVERR_TOKEN and give a zero row.
@@ -26,22 +55,30 @@ hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int
 hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
                                  const float* inv_freq, float eps, float* q_out, void* kc, void* vc,
-                                 int kv_bf16, int t_cap, int Hq, int Hkv, hipStream_t s, int nparts = 1);
+                                 int kv_bf16, int t_cap, const KvLayout& lay, int Hq, int Hkv, hipStream_t s,
+                                 int nparts = 1);
 // SwiGLU of the summed split-K partials [nparts][B][2F] of the packed gate/up projection,
 // to bf16 pair rows [B][2F].
 hipError_t launch_swiglu_parts(const float* parts, int nparts, int B, int F, void* out_pair, hipStream_t s);
-// Prefill rows of one sequence at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] float32.
-// kc/vc: cache of this (layer, sequence): [Hkv][t_cap][128] bf16.
+// Prefill rows of sequence seq at slots/positions t0 .. t0+M-1. q_out: [Hq][M][128] float32.
+// kc/vc: the layer's cache base, bf16, addressed through lay.
 hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* q_norm,
                                   const float* k_norm, const float* inv_freq, float eps,
-                                  float* q_out, uint16_t* kc, uint16_t* vc, int t_cap, int Hq,
+                                  float* q_out, uint16_t* kc, uint16_t* vc, const KvLayout& lay, int seq, int Hq,
                                   int Hkv, hipStream_t s);
 // lens[seq_base + b] += by for b < B.
 hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s);
-// Slots 0 .. len-1 of sequence src into sequence dst for every layer and kv head of the K
-// and V caches ([L][S][Hkv][t_cap][128], kv_bytes per element); lens[dst] = len.
-hipError_t launch_kv_copy(void* kc, void* vc, size_t kv_layer_elems, size_t kv_seq_elems, int t_cap, int n_layers,
-                          int Hkv, int kv_bytes, int src, int dst, int len, int32_t* lens, hipStream_t s);
+// Slots 0 .. n-1 of page src_page into page dst_page, for every layer and kv head of the K and
+// V page pools (pages of [n_layers][Hkv][kKvPage][128], kv_bytes per element).
+hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, int n_layers, int Hkv, int kv_bytes,
+                               int src_page, int dst_page, int n, hipStream_t s);
+// Slots 0 .. len-1 of one (sequence, layer) between the paged cache and a dense buffer
+// [Hkv][len][128] (device memory): to_cache = true writes the cache (an import), false reads it.
+hipError_t launch_kv_dense(void* kc_layer, void* vc_layer, const KvLayout& lay, int seq, int Hkv, int kv_bytes,
+                           void* dk, void* dv, int len, bool to_cache, hipStream_t s);
+// pt[seq * max_pages + first + i] = pages[i] for i < n (n <= 64); lens[seq] = len when len >= 0.
+hipError_t launch_set_pages(int32_t* pt, int max_pages, int seq, int first, const int32_t* pages, int n,
+                            int32_t* lens, int len, hipStream_t s);
 // dst[i] = v for i < n (64-bit words); graph-safe replacement for a memset.
 hipError_t launch_fill_u64(unsigned long long* dst, unsigned long long v, int n, hipStream_t s);
 
@@ -60,8 +97,8 @@ hipError_t launch_lmhead(const void* E, int wdt, const float* h, float* logits,
 size_t attn_decode_workspace_bytes(int B, int Hkv, int max_T);
 // o: float32 [B][Hq*128], or (o_pair) bf16 pair rows [B][2*Hq*128].
 hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, int kv_bf16,
-                              int t_cap, const int32_t* lens, int len_extra, int seq_base, int B,
-                              int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s);
+                              int t_cap, const KvLayout& lay, const int32_t* lens, int len_extra, int seq_base,
+                              int B, int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s);
 
 // ---- gemm.hip (prefill projections on MFMA: A [M,K] x bf16 W [N,K]^T, fp32 accumulate)
 // a_mode: A bf16 [M][K]; float32 [M][K] split into bf16 hi + lo while staging; or a bf16
@@ -77,10 +114,11 @@ hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, in
                        hipStream_t s, int splits = 1, const float* colscale = nullptr);
 
 // ---- attn_prefill.hip (causal GQA flash attention on MFMA)
-// q: [Hq][M][128] float32 rows at slots t0..t0+M-1; kc/vc: [Hkv][t_cap][128] bf16;
-// o: [M][Hq*128] float32, or (o_pair) bf16 pair rows [M][2*Hq*128] (hi parts, then lo parts).
-hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, int t_cap,
-                               int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s);
+// q: [Hq][M][128] float32 rows at slots t0..t0+M-1 of sequence seq; kc/vc: the layer's
+// cache base (bf16) addressed through lay; o: [M][Hq*128] float32, or (o_pair) bf16 pair
+// rows [M][2*Hq*128] (hi parts, then lo parts).
+hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, const KvLayout& lay,
+                               int seq, int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s);
 
 // ---- decode_mega.hip (whole decode step in one cooperative launch; fixed Qwen3-0.6B layer
 // shape: hidden 1024, 16/8 heads of 128, FFN 3072; bf16 weights and KV; 1..4 rows)
@@ -102,8 +140,9 @@ struct MegaParams {
     const MegaLayer* layers;        // device array [n_layers]
     const uint16_t* embed;          // bf16 [vocab][hidden], or int8 codes followed by the row scales
     const float *final_norm, *inv_freq;
-    uint16_t *kc, *vc;
-    size_t kv_layer_elems, kv_seq_elems;
+    uint16_t *kc, *vc;              // cache bases (layer l at + l * kv_layer_elems)
+    size_t kv_layer_elems;
+    KvLayout kv;                    // slot addressing from a layer's base
     const int32_t* tokens;
     const int32_t* positions;       // may be NULL (position = slot)
     float* ex;                      // exchange words (sentinel = not written), (n_layers + 1) * ex_layer
@@ -132,6 +171,11 @@ hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* 
 hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);
 size_t decode_mega_exchange_words_per_layer();
 constexpr int kMegaMaxRows = 4;
+// cache page ids a persistent-kernel workgroup holds per row (its attention range of at most
+// 32 chunks' share, plus one when the range does not start on a page), and the longest
+// context that bounds: ceil(T / 32) rounded to 64 keys spans at most 33 whole pages
+constexpr int kMegaPageIds = 34;
+constexpr int kMegaMaxSlots = 32 * (kMegaPageIds - 1) * kKvPage;
 constexpr int kMegaShortSlots = 240;   // launches whose rows see at most this many slots run the
                                        // short-context instance (the only one that takes causal rows)
 constexpr int kMegaMaxLayers = 64;

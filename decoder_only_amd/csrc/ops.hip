@@ -70,7 +70,8 @@ extern "C" q3_status q3_op_qk_norm_rope(const float* qkv, const float* q_norm, c
     if (!sc.get(64 * sizeof(float))) return Q3_ERR_OOM;
     if (hipMemcpyAsync(sc.p, f.data(), 64 * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess) return Q3_ERR_HIP;
     return st(launch_qk_rope_decode(qkv, positions, slots, 0, B, q_norm, k_norm, (const float*)sc.p, eps, q_out,
-                                    k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, n_heads, n_kv_heads, s));
+                                    k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, kv_contiguous(n_kv_heads, t_cap), n_heads,
+                                    n_kv_heads, s));
 }
 
 extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
@@ -83,7 +84,8 @@ extern "C" q3_status q3_op_attn_decode(const float* q, const void* k_cache, cons
     hipStream_t s = (hipStream_t)stream;
     Scratch sc(s);
     if (!sc.get(attn_decode_workspace_bytes(B, n_kv_heads, max_len))) return Q3_ERR_OOM;
-    return st(launch_attn_decode(q, k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, lens, 0, 0, B, n_heads,
+    return st(launch_attn_decode(q, k_cache, v_cache, kv_dtype == Q3_BF16, t_cap, kv_contiguous(n_kv_heads, t_cap), lens,
+                                 0, 0, B, n_heads,
                                  n_kv_heads, max_len, (float*)sc.p, o, 0, s));
 }
 
@@ -94,7 +96,8 @@ extern "C" q3_status q3_op_attn_prefill(const float* q, const uint16_t* k_cache,
         (o_dtype != Q3_F32 && o_dtype != Q3_OP_PAIR))
         return Q3_ERR_ARG;
     if (n_heads != 2 * n_kv_heads) return Q3_ERR_SHAPE;
-    return st(launch_attn_prefill(q, k_cache, v_cache, t_cap, M, t0, n_heads, n_kv_heads, o, o_dtype == Q3_OP_PAIR,
+    return st(launch_attn_prefill(q, k_cache, v_cache, kv_contiguous(n_kv_heads, t_cap), 0, M, t0, n_heads, n_kv_heads, o,
+                                  o_dtype == Q3_OP_PAIR,
                                   (hipStream_t)stream));
 }
 

@@ -23,7 +23,7 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
     "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export", "q3_kv_fork",
-    "q3_seq_len", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end", "q3_quantize_i8",
+    "q3_seq_len", "q3_kv_free_pages", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end", "q3_quantize_i8",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
     "q3_op_attn_prefill", "q3_op_sample", "q3_op_sample_noalloc",
@@ -44,7 +44,7 @@ class Q3Config(ctypes.Structure):
                 ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn", c_int32),
                 ("vocab", c_int32), ("rms_eps", c_float), ("rope_theta", c_float),
                 ("tie_embeddings", c_int32), ("weight_dtype", c_int32), ("kv_dtype", c_int32),
-                ("max_batch", c_int32), ("max_seq", c_int32)]
+                ("max_batch", c_int32), ("max_seq", c_int32), ("kv_pages", c_int32)]
 
 
 class Q3Tensor(ctypes.Structure):
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_kv_export": ([vp, i32, i32, vp, vp, i32], i32),
         "q3_kv_fork": ([vp, i32, i32, i32], i32),
         "q3_seq_len": ([vp, i32], i32),
+        "q3_kv_free_pages": ([vp], i32),
         "q3_quantize_i8": ([vp, i32, c_int64, c_int64, vp, vp], i32),
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
@@ -125,15 +126,16 @@ def _check(code: int, what: str = "", eng=None) -> None:
         raise Q3Error(code, msg)
 
 
-def config(w, max_batch: int, max_seq: int, int8: bool = False) -> Q3Config:
+def config(w, max_batch: int, max_seq: int, int8: bool = False, kv_pages: int = 0) -> Q3Config:
     """q3_config of a model description with the synth.Workload fields; int8: weight-only
-    int8 (the engine quantises the given weights at load)."""
+    int8 (the engine quantises the given weights at load); kv_pages: KV-cache pool size in
+    pages of 256 slots (0: enough for every sequence slot to reach max_seq)."""
     return Q3Config(n_layers=w.n_layers, hidden=w.hidden, n_heads=w.n_heads,
                     n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn, vocab=w.vocab,
                     rms_eps=w.rms_eps, rope_theta=w.rope_theta, tie_embeddings=1,
                     weight_dtype=I8 if int8 else (BF16 if w.weight_dtype == "bf16" else F32),
                     kv_dtype=BF16 if w.kv_dtype == "bf16" else F32,
-                    max_batch=max_batch, max_seq=max_seq)
+                    max_batch=max_batch, max_seq=max_seq, kv_pages=kv_pages)
 
 
 class Engine:
@@ -224,6 +226,10 @@ class Engine:
 
     def seq_len(self, seq: int) -> int:
         return load_library().q3_seq_len(self._h, seq)
+
+    def kv_free_pages(self) -> int:
+        """Pages of 256 token slots in the KV-cache pool that no sequence holds."""
+        return load_library().q3_kv_free_pages(self._h)
 
     def sync(self) -> None:
         _check(load_library().q3_sync(self._h), "q3_sync", self._h)

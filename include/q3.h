@@ -35,7 +35,8 @@ typedef enum {
     Q3_ERR_ARG = -1,       /* null pointer, bad enum, out-of-range scalar */
     Q3_ERR_SHAPE = -2,     /* tensor shape/size does not match the config */
     Q3_ERR_TOKEN = -3,     /* a token id outside [0, vocab) reached the device (sticky) */
-    Q3_ERR_CAPACITY = -4,  /* the KV cache of a sequence would exceed max_seq ("KV cache full") */
+    Q3_ERR_CAPACITY = -4,  /* a sequence would exceed max_seq, or the page pool has no free page
+                              ("KV cache full"); nothing was changed */
     Q3_ERR_OOM = -5,       /* device allocation failed */
     Q3_ERR_HIP = -6,       /* a HIP runtime call failed (also: no usable GPU) */
     Q3_ERR_STATE = -7,     /* call not valid in the engine's current state */
@@ -67,6 +68,11 @@ typedef struct {
     int32_t kv_dtype;      /* q3_dtype of the KV cache */
     int32_t max_batch;     /* number of sequence slots (rows of a decode step) */
     int32_t max_seq;       /* KV-cache capacity per sequence, in tokens */
+    int32_t kv_pages;      /* KV-cache pool, in pages of 256 token slots (each page holds those
+                              slots' K and V for every layer and kv head) shared by all sequence
+                              slots; 0: max_batch * ceil(max_seq / 256), enough for every slot
+                              to reach max_seq. A sequence holds ceil(len / 256) pages; pages a
+                              fork shares are counted once. */
 } q3_config;
 
 /* One named weight tensor in host memory, under the article's tensor names:
@@ -87,8 +93,8 @@ typedef struct {
 } q3_tensor;
 
 /* Create an engine on the current HIP device: copies (and repacks) every weight
- * to the device, reserves the KV cache (max_batch * max_seq slots per layer) and
- * the decode workspace. `stream` is a hipStream_t (NULL = the null stream). The
+ * to the device, reserves the KV-cache page pool (kv_pages pages) and the decode
+ * workspace. `stream` is a hipStream_t (NULL = the null stream). The
  * caller may free the host tensors when the call returns.
  * Errors: Q3_ERR_ARG / Q3_ERR_SHAPE (config or a tensor missing / mis-sized),
  * Q3_ERR_OOM, Q3_ERR_HIP (no device). On error *out is set to NULL. */
@@ -101,7 +107,7 @@ q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int32_t n_weig
  * running every layer and writing their K/V. If `logits` is not NULL it receives
  * the logits of the last token (device float32 [vocab]); they are also kept as the
  * engine's current logits for q3_sample. Errors: Q3_ERR_ARG (seq out of range,
- * n < 1), Q3_ERR_CAPACITY (len + n > max_seq). */
+ * n < 1), Q3_ERR_CAPACITY (len + n > max_seq, or too few free pages). */
 q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens, int32_t n,
                      float* logits);
 
@@ -135,25 +141,31 @@ q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch, float temp
  * Host code only (no GPU). This is the rule q3_load applies for Q3_I8. Errors: Q3_ERR_ARG. */
 q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q, float* scale);
 
-/* Empty sequence slot `seq` (its cache length becomes 0). */
+/* Empty sequence slot `seq` (its cache length becomes 0) and return its cache pages to the
+ * pool (a page shared with another slot by q3_kv_fork stays with that slot). A slot can be
+ * emptied and refilled (q3_prefill) between two decode steps of the others: continuous
+ * batching. */
 q3_status q3_reset(q3_engine* e, int32_t seq);
 
 /* Fill slots 0 .. len-1 of one (sequence, layer) of the KV cache from k and v
  * (host or device, kv_dtype, layout [n_kv_heads][len][head_dim]) -- a cache that
  * was computed elsewhere. Sets the sequence's length to len once it is
- * called for every layer with the same len (the length is set on each call).
- * Errors: Q3_ERR_ARG, Q3_ERR_CAPACITY (len > max_seq). */
+ * called for every layer with the same len (the length is set on each call); pages beyond
+ * len are returned to the pool. Waits for the engine's stream before returning.
+ * Errors: Q3_ERR_ARG, Q3_ERR_CAPACITY (len > max_seq, or no free page). */
 q3_status q3_kv_import(q3_engine* e, int32_t seq, int32_t layer, const void* k,
                        const void* v, int32_t len);
 
-/* Prefix reuse: sequence slot dst becomes a copy of the first len cached tokens of slot src
- * (every layer's K and V; len <= src's length) and its length becomes len, so a prompt
- * prefix shared by several sequences is prefilled once and each copy continues with its
- * own tokens (q3_prefill / q3_decode_step append after slot len-1). Whatever dst held is
- * replaced; src is unchanged. One device copy on the engine's stream (no host wait).
- * The result equals prefilling the prefix into dst itself (Step 5's cache holds only the
- * prefix's K/V, which depend on nothing after it). Errors: Q3_ERR_ARG (bad slots, src ==
- * dst, len above src's length). */
+/* Prefix reuse: sequence slot dst gets the first len cached tokens of slot src (every
+ * layer's K and V; len <= src's length) and its length becomes len, so a prompt prefix
+ * shared by several sequences is prefilled once and each continues with its own tokens
+ * (q3_prefill / q3_decode_step append after slot len-1). No data moves: dst's page table
+ * points at src's first ceil(len / 256) pages. A shared page is copied (copy on write) by
+ * the first sequence that appends into it, so each keeps its own tokens after the prefix.
+ * Whatever dst held is released; src is unchanged. The result equals prefilling the prefix
+ * into dst itself (Step 5's cache holds only the prefix's K/V, which depend on nothing
+ * after it). fork(a, b, len(a)) followed by q3_reset(a) moves a sequence to another slot.
+ * Errors: Q3_ERR_ARG (bad slots, src == dst, len above src's length). */
 q3_status q3_kv_fork(q3_engine* e, int32_t src, int32_t dst, int32_t len);
 
 /* Copy slots 0 .. len-1 of one (sequence, layer) of the KV cache out to k and v (host or
@@ -165,6 +177,9 @@ q3_status q3_kv_export(q3_engine* e, int32_t seq, int32_t layer, void* k, void* 
 
 /* Current cache length of a sequence slot, as tracked by the host (-1 on error). */
 int32_t q3_seq_len(const q3_engine* e, int32_t seq);
+
+/* Pages of the KV-cache pool not held by any sequence slot (-1 on error). */
+int32_t q3_kv_free_pages(const q3_engine* e);
 
 /* Wait for the engine's stream; report (and clear) the sticky device error word:
  * Q3_ERR_TOKEN or Q3_ERR_NUMERIC, else Q3_OK (or Q3_ERR_HIP on a runtime error).

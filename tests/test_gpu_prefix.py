@@ -1,11 +1,12 @@
 """Prefix reuse (q3_kv_fork): a prompt prefix shared by several sequences is prefilled
-once, copied into other sequence slots, and each copy continues with its own suffix
-(a chunked prefill into the non-empty cache: row i of the suffix sees slots j <= t0 + i),
-then all of them decode together. Every sequence must match the oracle run of its whole
-prompt from scratch (logits within max-abs 2e-2 and relative L2 1e-3, same greedy
-token), and a sequence whose prefix was recomputed instead of copied must give
-bit-identical logits to its forked twin (the copy is exact and the cache depends on
-nothing after the prefix, Step 5)."""
+once, handed to other sequence slots (their page tables point at its cache pages; the
+page holding the prefix's last tokens is copied by the first sequence that appends into
+it), and each continues with its own suffix (a chunked prefill into the non-empty cache:
+row i of the suffix sees slots j <= t0 + i), then all of them decode together. Every
+sequence must match the oracle run of its whole prompt from scratch (logits within
+max-abs 2e-2 and relative L2 1e-3, same greedy token), and a sequence whose prefix was
+recomputed instead of forked must give bit-identical logits to its forked twin (pages and
+copies are exact and the cache depends on nothing after the prefix, Step 5)."""
 import numpy as np
 import pytest
 
