@@ -477,8 +477,8 @@ def stored_traffic(md_name, sources):
     return int(t.group(1))
 
 
-MEGA_SOURCES = ("decoder_only_amd/csrc/decode_mega.hip", "decoder_only_amd/csrc/common.h",
-                "decoder_only_amd/csrc/kernels.h")
+MEGA_SOURCES = ("decoder_only_amd/csrc/decode_mega.hip", "decoder_only_amd/csrc/decode_mega.h",
+                "decoder_only_amd/csrc/kv_layout.h", "decoder_only_amd/csrc/common.h")
 
 
 def host_cpu():

@@ -44,7 +44,7 @@
 // Fixed shape: hidden 1024, 16 query / 8 kv heads of 128, FFN 3072, bf16 weights and KV
 // cache, 1..4 rows.
 #include "common.h"
-#include "kernels.h"
+#include "decode_mega.h"
 
 namespace q3 {
 

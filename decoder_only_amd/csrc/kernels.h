@@ -5,38 +5,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "decode_mega.h"
+#include "kv_layout.h"
+
 namespace q3 {
 
 enum WDtype { DT_F32 = 0, DT_BF16 = 1 };
 
-// Where the K (or V) cache keeps slot `slot` of kv head g of sequence `seq`, as an element
-// offset from the cache's base for the layer in question.
-//   paged (pt != NULL): a page holds kKvPage consecutive slots of one sequence, for every
-//     layer and kv head ([layer][head][kKvPage][128]); pt[seq][slot / kKvPage] is the page
-//     id; page_stride = elements per page, head_stride = kKvPage * 128 (the layer's base
-//     already points at its part of page 0);
-//   contiguous (pt == NULL): [seq][head][t_cap][128] from the layer's base; page_stride =
-//     elements per sequence, head_stride = t_cap * 128.
-// Within one page (or one contiguous run) consecutive slots of a head are 128 elements
-// apart, so a range that does not cross a page boundary is one strided run.
-constexpr int kKvPage = 256;
-struct KvLayout {
-    const int32_t* pt;
-    int max_pages;          // page-table entries per sequence
-    size_t page_stride, head_stride;
-#ifdef __HIPCC__
-    __host__ __device__ __forceinline__ size_t off(int seq, int g, int slot) const {
-        if (pt)
-            return (size_t)pt[(size_t)seq * max_pages + (slot >> 8)] * page_stride + (size_t)g * head_stride +
-                   (size_t)(slot & (kKvPage - 1)) * 128;
-        return (size_t)seq * page_stride + (size_t)g * head_stride + (size_t)slot * 128;
-    }
-#endif
-};
-static_assert(kKvPage == 256, "KvLayout::off divides by shifting");
-inline KvLayout kv_contiguous(int Hkv, int t_cap) {
-    return KvLayout{nullptr, 0, (size_t)Hkv * t_cap * 128, (size_t)t_cap * 128};
-}
+// (the cache layout, KvLayout, is in kv_layout.h; the persistent decode kernel's
+// parameters in decode_mega.h)
 
 // ---- elementwise.hip
 // x[r, :] = E[tok[r], :] widened to float32 (times rowscale[tok[r]] when given: int8 codes held
@@ -50,7 +27,8 @@ hipError_t launch_rmsnorm(float* x, const float* w, void* out, int out_mode, int
                           float eps, hipStream_t s, const float* parts = nullptr, int nparts = 0);
 // Decode rows: per-head RMSNorm of q and k, RoPE at the row's position, K/V append at
 // slot lens[seq]. qkv: [B][(Hq + 2 Hkv) * 128] float32. q_out: [B][Hq][128] float32.
-// kc/vc: layer base of the cache [S][Hkv][t_cap][128]. positions may be NULL (= slot).
+// kc/vc: the layer's cache base, slots addressed through lay (t_cap bounds the slot).
+// positions may be NULL (= slot).
 // With nparts > 1, qkv holds nparts split-K partials [nparts][B][...], summed in order.
 hipError_t launch_qk_rope_decode(const float* qkv, const int32_t* positions, const int32_t* lens,
                                  int seq_base, int B, const float* q_norm, const float* k_norm,
@@ -119,67 +97,6 @@ hipError_t launch_gemm(const void* A, int a_mode, const uint16_t* W, void* C, in
 // rows [M][2*Hq*128] (hi parts, then lo parts).
 hipError_t launch_attn_prefill(const float* q, const uint16_t* kc, const uint16_t* vc, const KvLayout& lay,
                                int seq, int M, int t0, int Hq, int Hkv, void* o, int o_pair, hipStream_t s);
-
-// ---- decode_mega.hip (whole decode step in one cooperative launch; fixed Qwen3-0.6B layer
-// shape: hidden 1024, 16/8 heads of 128, FFN 3072; bf16 weights and KV; 1..4 rows)
-// Matrices of one layer: bf16 weights, or (int8 weights) one buffer per matrix holding the
-// int8 codes [rows][cols] followed by the rows' float32 scales [rows].
-struct MegaLayer {
-    const uint16_t *wqkv, *wo, *wgu, *wd;
-    const float *in_norm, *post_norm, *q_norm, *k_norm;
-};
-struct MegaParams {
-    int n_layers, vocab, B, seq_base, t_cap;
-    int slots[4];                   // cache slot (= current length) of each row
-    int causal;                     // 0: row b is sequence seq_base + b; 1: every row is sequence
-                                    // seq_base at consecutive slots, and row b also attends the
-                                    // rows before it in this launch (a short prompt)
-    int head_first;                 // rows b >= head_first get the LM head: logits row b - head_first
-                                    // and argmax candidates; B: no LM head at all
-    float eps;
-    const MegaLayer* layers;        // device array [n_layers]
-    const uint16_t* embed;          // bf16 [vocab][hidden], or int8 codes followed by the row scales
-    const float *final_norm, *inv_freq;
-    uint16_t *kc, *vc;              // cache bases (layer l at + l * kv_layer_elems)
-    size_t kv_layer_elems;
-    KvLayout kv;                    // slot addressing from a layer's base
-    const int32_t* tokens;
-    const int32_t* positions;       // may be NULL (position = slot)
-    float* ex;                      // exchange words (sentinel = not written), (n_layers + 1) * ex_layer
-    size_t ex_layer;
-    float* logits;
-    unsigned long long* cand;       // [4][256] per-workgroup argmax candidates
-    unsigned* err;
-    unsigned long long* trace;      // optional phase timestamps [2][trace_n] (NULL: off)
-    int trace_n;
-    int w8;                         // 1: every matrix (and the embedding) is int8 codes + row scales
-};
-hipError_t decode_mega_prepare();
-// cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.
-hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s);
-// Attention chunks whose partials a launch over rows of visible lengths T[0..B) writes per
-// row (the largest count over the rows; 0 without split-K attention).
-int decode_mega_chunks(const int* T, int B);
-// After each launch: argmax over the per-workgroup candidates of the nout rows that had the
-// LM head, the lengths advanced (lens[seq_base + b] += 1 per row; causal: lens[seq_base] += B),
-// the initial state back into the exchange words used (pt_chunks from decode_mega_chunks),
-// and the greedy token of each output row into greedy_out when it is not NULL.
-hipError_t launch_mega_tail(const unsigned long long* cand, unsigned long long* amax, int* lens, int seq_base,
-                            int B, float* ex, size_t ex_layer, int n_layers, int pt_chunks, int32_t* greedy_out,
-                            hipStream_t s, int nout, int causal);
-// Sentinel into all `words` exchange words (at load).
-hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s);
-size_t decode_mega_exchange_words_per_layer();
-constexpr int kMegaMaxRows = 4;
-// cache page ids a persistent-kernel workgroup holds per row (its attention range of at most
-// 32 chunks' share, plus one when the range does not start on a page), and the longest
-// context that bounds: ceil(T / 32) rounded to 64 keys spans at most 33 whole pages
-constexpr int kMegaPageIds = 34;
-constexpr int kMegaMaxSlots = 32 * (kMegaPageIds - 1) * kKvPage;
-constexpr int kMegaShortSlots = 240;   // launches whose rows see at most this many slots run the
-                                       // short-context instance (the only one that takes causal rows)
-constexpr int kMegaMaxLayers = 64;
-constexpr int kMegaWorkgroups = 256;
 
 // ---- sample.hip
 hipError_t launch_argmax_rows(const float* logits, unsigned long long* amax, int V, int B,
