@@ -31,7 +31,7 @@ using namespace q3;
 namespace {
 constexpr int kPrefillMfmaMin = 16;   // prompts shorter than this run row by row
 constexpr int kPrefillSplitRows = 8192;   // prefill below this many rows: split-K O / down projections
-constexpr int kPrefillSplits = 3;         // at most this many K splits there
+constexpr int kPrefillSplits = 4;         // at most this many K splits there
 }
 
 struct q3_engine {
@@ -904,8 +904,8 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
     const int t0 = e->h_len[seq];
     HIPCHK(e, launch_embed(tokens, e->embed, DT_BF16, e->pf_x, M, d, V, e->d_err, s, e->escale));
     const bool sk = M < kPrefillSplitRows;
-    const int split_o = sk ? std::min(kPrefillSplits, Hq * 128 / 1024) : 1;
-    const int split_d = sk ? std::min(kPrefillSplits, F / 1024) : 1;
+    const int split_o = sk ? std::min(kPrefillSplits, Hq * 128 / 512) : 1;
+    const int split_d = sk ? std::min(kPrefillSplits, F / 512) : 1;
     int pending = 0;                                   // partials not yet added to pf_x
     for (int l = 0; l < c.n_layers; ++l) {
         const auto& L = e->layers[l];

@@ -63,7 +63,24 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
     __shared__ u32x4 sB[NB][BN * 8];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    // Tile of this block. Workgroup b (in launch order) runs on XCD b % 8, and the XCD's
+    // blocks in flight together are consecutive in b / 8. So XCD c takes a contiguous range
+    // of the tiles, ordered in column groups of 4 row tiles: the blocks an XCD runs at once
+    // then cover a compact patch of C, and their A and W rows are shared in its L2.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    {
+        const int nx = gridDim.x, ny = gridDim.y;
+        const int total = nx * ny * gridDim.z;
+        if (total % 8 == 0) {
+            const int b = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+            const int t = (b % 8) * (total / 8) + b / 8;
+            bz = t / (nx * ny);
+            const int r = t % (nx * ny), g = r / (4 * nx), rows = min(4, ny - 4 * g), i = r % (4 * nx);
+            by = 4 * g + i % rows;
+            bx = i / rows;
+        }
+    }
+    const int m0 = by * BM, n0 = bx * BN;
     const size_t lda = AM == GEMM_A_PAIR ? 2 * (size_t)K : (size_t)K;
 
     u32x4 ra[AJ], rl[AJ], rb[4];
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // split-K: block z of gridDim.z takes k-tiles [z nk / S, (z + 1) nk / S)
-    const int nkt = K / BK, S = gridDim.z, z = blockIdx.z;
+    const int nkt = K / BK, S = gridDim.z, z = bz;
     const int kt0 = (int)((long long)nkt * z / S), nk = (int)((long long)nkt * (z + 1) / S);
     gload(kt0);
     sstore(0);

@@ -46,13 +46,15 @@ extern "C" q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, 
 }
 
 extern "C" q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
-                                int32_t K, int32_t epilogue, void* stream) {
-    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 4 ||
+                                int32_t K, int32_t epilogue, int32_t splits, const float* colscale,
+                                void* stream) {
+    if (!A || !W || !C || M < 0 || N <= 0 || K <= 0 || epilogue < 0 || epilogue > 5 ||
         (a_dtype != Q3_F32 && a_dtype != Q3_BF16 && a_dtype != Q3_OP_PAIR))
         return Q3_ERR_ARG;
     if (N % 128 || K % 64) return Q3_ERR_SHAPE;
+    if (splits < 1 || splits > K / 64 || (splits > 1 && epilogue != GEMM_PARTIAL_F32)) return Q3_ERR_ARG;
     const int mode = a_dtype == Q3_F32 ? GEMM_A_F32 : (a_dtype == Q3_BF16 ? GEMM_A_BF16 : GEMM_A_PAIR);
-    return st(launch_gemm(A, mode, W, C, M, N, K, epilogue, (hipStream_t)stream));
+    return st(launch_gemm(A, mode, W, C, M, N, K, epilogue, (hipStream_t)stream, splits, colscale));
 }
 
 extern "C" q3_status q3_op_qk_norm_rope(const float* qkv, const float* q_norm, const float* k_norm,

@@ -30,7 +30,7 @@ EXPORTS = [
 ]
 GEMV_STORE, GEMV_RESID, GEMV_SWIGLU = 0, 1, 2
 PROF_DECODE_STEP, PROF_GEMV, PROF_LMHEAD, PROF_ATTN_DECODE, PROF_GEMM, PROF_ATTN_PREFILL = range(6)
-GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_F32, GEMM_BF16, GEMM_SWIGLU_PAIR = 0, 1, 2, 3, 4
+GEMM_F32, GEMM_RESID_F32, GEMM_SWIGLU_F32, GEMM_BF16, GEMM_SWIGLU_PAIR, GEMM_PARTIAL_F32 = 0, 1, 2, 3, 4, 5
 
 
 class Q3Error(RuntimeError):
@@ -87,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             POINTER(ctypes.c_double)], i32),
         "q3_op_rmsnorm": ([vp, vp, vp, i32, i32, i32, f32, vp], i32),
         "q3_op_gemv": ([vp, i32, vp, vp, i32, i32, i32, i32, vp], i32),
-        "q3_op_gemm": ([vp, i32, vp, vp, i32, i32, i32, i32, vp], i32),
+        "q3_op_gemm": ([vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp], i32),
         "q3_op_qk_norm_rope": ([vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, i32, i32, vp], i32),
         "q3_op_attn_decode": ([vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, vp, vp], i32),
         "q3_op_attn_prefill": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp], i32),
@@ -275,16 +275,18 @@ def op_gemv(W, x, y, epilogue: int = GEMV_STORE) -> None:
                                      x.shape[0], epilogue, _stream()), "q3_op_gemv")
 
 
-def op_gemm(A, W, C, epilogue: int = GEMM_F32, a_pair: bool = False) -> None:
-    """A: bf16 or float32 [M, K], or (a_pair) bf16 pair rows [M, 2K]; W: bf16 [N, K]."""
+def op_gemm(A, W, C, epilogue: int = GEMM_F32, a_pair: bool = False, splits: int = 1, colscale=None) -> None:
+    """A: bf16 or float32 [M, K], or (a_pair) bf16 pair rows [M, 2K]; W: bf16 [N, K];
+    colscale: optional float32 [N] column scales."""
     import torch
     M, K = A.shape
     N = W.shape[0]
     if a_pair:
         K //= 2
     adt = OP_PAIR if a_pair else (F32 if A.dtype == torch.float32 else BF16)
+    cs = _ptr(colscale, torch.float32) if colscale is not None else None
     _check(load_library().q3_op_gemm(_ptr(A, (torch.bfloat16, torch.float32)), adt, _ptr(W, torch.bfloat16),
-                                     _ptr(C), M, N, K, epilogue, _stream()), "q3_op_gemm")
+                                     _ptr(C), M, N, K, epilogue, splits, cs, _stream()), "q3_op_gemm")
 
 
 def op_qk_norm_rope(qkv, q_norm, k_norm, positions, slots, n_heads, n_kv_heads, eps, theta,

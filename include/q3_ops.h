@@ -45,9 +45,14 @@ q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, i
  * already such pairs (Q3_OP_PAIR, A bf16 [M][2K]).
  * epilogue 0: C float32 [M][N]; 1: C float32 [M][N] += result; 2: SwiGLU (W packed as
  * for q3_op_gemv), C float32 [M][N/2]; 3: C bf16 [M][N]; 4: SwiGLU to bf16 pair rows,
- * C bf16 [M][N] (N/2 hi parts, then N/2 lo parts). */
+ * C bf16 [M][N] (N/2 hi parts, then N/2 lo parts); 5: split-K partials, C float32
+ * [splits][M][N], partial z = the product over k-tiles [z n / splits, (z+1) n / splits) of
+ * the n = K / 64 tiles (1 <= splits <= K / 64; splits must be 1 for the other epilogues).
+ * colscale (NULL or float32 [N]): output column n is multiplied by colscale[n] before the
+ * epilogue (for SwiGLU, gate and up columns each by their own) -- the per-row scales of
+ * int8 weights whose codes W holds as bf16. */
 q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
-                     int32_t K, int32_t epilogue, void* stream);
+                     int32_t K, int32_t epilogue, int32_t splits, const float* colscale, void* stream);
 
 /* Per-head QK-norm and RoPE of one decode row per sequence, plus the KV append
  * (Steps 4 and 5). qkv: float32 [B][(n_heads + 2 n_kv_heads) * 128] (q heads, k heads,

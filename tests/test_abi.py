@@ -108,15 +108,18 @@ def test_null_engine_and_op_argument_errors(lib):
     assert lib.q3_last_error(None) == b"engine is NULL"
     lib.q3_free(None)
     fake = ctypes.c_void_p(0x1000)    # never dereferenced: shape checks come first
-    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 100, 64, 0, None) == -2       # N % 128
-    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 60, 0, None) == -2       # K % 64
-    assert lib.q3_op_gemm(None, 1, fake, fake, 4, 128, 64, 0, None) == -1
-    assert lib.q3_op_gemm(fake, 5, fake, fake, 4, 128, 64, 0, None) == -1       # bad A dtype
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 100, 64, 0, 1, None, None) == -2       # N % 128
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 60, 0, 1, None, None) == -2       # K % 64
+    assert lib.q3_op_gemm(None, 1, fake, fake, 4, 128, 64, 0, 1, None, None) == -1
+    assert lib.q3_op_gemm(fake, 5, fake, fake, 4, 128, 64, 0, 1, None, None) == -1       # bad A dtype
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 64, 5, 0, None, None) == -1       # splits < 1
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 128, 5, 3, None, None) == -1     # splits > K / 64
+    assert lib.q3_op_gemm(fake, 1, fake, fake, 4, 128, 128, 0, 2, None, None) == -1     # splits, not partials
     assert lib.q3_op_gemv(fake, 1, fake, fake, 6, 12, 1, 0, None) == -2         # K % 8
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 7, 4, fake, None) == -2
     assert lib.q3_op_attn_decode(fake, fake, fake, 1, 16, fake, 1, 16, 8, 17, fake, None) == -1
     assert lib.q3_op_attn_prefill(fake, fake, fake, 10, 8, 3, 16, 8, fake, 0, None) == -1   # t0+M > t_cap
     assert lib.q3_op_attn_prefill(fake, fake, fake, 16, 8, 3, 16, 8, fake, 1, None) == -1   # bad o dtype
-    assert lib.q3_op_gemm(fake, 2, fake, fake, 4, 128, 64, 5, None) == -1       # bad epilogue
+    assert lib.q3_op_gemm(fake, 2, fake, fake, 4, 128, 64, 6, 1, None, None) == -1       # bad epilogue
     assert lib.q3_op_sample(fake, 1, 10, -1.0, 0.9, fake, fake, None) == -1
     assert lib.q3_op_sample(fake, 1, 10, 0.7, 0.9, None, fake, None) == -1

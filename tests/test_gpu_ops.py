@@ -184,6 +184,70 @@ def test_gemm_pair_activations_equal_split(q3, M, N, K):
     assert np.abs(Cp.cpu().numpy()[rows] - ref).max() <= 3e-5 * np.sqrt(K) * 0.02
 
 
+# Prefill shapes (QKV and gate/up at 2047 rows) and ragged ones.
+EPILOGUE_SHAPES = [(2047, 4096, 1024), (2047, 6144, 1024), (1000, 1024, 3072), (129, 256, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", EPILOGUE_SHAPES)
+def test_gemm_pair_epilogues_equal_split(q3, M, N, K):
+    """Every epilogue, with and without column scales (the int8 weights' row scales): pair-A
+    products equal, bit for bit, float32-A products split into the same hi / lo parts while
+    staging (the same matrix-core sequence per output); sampled rows also against a float64
+    product."""
+    import torch
+    announce("gemm epilogues", M, N, K)
+    A = synth.normal((21, M, K), (M, K))
+    Wf = f32_of_bits(_bf16(synth.normal((22, N, K), (N, K), 0.02)))
+    W = bf16_dev(_bf16(Wf))
+    At, Ap = torch.from_numpy(A).cuda(), bf16_dev(_pair_bits(A))
+    cs = torch.from_numpy(synth.normal((24, N), (N,)).astype(np.float32)).cuda()
+    R = torch.from_numpy(synth.normal((23, M, N), (M, N))).cuda()
+    cases = [(q3.GEMM_F32, (M, N), torch.float32), (q3.GEMM_BF16, (M, N), torch.bfloat16),
+             (q3.GEMM_SWIGLU_F32, (M, N // 2), torch.float32), (q3.GEMM_SWIGLU_PAIR, (M, N), torch.bfloat16),
+             (q3.GEMM_RESID_F32, (M, N), torch.float32)]
+    for epi, shape, dt in cases:
+        for scale in (None, cs):
+            C1 = R.clone() if epi == q3.GEMM_RESID_F32 else torch.empty(shape, dtype=dt, device="cuda")
+            C2 = C1.clone()
+            q3.op_gemm(At, W, C1, epi, colscale=scale)
+            q3.op_gemm(Ap, W, C2, epi, a_pair=True, colscale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(C1, C2), (epi, scale is not None)
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    q3.op_gemm(Ap, W, C, q3.GEMM_F32, a_pair=True)
+    rows = [0, 1, M // 2, M - 2, M - 1]
+    ref = A[rows].astype(np.float64) @ Wf.T.astype(np.float64)
+    assert np.abs(C.cpu().numpy()[rows] - ref).max() <= 3e-5 * np.sqrt(K) * 0.02
+
+
+@pytest.mark.parametrize("M,N,K,S", [(2047, 1024, 2048, 2), (2047, 1024, 3072, 3), (300, 1024, 3072, 4),
+                                     (1000, 1024, 2048, 32)])
+def test_gemm_split_k_partials(q3, M, N, K, S):
+    """Split-K partials (the prefill O and down projections): partial z is the product over
+    the 64-wide k-tiles [z n / S, (z+1) n / S), n = K / 64, checked against float64 on
+    sampled rows, and equal bit for bit between pair A and float32 A."""
+    import torch
+    announce("gemm split-K", M, N, K, S)
+    A = synth.normal((25, M, K), (M, K))
+    Wf = f32_of_bits(_bf16(synth.normal((26, N, K), (N, K), 0.02)))
+    W = bf16_dev(_bf16(Wf))
+    P1 = torch.empty(S, M, N, dtype=torch.float32, device="cuda")
+    P2 = torch.empty_like(P1)
+    q3.op_gemm(torch.from_numpy(A).cuda(), W, P1, q3.GEMM_PARTIAL_F32, splits=S)
+    q3.op_gemm(bf16_dev(_pair_bits(A)), W, P2, q3.GEMM_PARTIAL_F32, a_pair=True, splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(P1, P2)
+    got = P2.cpu().numpy()
+    n = K // 64
+    rows = [0, M // 3, M - 1]
+    for z in range(S):
+        k0, k1 = 64 * (n * z // S), 64 * (n * (z + 1) // S)
+        ref = A[rows, k0:k1].astype(np.float64) @ Wf[:, k0:k1].T.astype(np.float64)
+        assert np.abs(got[z][rows] - ref).max() <= 3e-5 * np.sqrt(max(k1 - k0, 1)) * 0.02, z
+    with pytest.raises(q3.Q3Error):
+        q3.op_gemm(bf16_dev(_pair_bits(A)), W, P2, q3.GEMM_F32, a_pair=True, splits=2)
+
+
 def test_gemm_swiglu(q3):
     import torch
     announce("gemm swiglu")
