@@ -12,13 +12,16 @@
 //   (N = S when no token qualifies, i.e. the whole vocabulary is kept);
 //   the drawn token is the first with C >= floor(u * N) + 1, i.e. C > u * N.
 // The search is a radix select on the order-preserving 32-bit key of the logit:
-// a 65536-bucket histogram of masses over the key's upper 16 bits (many blocks,
-// integer atomics); one block finds the bucket where the cumulative mass crosses the
-// threshold; many blocks gather that bucket's members as packed (key, ~id) words; one
-// block sorts them (key descending, id ascending -- independent of the gather order) and
-// walks their masses to the crossing token. A bucket with more members than the sort
-// holds falls back to two 8-bit refinement levels and an id-ordered tie pass over the
-// whole row.
+// a 65536-bucket histogram of masses over the key's upper 16 bits and the sums of its
+// 256-bucket groups (many blocks, integer atomics); many blocks each find the bucket where
+// the cumulative mass crosses the threshold (the same result in every block, from the
+// group sums and one group's buckets) and gather that bucket's members as packed (key,
+// ~id) words; one block sorts them (key descending, id ascending -- independent of the
+// gather order) and walks their masses to the crossing token. A bucket with more members
+// than the sort holds falls back to two 8-bit refinement levels and an id-ordered tie pass
+// over the whole row. Five launches per draw with a nucleus (histogram; nucleus gather;
+// nucleus walk; draw gather; draw walk, which also leaves the workspace zeroed), three
+// without.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,7 +41,8 @@ struct RowWs {           // per-row workspace layout (in u64 words)
     static constexpr size_t list = NB1 + 264;  // [V] members of the crossing bucket
     static size_t words(int V) { return NB1 + 264 + (size_t)V; }
 };
-// state words of a row
+// state words of a row (SW_COUNT is zero whenever a gather starts: the walk that reads it
+// clears it)
 enum SelWord { SW_ABOVE = 0, SW_THR = 1, SW_N = 2, SW_BUCKET = 3, SW_COUNT = 4, SW_S = 5 };
 
 __global__ void k_argmax_rows(const float* __restrict__ logits, u64* __restrict__ amax, int V,
@@ -82,12 +86,13 @@ __device__ __forceinline__ double row_zmax(const u64* amax, int b, double T) {
     return __ddiv_rn((double)key_to_float((uint32_t)(amax[b] >> 32)), T);
 }
 
-// Fixed-point masses into the row's 65536-bucket histogram (keyed by the upper 16 bits).
-// Each block first sums its tokens' masses per bucket in shared memory (a direct-mapped
-// table of HIST_SLOTS buckets, slot = bucket mod HIST_SLOTS; a bucket whose slot another
-// bucket holds goes straight to memory), then adds its non-empty slots to the row's
-// histogram: the memory-side atomics drop from one per token to about one per bucket and
-// block. Integer sums: the histogram does not depend on the order of the additions.
+// Fixed-point masses into the row's 65536-bucket histogram (keyed by the upper 16 bits)
+// and its 256 group sums. Each block first sums its tokens' masses per bucket in shared
+// memory (a direct-mapped table of HIST_SLOTS buckets, slot = bucket mod HIST_SLOTS; a
+// bucket whose slot another bucket holds goes straight to memory), then adds its
+// non-empty slots to the row's histogram: the memory-side atomics drop from one per token
+// to about one per bucket and block. Integer sums: the histogram does not depend on the
+// order of the additions.
 constexpr int HIST_SLOTS = 8192, HIST_THREADS = 1024, HIST_BLOCKS = 32;
 constexpr unsigned HIST_EMPTY = 0xFFFFFFFFu;
 __global__ __launch_bounds__(HIST_THREADS) void k_sample_hist(const float* __restrict__ logits,
@@ -95,13 +100,16 @@ __global__ __launch_bounds__(HIST_THREADS) void k_sample_hist(const float* __res
                                                               double scale, u64* __restrict__ ws, size_t row_words) {
     __shared__ unsigned lkey[HIST_SLOTS];
     __shared__ u64 lmass[HIST_SLOTS];
+    __shared__ u64 lgroup[256];          // this block's masses per 256-bucket group
     const int b = blockIdx.y;
     const float* l = logits + (size_t)b * V;
     u64* hist = ws + (size_t)b * row_words + RowWs::hist;
+    u64* gsum = ws + (size_t)b * row_words + RowWs::gsum;
     for (int i = threadIdx.x; i < HIST_SLOTS; i += HIST_THREADS) {
         lkey[i] = HIST_EMPTY;
         lmass[i] = 0ull;
     }
+    if (threadIdx.x < 256) lgroup[threadIdx.x] = 0ull;
     __syncthreads();
     const double zmax = row_zmax(amax, b, Td);
     for (int j = blockIdx.x * HIST_THREADS + threadIdx.x; j < V; j += gridDim.x * HIST_THREADS) {
@@ -110,12 +118,23 @@ __global__ __launch_bounds__(HIST_THREADS) void k_sample_hist(const float* __res
         if (!m) continue;
         const unsigned k = ordered_key(v) >> 16, slot = k % HIST_SLOTS;
         const unsigned old = atomicCAS(&lkey[slot], HIST_EMPTY, k);
-        if (old == HIST_EMPTY || old == k) atomicAdd(&lmass[slot], m);
-        else atomicAdd(hist + k, m);
+        if (old == HIST_EMPTY || old == k) {
+            atomicAdd(&lmass[slot], m);
+        } else {
+            atomicAdd(hist + k, m);
+            atomicAdd(&lgroup[k >> 8], m);
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < HIST_SLOTS; i += HIST_THREADS)
-        if (lkey[i] != HIST_EMPTY) atomicAdd(hist + lkey[i], lmass[i]);
+        if (lkey[i] != HIST_EMPTY) {
+            atomicAdd(hist + lkey[i], lmass[i]);
+            atomicAdd(&lgroup[lkey[i] >> 8], lmass[i]);
+        }
+    // the group sums: one memory-side atomic per block and non-empty group (a row's masses
+    // fall in a few groups; per-bucket atomics on those words would queue up)
+    __syncthreads();
+    if (threadIdx.x < 256 && lgroup[threadIdx.x]) atomicAdd(gsum + threadIdx.x, lgroup[threadIdx.x]);
 }
 
 // Exclusive prefix sum of one u64 per thread over a 1024-thread block; returns the total.
@@ -231,32 +250,20 @@ __device__ void select_refine(const float* __restrict__ l, int V, double Td, dou
     __syncthreads();
 }
 
-// Sums of the 256-bucket groups of each row's histogram: block g of row b.
-__global__ __launch_bounds__(256) void k_hist_groups(u64* __restrict__ ws, size_t row_words) {
-    __shared__ u64 red[4];
-    u64* w = ws + (size_t)blockIdx.y * row_words;
-    u64 v = w[RowWs::hist + 256 * blockIdx.x + threadIdx.x];
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) w[RowWs::gsum + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// Leave each row's histogram zeroed for the next call.
-__global__ __launch_bounds__(256) void k_hist_zero(u64* __restrict__ ws, size_t row_words) {
-    ws[(size_t)blockIdx.y * row_words + RowWs::hist + 256 * blockIdx.x + threadIdx.x] = 0ull;
-}
-
 // Stage of a selection: NUC finds the nucleus mass N (top_p < 1), DRAW the drawn token.
 enum { SEL_NUC = 0, SEL_DRAW = 1 };
 
-// One block per row: the threshold of this stage and its crossing bucket.
+// Many blocks: the threshold of this stage, its crossing bucket (every block finds the
+// same; block 0 records it for the walk), and the bucket's members into the row's list as
+// (key << 32) | (~id).
 template <int STAGE>
-__global__ __launch_bounds__(1024) void k_sel_bucket(u64* __restrict__ ws, size_t row_words, float top_p,
-                                                     const float* __restrict__ u) {
+__global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ logits, u64* __restrict__ ws,
+                                                    size_t row_words, int V, float top_p,
+                                                    const float* __restrict__ u) {
     __shared__ u64 scan_lds[16];
     __shared__ SelState st;
-    const int b = blockIdx.x;
+    const int b = blockIdx.y;
+    const float* l = logits + (size_t)b * V;
     u64* w = ws + (size_t)b * row_words;
     const u64* hist = w + RowWs::hist;
     const u64* gs = w + RowWs::gsum;
@@ -273,23 +280,14 @@ __global__ __launch_bounds__(1024) void k_sel_bucket(u64* __restrict__ ws, size_
         if (thr < 1) thr = 1;
     }
     select_bucket(hist, gs, thr, true, scan_lds, &st);
-    if (threadIdx.x == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         sw[SW_ABOVE] = st.above;
         sw[SW_THR] = thr;
         sw[SW_BUCKET] = st.prefix;
-        sw[SW_COUNT] = 0ull;
         if (STAGE == SEL_NUC) sw[SW_S] = S;
     }
-}
-
-// Many blocks: the members of each row's crossing bucket, as (key << 32) | (~id).
-__global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ logits, u64* __restrict__ ws,
-                                                    size_t row_words, int V) {
-    const int b = blockIdx.y;
-    const float* l = logits + (size_t)b * V;
-    u64* w = ws + (size_t)b * row_words;
-    const uint32_t want = (uint32_t)w[RowWs::state + SW_BUCKET];
-    unsigned* count = reinterpret_cast<unsigned*>(w + RowWs::state + SW_COUNT);
+    const uint32_t want = st.prefix;
+    unsigned* count = reinterpret_cast<unsigned*>(sw + SW_COUNT);
     u64* list = w + RowWs::list;
     for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x) {
         const uint32_t key = ordered_key(l[j]);
@@ -303,6 +301,7 @@ __global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ lo
 // One block per row: sort the bucket's members (descending packed word = key descending,
 // id ascending), walk their masses from SW_ABOVE to the first cumulative mass >= SW_THR.
 // NUC stores that mass as N; DRAW writes the token and zeroes the row's histogram.
+// Runs with 1024 threads (the walk takes 4 members per thread).
 template <int STAGE>
 __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ logits, const u64* __restrict__ amax,
                                                     int V, double Td, double scale, u64* __restrict__ ws,
@@ -321,22 +320,39 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
     const int n = (int)min((u64)V, sw[SW_COUNT] & 0xFFFFFFFFull);
     if (tid == 0) { st.found = 0; st.id = 0; st.cum = 0; st.above = above; st.prefix = (uint32_t)sw[SW_BUCKET]; }
     if (n <= SORT_CAP) {
-        int P = 64;
-        while (P < n) P <<= 1;
-        for (int i = tid; i < P; i += blockDim.x) e[i] = i < n ? w[RowWs::list + i] : 0ull;
-        __syncthreads();
-        for (int k = 2; k <= P; k <<= 1)          // bitonic sort, descending
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = tid; i < P; i += blockDim.x) {
-                    const int pr = i ^ j;
-                    if (pr > i) {
-                        const u64 a = e[i], c = e[pr];
-                        const bool desc = (i & k) == 0;
-                        if (desc ? a < c : a > c) { e[i] = c; e[pr] = a; }
+        if (n <= (int)blockDim.x && 2 * n <= SORT_CAP) {
+            // one member per thread: its place in the descending order is the number of
+            // larger words (all distinct: the ids differ), so it is written straight there
+            // (past the unsorted copy, which every thread reads meanwhile)
+            u64 mine = 0ull;
+            if (tid < n) e[tid] = mine = w[RowWs::list + tid];
+            __syncthreads();
+            int rank = 0;
+            if (tid < n)
+                for (int j = 0; j < n; ++j) rank += e[j] > mine;
+            __syncthreads();
+            if (tid < n) e[SORT_CAP / 2 + rank] = mine;
+            __syncthreads();
+            if (tid < n) e[tid] = e[SORT_CAP / 2 + tid];
+            __syncthreads();
+        } else {
+            int P = 64;
+            while (P < n) P <<= 1;
+            for (int i = tid; i < P; i += blockDim.x) e[i] = i < n ? w[RowWs::list + i] : 0ull;
+            __syncthreads();
+            for (int k = 2; k <= P; k <<= 1)          // bitonic sort, descending
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int i = tid; i < P; i += blockDim.x) {
+                        const int pr = i ^ j;
+                        if (pr > i) {
+                            const u64 a = e[i], c = e[pr];
+                            const bool desc = (i & k) == 0;
+                            if (desc ? a < c : a > c) { e[i] = c; e[pr] = a; }
+                        }
                     }
+                    __syncthreads();
                 }
-                __syncthreads();
-            }
+        }
         // masses in order: thread t takes entries 4t .. 4t+3
         u64 m[4], sum = 0;
 #pragma unroll
@@ -370,7 +386,17 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
         if (tid == 0) sw[SW_N] = st.found ? st.cum : sw[SW_S];
     } else {
         if (tid == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
+        // leave the histogram zeroed for the next call: the groups that received mass
+        // (a group sum is zero only if all of its buckets are), then the group sums
+        const u64* gs = w + RowWs::gsum;
+        u64* hist = w + RowWs::hist;
+        const int g = tid >> 2, quarter = tid & 3;
+        if (gs[g] != 0ull)
+            for (int i = 0; i < 64; ++i) hist[256 * g + 64 * quarter + i] = 0ull;
+        __syncthreads();
+        if (tid < 256) w[RowWs::gsum + tid] = 0ull;
     }
+    if (tid == 0) sw[SW_COUNT] = 0ull;   // the next gather starts from zero
 }
 
 }  // namespace
@@ -409,18 +435,14 @@ hipError_t launch_sample(const float* logits, const unsigned long long* amax, in
     if (!ws_zeroed && (e = launch_fill_u64(w, 0ull, (int)(B * rw), s)) != hipSuccess) return e;
     const int nblk = (V + 255) / 256 < 512 ? (V + 255) / 256 : 512;
     hipLaunchKernelGGL(k_sample_hist, dim3(HIST_BLOCKS, B), dim3(HIST_THREADS), 0, s, logits, amax, V, Td, scale, w, rw);
-    hipLaunchKernelGGL(k_hist_groups, dim3(256, B), dim3(256), 0, s, w, rw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (top_p < 1.0f) {
-        hipLaunchKernelGGL(k_sel_bucket<SEL_NUC>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
-        hipLaunchKernelGGL(k_sel_gather, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V);
+        hipLaunchKernelGGL(k_sel_gather<SEL_NUC>, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V, top_p, u);
         hipLaunchKernelGGL(k_sel_final<SEL_NUC>, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, w, rw, out);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_sel_bucket<SEL_DRAW>, dim3(B), dim3(1024), 0, s, w, rw, top_p, u);
-    hipLaunchKernelGGL(k_sel_gather, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V);
+    hipLaunchKernelGGL(k_sel_gather<SEL_DRAW>, dim3(nblk, B), dim3(256), 0, s, logits, w, rw, V, top_p, u);
     hipLaunchKernelGGL(k_sel_final<SEL_DRAW>, dim3(B), dim3(1024), 0, s, logits, amax, V, Td, scale, w, rw, out);
-    hipLaunchKernelGGL(k_hist_zero, dim3(256, B), dim3(256), 0, s, w, rw);
     return hipGetLastError();
 }
 
