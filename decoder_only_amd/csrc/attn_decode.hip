@@ -82,8 +82,10 @@ __global__ __launch_bounds__(256) void k_attn_decode_part(
     }
     const int kbeg = c * CHUNK + wid * 64;
     const int kend = min(kbeg + 64, T);
-    // the chunk is one page (CHUNK == kKvPage): its keys are one strided run
-    const size_t chunk_base = kbeg < kend ? lay.off(seq, g, c * CHUNK) : 0;
+    // the chunk is one page (CHUNK == kKvPage): its keys are one strided run. The page is
+    // looked up whatever the length (c < the table's width: c * CHUNK < max_T <= t_cap), so
+    // that lookup and the length load go out together; it is used only for keys < T.
+    const size_t chunk_base = lay.off(seq, g, c * CHUNK);
     for (int kk = kbeg + grp; kk < kend; kk += 4) {
         float kv[8], vv[8];
         ld8(kc + chunk_base + (size_t)(kk - c * CHUNK) * 128 + sub * 8, kv);
@@ -167,8 +169,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
     const int seq = seq_base + b;
     const int T = min(lens[seq] + len_extra, t_cap);
     const int k0 = c * CHUNK + wid * 64;             // this wave's first key
-    // the chunk is one page (CHUNK == kKvPage): keys key, offset head_base + key * 128
-    const size_t head_base = c * CHUNK < T ? lay.off(seq, g, c * CHUNK) - (size_t)c * CHUNK * 128 : 0;
+    // the chunk is one page (CHUNK == kKvPage): keys key, offset head_base + key * 128. The
+    // page is looked up whatever the length (c < the table's width: c * CHUNK < max_T <=
+    // t_cap), so that lookup and the length load go out together; it is used for keys < T.
+    const size_t head_base = lay.off(seq, g, c * CHUNK) - (size_t)c * CHUNK * 128;
     const float scale = 0.088388346f;                // fl32(128^-0.5)
 
     // V rows for P.V: lane group (wid, quad) takes keys k0 + quad + 4 i, lane col dims 8 col ..
@@ -337,7 +341,7 @@ hipError_t launch_attn_decode(const float* q, const void* kc, const void* vc, in
                               int t_cap, const KvLayout& lay, const int32_t* lens, int len_extra, int seq_base,
                               int B, int Hq, int Hkv, int max_T, float* ws, void* o, int o_pair, hipStream_t s) {
     if (B <= 0) return hipSuccess;
-    if (Hq != G * Hkv) return hipErrorInvalidValue;
+    if (Hq != G * Hkv || max_T > t_cap) return hipErrorInvalidValue;   // (chunks index the page table)
     const int nchunk = (max_T + CHUNK - 1) / CHUNK;
     dim3 grid(nchunk, Hkv, B);
     if (kv_bf16)

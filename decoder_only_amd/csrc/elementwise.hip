@@ -266,25 +266,26 @@ hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStr
 }
 
 // Page copy (prefix reuse): slots 0 .. n-1 of page src into page dst, for every (layer,
-// kv head) run of a page ([layer][head][kKvPage][128]) in the K and V pools; blockIdx.y =
-// (layer * Hkv + head) * 2 + (0: K, 1: V), one 16-byte unit per thread.
-__global__ void k_kv_page_copy(uint4* __restrict__ kc, uint4* __restrict__ vc, size_t page_u, int Hkv, int src,
-                               int dst, size_t run_u, size_t n_u) {
+// kv head) run of the page ([layer][page][head][kKvPage][128]) in the K and V pools;
+// blockIdx.y = (layer * Hkv + head) * 2 + (0: K, 1: V), one 16-byte unit per thread.
+__global__ void k_kv_page_copy(uint4* __restrict__ kc, uint4* __restrict__ vc, size_t page_u, size_t layer_u, int Hkv,
+                               int src, int dst, size_t run_u, size_t n_u) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint4* base = ((int)blockIdx.y & 1) ? vc : kc;
-    const size_t off = (size_t)((int)blockIdx.y >> 1) * run_u + i;
+    const int r = (int)blockIdx.y >> 1, layer = r / Hkv, head = r % Hkv;
+    const size_t off = (size_t)layer * layer_u + (size_t)head * run_u + i;
     if (i < n_u) base[(size_t)dst * page_u + off] = base[(size_t)src * page_u + off];
 }
 
-hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, int n_layers, int Hkv, int kv_bytes,
-                               int src_page, int dst_page, int n, hipStream_t s) {
+hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, size_t layer_elems, int n_layers, int Hkv,
+                               int kv_bytes, int src_page, int dst_page, int n, hipStream_t s) {
     if (n_layers <= 0 || n <= 0) return hipSuccess;
     if (n > kKvPage || (128 * kv_bytes) % 16) return hipErrorInvalidValue;
     const size_t u = 16 / kv_bytes;     // elements per 16-byte unit
     const size_t n_u = (size_t)n * 128 / u;
     const dim3 grid((unsigned)((n_u + 255) / 256), (unsigned)(n_layers * Hkv * 2));
-    hipLaunchKernelGGL(k_kv_page_copy, grid, dim3(256), 0, s, (uint4*)kc, (uint4*)vc, page_elems / u, Hkv, src_page,
-                       dst_page, (size_t)kKvPage * 128 / u, n_u);
+    hipLaunchKernelGGL(k_kv_page_copy, grid, dim3(256), 0, s, (uint4*)kc, (uint4*)vc, page_elems / u, layer_elems / u,
+                       Hkv, src_page, dst_page, (size_t)kKvPage * 128 / u, n_u);
     return hipGetLastError();
 }
 

@@ -55,13 +55,14 @@ struct q3_engine {
     float* inv_freq = nullptr;
 
     // KV cache: a pool of pages, page = kKvPage token slots of every layer and kv head,
-    // [page][layer][kv head][slot][head_dim] in each of kc, vc. A sequence's page table row
-    // lists its pages in slot order; a page held by several sequences (q3_kv_fork) is copied
-    // by the first one that writes into it.
+    // stored layer-major, [layer][page][kv head][slot][head_dim] in each of kc, vc (one
+    // layer's cache is one region, as the kernels of a layer stream it). A sequence's page
+    // table row lists its pages in slot order; a page held by several sequences
+    // (q3_kv_fork) is copied by the first one that writes into it.
     void* kc = nullptr;
     void* vc = nullptr;
-    size_t kv_layer_elems = 0;     // one layer's run within a page
-    size_t page_elems = 0;         // one page (every layer)
+    size_t kv_layer_elems = 0;     // one layer's region (every page)
+    size_t page_elems = 0;         // one page within a layer
     int n_pages = 0, max_pages = 0;                // pool size; table entries per sequence
     int32_t* d_pt = nullptr;                       // page table [max_batch][max_pages]
     std::vector<int32_t> h_pt;                     // its host copy
@@ -438,9 +439,9 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
     // KV-cache page pool and page table
     e->max_pages = (c.max_seq + kKvPage - 1) / kKvPage;
     e->n_pages = c.kv_pages > 0 ? c.kv_pages : c.max_batch * e->max_pages;
-    e->kv_layer_elems = (size_t)Hkv * kKvPage * dh;
-    e->page_elems = e->kv_layer_elems * (size_t)(c.n_layers > 0 ? c.n_layers : 1);
-    const size_t kvb = e->page_elems * (size_t)e->n_pages * e->kvbytes();
+    e->page_elems = (size_t)Hkv * kKvPage * dh;
+    e->kv_layer_elems = e->page_elems * (size_t)e->n_pages;
+    const size_t kvb = e->kv_layer_elems * (size_t)(c.n_layers > 0 ? c.n_layers : 1) * e->kvbytes();
     if (!(e->kc = e->alloc(kvb)) || !(e->vc = e->alloc(kvb))) return oom();
     const size_t ptn = (size_t)c.max_batch * e->max_pages;
     e->h_pt.assign(ptn, 0);       // entry 0 until a sequence holds the page: never read
@@ -627,8 +628,9 @@ static q3_status claim_pages(q3_engine* e, int seq, int slot0, int n) {
         e->refs[pg] = 1;
         if (!missing) {      // copy on write
             --e->refs[row[p]];
-            HIPCHK(e, launch_kv_page_copy(e->kc, e->vc, e->page_elems, e->cfg.n_layers, e->cfg.n_kv_heads,
-                                          (int)e->kvbytes(), row[p], pg, page_valid(e, seq, p), e->stream));
+            HIPCHK(e, launch_kv_page_copy(e->kc, e->vc, e->page_elems, e->kv_layer_elems, e->cfg.n_layers,
+                                          e->cfg.n_kv_heads, (int)e->kvbytes(), row[p], pg, page_valid(e, seq, p),
+                                          e->stream));
         }
         row[p] = pg;
         if (lo < 0) lo = p;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 3 - NB) void k_gemm(const void* __restrict__ A
     {
         const int nx = gridDim.x, ny = gridDim.y;
         const int total = nx * ny * gridDim.z;
-        if (total % 8 == 0) {
+        if (total % 8 == 0 && ny > 1) {            // (one row tile: no A to share)
             const int b = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
             const int t = (b % 8) * (total / 8) + b / 8;
             bz = t / (nx * ny);

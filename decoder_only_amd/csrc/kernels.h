@@ -47,9 +47,10 @@ hipError_t launch_qk_rope_prefill(const float* qkv, int M, int t0, const float* 
 // lens[seq_base + b] += by for b < B.
 hipError_t launch_len_advance(int32_t* lens, int seq_base, int B, int by, hipStream_t s);
 // Slots 0 .. n-1 of page src_page into page dst_page, for every layer and kv head of the K and
-// V page pools (pages of [n_layers][Hkv][kKvPage][128], kv_bytes per element).
-hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, int n_layers, int Hkv, int kv_bytes,
-                               int src_page, int dst_page, int n, hipStream_t s);
+// V page pools ([n_layers][pages][Hkv][kKvPage][128], kv_bytes per element; page_elems and
+// layer_elems are the strides of a page and of a layer).
+hipError_t launch_kv_page_copy(void* kc, void* vc, size_t page_elems, size_t layer_elems, int n_layers, int Hkv,
+                               int kv_bytes, int src_page, int dst_page, int n, hipStream_t s);
 // Slots 0 .. len-1 of one (sequence, layer) between the paged cache and a dense buffer
 // [Hkv][len][128] (device memory): to_cache = true writes the cache (an import), false reads it.
 hipError_t launch_kv_dense(void* kc_layer, void* vc_layer, const KvLayout& lay, int seq, int Hkv, int kv_bytes,

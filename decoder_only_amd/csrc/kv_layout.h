@@ -9,9 +9,9 @@ namespace q3 {
 // Where the K (or V) cache keeps slot `slot` of kv head g of sequence `seq`, as an element
 // offset from the cache's base for the layer in question.
 //   paged (pt != NULL): a page holds kKvPage consecutive slots of one sequence, for every
-//     layer and kv head ([layer][head][kKvPage][128]); pt[seq][slot / kKvPage] is the page
-//     id; page_stride = elements per page, head_stride = kKvPage * 128 (the layer's base
-//     already points at its part of page 0);
+//     kv head ([page][head][kKvPage][128] within a layer's region; every layer has its own
+//     region, with the same page ids); pt[seq][slot / kKvPage] is the page id;
+//     page_stride = elements per page of one layer, head_stride = kKvPage * 128;
 //   contiguous (pt == NULL): [seq][head][t_cap][128] from the layer's base; page_stride =
 //     elements per sequence, head_stride = t_cap * 128.
 // Within one page (or one contiguous run) consecutive slots of a head are 128 elements
