@@ -52,6 +52,10 @@ def main() -> int:
                          "ordinary launch: every workgroup is resident at once either way, and the "
                          "ordinary dispatch starts ~13 us sooner per step")
     ap.add_argument("--plain-launch", action="store_true", help="(the default; kept for old command lines)")
+    ap.add_argument("--prefill-only-extras", action="store_true",
+                    help="of the extra lines run only the 2048-token prefill (counter passes over its kernels)")
+    ap.add_argument("--one-launch-mode", action="store_true",
+                    help="skip the bs1 line under the other launch mode (profiling runs keep to ordinary launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain streaming kernel (torch.neg) over MIB MiB of float32, three "
                          "times: a known-size reference for hardware byte counters")
@@ -112,18 +116,20 @@ def main() -> int:
     ms_per_step = 1000.0 * elapsed / args.steps
     log(f"bs1 decode: {value:.1f} tok/s, {ms_per_step:.2f} ms per generation")
     # the same generations with the other launch mode of the persistent kernel, for comparison
-    eng.set_decode_path(0 if not args.cooperative else 3)
-    generation()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        generation()
-    torch.cuda.synchronize()
-    other = n_dec * args.steps / (time.perf_counter() - t0)
-    eng.set_decode_path(3 if not args.cooperative else 0)
     launch_mode = "cooperative" if args.cooperative else "ordinary"
     other_mode = "ordinary" if args.cooperative else "cooperative"
-    log(f"bs1 decode with the {other_mode} launch: {other:.1f} tok/s")
+    other = None
+    if not args.one_launch_mode:
+        eng.set_decode_path(0 if not args.cooperative else 3)
+        generation()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            generation()
+        torch.cuda.synchronize()
+        other = n_dec * args.steps / (time.perf_counter() - t0)
+        eng.set_decode_path(3 if not args.cooperative else 0)
+        log(f"bs1 decode with the {other_mode} launch: {other:.1f} tok/s")
 
     # Roofline of the dominant kernel, event-timed on the engine's stream over a second pass
     # of the same steps. With the persistent decode kernel (one launch per decode step) that
@@ -139,7 +145,9 @@ def main() -> int:
     step_gbs = step["bytes"] / (step["ms"] / 1e3) / 1e9
     step_us = 1e3 * step["ms"] / step["launches"]
     extras = {"decode_step_us": round(step_us, 2), "decode_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-              "bs1_launch": launch_mode, f"bs1_decode_tok_s_{other_mode}_launch": round(other, 2)}
+              "bs1_launch": launch_mode}
+    if other is not None:
+        extras[f"bs1_decode_tok_s_{other_mode}_launch"] = round(other, 2)
     if gemv["launches"] == 0:
         roofline = {"kernel": "k_decode_mega (persistent decode step: all layers, LM head, argmax)",
                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -161,6 +169,7 @@ def main() -> int:
             extras.update(prefill_line(eng, w, q3, torch, synth))
         except Exception as ex:  # the main line is still reported
             extras["prefill_error"] = repr(ex)
+    if not args.no_extras and not args.prefill_only_extras:
         try:
             extras.update(c3_decode_line(eng, q3, torch, synth))
         except Exception as ex:
@@ -169,8 +178,6 @@ def main() -> int:
             extras.update(bs64_line(eng, w, q3, torch, synth, max_seq))
         except Exception as ex:
             extras["bs64_error"] = repr(ex)
-
-    if not args.no_extras:
         try:
             extras.update(int8_line(weights, q3, torch, synth, args.steps))
         except Exception as ex:
@@ -183,7 +190,7 @@ def main() -> int:
         except Exception as ex:
             cpu = {"error": repr(ex)}
     eng.close()
-    if not args.no_extras and not args.no_long:
+    if not args.no_extras and not args.no_long and not args.prefill_only_extras:
         try:
             extras.update(c5_lines(weights, q3, torch, synth))
         except Exception as ex:
