@@ -375,7 +375,8 @@ def test_attn_decode_full_shapes_sampled(q3):
 
 # ------------------------------------------------------------------ prefill attention (flash, matrix cores)
 
-@pytest.mark.parametrize("M,t0", [(1, 0), (63, 0), (64, 0), (65, 0), (200, 0), (130, 37), (1, 500), (700, 0), (1000, 24)])
+@pytest.mark.parametrize("M,t0", [(1, 0), (63, 0), (64, 0), (65, 0), (200, 0), (130, 37), (1, 500), (700, 0), (1000, 24),
+                                  (4100, 3)])
 def test_attn_prefill(q3, M, t0):
     import torch
     announce("attn_prefill", M, t0)
