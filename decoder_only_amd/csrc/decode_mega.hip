@@ -615,7 +615,7 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // on scores scaled by log2(e)). Writes the normalised output of both heads to o_out, or,
 // when o_out is null, leaves the merged per-head state (base-2 max, sum, unnormalised
 // acc[128]) in sm.att.
-template <bool DB, bool CAUSAL>
+template <bool DB, bool CAUSAL, bool SHORT = false>
 __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, const KvHead& hb, int k0, int k1, int T, float* o_out,
                                        int b, int nnew_rt) {
     const int nnew = CAUSAL ? nnew_rt : 1;
@@ -698,6 +698,91 @@ __device__ __forceinline__ void attend(const MegaParams& p, Smem& sm, const KvHe
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.sp[16 * t + 4 * quad + r][col] = (sh[r] + sl[r]) * scale;
             }
+        }
+        if constexpr (SHORT) {
+            // Whole range in this one shot (nk <= 256 keys): the softmax of head h over all
+            // nk scores by wave h alone (lane: keys lane + 64 i; keys past nk get probability
+            // 0), so P.V needs no running maxima and the four waves' partial products are a
+            // plain sum.
+            __syncthreads();                       // every wave's scores are in sm.sp
+            if (wid < 2) {
+                float x[4], mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = lane + 64 * i;
+                    x[i] = key < nk ? sm.sp[key][wid] : -INFINITY;
+                    mx = fmaxf(mx, x[i]);
+                }
+                mx = wave_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = lane + 64 * i < nk ? __builtin_amdgcn_exp2f(x[i] - mx) : 0.f;
+                    sm.sp[lane + 64 * i][wid] = pr;
+                    sum += pr;
+                }
+                sum = wave_sum(sum);
+                if (lane == 0) sm.wl[wid][0] = sum;
+            }
+            // value rows past the last key of its tile: zero (their probabilities are zero, and
+            // a stale row could hold anything); the wave that owns the tile writes and reads them
+            if (wid == ((ntile - 1) & 3)) {
+                for (int r = nk + (lane >> 4); r < 16 * ntile; r += 4)
+                    *reinterpret_cast<u32x4*>(&sm.u.kv.v[ro + r][8 * col]) = u32x4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();                       // probabilities visible to every wave
+            // P.V of this wave's tiles: lane group quad takes keys 16 t + 4 i + quad, lane col
+            // dims 8 col .. 8 col + 7
+            for (int t = wid; t < ntile; t += 4) {
+                u32x4 vv[4];
+                f32x2 pp[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * t + 4 * i + quad;
+                    vv[i] = *reinterpret_cast<const u32x4*>(&sm.u.kv.v[ro + r][8 * col]);
+                    pp[i] = *reinterpret_cast<const f32x2*>(&sm.sp[r][0]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // all reads of the tile first
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[8];
+                    unpack8(vv[i], v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        acc[0][e] += pp[i][0] * v[e];
+                        acc[1][e] += pp[i][1] * v[e];
+                    }
+                }
+            }
+            // sum over the four lane groups (the keys of a tile): lanes col, col + 16, +32, +48
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = acc[h][e];
+                    auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                    x = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+                    auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                    acc[h][e] = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+                }
+            // the waves' partial products go into the K staging rows (not read after the first
+            // barrier above): [wave][head][128]
+            float* part = reinterpret_cast<float*>(&sm.u.kv.k[0][0]);
+            if (quad == 0) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) part[(wid * 2 + h) * DH + 8 * col + e] = acc[h][e];
+            }
+            __syncthreads();
+            {
+                const int h = tid >> 7, dd = tid & 127;
+                const float tot = (part[(0 * 2 + h) * DH + dd] + part[(1 * 2 + h) * DH + dd]) +
+                                  (part[(2 * 2 + h) * DH + dd] + part[(3 * 2 + h) * DH + dd]);
+                o_out[h * DH + dd] = tot / sm.wl[h][0];
+            }
+            __syncthreads();                       // o complete; shared memory free again
+            return;
         }
         // this wave's softmax statistics over the shot: lane (tile slot quad, key col)
         for (int t0 = wid; t0 < ntile; t0 += 16) {
@@ -1045,7 +1130,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep<CAUSAL>(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
-                attend<false, CAUSAL>(p, sm, hb, 0, T, T, sm.o[b], b, nnew);
+                attend<false, CAUSAL, true>(p, sm, hb, 0, T, T, sm.o[b], b, nnew);
             }
         } else {
             // B1: unit w = (group w % 8, chunk w / 8) attends its chunk, per row
