@@ -31,6 +31,7 @@ namespace {
 
 constexpr int NB1 = 65536;
 typedef unsigned long long u64;
+typedef __attribute__((ext_vector_type(2))) unsigned long long u64x2;
 
 constexpr int SORT_CAP = 4096;   // bucket members sorted in shared memory
 
@@ -167,19 +168,20 @@ struct SelState {
 };
 
 // Level 1 of the search: the bucket (upper 16 key bits) where the cumulative mass in
-// order reaches thr, and the mass of all buckets before it: first over the 256 group sums
-// (descending), then over the 256 buckets of the crossing group. Threads 0..255 of the
-// block scan; all threads return after the result is in *st. Also returns S (the sum of
-// all masses).
-__device__ u64 select_bucket(const u64* __restrict__ hist, const u64* __restrict__ gsum, u64 thr, bool find,
-                             u64* scan_lds, SelState* st) {
+// order reaches thr = thr_of(S), S being the sum of all masses, and the mass of all buckets
+// before it: first over the 256 group sums (descending), then over the 256 buckets of the
+// crossing group. Threads 0..255 of the block scan; every thread returns thr after the
+// result is in *st, and S in S_out.
+template <typename ThrFn>
+__device__ u64 select_bucket(const u64* __restrict__ hist, const u64* __restrict__ gsum, ThrFn thr_of,
+                             u64* scan_lds, SelState* st, u64& S_out) {
     const int tid = threadIdx.x;
     __shared__ u64 lv[2];                  // crossing group, mass before it
     if (tid == 0) { st->found = 0; st->prefix = 0; st->above = 0; lv[0] = 0; lv[1] = 0; }
     const u64 g = tid < 256 ? gsum[255 - tid] : 0ull;
     u64 excl;
     const u64 S = block_scan_excl(g, scan_lds, excl);   // synchronises
-    if (!find) return S;
+    const u64 thr = thr_of(S);
     if (tid < 256 && excl < thr && excl + g >= thr) { lv[0] = 255 - tid; lv[1] = excl; }
     __syncthreads();
     const uint32_t G = (uint32_t)lv[0];
@@ -192,7 +194,8 @@ __device__ u64 select_bucket(const u64* __restrict__ hist, const u64* __restrict
         st->above = above0 + ex2;
     }
     __syncthreads();
-    return S;
+    S_out = S;
+    return thr;
 }
 
 // The rest of the search over the whole row, from st->prefix (bucket) and st->above.
@@ -268,18 +271,23 @@ __global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ lo
     const u64* hist = w + RowWs::hist;
     const u64* gs = w + RowWs::gsum;
     u64* sw = w + RowWs::state;
-    const u64 S = select_bucket(hist, gs, 0, false, scan_lds, &st);
-    u64 thr;
-    if (STAGE == SEL_NUC) {
-        const double tA = ceil((double)top_p * (double)S);
-        thr = tA < 1.0 ? 1ull : (tA >= (double)S ? S : (u64)tA);
-    } else {
-        const u64 N = top_p < 1.0f ? sw[SW_N] : S;
-        const double tB = floor((double)u[b] * (double)N) + 1.0;
-        thr = tB >= (double)N ? N : (u64)tB;
-        if (thr < 1) thr = 1;
-    }
-    select_bucket(hist, gs, thr, true, scan_lds, &st);
+    // this thread's first two logits and the nucleus mass, requested together with the sums
+    const int j0 = blockIdx.x * blockDim.x + threadIdx.x, js = gridDim.x * blockDim.x;
+    const float v0 = j0 < V ? l[j0] : 0.f;
+    const float v1 = j0 + js < V ? l[j0 + js] : 0.f;
+    const u64 Nw = (STAGE == SEL_DRAW && top_p < 1.0f) ? sw[SW_N] : 0ull;
+    const float ub = STAGE == SEL_DRAW ? u[b] : 0.f;
+    u64 S;
+    const u64 thr = select_bucket(hist, gs, [&](u64 s) {
+        if (STAGE == SEL_NUC) {
+            const double tA = ceil((double)top_p * (double)s);
+            return tA < 1.0 ? 1ull : (tA >= (double)s ? s : (u64)tA);
+        }
+        const u64 N = top_p < 1.0f ? Nw : s;
+        const double tB = floor((double)ub * (double)N) + 1.0;
+        const u64 t = tB >= (double)N ? N : (u64)tB;
+        return t < 1 ? 1ull : t;
+    }, scan_lds, &st, S);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sw[SW_ABOVE] = st.above;
         sw[SW_THR] = thr;
@@ -289,13 +297,16 @@ __global__ __launch_bounds__(256) void k_sel_gather(const float* __restrict__ lo
     const uint32_t want = st.prefix;
     unsigned* count = reinterpret_cast<unsigned*>(sw + SW_COUNT);
     u64* list = w + RowWs::list;
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < V; j += gridDim.x * blockDim.x) {
-        const uint32_t key = ordered_key(l[j]);
+    auto visit = [&](float v, int j) {
+        const uint32_t key = ordered_key(v);
         if ((key >> 16) == want) {
             const unsigned i = atomicAdd(count, 1u);
             if (i < (unsigned)V) list[i] = ((u64)key << 32) | (u64)(0xFFFFFFFFu - (uint32_t)j);
         }
-    }
+    };
+    if (j0 < V) visit(v0, j0);
+    if (j0 + js < V) visit(v1, j0 + js);
+    for (int j = j0 + 2 * js; j < V; j += js) visit(l[j], j);
 }
 
 // One block per row: sort the bucket's members (descending packed word = key descending,
@@ -306,7 +317,7 @@ template <int STAGE>
 __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ logits, const u64* __restrict__ amax,
                                                     int V, double Td, double scale, u64* __restrict__ ws,
                                                     size_t row_words, int32_t* __restrict__ out) {
-    __shared__ u64 e[SORT_CAP];
+    __shared__ __align__(16) u64 e[SORT_CAP];
     __shared__ u64 scan_lds[16];
     __shared__ u64 h2[256];
     __shared__ SelState st;
@@ -315,21 +326,37 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
     const float* l = logits + (size_t)b * V;
     u64* w = ws + (size_t)b * row_words;
     u64* sw = w + RowWs::state;
+    // one round of reads: the state words, the first blockDim members of the list (read
+    // whether or not they were written this call; only the first n are used), the maximum
+    // and, for the draw, the group sums that tell which histogram groups to clear
+    const u64 above = sw[SW_ABOVE], thr = sw[SW_THR], cw = sw[SW_COUNT], bucket = sw[SW_BUCKET];
+    const u64 first = tid < V ? w[RowWs::list + tid] : 0ull;
+    const u64 gsv = STAGE == SEL_DRAW ? w[RowWs::gsum + (tid >> 2)] : 0ull;
     const double zmax = row_zmax(amax, b, Td);
-    const u64 above = sw[SW_ABOVE], thr = sw[SW_THR];
-    const int n = (int)min((u64)V, sw[SW_COUNT] & 0xFFFFFFFFull);
-    if (tid == 0) { st.found = 0; st.id = 0; st.cum = 0; st.above = above; st.prefix = (uint32_t)sw[SW_BUCKET]; }
+    const int n = (int)min((u64)V, cw & 0xFFFFFFFFull);
+    if (tid == 0) { st.found = 0; st.id = 0; st.cum = 0; st.above = above; st.prefix = (uint32_t)bucket; }
     if (n <= SORT_CAP) {
         if (n <= (int)blockDim.x && 2 * n <= SORT_CAP) {
             // one member per thread: its place in the descending order is the number of
             // larger words (all distinct: the ids differ), so it is written straight there
-            // (past the unsorted copy, which every thread reads meanwhile)
-            u64 mine = 0ull;
-            if (tid < n) e[tid] = mine = w[RowWs::list + tid];
+            // (past the unsorted copy, which every thread reads meanwhile); the count reads
+            // 16 members per round of eight 16-byte shared-memory reads
+            const u64 mine = first;
+            if (tid < n) e[tid] = mine;
             __syncthreads();
             int rank = 0;
-            if (tid < n)
-                for (int j = 0; j < n; ++j) rank += e[j] > mine;
+            if (tid < n) {
+                const u64x2* e2 = reinterpret_cast<const u64x2*>(e);
+                int j = 0;
+                for (; j + 16 <= n; j += 16) {
+                    u64x2 a[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) a[k] = e2[(j >> 1) + k];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) rank += (int)(a[k][0] > mine) + (int)(a[k][1] > mine);
+                }
+                for (; j < n; ++j) rank += e[j] > mine;
+            }
             __syncthreads();
             if (tid < n) e[SORT_CAP / 2 + rank] = mine;
             __syncthreads();
@@ -338,7 +365,7 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
         } else {
             int P = 64;
             while (P < n) P <<= 1;
-            for (int i = tid; i < P; i += blockDim.x) e[i] = i < n ? w[RowWs::list + i] : 0ull;
+            for (int i = tid; i < P; i += blockDim.x) e[i] = i < n ? (i == tid ? first : w[RowWs::list + i]) : 0ull;
             __syncthreads();
             for (int k = 2; k <= P; k <<= 1)          // bitonic sort, descending
                 for (int j = k >> 1; j > 0; j >>= 1) {
@@ -388,10 +415,9 @@ __global__ __launch_bounds__(1024) void k_sel_final(const float* __restrict__ lo
         if (tid == 0) out[b] = st.found ? st.id : (int32_t)(0xFFFFFFFFu - (uint32_t)(amax[b] & 0xFFFFFFFFull));
         // leave the histogram zeroed for the next call: the groups that received mass
         // (a group sum is zero only if all of its buckets are), then the group sums
-        const u64* gs = w + RowWs::gsum;
         u64* hist = w + RowWs::hist;
         const int g = tid >> 2, quarter = tid & 3;
-        if (gs[g] != 0ull)
+        if (gsv != 0ull)
             for (int i = 0; i < 64; ++i) hist[256 * g + 64 * quarter + i] = 0ull;
         __syncthreads();
         if (tid < 256) w[RowWs::gsum + tid] = 0ull;
