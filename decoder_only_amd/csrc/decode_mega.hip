@@ -145,7 +145,10 @@ __device__ __forceinline__ float dot_chunks(const u32x4* w, const float* x, int 
 // which also count against the LDS wait counter -- every LDS access or lane shuffle would
 // then wait for all weight prefetches in flight.
 #define GLOBAL_AS __attribute__((address_space(1)))
-__device__ __forceinline__ u32x4 ldw16(const bf16* p) { return *(const GLOBAL_AS u32x4*)(p); }
+// Weight chunks: every weight byte of a step is read by exactly one workgroup, once, so
+// they are loaded non-temporally (streaming reads reach ~7 TB/s this way on MI355X against
+// ~6 TB/s with the default cache policy).
+__device__ __forceinline__ u32x4 ldw16(const bf16* p) { return __builtin_nontemporal_load((const GLOBAL_AS u32x4*)(p)); }
 // Lanes 2m and 2m + 1 each hold 4 consecutive elements (lo: elements 8m .. 8m + 3 in lane
 // 2m, hi: 8m + 4 .. 8m + 7 in lane 2m + 1); after pair8 both hold all 8, as (lo, hi).
 __device__ __forceinline__ void pair8(const f32x4 mine, f32x4& lo, f32x4& hi) {
@@ -172,7 +175,7 @@ __device__ __forceinline__ float dot8v(const u32x4 w, const f32x4 lo, const f32x
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 template <bool W8> struct WChunk { typedef u32x4 T; };
 template <> struct WChunk<true> { typedef u32x2 T; };
-__device__ __forceinline__ u32x2 ldw8(const uint8_t* p) { return *(const GLOBAL_AS u32x2*)(p); }
+__device__ __forceinline__ u32x2 ldw8(const uint8_t* p) { return __builtin_nontemporal_load((const GLOBAL_AS u32x2*)(p)); }
 template <bool W8>
 __device__ __forceinline__ typename WChunk<W8>::T ldwc(const void* base, size_t e) {
     if constexpr (W8) return ldw8(static_cast<const uint8_t*>(base) + e);
