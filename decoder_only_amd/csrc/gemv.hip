@@ -15,6 +15,8 @@ namespace {
 
 enum { EPI_LMHEAD = 3 };
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
 __device__ __forceinline__ void load8(const bf16* p, float* w) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -30,6 +32,25 @@ __device__ __forceinline__ void load8(const float* p, float* w) {
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// Weight chunks: read once per call, non-temporally (streaming reads reach ~7 TB/s this
+// way on MI355X against ~6 TB/s with the default cache policy).
+__device__ __forceinline__ void loadw8(const bf16* p, float* w) {
+    const u32x4 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[2 * i] = __uint_as_float(v[i] << 16);
+        w[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ void loadw8(const float* p, float* w) {
+    typedef __attribute__((ext_vector_type(4))) float f4;
+    const f4 a = __builtin_nontemporal_load((const __attribute__((address_space(1))) f4*)(p));
+    const f4 b = __builtin_nontemporal_load((const __attribute__((address_space(1))) f4*)(p + 4));
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
@@ -62,8 +83,8 @@ __global__ __launch_bounds__(256) void k_gemv(const WT* __restrict__ W, const fl
         const WT* w1p = W + (size_t)r1 * K;
         for (int k = lane * 8; k < K; k += 512) {
             float w0[8], w1[8];
-            load8(w0p + k, w0);
-            load8(w1p + k, w1);
+            loadw8(w0p + k, w0);
+            loadw8(w1p + k, w1);
 #pragma unroll
             for (int b = 0; b < BB; ++b) {
                 if (b < nb) {
