@@ -176,11 +176,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
     const float scale = 0.088388346f;                // fl32(128^-0.5)
 
     // V rows for P.V: lane group (wid, quad) takes keys k0 + quad + 4 i, lane col dims 8 col ..
+    // (16 lanes read a whole 256-byte row, once: non-temporal loads)
     u32x4 vr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int key = k0 + quad + 4 * i;
-        vr[i] = key < T ? *reinterpret_cast<const u32x4*>(vc + head_base + (size_t)key * 128 + 8 * col)
+        vr[i] = key < T ? __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(vc + head_base + (size_t)key * 128 + 8 * col))
                         : u32x4{0u, 0u, 0u, 0u};
     }
     // q^T (B operand): lane holds q[head col][32 ks + 8 quad + e] for col < 2, else zeros
