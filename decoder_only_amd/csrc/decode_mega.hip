@@ -584,9 +584,9 @@ __device__ __forceinline__ void kv_stage_db(const MegaParams& p, Smem& sm, const
             const int slot = base + r;
             const size_t row = ((slot >> 8) == pa ? offa : offb) + (size_t)(slot & (kKvPage - 1)) * DH;
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.kc + row + 8 * kslot(r0 + (lane >> 4), sl)),
-                                             (LDS_AS void*)&sm.u.kv.k[128 * half + r0][0], 16, 0, 0);
+                                             (LDS_AS void*)&sm.u.kv.k[128 * half + r0][0], 16, 0, 2);
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(p.vc + row + 8 * sl),
-                                             (LDS_AS void*)&sm.u.kv.v[128 * half + r0][0], 16, 0, 0);
+                                             (LDS_AS void*)&sm.u.kv.v[128 * half + r0][0], 16, 0, 2);
         }
     }
 }
