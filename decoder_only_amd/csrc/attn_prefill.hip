@@ -284,11 +284,22 @@ __global__ __launch_bounds__(256 * HB, 1) void k_attn_prefill(const float* __res
         scores(0, sa);
         using Plain = std::integral_constant<bool, false>;
         using Masked = std::integral_constant<bool, true>;
-        for (int kt = 0; kt < ntiles; kt += 2) {
-            if (kt < kdiag) step(kt, sa, sb, Plain{}); else step(kt, sa, sb, Masked{});
-            if (kt + 1 < ntiles) {
-                if (kt + 1 < kdiag) step(kt + 1, sb, sa, Plain{}); else step(kt + 1, sb, sa, Masked{});
-            }
+        // Pairs of unmasked tiles in a loop without branches (one register assignment for
+        // the two score buffers, no moves between differently compiled copies of a step),
+        // then the rest: at most one unmasked tile (even) and the masked ones.
+        const int nplain = min(kdiag, ntiles);
+        int kt = 0;
+        for (; kt + 2 <= nplain; kt += 2) {
+            step(kt, sa, sb, Plain{});
+            step(kt + 1, sb, sa, Plain{});
+        }
+        if (kt < nplain) {
+            step(kt, sa, sb, Plain{});
+            ++kt;
+        }
+        for (; kt < ntiles; ++kt) {
+            if (kt & 1) step(kt, sb, sa, Masked{});
+            else step(kt, sa, sb, Masked{});
         }
 
         // O^T accumulator: lane holds query row (l16), dims dt*16 + 4*lg + r.
