@@ -218,9 +218,14 @@ __global__ __launch_bounds__(256 * HB, 1) void k_attn_prefill(const float* __res
                     cur[j][r] = v;
                     mx = fmaxf(mx, v);
                 }
-            // the scale is positive, so the max of the scaled scores is the scaled max
-            const float mnew = fmaxf(mrow, row_max4(mx) * scale_log2);
-            const float corr = __builtin_amdgcn_exp2f(mrow - mnew);   // 0 on the first tile
+            // the scale is positive, so the max of the scaled scores is the scaled max. The
+            // row's reference moves only when its max outgrows it by more than 8 (base 2):
+            // the probabilities stay below 2^8 (exact as hi + lo operands, summed in float32)
+            // and the accumulators are rescaled only on those rare tiles; the softmax does not
+            // depend on the reference chosen.
+            const float mcand = fmaxf(mrow, row_max4(mx) * scale_log2);
+            const float mnew = mcand > mrow + 8.0f ? mcand : mrow;
+            const float corr = __builtin_amdgcn_exp2f(mrow - mnew);   // 1 if kept; 0 on the first tile
             mrow = mnew;
             float ps = 0.f;
 #pragma unroll
