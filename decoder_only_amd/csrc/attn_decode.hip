@@ -163,7 +163,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
     float* __restrict__ part) {
     __shared__ float sp[G][CHUNK];     // scores, then probabilities
     __shared__ float hs[G][4];         // per-head wave maxima [0..1] and sums [2..3]
-    __shared__ float wm[16][G][128];   // P.V partials of the 16 lane groups
+    // each wave's 64 K rows (16-byte chunk c of row r at c ^ (r & 15)); after the scores the
+    // same memory holds the P.V partials of the 16 lane groups
+    __shared__ u32x4 sK[4][64 * 16];
+    float (*wm)[G][128] = reinterpret_cast<float (*)[G][128]>(&sK[0][0]);
+    static_assert(sizeof(float) * 16 * G * 128 <= sizeof(u32x4) * 4 * 64 * 16, "P.V partials fit the K rows");
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, quad = lane >> 4, col = lane & 15;
     const int seq = seq_base + b;
@@ -197,22 +201,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode_mfma(
         qh[ks] = __builtin_convertvector(x, bf16x8);
         ql[ks] = __builtin_convertvector(x - __builtin_convertvector(qh[ks], f32x8), bf16x8);
     }
-    // K rows (A operand): tile t row col = key k0 + 16 t + col, dims 32 ks + 8 quad ..
-    u32x4 kr[4][4];
+    // K rows, whole: instruction i brings keys k0 + 4 i + quad, lane col their chunk col (16
+    // lanes read a 256-byte row once: non-temporal loads). Through this wave's LDS rows into
+    // the A-operand layout (tile t row col = key k0 + 16 t + col, dims 32 ks + 8 quad ..);
+    // the wave reads only what it wrote, so no barrier.
+    u32x4 kraw[16];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int key = k0 + 16 * t + col;
+    for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 4 * i + quad;
+        kraw[i] = key < T ? __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(kc + head_base + (size_t)key * 128 + 8 * col))
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            kr[t][ks] = key < T ? *reinterpret_cast<const u32x4*>(kc + head_base + (size_t)key * 128 + 32 * ks + 8 * quad)
-                                : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + quad;
+        sK[wid][r * 16 + (col ^ (r & 15))] = kraw[i];
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 ka[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, kr[t][ks]);
+            const int r = 16 * t + col;
+            ka[ks] = __builtin_bit_cast(bf16x8, sK[wid][r * 16 + ((4 * ks + quad) ^ (r & 15))]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = ka[ks];
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sc, 0, 0, 0);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sc, 0, 0, 0);
         }
