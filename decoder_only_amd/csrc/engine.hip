@@ -891,13 +891,16 @@ static q3_status ensure_prefill_ws(q3_engine* e, int M) {
 }
 
 // Rows tokens[0..M) of sequence `seq` at slots t0 .. t0+M-1 through the matrix-core path.
-// These rows only have to leave their K/V in the cache (the caller runs the last prompt
-// row through the decode path for the logits), so the last layer stops after its K/V
-// append: its attention, O projection and FFN feed nothing. Below kPrefillSplitRows rows
+// Only the last row's logits are wanted (Step 8 takes the last position), so the last
+// layer stops after the K/V append of all rows: its attention, O projection and FFN feed
+// nothing but the last row. With `logits` (bf16 weights) that row then finishes the last
+// layer on the single-row kernels -- attention over the cache, O projection, RMSNorm,
+// SwiGLU FFN, final RMSNorm and the LM head with its argmax -- in float32 activations;
+// without, the caller runs the last prompt row through the decode path. Below kPrefillSplitRows rows
 // the two hidden-width projections (N = 1024) would give too few 128-row tiles to fill the
 // chip; they run split-K instead, and the next RMSNorm adds the partials to the residual
 // in a fixed order.
-static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, int M) {
+static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, int M, float* logits = nullptr) {
     const q3_config& c = e->cfg;
     const int d = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
     hipStream_t s = e->stream;
@@ -922,7 +925,30 @@ static q3_status run_prefill_mfma(q3_engine* e, int seq, const int32_t* tokens, 
         prof_mark(e, Q3_PROF_GEMM, false);
         HIPCHK(e, launch_qk_rope_prefill(e->pf_qkv, M, t0, L.q_norm, L.k_norm, e->inv_freq, c.rms_eps,
                                          e->pf_q, kcs, vcs, lay, seq, Hq, Hkv, s));
-        if (l + 1 == c.n_layers) break;               // the last layer's K/V are written
+        if (l + 1 == c.n_layers) {                    // the last layer's K/V are written
+            if (!logits) break;
+            // row M - 1 alone: its q gathered from the [Hq][M][128] prefill layout, attention
+            // over its t0 + M visible slots (lens[seq] still holds t0), then the rest of the
+            // layer and the LM head on that row of pf_x (complete: the input RMSNorm above
+            // added every pending partial)
+            const int HD = Hq * 128;
+            float* xr = e->pf_x + (size_t)(M - 1) * d;
+            HIPCHK(e, hipMemcpy2DAsync(e->q, 128 * sizeof(float), e->pf_q + (size_t)(M - 1) * 128,
+                                       (size_t)M * 128 * sizeof(float), 128 * sizeof(float), Hq,
+                                       hipMemcpyDeviceToDevice, s));
+            HIPCHK(e, launch_attn_decode(e->q, kcs, vcs, 1, c.max_seq, lay, e->d_len, M, seq, 1, Hq, Hkv, t0 + M,
+                                         e->attn_ws, e->o, 0, s));
+            HIPCHK(e, launch_gemv(L.wo, DT_BF16, e->o, xr, d, HD, 1, GEMV_RESID, s));
+            HIPCHK(e, launch_rmsnorm(xr, L.post_norm, e->h, 0, 1, d, c.rms_eps, s));
+            HIPCHK(e, launch_gemv(L.wgu, DT_BF16, e->h, e->a, 2 * F, d, 1, GEMV_SWIGLU, s));
+            HIPCHK(e, launch_gemv(L.wd, DT_BF16, e->a, xr, d, F, 1, GEMV_RESID, s));
+            HIPCHK(e, launch_rmsnorm(xr, e->final_norm, e->h, 0, 1, d, c.rms_eps, s));
+            HIPCHK(e, launch_fill_u64(e->amax, 0ull, 1, s));
+            HIPCHK(e, launch_lmhead(e->embed, DT_BF16, e->h, logits, e->amax, V, d, 1, e->d_err, s));
+            e->cur_logits = logits;
+            e->cur_rows = 1;
+            break;
+        }
         prof_mark(e, Q3_PROF_ATTN_PREFILL, true, 0, attn_prefill_flops(M, t0, Hq));
         HIPCHK(e, launch_attn_prefill(e->pf_q, kcs, vcs, lay, seq, M, t0, Hq, Hkv, e->pf_o, 1, s));
         prof_mark(e, Q3_PROF_ATTN_PREFILL, false);
@@ -976,7 +1002,13 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
         }
         return Q3_OK;
     }
-    if ((e->cfg.weight_dtype == Q3_BF16 || e->i8()) && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+    if (e->cfg.weight_dtype == Q3_BF16 && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+        // every row on the matrix cores, the last one finishing its last layer and the LM
+        // head on the single-row kernels
+        return run_prefill_mfma(e, seq, tokens, n, logits ? logits : e->logits);
+    }
+    if (e->i8() && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+        // int8 weights (no single-row kernels for them): the last row through the decode path
         if ((st = run_prefill_mfma(e, seq, tokens, n - 1)) != Q3_OK) return st;
         done = n - 1;
     }
