@@ -7,12 +7,12 @@
 // SwiGLU FFN + residual] -> final RMSNorm -> tied LM head -> sampling.
 //
 // Precision plan: decode rows keep float32 activations (bf16 or float32 weights, float32
-// accumulation). Prefill of a long prompt runs all rows but the last through the
-// matrix-core path: float32 activations enter every MFMA product as a bf16 hi + lo pair
-// (two MFMAs; the bf16 weights and the bf16 K/V cache are exact operands), so the path
-// keeps ~16 significant bits where a single bf16 rounding would cost ~5e-3 relative
-// error in the logits. The last row then goes through the float32 decode path, which
-// gives the same result as a full prefill by causality (a row only sees earlier slots).
+// accumulation). Prefill of a long prompt runs its rows through the matrix-core path:
+// float32 activations enter every MFMA product as a bf16 hi + lo pair (two MFMAs; the
+// bf16 weights and the bf16 K/V cache are exact operands), so the path keeps ~16
+// significant bits where a single bf16 rounding would cost ~5e-3 relative error in the
+// logits. The last row's last layer after its K/V append, and its LM head, run on the
+// single-row float32 kernels (with int8 weights the last row takes the decode path).
 #include <algorithm>
 #include <climits>
 #include <cmath>
