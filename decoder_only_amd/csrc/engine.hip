@@ -197,23 +197,25 @@ std::vector<float> to_f32(const q3_tensor& t) {
 
 }  // namespace
 
-// Weight-only int8 rule of one row (q3_quantize_i8): s = fl32(max |w| / 127), q = round half
-// to even of fl32(w / s), clamped to [-127, 127]; an all-zero row gives s = 0, q = 0. Every
-// step is one IEEE float32 operation (no contraction), so any implementation agrees.
-static void quantize_row_i8(const float* w, int64_t n, int8_t* q, float* s) {
+// Weight-only rule of one row (q3_quantize_i8, Q = 127; q3_quantize_i4, Q = 7):
+// s = fl32(max |w| / Q), q = round half to even of fl32(w / s), clamped to [-Q, Q]; an
+// all-zero row gives s = 0, q = 0. Every step is one IEEE float32 operation (no
+// contraction), so any implementation agrees.
+static void quantize_row(const float* w, int64_t n, int qmax, int8_t* q, float* s) {
     float amax = 0.f;
     for (int64_t k = 0; k < n; ++k) amax = std::max(amax, std::fabs(w[k]));
-    const float sc = amax / 127.0f;
+    const float fq = (float)qmax;
+    const float sc = amax / fq;
     *s = sc;
     for (int64_t k = 0; k < n; ++k) {
         float r = sc > 0.f ? std::nearbyint(w[k] / sc) : 0.f;
-        r = std::min(127.f, std::max(-127.f, r));
+        r = std::min(fq, std::max(-fq, r));
         q[k] = (int8_t)r;
     }
 }
 
-extern "C" q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q,
-                                    float* scale) {
+static q3_status quantize_matrix(const void* w, int32_t dtype, int64_t rows, int64_t cols, int qmax, int8_t* q,
+                                 float* scale) {
     if (!w || !q || !scale || rows < 0 || cols <= 0 || (dtype != Q3_F32 && dtype != Q3_BF16)) return Q3_ERR_ARG;
     std::vector<float> row((size_t)cols);
     for (int64_t r = 0; r < rows; ++r) {
@@ -225,9 +227,19 @@ extern "C" q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, 
                 memcpy(&row[k], &bits, 4);
             }
         }
-        quantize_row_i8(row.data(), cols, q + r * cols, scale + r);
+        quantize_row(row.data(), cols, qmax, q + r * cols, scale + r);
     }
     return Q3_OK;
+}
+
+extern "C" q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q,
+                                    float* scale) {
+    return quantize_matrix(w, dtype, rows, cols, 127, q, scale);
+}
+
+extern "C" q3_status q3_quantize_i4(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q,
+                                    float* scale) {
+    return quantize_matrix(w, dtype, rows, cols, 7, q, scale);
 }
 
 static_assert(kMegaMaxSlots == 270336, "the int8 limit quoted below");
@@ -346,7 +358,7 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
                     memcpy(&rowf[k], &bits, 4);
                 }
             }
-            quantize_row_i8(rowf.data(), cols, qrow.data(), &hs[r]);
+            quantize_row(rowf.data(), cols, 127, qrow.data(), &hs[r]);
             for (int k = 0; k < cols; ++k) {
                 const float f = (float)qrow[k];
                 uint32_t b;

@@ -23,7 +23,7 @@ STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -8: "Q3_ERR_NUMERIC"}
 EXPORTS = [
     "q3_load", "q3_prefill", "q3_decode_step", "q3_sample", "q3_reset", "q3_kv_import", "q3_kv_export", "q3_kv_fork",
-    "q3_seq_len", "q3_kv_free_pages", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end", "q3_quantize_i8",
+    "q3_seq_len", "q3_kv_free_pages", "q3_sync", "q3_last_error", "q3_free", "q3_profile_begin", "q3_profile_end", "q3_quantize_i8", "q3_quantize_i4",
     "q3_set_decode_path", "q3_profile_trace",
     "q3_op_rmsnorm", "q3_op_gemv", "q3_op_gemm", "q3_op_qk_norm_rope", "q3_op_attn_decode",
     "q3_op_attn_prefill", "q3_op_sample", "q3_op_sample_noalloc",
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "q3_seq_len": ([vp, i32], i32),
         "q3_kv_free_pages": ([vp], i32),
         "q3_quantize_i8": ([vp, i32, c_int64, c_int64, vp, vp], i32),
+        "q3_quantize_i4": ([vp, i32, c_int64, c_int64, vp, vp], i32),
         "q3_sync": ([vp], i32),
         "q3_last_error": ([vp], c_char_p),
         "q3_free": ([vp], None),

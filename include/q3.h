@@ -141,6 +141,13 @@ q3_status q3_sample(q3_engine* e, const float* logits, int32_t batch, float temp
  * Host code only (no GPU). This is the rule q3_load applies for Q3_I8. Errors: Q3_ERR_ARG. */
 q3_status q3_quantize_i8(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q, float* scale);
 
+/* Weight-only int4 codes, the same rule with 7 in place of 127 (the article's 4-bit
+ * production weights; one scale per row, no group size being given): s = fl32(max_k |w_k| / 7),
+ * q_k = round-half-even(fl32(w_k / s)) clamped to [-7, 7]. q: host int8 [rows, cols], one code
+ * per byte (the engine packs two per byte on the device); scale: host float [rows].
+ * Host code only (no GPU). This is the rule q3_load applies for Q3_I4. Errors: Q3_ERR_ARG. */
+q3_status q3_quantize_i4(const void* w, int32_t dtype, int64_t rows, int64_t cols, int8_t* q, float* scale);
+
 /* Empty sequence slot `seq` (its cache length becomes 0) and return its cache pages to the
  * pool (a page shared with another slot by q3_kv_fork stays with that slot). A slot can be
  * emptied and refilled (q3_prefill) between two decode steps of the others: continuous

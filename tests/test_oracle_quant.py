@@ -1,5 +1,6 @@
-"""Pins of the oracle's weight-only int8 rule (CPU only): per output row, s = max|w|/127
-in float32, q = round-half-even(w / s) clamped to +-127, weights s * q.
+"""Pins of the oracle's weight-only int8 and int4 rules (CPU only): per output row,
+s = max|w|/Q in float32, q = round-half-even(w / s) clamped to +-Q, weights s * q, with
+Q = 127 (int8) or 7 (int4).
 
 * closed form: a row whose largest magnitude is 127 * 2^-10 has s = 2^-10 exactly, so
   every code is w * 2^10 rounded half to even (2.5 -> 2, 3.5 -> 4, -2.5 -> -2, 0.49 -> 0,
@@ -11,7 +12,9 @@ in float32, q = round-half-even(w / s) clamped to +-127, weights s * q.
 * the engine's host quantiser (q3_quantize_i8 in libq3.so, host code only) gives the
   same codes and scales bit for bit, on bf16 and float32 input;
 * the noise floor behind the int8 parity bar: float32-sized noise on the residual stream
-  moves the 28-layer int8 model's logits further than the bf16 model's.
+  moves the 28-layer int8 model's logits further than the bf16 model's;
+* the same pins for Q = 7 (closed form with s = 2^-10, zero row, half-step bound on model
+  rows, q3_quantize_i4 bit for bit) and the int4 model's noise floor.
 """
 import ctypes
 import os
@@ -129,3 +132,92 @@ def test_int8_model_noise_floor():
     print(out)
     assert 3e-4 < out["bf16"] < 1e-3 / 1.4
     assert out["int8"] > 1.4 * out["bf16"] and out["int8"] < 2e-3 / 1.4
+
+
+def test_quantize_i4_closed_form_power_of_two_scale():
+    k = np.array([7, -7, 2.5, 3.5, -2.5, 0.49, 0.51, 0, -4, 6.5, -6.5, 5.5], dtype=np.float64)
+    w = (k * 2.0 ** -10).astype(np.float32)
+    q, s = quant.quantize_rows_i4(w[None, :])
+    assert s[0] == np.float32(2.0 ** -10)
+    assert q.tolist() == [[7, -7, 2, 4, -2, 0, 1, 0, -4, 6, -6, 6]]
+    # the 8-bit rule on the same row has s = 7 * 2^-10 / 127, so the codes differ
+    q8, s8 = quant.quantize_rows_i8(w[None, :])
+    assert s8[0] == np.float32(7 * 2.0 ** -10 / 127) and q8[0, 0] == 127
+
+
+def test_quantize_i4_zero_row_and_bound_on_model_rows():
+    z, sz = quant.quantize_rows_i4(np.zeros((1, 16), np.float32))
+    assert sz[0] == 0 and not z.any()
+    w = synth.workload("toy").with_(weight_dtype="bf16", n_layers=1)
+    ws = synth.make_weights(w)
+    for name in ("model.layers.0.self_attn.k_proj.weight", "model.layers.0.mlp.gate_proj.weight",
+                 "model.embed_tokens.weight"):
+        f = oracle.bf16_bits_to_f32(ws[name])
+        q, s = quant.quantize_rows_i4(f)
+        assert q.min() >= -7 and q.max() <= 7
+        err = np.abs(f.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+        assert (err <= s[:, None].astype(np.float64) * (0.5 + 7.5 * 2.0 ** -24 * 1.01)).all(), name
+        arg = np.argmax(np.abs(f), axis=1)
+        assert (np.abs(q[np.arange(len(q)), arg]) == 7).all(), name
+    qw = quant.quantized_weights(ws, bits=4)
+    for name, a in qw.items():
+        f = oracle.bf16_bits_to_f32(ws[name])
+        if name.endswith("norm.weight"):
+            assert np.array_equal(a, f)
+        else:
+            assert np.abs(a - f).max() <= np.abs(f).max() / 14 * 1.0001
+            assert len(np.unique(a[0])) <= 15                  # at most 15 levels per row
+    with pytest.raises(ValueError):
+        quant.quantized_weights(ws, bits=6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_engine_host_quantizer_i4_matches_oracle_bit_for_bit(dtype):
+    from decoder_only_amd import q3
+    if not os.path.exists(q3.LIB_PATH):
+        pytest.skip("libq3.so not built")
+    L = q3.load_library()
+    rng = np.random.default_rng(11)
+    f = (rng.standard_normal((61, 256)) * rng.choice([0.02, 1.0, 300.0], (61, 1))).astype(np.float32)
+    f[2] = 0.0
+    f[4, :] = np.float32(2.5 * 2.0 ** -10)
+    f[4, 0] = np.float32(7 * 2.0 ** -10)
+    src = synth.f32_to_bf16_bits(f) if dtype == "bf16" else f
+    ref_in = oracle.bf16_bits_to_f32(src) if dtype == "bf16" else f
+    q_ref, s_ref = quant.quantize_rows_i4(ref_in)
+    q = np.empty(f.shape, np.int8)
+    s = np.empty(f.shape[0], np.float32)
+    rc = L.q3_quantize_i4(np.ascontiguousarray(src).ctypes.data, q3.BF16 if dtype == "bf16" else q3.F32,
+                          f.shape[0], f.shape[1], q.ctypes.data, s.ctypes.data)
+    assert rc == 0
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q, q_ref)
+
+
+def test_int4_model_noise_floor():
+    """The same 1e-7 residual noise (six draws) moves the int4-quantised model's logits by
+    at most ~1.9e-3 relative L2 (its draws fall into two clusters, ~6e-4 and ~1.8e-3), more
+    than the bf16 model's ~6e-4: the int4 GPU parity bar is 3e-3, about 1.6x the worst
+    floor, the margin the bf16 bar keeps over its own."""
+    w = synth.workload("bs1_short")
+    weights = synth.make_weights(w)
+    prompt = synth.prompt_tokens(w)
+    model = oracle.Model(oracle.Config.from_workload(w), quant.quantized_weights(weights, bits=4))
+    base = model.forward(prompt, model.new_cache(8), 0)
+    orig = oracle.Model.block
+    vals = []
+    for seed in range(6):
+        rng = np.random.default_rng(seed)
+
+        def noisy(self, x, layer, cache, positions):
+            y = orig(self, x, layer, cache, positions)
+            return (y * (1 + 1e-7 * rng.standard_normal(y.shape))).astype(np.float32)
+
+        oracle.Model.block = noisy
+        try:
+            pert = model.forward(prompt, model.new_cache(8), 0)
+        finally:
+            oracle.Model.block = orig
+        vals.append(float(np.linalg.norm(pert - base) / np.linalg.norm(base)))
+    print(vals)
+    assert max(vals) > 1e-3 and max(vals) < 3e-3 / 1.4
