@@ -41,7 +41,8 @@ struct MegaParams {
     unsigned* err;
     unsigned long long* trace;      // optional phase timestamps [2][trace_n] (NULL: off)
     int trace_n;
-    int w8;                         // 1: every matrix (and the embedding) is int8 codes + row scales
+    int wq;                         // 0: bf16 matrices; 1 (2): every matrix (and the embedding) is int8
+                                    // (int4) codes + row scales
 };
 hipError_t decode_mega_prepare();
 // cooperative: hipLaunchCooperativeKernel (co-residency guaranteed); else an ordinary launch.

@@ -172,18 +172,29 @@ __device__ __forceinline__ float dot8v(const u32x4 w, const f32x4 lo, const f32x
 // the result: measured 2e-3 relative L2 on the 28-layer logits against ~5e-4). The row's
 // scale multiplies the finished row sum. A chunk is 8 codes (8 bytes), at the same columns
 // as a bf16 chunk of 16 bytes.
+// Weight-only int4: codes q in [-7, 7], two per byte (code k of a row in byte k / 2, the
+// low nibble for even k), so a chunk of 8 codes is one 32-bit word, code i in bits
+// 4i .. 4i + 3; each code is sign-extended exactly as the int8 ones, with the row scale
+// applied the same way.
+// WQ: 0 bf16 weights, 1 int8 codes, 2 int4 codes.
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-template <bool W8> struct WChunk { typedef u32x4 T; };
-template <> struct WChunk<true> { typedef u32x2 T; };
+template <int WQ> struct WChunk { typedef u32x4 T; };
+template <> struct WChunk<1> { typedef u32x2 T; };
+template <> struct WChunk<2> { typedef unsigned T; };
 __device__ __forceinline__ u32x2 ldw8(const uint8_t* p) { return __builtin_nontemporal_load((const GLOBAL_AS u32x2*)(p)); }
-template <bool W8>
-__device__ __forceinline__ typename WChunk<W8>::T ldwc(const void* base, size_t e) {
-    if constexpr (W8) return ldw8(static_cast<const uint8_t*>(base) + e);
+__device__ __forceinline__ unsigned ldw4(const uint8_t* p) { return __builtin_nontemporal_load((const GLOBAL_AS unsigned*)(p)); }
+// the chunk of the 8 weights at element e (a multiple of 8) of the matrix
+template <int WQ>
+__device__ __forceinline__ typename WChunk<WQ>::T ldwc(const void* base, size_t e) {
+    if constexpr (WQ == 1) return ldw8(static_cast<const uint8_t*>(base) + e);
+    else if constexpr (WQ == 2) return ldw4(static_cast<const uint8_t*>(base) + e / 2);
     else return ldw16(static_cast<const bf16*>(base) + e);
 }
-// int8 matrix buffer: codes [rows][cols] (n_codes bytes), then the rows' float32 scales
+// quantised matrix buffer: the codes of its n_codes weights (n_codes bytes for int8,
+// n_codes / 2 for int4), then the rows' float32 scales
+template <int WQ>
 __device__ __forceinline__ const float* row_scales(const void* m, size_t n_codes) {
-    return reinterpret_cast<const float*>(static_cast<const uint8_t*>(m) + n_codes);
+    return reinterpret_cast<const float*>(static_cast<const uint8_t*>(m) + (WQ == 2 ? n_codes / 2 : n_codes));
 }
 __device__ __forceinline__ float sb(unsigned w, int k) { return (float)((int)(w << (24 - 8 * k)) >> 24); }
 // 8 codes dotted with (lo, hi)
@@ -195,6 +206,32 @@ __device__ __forceinline__ float dot8v(const u32x2 w, const f32x4 lo, const f32x
 // dot_chunks: every shared-memory read first, one accumulator per chunk
 template <int N>
 __device__ __forceinline__ float dot_chunks(const u32x2* w, const float* x, int first, int step) {
+    f32x4 a[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(x + (first + step * i) * 8);
+        a[2 * i] = src[0];
+        a[2 * i + 1] = src[1];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * N, 0);
+    float part[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) part[i] = dot8v(w[i], a[2 * i], a[2 * i + 1]);
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+        for (int i = 0; i + h < N; i += 2 * h) part[i] += part[i + h];
+    return part[0];
+}
+
+__device__ __forceinline__ float sn(unsigned w, int k) { return (float)((int)(w << (28 - 4 * k)) >> 28); }
+// 8 int4 codes dotted with (lo, hi)
+__device__ __forceinline__ float dot8v(const unsigned w, const f32x4 lo, const f32x4 hi) {
+    return ((sn(w, 0) * lo[0] + sn(w, 1) * lo[1]) + (sn(w, 2) * lo[2] + sn(w, 3) * lo[3])) +
+           ((sn(w, 4) * hi[0] + sn(w, 5) * hi[1]) + (sn(w, 6) * hi[2] + sn(w, 7) * hi[3]));
+}
+template <int N>
+__device__ __forceinline__ float dot_chunks(const unsigned* w, const float* x, int first, int step) {
     f32x4 a[2 * N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -893,7 +930,7 @@ __device__ __forceinline__ void oproj_partial(Smem& sm, const WT* pf, float* P, 
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<4>(pf, sm.o[b], sub, 8);
         s = sum8(s);
-        if constexpr (sizeof(WT) == 8) s *= sc;   // int8 row scale
+        if constexpr (sizeof(WT) < 16) s *= sc;   // quantised weights: row scale
         if (g == 0) s = sm.xg[b][r] + s;
         if (sub == 0) fx_add(reinterpret_cast<u64*>(P + (size_t)b * W_P) + 32 * j + r, s);
     }
@@ -908,19 +945,19 @@ __device__ __forceinline__ void down_partial(Smem& sm, const WT* pf, float* Xn, 
     for (int b = 0; b < B; ++b) {
         float s = dot_chunks<6>(pf, sm.u.s.act[b], sub, 8);
         s = sum8(s);
-        if constexpr (sizeof(WT) == 8) s *= sc;   // int8 row scale
+        if constexpr (sizeof(WT) < 16) s *= sc;   // quantised weights: row scale
         if (g == 0) s = sm.xr[b][r] + s;
         if (sub == 0) fx_add(reinterpret_cast<u64*>(Xn + (size_t)b * W_X) + 32 * j + r, s);
     }
 }
 
-template <bool W8>
-__device__ __forceinline__ void pf_oproj(const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre, int g, int j) {
+template <int WQ>
+__device__ __forceinline__ void pf_oproj(const MegaLayer& L, typename WChunk<WQ>::T* pf, Pre& pre, int g, int j) {
     const int r = threadIdx.x >> 3, sub = threadIdx.x & 7;
     const size_t base = (size_t)(32 * j + r) * (HQ * DH) + 256 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = ldwc<W8>(L.wo, base + (sub + 8 * i) * 8);
-    if constexpr (W8) pre.so = ldf(row_scales(L.wo, (size_t)D * HQ * DH) + 32 * j + r);
+    for (int i = 0; i < 4; ++i) pf[i] = ldwc<WQ>(L.wo, base + (sub + 8 * i) * 8);
+    if constexpr (WQ) pre.so = ldf(row_scales<WQ>(L.wo, (size_t)D * HQ * DH) + 32 * j + r);
 }
 
 // Rows of phase C: rr < 12 the gate rows of the workgroup's 12 SwiGLU columns, then their
@@ -942,14 +979,14 @@ __device__ __forceinline__ int qkv_row0(int w) {
 // Phases A, C, D: thread t polls 4 consecutive columns; with its pair lane t ^ 1 it holds
 // the 8 columns 8 (t >> 1) .. + 7 (pair8), and it owns half of the phase's rows
 // (by t & 1) at those columns: one 16-byte chunk per row.
-template <bool W8>
-__device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre,
+template <int WQ>
+__device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, typename WChunk<WQ>::T* pf, Pre& pre,
                                        int w) {
     const size_t base = (size_t)(qkv_row0(w) + 8 * (threadIdx.x & 1)) * D + 8 * (threadIdx.x >> 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        pf[i] = ldwc<W8>(L.wqkv, base + (size_t)i * D);
-    if constexpr (W8) pre.sa = ldf(row_scales(L.wqkv, (size_t)NQKV * D) + qkv_row0(w) + (threadIdx.x >> 4));
+        pf[i] = ldwc<WQ>(L.wqkv, base + (size_t)i * D);
+    if constexpr (WQ) pre.sa = ldf(row_scales<WQ>(L.wqkv, (size_t)NQKV * D) + qkv_row0(w) + (threadIdx.x >> 4));
     pre.nw = ldf4(L.in_norm + 4 * threadIdx.x);
     const int i = threadIdx.x & 63;
     const float* qk = (threadIdx.x >> 6) < 2 ? L.q_norm : L.k_norm;
@@ -958,23 +995,23 @@ __device__ __forceinline__ void pf_qkv(const MegaParams& p, const MegaLayer& L, 
 }
 // gate/up rows i < 12 of the thread into pf[4 + i], in two parts: rows i0 <= i < i1
 // (int8: the second part also loads the scale of the row this thread finishes in phase C)
-template <bool W8, int I0, int I1>
-__device__ __forceinline__ void pf_gu(const void* wgu, typename WChunk<W8>::T* pf, Pre& pre, int w) {
+template <int WQ, int I0, int I1>
+__device__ __forceinline__ void pf_gu(const void* wgu, typename WChunk<WQ>::T* pf, Pre& pre, int w) {
     const size_t base = 8 * (threadIdx.x >> 1);
     const int r0 = 12 * (threadIdx.x & 1);
 #pragma unroll
-    for (int i = I0; i < I1; ++i) pf[4 + i] = ldwc<W8>(wgu, base + (size_t)gu_row(w, r0 + i) * D);
-    if constexpr (W8 && I1 == 12) {
-        if (threadIdx.x < 192) pre.sg = ldf(row_scales(wgu, (size_t)2 * F * D) + gu_row(w, threadIdx.x >> 3));
+    for (int i = I0; i < I1; ++i) pf[4 + i] = ldwc<WQ>(wgu, base + (size_t)gu_row(w, r0 + i) * D);
+    if constexpr (WQ && I1 == 12) {
+        if (threadIdx.x < 192) pre.sg = ldf(row_scales<WQ>(wgu, (size_t)2 * F * D) + gu_row(w, threadIdx.x >> 3));
     }
 }
 // pf[i] = row 32j + (t >> 3) of Wd at columns DCOLS g + 8 ((t & 7) + 8 i) .. + 7 (i < 6)
-template <bool W8>
-__device__ __forceinline__ void pf_down(const MegaLayer& L, typename WChunk<W8>::T* pf, Pre& pre, int g, int j) {
+template <int WQ>
+__device__ __forceinline__ void pf_down(const MegaLayer& L, typename WChunk<WQ>::T* pf, Pre& pre, int g, int j) {
     const size_t base = (size_t)(32 * j + (threadIdx.x >> 3)) * F + DCOLS * g + 8 * (threadIdx.x & 7);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pf[i] = ldwc<W8>(L.wd, base + 64 * i);
-    if constexpr (W8) pre.sd = ldf(row_scales(L.wd, (size_t)D * F) + 32 * j + (threadIdx.x >> 3));
+    for (int i = 0; i < 6; ++i) pf[i] = ldwc<WQ>(L.wd, base + 64 * i);
+    if constexpr (WQ) pre.sd = ldf(row_scales<WQ>(L.wd, (size_t)D * F) + 32 * j + (threadIdx.x >> 3));
 }
 
 static_assert(MAXCH == 32, "kMegaMaxSlots assumes 32 chunks");
@@ -996,7 +1033,7 @@ __device__ __forceinline__ size_t group_chunk(int gg, int i) {
 // the whole range); 1: split-K attention over chunks; 2: the same with the chunk rows staged
 // in double-buffered halves (contexts above LONG_T). Separate instances, so the code and
 // registers of one path do not touch the others.
-template <int MODE, bool CAUSAL, bool W8>
+template <int MODE, bool CAUSAL, int WQ>
 __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     constexpr bool LONG = MODE == 2;
     static_assert(!CAUSAL || MODE == 0, "causal rows run in the short-context instance only");
@@ -1004,7 +1041,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int B = p.B;
-    typedef typename WChunk<W8>::T WT;   // one weight chunk: 8 bf16, or 8 int8 codes
+    typedef typename WChunk<WQ>::T WT;   // one weight chunk: 8 bf16, 8 int8 codes or 8 int4 codes
     WT pf[16];
     Pre pre;
     // kv group and row block: the 32 workgroups of group g are those with w % 8 == g, which
@@ -1052,7 +1089,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         sm.rs[b][i] = (float)sd;
     }
     __syncthreads();
-    pf_qkv<W8>(p, sm.layers[0], pf, pre, w);
+    pf_qkv<WQ>(p, sm.layers[0], pf, pre, w);
     int tslot = 0;
     trace_at(p, sm, tslot++);
 
@@ -1074,11 +1111,16 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             f32x4 v;                      // this thread's elements 4 tid .. 4 tid + 3 of x
             if (layer == 0) {
                 const int t = clamp_tok(p, b);
-                if constexpr (W8) {     // row t of the embedding: codes times the row's scale
+                if constexpr (WQ == 1) {     // row t of the embedding: codes times the row's scale
                     const uint8_t* e8p = reinterpret_cast<const uint8_t*>(p.embed);
                     const unsigned e8 = *(const GLOBAL_AS unsigned*)(e8p + (size_t)t * D + 4 * tid);
-                    const float es = ldf(row_scales(p.embed, (size_t)p.vocab * D) + t);
+                    const float es = ldf(row_scales<WQ>(p.embed, (size_t)p.vocab * D) + t);
                     v = f32x4{sb(e8, 0) * es, sb(e8, 1) * es, sb(e8, 2) * es, sb(e8, 3) * es};
+                } else if constexpr (WQ == 2) {   // (int4: the 4 codes in 2 bytes)
+                    const uint8_t* e4p = reinterpret_cast<const uint8_t*>(p.embed);
+                    const unsigned e4 = *(const GLOBAL_AS unsigned short*)(e4p + ((size_t)t * D + 4 * tid) / 2);
+                    const float es = ldf(row_scales<WQ>(p.embed, (size_t)p.vocab * D) + t);
+                    v = f32x4{sn(e4, 0) * es, sn(e4, 1) * es, sn(e4, 2) * es, sn(e4, 3) * es};
                 } else {
                     const unsigned* e = reinterpret_cast<const unsigned*>(p.embed + (size_t)t * D + 4 * tid);
                     const unsigned e0 = *(const GLOBAL_AS unsigned*)e, e1 = *(const GLOBAL_AS unsigned*)(e + 1);
@@ -1109,11 +1151,11 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 const f32x4 q0 = src[sub], q1 = src[sub + 16];
                 float s = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
                 s = sum16(s) * norm_scale(p, sm, b);
-                if constexpr (W8) s *= pre.sa;
+                if constexpr (WQ) s *= pre.sa;
                 if (sub == 0) put_xcd(QKV + (size_t)b * W_QKV + qkv_row0(w) + r, s);
             }
         }
-        pf_oproj<W8>(L, pf, pre, g, j);
+        pf_oproj<WQ>(L, pf, pre, g, j);
         trace_at(p, sm, tslot++);
 
         // ---------------- B: attention of kv group g and its O-projection partial
@@ -1129,7 +1171,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 if (!poll<1>(QKV + (size_t)b * W_QKV, W_QKV, [&](int i) { return group_chunk(g, i); }, DH, sm.in[b], p.err))
                     return;
                 __builtin_amdgcn_s_waitcnt(0);                  // staged rows landed (barrier below)
-                if (b == 0) pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
+                if (b == 0) pf_gu<WQ, 0, 4>(L.wgu, pf, pre, w);
                 if (b == 0) trace_at(p, sm, tslot++);
                 group_prep<CAUSAL>(p, sm, pre, layer, b, g, slot, j == 0);
                 if (b == 0) trace_at(p, sm, tslot++);
@@ -1151,7 +1193,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                                  p.err))
                         return;
                     __builtin_amdgcn_s_waitcnt(0);
-                    if (b == 0) pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
+                    if (b == 0) pf_gu<WQ, 0, 4>(L.wgu, pf, pre, w);
                     if (b == 0) trace_at(p, sm, tslot++);
                     group_prep<false>(p, sm, pre, layer, b, gg, slot, k1 == T);
                     if (b == 0) trace_at(p, sm, tslot++);
@@ -1160,7 +1202,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                     for (int e = tid; e < 2 * PART; e += NT) put_xcd(pt + e, sm.att[e / PART][e % PART]);
                     __syncthreads();
                 } else if (b == 0) {
-                    pf_gu<W8, 0, 4>(L.wgu, pf, pre, w);
+                    pf_gu<WQ, 0, 4>(L.wgu, pf, pre, w);
                     trace_at(p, sm, tslot++);
                     trace_at(p, sm, tslot++);
                 }
@@ -1220,7 +1262,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
             const bf16* wgu = uniform_ptr(L.wgu);
             const float* pnorm = uniform_ptr(L.post_norm);
             oproj_partial(sm, pf, P, g, j, B, pre.so);
-            pf_gu<W8, 4, 12>(wgu, pf, pre, w);
+            pf_gu<WQ, 4, 12>(wgu, pf, pre, w);
             pre.nw = ldf4(pnorm + 4 * tid);
         }
         trace_at(p, sm, tslot++);
@@ -1257,7 +1299,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) s += (q[i][0] + q[i][1]) + (q[i][2] + q[i][3]);
                     s = sum8(s);
-                    if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b) * (W8 ? pre.sg : 1.0f);
+                    if (sub == 0) sm.gu[rr][b] = s * norm_scale(p, sm, b) * (WQ ? pre.sg : 1.0f);
                 }
             }
             __syncthreads();
@@ -1267,7 +1309,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 put_xcd(A + (size_t)b * W_A + gu_col0(w) + c, gt / (1.0f + expf(-gt)) * up);
             }
         }
-        pf_down<W8>(L, pf, pre, g, j);
+        pf_down<WQ>(L, pf, pre, g, j);
         trace_at(p, sm, tslot++);
 
         // ---------------- D: rows 32j..32j+31 of Wd[:, DCOLS g : DCOLS (g + 1)] . a (plus x' for
@@ -1292,7 +1334,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         }
         trace_at(p, sm, tslot++);
         down_partial(sm, pf, Xn, g, j, B, pre.sd);
-        if (layer + 1 < p.n_layers) pf_qkv<W8>(p, sm.layers[layer + 1], pf, pre, w);
+        if (layer + 1 < p.n_layers) pf_qkv<WQ>(p, sm.layers[layer + 1], pf, pre, w);
         else pre.nw = ldf4(p.final_norm + 4 * tid);
         trace_at(p, sm, tslot++);
         __syncthreads();
@@ -1313,8 +1355,8 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
         const int row = base + rsub;
         if (row < r1) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = ldwc<W8>(p.embed, (size_t)row * D + (sub + 16 * i) * 8);
-            if constexpr (W8) sc = ldf(row_scales(p.embed, (size_t)p.vocab * D) + row);
+            for (int i = 0; i < 8; ++i) dst[i] = ldwc<WQ>(p.embed, (size_t)row * D + (sub + 16 * i) * 8);
+            if constexpr (WQ) sc = ldf(row_scales<WQ>(p.embed, (size_t)p.vocab * D) + row);
         }
     };
     load_rows(r0, b0, s0);                         // in flight while the last layer finishes
@@ -1345,7 +1387,7 @@ __global__ __launch_bounds__(NT, 1) void k_decode_mega(MegaParams p) {
                 float s = 0.f;
                 if (row < r1) s = dot_chunks<8>(wv, sm.u.s.act[b], sub, 16);
                 s = sum16(s) * rn[b];
-                if constexpr (W8) s *= sc;
+                if constexpr (WQ) s *= sc;
                 if (row < r1 && sub == 0) {
                     p.logits[(size_t)(b - hf) * p.vocab + row] = s;
                     bad |= !isfinite(s);
@@ -1488,16 +1530,18 @@ hipError_t launch_mega_fill(float* ex, size_t words, hipStream_t s) {
     return hipGetLastError();
 }
 
-// [bf16 / int8 weights][short, split-K, split-K double-buffered, short with causal rows]
-static const void* const kInstances[2][4] = {
-    {(const void*)k_decode_mega<0, false, false>, (const void*)k_decode_mega<1, false, false>,
-     (const void*)k_decode_mega<2, false, false>, (const void*)k_decode_mega<0, true, false>},
-    {(const void*)k_decode_mega<0, false, true>, (const void*)k_decode_mega<1, false, true>,
-     (const void*)k_decode_mega<2, false, true>, (const void*)k_decode_mega<0, true, true>}};
+// [bf16 / int8 / int4 weights][short, split-K, split-K double-buffered, short with causal rows]
+static const void* const kInstances[3][4] = {
+    {(const void*)k_decode_mega<0, false, 0>, (const void*)k_decode_mega<1, false, 0>,
+     (const void*)k_decode_mega<2, false, 0>, (const void*)k_decode_mega<0, true, 0>},
+    {(const void*)k_decode_mega<0, false, 1>, (const void*)k_decode_mega<1, false, 1>,
+     (const void*)k_decode_mega<2, false, 1>, (const void*)k_decode_mega<0, true, 1>},
+    {(const void*)k_decode_mega<0, false, 2>, (const void*)k_decode_mega<1, false, 2>,
+     (const void*)k_decode_mega<2, false, 2>, (const void*)k_decode_mega<0, true, 2>}};
 
 hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t s) {
     if (p.B < 1 || p.B > BMAX || p.n_layers < 1 || p.n_layers > kMegaMaxLayers || p.head_first < 0 ||
-        p.head_first > p.B)
+        p.head_first > p.B || p.wq < 0 || p.wq > 2)
         return hipErrorInvalidValue;
     int Tmax = 0;
     for (int b = 0; b < p.B; ++b) Tmax = std::max(Tmax, p.slots[b] + 1);
@@ -1508,7 +1552,7 @@ hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t
     }
     if (!p.causal && p.head_first != 0) return hipErrorInvalidValue;
     const int mode = p.causal ? 3 : Tmax <= SHORT_T ? 0 : Tmax <= LONG_T ? 1 : 2;
-    const void* fn = kInstances[p.w8 ? 1 : 0][mode];
+    const void* fn = kInstances[p.wq][mode];
     if (cooperative) {
         void* args[] = {(void*)&p};
         return hipLaunchCooperativeKernel(fn, dim3(NWG), dim3(NT), args, sizeof(Smem), s);
@@ -1518,8 +1562,8 @@ hipError_t launch_decode_mega(const MegaParams& p, bool cooperative, hipStream_t
 }
 
 hipError_t decode_mega_prepare() {
-    for (int w8 = 0; w8 < 2; ++w8) {
-        for (const void* fn : kInstances[w8]) {
+    for (int wq = 0; wq < 3; ++wq) {
+        for (const void* fn : kInstances[wq]) {
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
             if (e != hipSuccess) return e;
         }

@@ -119,8 +119,13 @@ struct q3_engine {
           *pf_a = nullptr;
 
     bool i8() const { return cfg.weight_dtype == Q3_I8; }
-    // bytes per weight a decode step streams (int8: the codes; their row scales are counted apart)
-    size_t wbytes() const { return cfg.weight_dtype == Q3_F32 ? 4 : (cfg.weight_dtype == Q3_BF16 ? 2 : 1); }
+    bool i4() const { return cfg.weight_dtype == Q3_I4; }
+    bool quant() const { return i8() || i4(); }   // weight-only int8 or int4
+    // bytes per weight a decode step streams (int8 / int4: the codes; their row scales are
+    // counted apart)
+    double wbytes() const {
+        return cfg.weight_dtype == Q3_F32 ? 4.0 : cfg.weight_dtype == Q3_BF16 ? 2.0 : cfg.weight_dtype == Q3_I8 ? 1.0 : 0.5;
+    }
     size_t kvbytes() const { return cfg.kv_dtype == Q3_BF16 ? 2 : 4; }
     int qkv_rows() const { return (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim; }
 
@@ -252,14 +257,15 @@ static q3_status validate_config(const q3_config* c, std::string& why) {
     if (c->hidden % 128 || c->ffn % 128 || (c->n_heads * 128) % 128) { why = "hidden and ffn must be multiples of 128"; return Q3_ERR_ARG; }
     if (c->vocab % 2) { why = "vocab must be even"; return Q3_ERR_ARG; }
     if (c->tie_embeddings != 1) { why = "only a tied LM head is supported"; return Q3_ERR_ARG; }
-    if ((c->weight_dtype != Q3_F32 && c->weight_dtype != Q3_BF16 && c->weight_dtype != Q3_I8) ||
+    if ((c->weight_dtype != Q3_F32 && c->weight_dtype != Q3_BF16 && c->weight_dtype != Q3_I8 &&
+         c->weight_dtype != Q3_I4) ||
         (c->kv_dtype != Q3_F32 && c->kv_dtype != Q3_BF16)) { why = "bad dtype"; return Q3_ERR_ARG; }
-    if (c->weight_dtype == Q3_I8 && (c->kv_dtype != Q3_BF16 || c->hidden != 1024 || c->n_heads != 16 ||
+    if ((c->weight_dtype == Q3_I8 || c->weight_dtype == Q3_I4) && (c->kv_dtype != Q3_BF16 || c->hidden != 1024 || c->n_heads != 16 ||
                                      c->n_kv_heads != 8 || c->ffn != 3072 || c->n_layers < 1 ||
                                      c->n_layers > kMegaMaxLayers || c->max_batch > kMegaMaxRows ||
                                      c->max_seq > kMegaMaxSlots)) {
-        why = "int8 weights need the Qwen3-0.6B layer shape, a bf16 cache, at most 4 sequence slots and "
-              "max_seq <= 270336";
+        why = "int8 and int4 weights need the Qwen3-0.6B layer shape, a bf16 cache, at most 4 sequence slots "
+              "and max_seq <= 270336";
         return Q3_ERR_ARG;
     }
     if (c->kv_pages < 0) { why = "kv_pages must be >= 0"; return Q3_ERR_ARG; }
@@ -286,7 +292,8 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         byname[weights[i].name] = &weights[i];
     }
     const int d = c.hidden, dh = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.ffn, V = c.vocab;
-    const bool i8 = c.weight_dtype == Q3_I8;
+    const bool i8 = c.weight_dtype == Q3_I8 || c.weight_dtype == Q3_I4;   // quantised weights
+    const bool i4 = c.weight_dtype == Q3_I4;
     const size_t wb = c.weight_dtype == Q3_F32 ? 4 : 2;   // bytes per element of L.wqkv etc.
 
     auto need = [&](const std::string& name, int64_t numel, bool norm, const q3_tensor** t) -> q3_status {
@@ -337,14 +344,17 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         return (float*)upload(f.data(), f.size() * 4);
     };
 
-    // int8 weights: each matrix, its rows in the engine's packed order, quantised row by row;
-    // uploaded as the codes (the persistent decode kernel), as the codes in bf16 (exact:
-    // |q| <= 127; the prefill GEMMs, which apply the scale per output column) and the scales
+    // int8 / int4 weights: each matrix, its rows in the engine's packed order, quantised row
+    // by row; uploaded as the codes (the persistent decode kernel: one byte each, or two
+    // int4 codes per byte, code k in byte k / 2, the low nibble for even k), as the codes in
+    // bf16 (exact: |q| <= 127; the prefill GEMMs, which apply the scale per output column)
+    // and the scales
     auto quant_upload = [&](const std::vector<std::pair<const q3_tensor*, int64_t>>& rows, int cols, void** bf16q,
                             uint8_t** u8, float** sc) -> bool {
         const size_t R = rows.size();
+        const size_t cbytes = i4 ? R * cols / 2 : R * cols;   // (cols is even)
         std::vector<uint16_t> hq(R * cols);
-        std::vector<uint8_t> hu(R * cols);
+        std::vector<uint8_t> hu(cbytes, 0);
         std::vector<float> hs(R), rowf(cols);
         std::vector<int8_t> qrow(cols);
         for (size_t r = 0; r < R; ++r) {
@@ -358,21 +368,26 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
                     memcpy(&rowf[k], &bits, 4);
                 }
             }
-            quantize_row(rowf.data(), cols, 127, qrow.data(), &hs[r]);
+            quantize_row(rowf.data(), cols, i4 ? 7 : 127, qrow.data(), &hs[r]);
             for (int k = 0; k < cols; ++k) {
                 const float f = (float)qrow[k];
                 uint32_t b;
                 memcpy(&b, &f, 4);
                 hq[r * cols + k] = (uint16_t)(b >> 16);
-                hu[r * cols + k] = (uint8_t)qrow[k];
+                if (i4) {
+                    const size_t at = r * cols + k;
+                    hu[at / 2] |= (uint8_t)(((unsigned)qrow[k] & 0xFu) << (4 * (at & 1)));
+                } else {
+                    hu[r * cols + k] = (uint8_t)qrow[k];
+                }
             }
         }
         // the persistent kernel's buffer: the codes, then the scales (it finds them at a fixed offset)
-        hu.resize(R * cols + 4 * R);
-        memcpy(hu.data() + R * cols, hs.data(), 4 * R);
+        hu.resize(cbytes + 4 * R);
+        memcpy(hu.data() + cbytes, hs.data(), 4 * R);
         if (!(*bf16q = upload(hq.data(), hq.size() * 2)) || !(*u8 = (uint8_t*)upload(hu.data(), hu.size())))
             return false;
-        *sc = (float*)(*u8 + R * cols);
+        *sc = (float*)(*u8 + cbytes);
         return true;
     };
     auto rows_of = [&](std::vector<std::pair<const q3_tensor*, int64_t>>& v, const std::string& name, int64_t r0,
@@ -496,13 +511,13 @@ extern "C" q3_status q3_load(const q3_config* cfg, const q3_tensor* weights, int
         (void)occ;
         if (i8 && !e->mega_ok) {
             q3_free(e);
-            return Q3_ERR_HIP;     // int8 decode runs only in the persistent kernel (a 256-CU GPU)
+            return Q3_ERR_HIP;     // int8 / int4 decode runs only in the persistent kernel (a 256-CU GPU)
         }
         if (e->mega_ok) {
             std::vector<MegaLayer> hl(c.n_layers);
             for (int l = 0; l < c.n_layers; ++l) {
                 const auto& L = e->layers[l];
-                // (int8: the matrix buffers of codes + scales)
+                // (int8 / int4: the matrix buffers of codes + scales)
                 hl[l] = i8 ? MegaLayer{(const uint16_t*)L.wqkv8, (const uint16_t*)L.wo8, (const uint16_t*)L.wgu8,
                                        (const uint16_t*)L.wd8, L.in_norm, L.post_norm, L.q_norm, L.k_norm}
                            : MegaLayer{(const uint16_t*)L.wqkv, (const uint16_t*)L.wo, (const uint16_t*)L.wgu,
@@ -560,11 +575,11 @@ static double kv_read_bytes(const q3_engine* e, int seq_base, int B) {
 // as the LM head), norm weights, K/V reads and writes, embedding rows and logits.
 static double step_bytes(const q3_engine* e, int seq_base, int B) {
     const q3_config& c = e->cfg;
-    const double wb = (double)e->wbytes();
+    const double wb = e->wbytes();
     const double per_layer = (double)e->qkv_rows() * c.hidden + (double)c.hidden * c.n_heads * c.head_dim +
                              3.0 * c.ffn * c.hidden;
     double weights = wb * (per_layer * c.n_layers + (double)c.vocab * c.hidden);
-    if (e->i8())                // the row scales (float32) of every matrix
+    if (e->quant())             // the row scales (float32) of every matrix
         weights += 4.0 * ((double)(e->qkv_rows() + c.hidden + 2 * c.ffn + c.hidden) * c.n_layers + c.vocab);
     const double norms = 4.0 * (c.n_layers * (2.0 * c.hidden + 2.0 * c.head_dim) + c.hidden);
     const double kv_write = (double)B * c.n_layers * 2.0 * c.n_kv_heads * c.head_dim * e->kvbytes();
@@ -682,8 +697,8 @@ static MegaParams mega_params(const q3_engine* e, const int32_t* tokens, const i
     mp.head_first = 0;
     mp.eps = c.rms_eps;
     mp.layers = e->d_layers;
-    mp.embed = e->i8() ? (const uint16_t*)e->embed8 : (const uint16_t*)e->embed;
-    mp.w8 = e->i8() ? 1 : 0;
+    mp.embed = e->quant() ? (const uint16_t*)e->embed8 : (const uint16_t*)e->embed;
+    mp.wq = e->i8() ? 1 : e->i4() ? 2 : 0;
     mp.final_norm = e->final_norm;
     mp.inv_freq = e->inv_freq;
     mp.kc = (uint16_t*)e->kc;
@@ -740,13 +755,13 @@ static q3_status run_decode(q3_engine* e, const int32_t* tokens, const int32_t* 
     hipStream_t s = e->stream;
     int maxT = 0;
     for (int b = 0; b < B; ++b) maxT = std::max(maxT, e->h_len[seq_base + b] + 1);
-    const double wb = (double)e->wbytes();
+    const double wb = e->wbytes();
     // the persistent kernel always computes the logits (into the engine's buffer when the
     // caller does not want them)
     const bool use_mega = e->mega_ok && B <= kMegaMaxRows && maxT <= kMegaMaxSlots && e->decode_path != 1;
     if (!use_mega && e->decode_path == 2) return e->fail(Q3_ERR_STATE, "persistent decode kernel not usable here");
-    if (!use_mega && e->i8())
-        return e->fail(Q3_ERR_STATE, "int8 weights: decode runs only in the persistent kernel (at most 4 rows)");
+    if (!use_mega && e->quant())
+        return e->fail(Q3_ERR_STATE, "int8 / int4 weights: decode runs only in the persistent kernel (at most 4 rows)");
     if (use_mega) {
         float* lg = logits_out ? logits_out : e->logits;
         MegaParams mp = mega_params(e, tokens, positions, seq_base, B, lg);
@@ -1019,8 +1034,8 @@ extern "C" q3_status q3_prefill(q3_engine* e, int32_t seq, const int32_t* tokens
         // head on the single-row kernels
         return run_prefill_mfma(e, seq, tokens, n, logits ? logits : e->logits);
     }
-    if (e->i8() && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
-        // int8 weights (no single-row kernels for them): the last row through the decode path
+    if (e->quant() && e->cfg.kv_dtype == Q3_BF16 && n >= kPrefillMfmaMin) {
+        // int8 / int4 weights (no single-row kernels for them): the last row through the decode path
         if ((st = run_prefill_mfma(e, seq, tokens, n - 1)) != Q3_OK) return st;
         done = n - 1;
     }
@@ -1202,7 +1217,7 @@ extern "C" q3_status q3_set_decode_path(q3_engine* e, int32_t path) {
     if (!e) return Q3_ERR_ARG;
     if (path < 0 || path > 3) return e->fail(Q3_ERR_ARG, "decode path must be 0, 1, 2 or 3");
     if (path == 2 && !e->mega_ok) return e->fail(Q3_ERR_STATE, "persistent decode kernel not available for this model/GPU");
-    if (path == 1 && e->i8()) return e->fail(Q3_ERR_STATE, "int8 weights: no per-operation decode path");
+    if (path == 1 && e->quant()) return e->fail(Q3_ERR_STATE, "int8 / int4 weights: no per-operation decode path");
     e->decode_path = path;
     return Q3_OK;
 }

@@ -16,7 +16,7 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq3.so")
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, I4 = 0, 1, 2, 3
 OP_PAIR = 2     # single operations: bf16 pair rows (n hi parts, then n lo parts)
 STATUS = {0: "Q3_OK", -1: "Q3_ERR_ARG", -2: "Q3_ERR_SHAPE", -3: "Q3_ERR_TOKEN",
           -4: "Q3_ERR_CAPACITY", -5: "Q3_ERR_OOM", -6: "Q3_ERR_HIP", -7: "Q3_ERR_STATE",
@@ -127,14 +127,17 @@ def _check(code: int, what: str = "", eng=None) -> None:
         raise Q3Error(code, msg)
 
 
-def config(w, max_batch: int, max_seq: int, int8: bool = False, kv_pages: int = 0) -> Q3Config:
-    """q3_config of a model description with the synth.Workload fields; int8: weight-only
-    int8 (the engine quantises the given weights at load); kv_pages: KV-cache pool size in
-    pages of 256 slots (0: enough for every sequence slot to reach max_seq)."""
+def config(w, max_batch: int, max_seq: int, int8: bool = False, kv_pages: int = 0, int4: bool = False) -> Q3Config:
+    """q3_config of a model description with the synth.Workload fields; int8 / int4:
+    weight-only int8 / int4 (the engine quantises the given weights at load); kv_pages:
+    KV-cache pool size in pages of 256 slots (0: enough for every sequence slot to reach
+    max_seq)."""
+    if int8 and int4:
+        raise ValueError("int8 and int4 exclude each other")
     return Q3Config(n_layers=w.n_layers, hidden=w.hidden, n_heads=w.n_heads,
                     n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn=w.ffn, vocab=w.vocab,
                     rms_eps=w.rms_eps, rope_theta=w.rope_theta, tie_embeddings=1,
-                    weight_dtype=I8 if int8 else (BF16 if w.weight_dtype == "bf16" else F32),
+                    weight_dtype=I8 if int8 else I4 if int4 else (BF16 if w.weight_dtype == "bf16" else F32),
                     kv_dtype=BF16 if w.kv_dtype == "bf16" else F32,
                     max_batch=max_batch, max_seq=max_seq, kv_pages=kv_pages)
 

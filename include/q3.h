@@ -43,7 +43,7 @@ typedef enum {
     Q3_ERR_NUMERIC = -8    /* a non-finite logit was produced (sticky) */
 } q3_status;
 
-typedef enum { Q3_F32 = 0, Q3_BF16 = 1, Q3_I8 = 2 } q3_dtype;
+typedef enum { Q3_F32 = 0, Q3_BF16 = 1, Q3_I8 = 2, Q3_I4 = 3 } q3_dtype;
 
 /* Model and capacity. Only the Qwen3 block structure is supported: head_dim 128,
  * n_heads a multiple of n_kv_heads, hidden and ffn multiples of 128, a tied LM
@@ -60,9 +60,10 @@ typedef struct {
     float rms_eps;         /* 1e-6 */
     float rope_theta;      /* 1e6 */
     int32_t tie_embeddings;/* must be 1: the LM head is the embedding matrix */
-    int32_t weight_dtype;  /* q3_dtype of the matrices: Q3_BF16, Q3_F32, or Q3_I8 (weight-only int8:
-                              the engine quantises the given bf16 / float32 matrices at load
-                              with the rule of q3_quantize_i8 and computes with scale * code;
+    int32_t weight_dtype;  /* q3_dtype of the matrices: Q3_BF16, Q3_F32, Q3_I8 or Q3_I4 (weight-only
+                              int8 / int4: the engine quantises the given bf16 / float32 matrices
+                              at load with the rule of q3_quantize_i8 / q3_quantize_i4 and
+                              computes with scale * code;
                               needs the Qwen3-0.6B layer shape, a bf16 cache, decode batches of at
                               most 4 rows and the persistent decode kernel) */
     int32_t kv_dtype;      /* q3_dtype of the KV cache */
@@ -82,7 +83,7 @@ typedef struct {
  * model.layers.{i}.self_attn.{q,k}_norm.weight [head_dim],
  * model.layers.{i}.post_attention_layernorm.weight [hidden],
  * model.layers.{i}.mlp.{gate,up,down}_proj.weight; and model.norm.weight.
- * Matrices must have dtype == weight_dtype (Q3_BF16 or Q3_F32 when weight_dtype is Q3_I8);
+ * Matrices must have dtype == weight_dtype (Q3_BF16 or Q3_F32 when weight_dtype is Q3_I8 or Q3_I4);
  * norm weights may be Q3_F32 or Q3_BF16.
  * lm_head.weight, if given, is ignored (tied head). */
 typedef struct {

@@ -68,23 +68,24 @@ class SamplerStat:
 
 def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
                sampler_stats: List[SamplerStat] | None = None, decode_path: int = 0,
-               int8: bool = False) -> List[StepStat]:
+               int8: bool = False, int4: bool = False) -> List[StepStat]:
     """Prefill a seeded prompt, then `steps` decode steps, batch 1, teacher-forced with the
     oracle's tokens (greedy at temperature 0, else drawn with the workload's uniforms).
     With sampling, the engine's sampler is also run on the oracle's own logits and must
     return the oracle's token whenever the decision margin exceeds 1e-9. int8: the engine
     quantises the weights at load (weight-only int8) and the oracle runs the model with
-    the same quantised weights (oracle.quant)."""
+    the same quantised weights (oracle.quant); int4 likewise with the 4-bit rule."""
     import torch
     from decoder_only_amd import q3
     from oracle import quant
 
     weights = synth.make_weights(w) if weights is None else weights
     max_seq = prompt_len + steps + 1
-    model = oracle.Model(oracle.Config.from_workload(w), quant.quantized_weights(weights) if int8 else weights)
+    qbits = 8 if int8 else 4 if int4 else 0
+    model = oracle.Model(oracle.Config.from_workload(w), quant.quantized_weights(weights, qbits) if qbits else weights)
     cache = model.new_cache(max_seq)
-    announce("e2e", w.name, w.n_layers, w.vocab, w.weight_dtype, prompt_len, steps, "int8" if int8 else "")
-    eng = q3.Engine(q3.config(w, 1, max_seq, int8=int8), weights)
+    announce("e2e", w.name, w.n_layers, w.vocab, w.weight_dtype, prompt_len, steps, f"int{qbits}" if qbits else "")
+    eng = q3.Engine(q3.config(w, 1, max_seq, int8=int8, int4=int4), weights)
     eng.set_decode_path(decode_path)
     prompt = synth.prompt_tokens(w, prompt_len)
     T, p = float(np.float32(w.temperature)), float(np.float32(w.top_p))
