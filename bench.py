@@ -11,7 +11,7 @@ Also reported (one JSON line, under "extras"): the 2048-token prompt's prefill t
 its 256 sampled decode steps, batch-64 decode tokens/s with 4096 pre-filled KV slots per
 sequence, the 32768-token prefill (GEMM and attention TFLOP/s) and its 512 sampled decode
 steps, each with its roofline fraction; a 262,136-token prefill and decode at ~262K cached
-slots; the bs1 workload on weight-only int8 weights; the roofline of the dominant kernel (event-timed on the engine's stream), and the CPU
+slots; the bs1 workload on weight-only int8 and int4 weights; the roofline of the dominant kernel (event-timed on the engine's stream), and the CPU
 oracle on this host (a bounded sample of decode steps and one 2048-token prefill).
 """
 from __future__ import annotations
@@ -179,9 +179,13 @@ def main() -> int:
         except Exception as ex:
             extras["bs64_error"] = repr(ex)
         try:
-            extras.update(int8_line(weights, q3, torch, synth, args.steps))
+            extras.update(quant_line(weights, q3, torch, synth, args.steps, 8))
         except Exception as ex:
             extras["int8_error"] = repr(ex)
+        try:
+            extras.update(quant_line(weights, q3, torch, synth, args.steps, 4))
+        except Exception as ex:
+            extras["int4_error"] = repr(ex)
 
     cpu = None
     if not args.no_cpu:
@@ -341,13 +345,13 @@ def c5_lines(weights, q3, torch, synth):
             "c5_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def int8_line(weights, q3, torch, synth, steps):
+def quant_line(weights, q3, torch, synth, steps, bits):
     """The bs1 workload (5-token prompt, 128 greedy steps per generation) on an engine whose
-    weights are quantised to int8 at load (one byte per weight plus a float scale per row):
-    decode tok/s over whole generations, and the persistent kernel's HBM fraction against
-    the int8 step's algorithmic bytes."""
+    weights are quantised to int8 (bits = 8: one byte per weight) or int4 (bits = 4: half a
+    byte) at load, plus a float scale per row: decode tok/s over whole generations, and the
+    persistent kernel's HBM fraction against the quantised step's algorithmic bytes."""
     w = synth.workload("bs1_short")
-    eng = q3.Engine(q3.config(w, 1, w.max_seq + 1, int8=True), weights)
+    eng = q3.Engine(q3.config(w, 1, w.max_seq + 1, int8=bits == 8, int4=bits == 4), weights)
     try:
         eng.set_decode_path(3)
         prompt = torch.from_numpy(synth.prompt_tokens(w)).cuda()
@@ -378,11 +382,12 @@ def int8_line(weights, q3, torch, synth, steps):
         eng.close()
     gbs = prof["bytes"] / (prof["ms"] / 1e3) / 1e9
     us = 1e3 * prof["ms"] / prof["launches"]
-    log(f"int8 bs1 decode: {w.decode_steps * steps / dt:.0f} tok/s; step {us:.1f} us "
+    k = f"int{bits}"
+    log(f"{k} bs1 decode: {w.decode_steps * steps / dt:.0f} tok/s; step {us:.1f} us "
         f"({prof['bytes'] / prof['launches'] / 1e9:.3f} GB, {gbs:.0f} GB/s)")
-    return {"int8_bs1_decode_tok_s": round(w.decode_steps * steps / dt, 2), "int8_decode_step_us": round(us, 2),
-            "int8_step_bytes": round(prof["bytes"] / prof["launches"]),
-            "int8_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {f"{k}_bs1_decode_tok_s": round(w.decode_steps * steps / dt, 2), f"{k}_decode_step_us": round(us, 2),
+            f"{k}_step_bytes": round(prof["bytes"] / prof["launches"]),
+            f"{k}_decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def ctx262k_lines(weights, q3, torch, synth):
