@@ -24,6 +24,7 @@ def _report(stats):
     (3, 5, 16),        # the same, ordinary launch
     (3, 512, 12),      # matrix-core prefill with per-column scales, then decode
     (3, 250, 12),      # split-K attention instance
+    (3, 8400, 4),      # double-buffered split-K instance (contexts above 8192 slots)
 ])
 def test_toy_int8(path, prompt, steps):
     w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
