@@ -12,7 +12,7 @@
 // bf16 weights and the bf16 K/V cache are exact operands), so the path keeps ~16
 // significant bits where a single bf16 rounding would cost ~5e-3 relative error in the
 // logits. The last row's last layer after its K/V append, and its LM head, run on the
-// single-row float32 kernels (with int8 weights the last row takes the decode path).
+// single-row float32 kernels (with int8 or int4 weights the last row takes the decode path).
 #include <algorithm>
 #include <climits>
 #include <cmath>
@@ -42,13 +42,13 @@ struct q3_engine {
     std::vector<void*> allocs;
 
     struct Layer {
-        void *wqkv, *wo, *wgu, *wd;       // bf16 (or float32) matrices; int8 engines: the codes as bf16
+        void *wqkv, *wo, *wgu, *wd;       // bf16 (or float32) matrices; int8 / int4 engines: the codes as bf16
         float *in_norm, *post_norm, *q_norm, *k_norm;
-        uint8_t *wqkv8 = nullptr, *wo8 = nullptr, *wgu8 = nullptr, *wd8 = nullptr;   // int8: the codes
-        float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;          // int8: row scales
+        uint8_t *wqkv8 = nullptr, *wo8 = nullptr, *wgu8 = nullptr, *wd8 = nullptr;   // int8 / int4: the codes (+ row scales)
+        float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sd = nullptr;          // int8 / int4: row scales
     };
     void* embed = nullptr;
-    uint8_t* embed8 = nullptr;     // int8: embedding codes and row scales
+    uint8_t* embed8 = nullptr;     // int8 / int4: embedding codes and row scales
     float* escale = nullptr;
     std::vector<Layer> layers;
     float* final_norm = nullptr;
@@ -247,7 +247,7 @@ extern "C" q3_status q3_quantize_i4(const void* w, int32_t dtype, int64_t rows, 
     return quantize_matrix(w, dtype, rows, cols, 7, q, scale);
 }
 
-static_assert(kMegaMaxSlots == 270336, "the int8 limit quoted below");
+static_assert(kMegaMaxSlots == 270336, "the int8 / int4 limit quoted below");
 static q3_status validate_config(const q3_config* c, std::string& why) {
     if (!c) { why = "config is NULL"; return Q3_ERR_ARG; }
     if (c->n_layers < 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->ffn <= 0 ||

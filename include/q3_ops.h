@@ -50,7 +50,7 @@ q3_status q3_op_gemv(const void* W, int32_t w_dtype, const float* x, float* y, i
  * the n = K / 64 tiles (1 <= splits <= K / 64; splits must be 1 for the other epilogues).
  * colscale (NULL or float32 [N]): output column n is multiplied by colscale[n] before the
  * epilogue (for SwiGLU, gate and up columns each by their own) -- the per-row scales of
- * int8 weights whose codes W holds as bf16. */
+ * int8 or int4 weights whose codes W holds as bf16. */
 q3_status q3_op_gemm(const void* A, int32_t a_dtype, const uint16_t* W, void* C, int32_t M, int32_t N,
                      int32_t K, int32_t epilogue, int32_t splits, const float* colscale, void* stream);
 
