@@ -121,19 +121,22 @@ def run_single(w: synth.Workload, prompt_len: int, steps: int, weights=None,
     return stats
 
 
-def run_ragged(w: synth.Workload, prompt_lens: List[int], steps: int, decode_path: int = 0) -> List[StepStat]:
+def run_ragged(w: synth.Workload, prompt_lens: List[int], steps: int, decode_path: int = 0,
+               qbits: int = 0) -> List[StepStat]:
     """Sequences of different lengths decoded together: sequence b is prefilled with a
     seeded prompt of prompt_lens[b] tokens, then `steps` batched decode steps (row b =
-    sequence b, greedy, teacher-forced with each row's oracle token)."""
+    sequence b, greedy, teacher-forced with each row's oracle token). qbits 8 / 4: the
+    engine quantises the weights at load and the oracle runs the same quantised weights."""
     import torch
     from decoder_only_amd import q3
+    from oracle import quant
 
     weights = synth.make_weights(w)
     B = len(prompt_lens)
     max_seq = max(prompt_lens) + steps + 1
-    model = oracle.Model(oracle.Config.from_workload(w), weights)
-    announce("e2e ragged", w.name, w.weight_dtype, prompt_lens, steps, decode_path)
-    eng = q3.Engine(q3.config(w, B, max_seq), weights)
+    model = oracle.Model(oracle.Config.from_workload(w), quant.quantized_weights(weights, qbits) if qbits else weights)
+    announce("e2e ragged", w.name, w.weight_dtype, prompt_lens, steps, decode_path, f"int{qbits}" if qbits else "")
+    eng = q3.Engine(q3.config(w, B, max_seq, int8=qbits == 8, int4=qbits == 4), weights)
     eng.set_decode_path(decode_path)
     caches, refs = [], []
     for b, n in enumerate(prompt_lens):

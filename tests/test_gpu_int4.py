@@ -9,7 +9,7 @@ tokens identical."""
 import pytest
 
 import synth
-from e2e import failures, run_single
+from e2e import failures, run_ragged, run_single
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,16 @@ def test_toy_int4_from_float32_weights():
         stats = run_single(w, prompt, steps, decode_path=3, int4=True)
         _report(stats)
         assert not failures(stats), failures(stats)[:5]
+
+
+@pytest.mark.parametrize("path", [0, 3])
+def test_toy_int4_ragged_rows(path):
+    """Three sequences of different lengths (one past the short-context limit) decoded
+    together in the persistent kernel, row by row against the oracle."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_ragged(w, [7, 180, 300], 6, decode_path=path, qbits=4)
+    _report(stats)
+    assert not failures(stats), failures(stats)[:5]
 
 
 @pytest.mark.timeout(900)

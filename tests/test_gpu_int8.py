@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from e2e import failures, run_single
+from e2e import failures, run_ragged, run_single
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,16 @@ def test_toy_int8(path, prompt, steps):
 # (1.0-1.15e-3; tests/test_oracle_quant.py::test_int8_model_noise_floor measures both), so
 # its bar keeps the same margin over its floor: 2e-3.
 INT8_REL_L2 = 2e-3
+
+
+@pytest.mark.parametrize("path", [0, 3])
+def test_toy_int8_ragged_rows(path):
+    """Three sequences of different lengths (one past the short-context limit) decoded
+    together in the persistent kernel, row by row against the oracle."""
+    w = synth.workload("toy").with_(weight_dtype="bf16", kv_dtype="bf16")
+    stats = run_ragged(w, [7, 180, 300], 6, decode_path=path, qbits=8)
+    _report(stats)
+    assert not failures(stats), failures(stats)[:5]
 
 
 @pytest.mark.timeout(900)
